@@ -1,0 +1,235 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE-layer hot path.
+ *
+ * The layer, as the pages state it ("Megatron-Bridge 深度剖析", section
+ * "MoE 加速深度剖析 / Expert Parallel 基础", three-step diagram): a router
+ * picks top-k experts per token with scores; tokens are regrouped by expert;
+ * every expert runs its SwiGLU FFN over its tokens as ONE grouped GEMM
+ * (section "计算融合 / Grouped GEMM"); results return to token order and are
+ * combined.  An optional shared expert sees every token (section "Shared
+ * Expert Overlap"), scaled by a per-token gate (TorchSpec pull request "Add
+ * Megatron-Core MTP training for Qwen3.5 MoE", "What's in it").  Training
+ * adds the grouped GEMM's dgrad and wgrad.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every array pointer is a caller-owned DEVICE pointer (HBM), row-major,
+ *    densely packed, 16-byte aligned.  The library never allocates, frees or
+ *    keeps a pointer after it returns; scratch memory is the caller's
+ *    workspace (`ws`, `ws_bytes`), sized by the matching *_workspace_size().
+ *  - All work is enqueued on `stream` (a hipStream_t; NULL = the legacy
+ *    default stream).  No call synchronises the host: expert counts and
+ *    offsets stay on the device and the kernels read them there.
+ *  - `dt` selects the element type of activations and weights: MOE_F32 or
+ *    MOE_BF16 (bf16 storage, fp32 accumulation).  Routing scores, routing
+ *    weights, gates and weight gradients are always fp32.
+ *  - Outputs must not alias inputs.  Calls are deterministic: the same
+ *    inputs give bit-identical outputs (no floating-point atomics).
+ *  - Errors: argument checks run on the host before anything is launched;
+ *    a failed check returns a non-zero moe_status and launches nothing.
+ *    A failed launch returns MOE_ERR_HIP.  Faults inside a kernel surface
+ *    at the caller's next synchronisation.  Nothing is printed; no C++
+ *    exception crosses this boundary.
+ *  - Index arithmetic is 32-bit for row and slot indices: T*k must be below
+ *    2^31.
+ */
+#ifndef MOE_MI355X_H_
+#define MOE_MI355X_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define MOE_API __attribute__((visibility("default")))
+#else
+#define MOE_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,  /* NULL where a pointer is required, bad enum   */
+  MOE_ERR_SHAPE = 2,        /* a dimension out of the supported range       */
+  MOE_ERR_DTYPE = 3,        /* unknown moe_dtype                            */
+  MOE_ERR_ALIGNMENT = 4,    /* pointer not 16-byte aligned / d, F not x8    */
+  MOE_ERR_WORKSPACE = 5,    /* ws NULL or smaller than *_workspace_size()   */
+  MOE_ERR_UNSUPPORTED = 6,  /* valid request this build does not implement  */
+  MOE_ERR_HIP = 7           /* a HIP launch failed                          */
+} moe_status;
+
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Score function of the router ("Megatron-Bridge 深度剖析", section
+ * "Megatron-Core 架构速览": moe_router_score_function; the step-1 diagram of
+ * "Expert Parallel 基础" shows top-6 sigmoid routing). */
+typedef enum moe_score_fn { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score_fn;
+
+/* Version of this ABI (incremented on any signature change). */
+MOE_API int32_t moe_abi_version(void);
+/* Static, human-readable name of a status code. */
+MOE_API const char* moe_status_string(moe_status s);
+
+/* ------------------------------------------------------------------------
+ * moe_route -- router logits, scores, top-k, weight normalisation, counts.
+ *
+ * Passage: "Megatron-Bridge 深度剖析", "Expert Parallel 基础", step 1
+ * ("Router 决策": the router maps each token to its top-k experts with
+ * scores).  For token t and expert e:
+ *     z[t,e] = sum_i x[t,i] * w_router[e,i] + logit_bias[e]
+ *     s[t,e] = softmax_e(z[t,:])  or  1 / (1 + exp(-z[t,e]))
+ * The k experts with the largest fp32 scores are chosen, in descending
+ * score order (equal scores: lower expert index first).  With `normalize`
+ * the weights are s / (sum of the k chosen s), else the raw scores.
+ * With w_gate, gate[t] = 1 / (1 + exp(-x[t] . w_gate)) (shared-expert gate).
+ *
+ *   x          [T, d]  dt        tokens
+ *   w_router   [E, d]  dt        router weight (Megatron's router.weight)
+ *   logit_bias [E]     fp32      or NULL
+ *   w_gate     [d]     dt        or NULL (then `gate` must be NULL too)
+ *   topk_idx   [T, k]  int32     out
+ *   topk_w     [T, k]  fp32      out
+ *   expert_counts [E]  int32     out: tokens routed to each expert
+ *   gate       [T]     fp32      out, or NULL
+ * Limits: 1 <= k <= min(E, 32); 1 <= E <= 1024; d % 8 == 0; T >= 1.
+ * No workspace.
+ * --------------------------------------------------------------------- */
+MOE_API moe_status moe_route(hipStream_t stream, moe_dtype dt, int64_t T, int64_t d,
+                     int32_t E, int32_t k, moe_score_fn fn, int32_t normalize,
+                     const void* x, const void* w_router,
+                     const float* logit_bias, const void* w_gate,
+                     int32_t* topk_idx, float* topk_w,
+                     int32_t* expert_counts, float* gate);
+
+/* ------------------------------------------------------------------------
+ * moe_permute -- regroup token copies into per-expert contiguous segments.
+ *
+ * Passage: "Megatron-Bridge 深度剖析", "Expert Parallel 基础" step 2 (after
+ * dispatch a GPU holds its tokens grouped by expert) and "Permute Fusion"
+ * (the permute is a memory copy of the hidden states).  The N = T*k
+ * (token, slot) pairs, taken token-major, are counting-sorted by expert
+ * (stable: ascending token inside a segment):
+ *     expert_offsets[e] = sum_{e' < e} count(e')          [E+1]
+ *     slot_of[t,j]      = row holding token t's j-th choice
+ *     row_token[r], row_w[r] = the token and routing weight of row r
+ *     x_perm[r,:]       = x[row_token[r], :]
+ *
+ *   x          [T, d]  dt        in
+ *   topk_idx   [T, k]  int32     in, values in [0, E)
+ *   topk_w     [T, k]  fp32      in, or NULL (then row_w must be NULL)
+ *   expert_offsets [E+1] int32   out
+ *   slot_of    [T, k]  int32     out
+ *   row_token  [T*k]   int32     out
+ *   row_w      [T*k]   fp32      out, or NULL
+ *   x_perm     [T*k, d] dt       out
+ * An entry of topk_idx outside [0, E) is dropped: its slot_of is -1 and it
+ * takes no row (rows past the last kept one are left unwritten).
+ * Workspace: moe_permute_workspace_size(T, E, k) bytes.
+ * Limits: 1 <= k <= 32; 1 <= E <= 1024; d*elt % 16 == 0.
+ * --------------------------------------------------------------------- */
+MOE_API size_t moe_permute_workspace_size(int64_t T, int32_t E, int32_t k);
+MOE_API moe_status moe_permute(hipStream_t stream, moe_dtype dt, int64_t T, int64_t d,
+                       int32_t E, int32_t k, const void* x,
+                       const int32_t* topk_idx, const float* topk_w,
+                       int32_t* expert_offsets, int32_t* slot_of,
+                       int32_t* row_token, float* row_w, void* x_perm,
+                       void* ws, size_t ws_bytes);
+
+/* ------------------------------------------------------------------------
+ * moe_grouped_swiglu_fwd -- every expert's SwiGLU FFN in one grouped GEMM.
+ *
+ * Passages: "Megatron-Bridge 深度剖析", "Grouped GEMM" (all experts' GEMMs
+ * as one call over segments of different length), "权重映射策略"
+ * (GatedMLPMapping: linear_fc1 = [gate_proj; up_proj], (2*ffn, hidden)),
+ * "Motivation" (gate_proj, up_proj, down_proj per expert).  For expert e
+ * with rows R_e = [expert_offsets[e], expert_offsets[e+1]):
+ *     G = X[R_e] W1[e, 0:F]^T,  U = X[R_e] W1[e, F:2F]^T   (fp32 accumulate)
+ *     A = silu(G) * U,          silu(z) = z / (1 + exp(-z))
+ *     y_perm[R_e] = (A W2[e]^T) * row_scale[R_e]
+ * For bf16, A is rounded to bf16 before the second GEMM.
+ *
+ *   x_perm     [N, d]      dt    in
+ *   w1         [E, 2F, d]  dt    in (rows 0..F-1 gate, F..2F-1 up)
+ *   w2         [E, d, F]   dt    in (down projection, (hidden, ffn))
+ *   expert_offsets [E+1]   int32 in, device; 0 = off[0] <= ... <= off[E] = N
+ *   row_scale  [N]         fp32  in, or NULL (= 1)
+ *   y_perm     [N, d]      dt    out
+ *   gu_save    [N, 2F]     dt    out, or NULL: G in cols 0..F-1, U in F..2F-1
+ *                                (saved for the backward)
+ * Workspace: moe_grouped_swiglu_fwd_workspace_size(N, F, dt) bytes.
+ * Limits: E <= 1024, d % 8 == 0, F % 8 == 0, N >= 0.
+ * --------------------------------------------------------------------- */
+MOE_API size_t moe_grouped_swiglu_fwd_workspace_size(int64_t N, int64_t F, moe_dtype dt);
+MOE_API moe_status moe_grouped_swiglu_fwd(hipStream_t stream, moe_dtype dt, int64_t N,
+                                  int64_t d, int64_t F, int32_t E,
+                                  const void* x_perm, const void* w1,
+                                  const void* w2, const int32_t* expert_offsets,
+                                  const float* row_scale, void* y_perm,
+                                  void* gu_save, void* ws, size_t ws_bytes);
+
+/* ------------------------------------------------------------------------
+ * moe_grouped_swiglu_bwd -- grouped-GEMM dgrad and wgrad of the forward.
+ *
+ * Passage: "Megatron-Bridge 深度剖析", "通信隐藏与混合精度 / TP 通信重叠"
+ * (the backward's dgrad and wgrad GEMMs) and "其他融合优化"
+ * (gradient_accumulation_fusion: weight gradients accumulate into fp32
+ * main grads).  Given dY = dL/dy_perm, for each expert e:
+ *     dYs = dY * row_scale;       dA = dYs W2[e]
+ *     dG  = dA * U * silu'(G);    dU = dA * silu(G);    dH = [dG | dU]
+ *     dx_perm[R_e] = dH W1[e]
+ *     dw2[e] (+)= dYs^T A;        dw1[e] (+)= dH^T X[R_e]
+ * silu'(z) = s (1 + z (1 - s)), s = sigmoid(z).  An expert with no rows
+ * gets dw = 0 (or is left unchanged when accumulating).
+ *
+ *   dy_perm    [N, d]      dt    in
+ *   x_perm, w1, w2, expert_offsets, row_scale: as in the forward
+ *   gu_save    [N, 2F]     dt    in (from the forward), or NULL: recompute
+ *   accumulate int32             0: dw = grad;  1: dw += grad
+ *   dx_perm    [N, d]      dt    out
+ *   dw1        [E, 2F, d]  fp32  out
+ *   dw2        [E, d, F]   fp32  out
+ * Workspace: moe_grouped_swiglu_bwd_workspace_size(N, F, dt, recompute).
+ * Only MOE_BF16 is implemented (MOE_F32 returns MOE_ERR_UNSUPPORTED).
+ * --------------------------------------------------------------------- */
+MOE_API size_t moe_grouped_swiglu_bwd_workspace_size(int64_t N, int64_t F, moe_dtype dt,
+                                             int32_t recompute);
+MOE_API moe_status moe_grouped_swiglu_bwd(hipStream_t stream, moe_dtype dt, int64_t N,
+                                  int64_t d, int64_t F, int32_t E,
+                                  const void* dy_perm, const void* x_perm,
+                                  const void* w1, const void* w2,
+                                  const int32_t* expert_offsets,
+                                  const void* gu_save, const float* row_scale,
+                                  int32_t accumulate, void* dx_perm,
+                                  float* dw1, float* dw2, void* ws,
+                                  size_t ws_bytes);
+
+/* ------------------------------------------------------------------------
+ * moe_unpermute_combine -- back to token order, weighted k-way sum.
+ *
+ * Passage: "Megatron-Bridge 深度剖析", "Expert Parallel 基础" step 3 (the
+ * results go back to the tokens' original layout) and "Shared Expert
+ * Overlap" (the shared expert's output joins the routed result):
+ *     y[t] = sum_j topk_w[t,j] * y_perm[slot_of[t,j]]  (+ y_shared[t])
+ * summed in fp32 in slot order j = 0..k-1, rounded once to dt.  With
+ * topk_w = NULL the rows are taken as already weighted (the forward can
+ * apply the weight through row_scale).  slot_of < 0 entries are skipped.
+ *
+ *   y_perm   [N, d] dt   in        slot_of [T, k] int32  in
+ *   topk_w   [T, k] fp32 in/NULL   y_shared [T, d] dt in/NULL
+ *   y        [T, d] dt   out
+ * No workspace.  Limits: 1 <= k <= 32, d*elt % 16 == 0.
+ * --------------------------------------------------------------------- */
+MOE_API moe_status moe_unpermute_combine(hipStream_t stream, moe_dtype dt, int64_t T,
+                                 int64_t d, int32_t k, int64_t N,
+                                 const void* y_perm, const int32_t* slot_of,
+                                 const float* topk_w, const void* y_shared,
+                                 void* y);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H_ */

@@ -1,0 +1,285 @@
+"""MI355X (gfx950) MoE-layer hot path: Python binding of libmoe_mi355x.so.
+
+The binding only marshals arguments: it turns torch tensors that live on
+the GPU into device pointers, passes torch's current HIP stream, allocates
+outputs and workspaces with torch, and raises on a non-zero status.  Every
+step of the layer runs in the library's HIP kernels; there is no fallback.
+
+Calls (same names and semantics as include/moe.h):
+    route, permute, grouped_swiglu_fwd, grouped_swiglu_bwd, unpermute_combine
+plus ``moe_layer_forward`` that chains them, and ``MoELayer`` that keeps its
+buffers between calls (no allocation per forward).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "MoEError", "lib", "route", "permute", "grouped_swiglu_fwd",
+    "grouped_swiglu_bwd", "unpermute_combine", "moe_layer_forward",
+    "MoELayer", "LIB_PATH", "EXPORTED",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+SCORE = {"softmax": 0, "sigmoid": 1}
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_sz = ctypes.c_size_t
+
+# name -> (restype, argtypes); the public symbols of include/moe.h
+EXPORTED = {
+    "moe_abi_version": (_i32, []),
+    "moe_status_string": (ctypes.c_char_p, [_i32]),
+    "moe_route": (_i32, [_vp, _i32, _i64, _i64, _i32, _i32, _i32, _i32,
+                         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_permute_workspace_size": (_sz, [_i64, _i32, _i32]),
+    "moe_permute": (_i32, [_vp, _i32, _i64, _i64, _i32, _i32, _vp, _vp, _vp,
+                           _vp, _vp, _vp, _vp, _vp, _vp, _sz]),
+    "moe_grouped_swiglu_fwd_workspace_size": (_sz, [_i64, _i64, _i32]),
+    "moe_grouped_swiglu_fwd": (_i32, [_vp, _i32, _i64, _i64, _i64, _i32,
+                                      _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz]),
+    "moe_grouped_swiglu_bwd_workspace_size": (_sz, [_i64, _i64, _i32, _i32]),
+    "moe_grouped_swiglu_bwd": (_i32, [_vp, _i32, _i64, _i64, _i64, _i32,
+                                      _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
+                                      _vp, _vp, _vp, _vp, _sz]),
+    "moe_unpermute_combine": (_i32, [_vp, _i32, _i64, _i64, _i32, _i64,
+                                     _vp, _vp, _vp, _vp, _vp]),
+}
+
+
+class MoEError(RuntimeError):
+    pass
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise MoEError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m mixture_experts_layer_05_amd.build` (or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in EXPORTED.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        name = lib().moe_status_string(status).decode()
+        raise MoEError(f"{what} failed: {name} ({status})")
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise MoEError(f"unsupported dtype {t.dtype}")
+
+
+def _p(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise MoEError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise MoEError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ws(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------------------
+def route(x, w_router, k, score="softmax", normalize=True, logit_bias=None,
+          w_gate=None, out=None):
+    """-> (topk_idx [T,k] int32, topk_w [T,k] fp32, counts [E] int32, gate [T] or None)"""
+    T, d = x.shape
+    E = w_router.shape[0]
+    dev = x.device
+    if out is None:
+        out = (torch.empty((T, k), dtype=torch.int32, device=dev),
+               torch.empty((T, k), dtype=torch.float32, device=dev),
+               torch.empty((E,), dtype=torch.int32, device=dev),
+               torch.empty((T,), dtype=torch.float32, device=dev) if w_gate is not None else None)
+    idx, w, cnt, gate = out
+    _check(lib().moe_route(_stream(), _dt(x), T, d, E, k, SCORE[score], int(bool(normalize)),
+                           _p(x), _p(w_router), _p(logit_bias), _p(w_gate), _p(idx), _p(w),
+                           _p(cnt), _p(gate)), "moe_route")
+    return idx, w, cnt, gate
+
+
+def permute_workspace_size(T, E, k):
+    return lib().moe_permute_workspace_size(T, E, k)
+
+
+def permute(x, topk_idx, topk_w, E, out=None, ws=None):
+    """-> (expert_offsets [E+1], slot_of [T,k], row_token [N], row_w [N] or None, x_perm [N,d])"""
+    T, d = x.shape
+    k = topk_idx.shape[1]
+    N = T * k
+    dev = x.device
+    if out is None:
+        out = (torch.empty((E + 1,), dtype=torch.int32, device=dev),
+               torch.empty((T, k), dtype=torch.int32, device=dev),
+               torch.empty((N,), dtype=torch.int32, device=dev),
+               torch.empty((N,), dtype=torch.float32, device=dev) if topk_w is not None else None,
+               torch.empty((N, d), dtype=x.dtype, device=dev))
+    off, slot, rtok, rw, xp = out
+    nbytes = permute_workspace_size(T, E, k)
+    if ws is None:
+        ws = _ws(nbytes, dev)
+    _check(lib().moe_permute(_stream(), _dt(x), T, d, E, k, _p(x), _p(topk_idx), _p(topk_w),
+                             _p(off), _p(slot), _p(rtok), _p(rw), _p(xp), _p(ws), ws.numel()),
+           "moe_permute")
+    return off, slot, rtok, rw, xp
+
+
+def fwd_workspace_size(N, F, dtype):
+    return lib().moe_grouped_swiglu_fwd_workspace_size(N, F, MOE_BF16 if dtype == torch.bfloat16 else MOE_F32)
+
+
+def grouped_swiglu_fwd(x_perm, w1, w2, expert_offsets, row_scale=None, save_gu=False,
+                       out=None, gu_out=None, ws=None):
+    """-> (y_perm [N,d], gu_save [N,2F] or None)"""
+    N, d = x_perm.shape
+    E, twoF, _ = w1.shape
+    F = twoF // 2
+    dev = x_perm.device
+    y = out if out is not None else torch.empty((N, d), dtype=x_perm.dtype, device=dev)
+    gu = gu_out
+    if save_gu and gu is None:
+        gu = torch.empty((N, 2 * F), dtype=x_perm.dtype, device=dev)
+    nbytes = fwd_workspace_size(N, F, x_perm.dtype)
+    if ws is None:
+        ws = _ws(nbytes, dev)
+    _check(lib().moe_grouped_swiglu_fwd(_stream(), _dt(x_perm), N, d, F, E, _p(x_perm), _p(w1),
+                                        _p(w2), _p(expert_offsets), _p(row_scale), _p(y), _p(gu),
+                                        _p(ws), ws.numel()), "moe_grouped_swiglu_fwd")
+    return y, gu
+
+
+def bwd_workspace_size(N, F, dtype, recompute):
+    return lib().moe_grouped_swiglu_bwd_workspace_size(
+        N, F, MOE_BF16 if dtype == torch.bfloat16 else MOE_F32, int(bool(recompute)))
+
+
+def grouped_swiglu_bwd(dy_perm, x_perm, w1, w2, expert_offsets, gu_save=None, row_scale=None,
+                       accumulate=False, dw1=None, dw2=None, dx_out=None, ws=None):
+    """-> (dx_perm [N,d], dw1 [E,2F,d] fp32, dw2 [E,d,F] fp32)"""
+    N, d = x_perm.shape
+    E, twoF, _ = w1.shape
+    F = twoF // 2
+    dev = x_perm.device
+    dx = dx_out if dx_out is not None else torch.empty((N, d), dtype=x_perm.dtype, device=dev)
+    if dw1 is None:
+        dw1 = torch.empty((E, 2 * F, d), dtype=torch.float32, device=dev)
+    if dw2 is None:
+        dw2 = torch.empty((E, d, F), dtype=torch.float32, device=dev)
+    nbytes = bwd_workspace_size(N, F, x_perm.dtype, gu_save is None)
+    if ws is None:
+        ws = _ws(nbytes, dev)
+    _check(lib().moe_grouped_swiglu_bwd(_stream(), _dt(x_perm), N, d, F, E, _p(dy_perm),
+                                        _p(x_perm), _p(w1), _p(w2), _p(expert_offsets),
+                                        _p(gu_save), _p(row_scale), int(bool(accumulate)),
+                                        _p(dx), _p(dw1), _p(dw2), _p(ws), ws.numel()),
+           "moe_grouped_swiglu_bwd")
+    return dx, dw1, dw2
+
+
+def unpermute_combine(y_perm, slot_of, topk_w=None, y_shared=None, out=None):
+    """-> y [T, d]"""
+    T, k = slot_of.shape
+    N, d = y_perm.shape
+    y = out if out is not None else torch.empty((T, d), dtype=y_perm.dtype, device=y_perm.device)
+    _check(lib().moe_unpermute_combine(_stream(), _dt(y_perm), T, d, k, N, _p(y_perm),
+                                       _p(slot_of), _p(topk_w), _p(y_shared), _p(y)),
+           "moe_unpermute_combine")
+    return y
+
+
+# ---------------------------------------------------------------------------
+class MoELayer:
+    """The whole forward of one MoE layer with buffers kept between calls.
+
+    route -> permute -> grouped SwiGLU (routing weight applied as the fc2
+    row scale) -> [shared expert as a one-expert grouped call, row scale =
+    gate] -> combine.  Only kernel launches happen in ``forward``.
+    """
+
+    def __init__(self, w_router, w1, w2, k, T, score="softmax", normalize=True,
+                 logit_bias=None, w_gate=None, ws1=None, ws2=None, save_gu=False):
+        self.w_router, self.w1, self.w2 = w_router, w1, w2
+        self.k, self.T, self.score, self.normalize = k, T, score, normalize
+        self.logit_bias, self.w_gate, self.ws1, self.ws2 = logit_bias, w_gate, ws1, ws2
+        dev, dt = w1.device, w1.dtype
+        E, twoF, d = w1.shape
+        self.E, self.F, self.d = E, twoF // 2, d
+        N = T * k
+        self.N = N
+        i32, f32 = torch.int32, torch.float32
+        self.route_out = (torch.empty((T, k), dtype=i32, device=dev),
+                          torch.empty((T, k), dtype=f32, device=dev),
+                          torch.empty((E,), dtype=i32, device=dev),
+                          torch.empty((T,), dtype=f32, device=dev) if w_gate is not None else None)
+        self.perm_out = (torch.empty((E + 1,), dtype=i32, device=dev),
+                         torch.empty((T, k), dtype=i32, device=dev),
+                         torch.empty((N,), dtype=i32, device=dev),
+                         torch.empty((N,), dtype=f32, device=dev),
+                         torch.empty((N, d), dtype=dt, device=dev))
+        self.perm_ws = _ws(permute_workspace_size(T, E, k), dev)
+        self.y_perm = torch.empty((N, d), dtype=dt, device=dev)
+        self.gu = torch.empty((N, 2 * self.F), dtype=dt, device=dev) if save_gu else None
+        ws_f = fwd_workspace_size(N, self.F, dt)
+        if ws1 is not None:
+            Fs = ws1.shape[0] // 2
+            ws_f = max(ws_f, fwd_workspace_size(T, Fs, dt))
+            self.shared_off = torch.tensor([0, T], dtype=i32, device=dev)
+            self.y_shared = torch.empty((T, d), dtype=dt, device=dev)
+            self.ws1_e = ws1.unsqueeze(0)
+            self.ws2_e = ws2.unsqueeze(0)
+        self.ffn_ws = _ws(ws_f, dev)
+        self.y = torch.empty((T, d), dtype=dt, device=dev)
+
+    def forward(self, x):
+        idx, w, cnt, gate = route(x, self.w_router, self.k, self.score, self.normalize,
+                                  self.logit_bias, self.w_gate, out=self.route_out)
+        off, slot, rtok, rw, xp = permute(x, idx, w, self.E, out=self.perm_out, ws=self.perm_ws)
+        grouped_swiglu_fwd(xp, self.w1, self.w2, off, row_scale=rw, out=self.y_perm,
+                           gu_out=self.gu, save_gu=self.gu is not None, ws=self.ffn_ws)
+        ysh = None
+        if self.ws1 is not None:
+            grouped_swiglu_fwd(x, self.ws1_e, self.ws2_e, self.shared_off, row_scale=gate,
+                               out=self.y_shared, ws=self.ffn_ws)
+            ysh = self.y_shared
+        return unpermute_combine(self.y_perm, slot, None, ysh, out=self.y)
+
+
+def moe_layer_forward(x, w_router, w1, w2, k, score="softmax", normalize=True,
+                      logit_bias=None, w_gate=None, ws1=None, ws2=None):
+    """Functional form of :class:`MoELayer` (allocates per call)."""
+    layer = MoELayer(w_router, w1, w2, k, x.shape[0], score, normalize, logit_bias, w_gate,
+                     ws1, ws2)
+    y = layer.forward(x)
+    return y, layer

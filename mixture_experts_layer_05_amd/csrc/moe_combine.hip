@@ -1,0 +1,100 @@
+// moe_unpermute_combine: y[t] = sum_j w[t,j] * y_perm[slot_of[t,j]] (+ y_shared[t])
+//
+// Passage: "Megatron-Bridge 深度剖析", section "Expert Parallel 基础", step 3
+// (expert results return to the tokens' original layout) and section
+// "Shared Expert Overlap" (the shared expert's output joins the routed one).
+//
+// One wavefront per token; each lane owns 16-byte column chunks.  The k rows
+// are summed in fp32 in slot order j = 0..k-1, the shared row is added last,
+// and the result is rounded to the storage type once.  Memory-bound: every
+// byte of y_perm is read exactly once, y once written.
+#include "moe_internal.h"
+
+namespace moe {
+
+constexpr int kCombThreads = 256;
+
+template <bool kBF16>
+__global__ __launch_bounds__(kCombThreads) void combine_kernel(
+    int T, int k, int N, int nchunk16, const u32x4* __restrict__ y_perm,
+    const int32_t* __restrict__ slot_of, const float* __restrict__ topk_w,
+    const u32x4* __restrict__ y_shared, u32x4* __restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kCombThreads / 64) + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int my_row = -1;
+  float my_w = 1.0f;
+  if (lane < k) {
+    my_row = slot_of[static_cast<size_t>(t) * k + lane];
+    if (my_row >= N) my_row = -1;
+    if (topk_w) my_w = topk_w[static_cast<size_t>(t) * k + lane];
+  }
+  constexpr int kVals = kBF16 ? 8 : 4;
+  for (int c = lane; c < nchunk16; c += 64) {
+    float acc[kVals];
+#pragma unroll
+    for (int q = 0; q < kVals; ++q) acc[q] = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const int row = __shfl(my_row, j, kWave);
+      const float w = __shfl(my_w, j, kWave);
+      if (row < 0) continue;
+      const u32x4 v = y_perm[static_cast<size_t>(row) * nchunk16 + c];
+      if constexpr (kBF16) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] = fmaf(w, bf16lo(v[q]), acc[2 * q]);
+          acc[2 * q + 1] = fmaf(w, bf16hi(v[q]), acc[2 * q + 1]);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] = fmaf(w, __uint_as_float(v[q]), acc[q]);
+      }
+    }
+    if (y_shared) {
+      const u32x4 v = y_shared[static_cast<size_t>(t) * nchunk16 + c];
+      if constexpr (kBF16) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] += bf16lo(v[q]);
+          acc[2 * q + 1] += bf16hi(v[q]);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] += __uint_as_float(v[q]);
+      }
+    }
+    u32x4 o;
+    if constexpr (kBF16) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = __float_as_uint(acc[q]);
+    }
+    y[static_cast<size_t>(t) * nchunk16 + c] = o;
+  }
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" moe_status moe_unpermute_combine(hipStream_t stream, moe_dtype dt, int64_t T,
+                                            int64_t d, int32_t k, int64_t N,
+                                            const void* y_perm, const int32_t* slot_of,
+                                            const float* topk_w, const void* y_shared,
+                                            void* y) {
+  if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_DTYPE;
+  if (!y_perm || !slot_of || !y) return MOE_ERR_INVALID_ARG;
+  if (T < 1 || d < 1 || k < 1 || k > 32 || N < 0 || N >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
+  const size_t row_bytes = static_cast<size_t>(d) * elt_size(dt);
+  if (row_bytes % 16) return MOE_ERR_ALIGNMENT;
+  if (!aligned16(y_perm) || !aligned16(slot_of) || !aligned16(topk_w) || !aligned16(y_shared) ||
+      !aligned16(y))
+    return MOE_ERR_ALIGNMENT;
+  auto kern = dt == MOE_BF16 ? combine_kernel<true> : combine_kernel<false>;
+  return hip_status(launch(kern, dim3(static_cast<unsigned>((T + 3) / 4)), dim3(kCombThreads), 0,
+                           stream, (int)T, k, (int)N, static_cast<int>(row_bytes / 16),
+                           static_cast<const u32x4*>(y_perm), slot_of, topk_w,
+                           static_cast<const u32x4*>(y_shared), static_cast<u32x4*>(y)));
+}

@@ -1,0 +1,217 @@
+// moe_permute: stable counting sort of the (token, slot) pairs by expert and
+// the row gather x -> x_perm.
+//
+// Passage: "Megatron-Bridge 深度剖析", section "Expert Parallel 基础", step 2
+// (after dispatch the tokens sit grouped by expert) and section "Permute
+// Fusion" (the permute is a memory copy of the hidden states).
+//
+// Pairs are taken token-major (pair p = t*k + j) and cut into blocks of
+// P = floor(256 / k) * k pairs.  Row of a pair with expert e in block b:
+//     off[e] + sum_{b' < b} H[b'][e] + #{earlier pairs of block b with e}
+// which is exactly the stable order (expert, token, slot).  No atomics
+// decide an order, so the result is deterministic.
+//   K1 hist    : H[b][e] per block (LDS histogram)
+//   K2 colscan : per expert, exclusive scan of H[.][e] over blocks, in
+//                place; total count per expert
+//   K3 rows    : every block rebuilds off[] from the totals (LDS scan),
+//                ranks its pairs, writes slot_of / row_token / row_w
+//   K4 copy    : one wavefront per token reads x[t] once (16-byte lanes)
+//                and writes it to its k rows
+#include "moe_internal.h"
+
+namespace moe {
+
+constexpr int kPermThreads = 256;
+
+__host__ __device__ inline int perm_tokens_per_block(int k) {
+  const int tb = kPermThreads / k;
+  return tb > 0 ? tb : 1;
+}
+
+// inclusive scan of one value per thread over a 256-thread block
+__device__ inline int block_incl_scan(int v, int* s_tmp) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o, kWave);
+    if (lane >= o) v += u;
+  }
+  if (lane == 63) s_tmp[wave] = v;
+  __syncthreads();
+  int add = 0;
+  for (int w = 0; w < wave; ++w) add += s_tmp[w];
+  __syncthreads();
+  return v + add;
+}
+
+__global__ __launch_bounds__(kPermThreads) void perm_hist_kernel(
+    int T, int E, int k, const int32_t* __restrict__ topk_idx, int32_t* __restrict__ H) {
+  extern __shared__ int s_cnt[];
+  const int tb = perm_tokens_per_block(k);
+  const int64_t p0 = static_cast<int64_t>(blockIdx.x) * tb * k;
+  const int64_t pend = static_cast<int64_t>(T) * k;
+  for (int e = threadIdx.x; e < E; e += kPermThreads) s_cnt[e] = 0;
+  __syncthreads();
+  const int64_t p = p0 + threadIdx.x;
+  if (threadIdx.x < tb * k && p < pend) {
+    const int e = topk_idx[p];
+    if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);
+  }
+  __syncthreads();
+  int32_t* hrow = H + static_cast<size_t>(blockIdx.x) * E;
+  for (int e = threadIdx.x; e < E; e += kPermThreads) hrow[e] = s_cnt[e];
+}
+
+// one block per expert: exclusive scan of column e of H (in place)
+__global__ __launch_bounds__(kPermThreads) void perm_colscan_kernel(
+    int nblk, int E, int32_t* __restrict__ H, int32_t* __restrict__ total) {
+  __shared__ int s_tmp[4];
+  __shared__ int s_last;
+  const int e = blockIdx.x;
+  int carry = 0;
+  for (int b0 = 0; b0 < nblk; b0 += kPermThreads) {
+    const int b = b0 + threadIdx.x;
+    const int v = b < nblk ? H[static_cast<size_t>(b) * E + e] : 0;
+    const int inc = block_incl_scan(v, s_tmp);
+    if (b < nblk) H[static_cast<size_t>(b) * E + e] = carry + inc - v;
+    if (threadIdx.x == kPermThreads - 1) s_last = inc;   // chunk total
+    __syncthreads();
+    carry += s_last;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) total[e] = carry;
+}
+
+__global__ __launch_bounds__(kPermThreads) void perm_rows_kernel(
+    int T, int E, int k, const int32_t* __restrict__ topk_idx,
+    const float* __restrict__ topk_w, const int32_t* __restrict__ H,
+    const int32_t* __restrict__ total, int32_t* __restrict__ expert_offsets,
+    int32_t* __restrict__ slot_of, int32_t* __restrict__ row_token,
+    float* __restrict__ row_w) {
+  extern __shared__ int smem[];
+  int* s_off = smem;               // [E + 1]
+  int* s_e = smem + E + 1;         // [256]
+  __shared__ int s_tmp[4];
+  const int tid = threadIdx.x;
+
+  // off[] = exclusive scan of the per-expert totals (each thread 4 experts)
+  int loc[4];
+  int sum = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = tid * 4 + q;
+    loc[q] = e < E ? total[e] : 0;
+    sum += loc[q];
+  }
+  const int incl = block_incl_scan(sum, s_tmp);
+  int run = incl - sum;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = tid * 4 + q;
+    if (e < E) s_off[e] = run;
+    run += loc[q];
+  }
+  if (tid == kPermThreads - 1) s_off[E] = incl;
+  __syncthreads();
+  if (blockIdx.x == 0)
+    for (int e = tid; e <= E; e += kPermThreads) expert_offsets[e] = s_off[e];
+
+  const int tb = perm_tokens_per_block(k);
+  const int64_t p = static_cast<int64_t>(blockIdx.x) * tb * k + tid;
+  const bool inblk = tid < tb * k && p < static_cast<int64_t>(T) * k;
+  int e = inblk ? topk_idx[p] : -1;
+  if (e < 0 || e >= E) e = -1;
+  s_e[tid] = e;
+  __syncthreads();
+  if (!inblk) return;
+  if (e < 0) {
+    slot_of[p] = -1;
+    return;
+  }
+  int rank = 0;
+  for (int q = 0; q < tid; ++q) rank += (s_e[q] == e);
+  const int row = s_off[e] + H[static_cast<size_t>(blockIdx.x) * E + e] + rank;
+  slot_of[p] = row;
+  row_token[row] = static_cast<int>(p / k);
+  if (row_w) row_w[row] = topk_w[p];
+}
+
+// one wavefront per token: read the row once, write it to its k rows
+__global__ __launch_bounds__(kPermThreads) void perm_copy_kernel(
+    int T, int k, int nchunk16, const int32_t* __restrict__ slot_of,
+    const u32x4* __restrict__ x, u32x4* __restrict__ x_perm) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kPermThreads / 64) + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int my_row = lane < k ? slot_of[static_cast<size_t>(t) * k + lane] : -1;
+  const u32x4* src = x + static_cast<size_t>(t) * nchunk16;
+  for (int c0 = 0; c0 < nchunk16; c0 += 64 * 4) {
+    u32x4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = c0 + i * 64 + lane;
+      if (c < nchunk16) v[i] = src[c];
+    }
+    for (int j = 0; j < k; ++j) {
+      const int row = __shfl(my_row, j, kWave);
+      if (row < 0) continue;
+      u32x4* dst = x_perm + static_cast<size_t>(row) * nchunk16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = c0 + i * 64 + lane;
+        if (c < nchunk16) dst[c] = v[i];
+      }
+    }
+  }
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" size_t moe_permute_workspace_size(int64_t T, int32_t E, int32_t k) {
+  if (T < 1 || E < 1 || k < 1) return 0;
+  const int64_t tb = perm_tokens_per_block(k);
+  const int64_t nblk = (T + tb - 1) / tb;
+  return static_cast<size_t>((nblk * E + E) * sizeof(int32_t) + 256);
+}
+
+extern "C" moe_status moe_permute(hipStream_t stream, moe_dtype dt, int64_t T, int64_t d,
+                                  int32_t E, int32_t k, const void* x,
+                                  const int32_t* topk_idx, const float* topk_w,
+                                  int32_t* expert_offsets, int32_t* slot_of,
+                                  int32_t* row_token, float* row_w, void* x_perm,
+                                  void* ws, size_t ws_bytes) {
+  if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_DTYPE;
+  if (!x || !topk_idx || !expert_offsets || !slot_of || !row_token || !x_perm)
+    return MOE_ERR_INVALID_ARG;
+  if ((topk_w == nullptr) != (row_w == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (T < 1 || d < 1 || E < 1 || E > 1024 || k < 1 || k > 32) return MOE_ERR_SHAPE;
+  if (T * static_cast<int64_t>(k) >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
+  const size_t row_bytes = static_cast<size_t>(d) * elt_size(dt);
+  if (row_bytes % 16) return MOE_ERR_ALIGNMENT;
+  if (!aligned16(x) || !aligned16(x_perm) || !aligned16(topk_idx) || !aligned16(topk_w) ||
+      !aligned16(expert_offsets) || !aligned16(slot_of) || !aligned16(row_token) ||
+      !aligned16(row_w) || !aligned16(ws))
+    return MOE_ERR_ALIGNMENT;
+  if (!ws || ws_bytes < moe_permute_workspace_size(T, E, k)) return MOE_ERR_WORKSPACE;
+
+  const int tb = perm_tokens_per_block(k);
+  const int nblk = static_cast<int>((T + tb - 1) / tb);
+  int32_t* H = static_cast<int32_t*>(ws);
+  int32_t* total = H + static_cast<size_t>(nblk) * E;
+
+  hipError_t err = launch(perm_hist_kernel, dim3(nblk), dim3(kPermThreads),
+                          E * sizeof(int), stream, (int)T, E, k, topk_idx, H);
+  if (err == hipSuccess)
+    err = launch(perm_colscan_kernel, dim3(E), dim3(kPermThreads), 0, stream, nblk, E, H, total);
+  if (err == hipSuccess)
+    err = launch(perm_rows_kernel, dim3(nblk), dim3(kPermThreads),
+                 (E + 1 + kPermThreads) * sizeof(int), stream, (int)T, E, k, topk_idx, topk_w,
+                 H, total, expert_offsets, slot_of, row_token, row_w);
+  if (err == hipSuccess)
+    err = launch(perm_copy_kernel, dim3(static_cast<unsigned>((T + 3) / 4)), dim3(kPermThreads),
+                 0, stream, (int)T, k, static_cast<int>(row_bytes / 16), slot_of,
+                 static_cast<const u32x4*>(x), static_cast<u32x4*>(x_perm));
+  return hip_status(err);
+}

@@ -1,0 +1,114 @@
+"""Host-only checks of the C ABI (no GPU needed, no kernel is launched).
+
+  * the built library loads and exports every symbol include/moe.h declares;
+  * the binding's ctypes table matches the header's declarations;
+  * workspace-size queries answer on the host;
+  * argument checks return the documented status before any launch.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import mixture_experts_layer_05_amd as moe
+
+ROOT = os.path.abspath(os.path.join(os.path.dirname(__file__), ".."))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^MOE_API\s+[^(]*?\b(moe_\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(moe.LIB_PATH):
+        pytest.fail("library not built: run `python -m mixture_experts_layer_05_amd.build`")
+    return moe.lib()
+
+
+def test_header_declares_the_five_calls():
+    names = _declared()
+    for n in ("moe_route", "moe_permute", "moe_grouped_swiglu_fwd",
+              "moe_grouped_swiglu_bwd", "moe_unpermute_combine"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s+(moe_\w+)$", out, flags=re.M))
+    for n in _declared():
+        assert n in exported, n
+        assert hasattr(L, n)
+    assert set(moe.EXPORTED) == set(_declared())
+
+
+def test_version_and_status_strings(L):
+    assert L.moe_abi_version() == 1
+    assert L.moe_status_string(0) == b"MOE_OK"
+    assert L.moe_status_string(5) == b"MOE_ERR_WORKSPACE"
+
+
+def test_workspace_sizes(L):
+    T, E, k = 4096, 128, 8
+    ws = L.moe_permute_workspace_size(T, E, k)
+    nblk = -(-T // (256 // k))
+    assert ws >= (nblk * E + E) * 4
+    assert L.moe_grouped_swiglu_fwd_workspace_size(32768, 768, 1) >= 32768 * 768 * 2
+    a = L.moe_grouped_swiglu_bwd_workspace_size(32768, 768, 1, 0)
+    b = L.moe_grouped_swiglu_bwd_workspace_size(32768, 768, 1, 1)
+    assert b > a >= 32768 * 768 * 3 * 2
+
+
+# fake, aligned, never-dereferenced addresses: validation must fail first
+P = 0x100000
+MIS = 0x100004
+
+
+def test_route_validation(L):
+    r = L.moe_route
+    args = dict(s=None, dt=1, T=16, d=64, E=8, k=2, fn=0, norm=1, x=P, w=P, b=None, g=None,
+                idx=P, tw=P, cnt=P, gate=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return r(a["s"], a["dt"], a["T"], a["d"], a["E"], a["k"], a["fn"], a["norm"], a["x"],
+                 a["w"], a["b"], a["g"], a["idx"], a["tw"], a["cnt"], a["gate"])
+
+    assert call(dt=7) == 3                 # MOE_ERR_DTYPE
+    assert call(fn=5) == 1                 # bad score function
+    assert call(x=None) == 1               # NULL input
+    assert call(g=P) == 1                  # gate weight without gate output
+    assert call(k=9) == 2                  # k > E
+    assert call(k=33, E=64) == 2           # k > 32
+    assert call(E=1025) == 2               # E > 1024
+    assert call(T=0) == 2
+    assert call(d=60) == 4                 # d not a multiple of 8
+    assert call(x=MIS) == 4                # misaligned pointer
+
+
+def test_permute_validation(L):
+    f = L.moe_permute
+    ok = (None, 1, 16, 64, 8, 2, P, P, P, P, P, P, P, P, P)
+    assert f(*ok, 0) == 5                                  # workspace too small
+    assert f(None, 1, 16, 64, 8, 2, P, P, None, P, P, P, P, P, P, 1 << 20) == 1  # row_w w/o topk_w
+    assert f(None, 1, 16, 60, 8, 2, P, P, P, P, P, P, P, P, P, 1 << 20) == 4     # 120 B rows
+    assert f(None, 1, 16, 64, 0, 2, P, P, P, P, P, P, P, P, P, 1 << 20) == 2
+
+
+def test_grouped_validation(L):
+    fwd = L.moe_grouped_swiglu_fwd
+    assert fwd(None, 1, 100, 64, 60, 4, P, P, P, P, None, P, None, P, 1 << 30) == 4  # F % 8
+    assert fwd(None, 1, 100, 64, 64, 4, P, P, P, P, None, P, None, P, 16) == 5       # workspace
+    assert fwd(None, 1, 100, 64, 64, 4, None, P, P, P, None, P, None, P, 1 << 30) == 1
+    assert fwd(None, 1, 100, 64, 64, 2000, P, P, P, P, None, P, None, P, 1 << 30) == 2
+    bwd = L.moe_grouped_swiglu_bwd
+    assert bwd(None, 0, 100, 64, 64, 4, P, P, P, P, P, P, None, 0, P, P, P, P, 1 << 30) == 6
+    assert bwd(None, 1, 100, 64, 64, 4, P, P, P, P, P, P, None, 0, P, P, P, P, 16) == 5
+    comb = L.moe_unpermute_combine
+    assert comb(None, 1, 16, 64, 0, 32, P, P, None, None, P) == 2
+    assert comb(None, 1, 16, 64, 2, 32, P, P, None, None, MIS) == 4

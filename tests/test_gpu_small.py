@@ -1,0 +1,264 @@
+"""GPU parity of each C-ABI call against the CPU oracle at small, odd shapes
+(several tiles plus ragged tails, empty experts, k = 1 and k = E, E not a
+multiple of 64, d and F not multiples of the tile sizes).
+
+Every output buffer is poison-filled first (NaN / -1) so an unwritten
+element fails, and every call is run twice to check bitwise determinism.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_workloads as mw
+from oracle import moe_oracle as mo
+import gpu_helpers as gh
+
+pytestmark = pytest.mark.gpu
+
+moe = pytest.importorskip("mixture_experts_layer_05_amd")
+
+
+def _dtype(s):
+    return torch.float32 if s == "f32" else torch.bfloat16
+
+
+ROUTE_CASES = [
+    # T, d, E, k, score, bias, gate, dtype
+    (1, 64, 8, 2, "softmax", False, False, "f32"),
+    (257, 128, 8, 2, "softmax", False, False, "f32"),
+    (300, 64, 33, 5, "sigmoid", True, True, "f32"),
+    (33, 136, 8, 8, "softmax", False, False, "bf16"),     # k = E
+    (513, 256, 130, 6, "sigmoid", False, False, "bf16"),
+    (700, 512, 256, 8, "softmax", True, True, "bf16"),
+    (129, 264, 1000, 32, "softmax", False, False, "bf16"),
+    (100, 64, 1, 1, "softmax", False, False, "bf16"),      # E = 1
+]
+
+
+@pytest.mark.parametrize("case", ROUTE_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_route_parity(case):
+    T, d, E, k, score, bias, gate, dt = case
+    inp = mw.make_small_layer_inputs(11 + T + E, T=T, d=d, E=E, F=8, dtype=dt,
+                                     Fs=8 if gate else 0, bias=bias)
+    ref = mo.route(inp.as_f32("x"), inp.as_f32("w_router"), k, score, True,
+                   inp.logit_bias, inp.as_f32("w_gate"))
+    x = gh.to_gpu(inp.x)
+    wr = gh.to_gpu(inp.w_router)
+    b = gh.to_gpu(inp.logit_bias) if bias else None
+    wg = gh.to_gpu(inp.w_gate) if gate else None
+    outs = []
+    for _ in range(2):
+        out = (gh.poison((T, k), torch.int32), gh.poison((T, k), torch.float32),
+               gh.poison((E,), torch.int32), gh.poison((T,), torch.float32) if gate else None)
+        moe.route(x, wr, k, score, True, b, wg, out=out)
+        torch.cuda.synchronize()
+        outs.append(out)
+    for a, c in zip(outs[0], outs[1]):
+        if a is not None:
+            assert gh.bits_equal(a, c)
+    idx, w, cnt, g = (o.cpu().numpy() if o is not None else None for o in outs[0])
+    gh.check_routing(idx, w, ref, k)
+    assert (cnt == np.bincount(idx.reshape(-1), minlength=E)).all()
+    if gate:
+        assert np.abs(g - ref.gate).max() <= gh.TOL_ROUTE_W
+
+
+PERM_CASES = [
+    # T, d, E, k, dtype, pattern
+    (1, 64, 4, 1, "bf16", "random"),
+    (300, 64, 16, 4, "bf16", "random"),
+    (1000, 136, 130, 6, "bf16", "random"),
+    (257, 128, 8, 2, "f32", "random"),
+    (500, 64, 64, 1, "bf16", "one_expert"),          # every token on expert 0
+    (300, 64, 40, 8, "bf16", "few_experts"),         # most experts empty
+    (99, 64, 1024, 32, "bf16", "random"),            # E = 1024, k = 32
+]
+
+
+def _idx(rng, T, E, k, pattern):
+    if pattern == "one_expert":
+        return np.zeros((T, k), dtype=np.int32)
+    pool = np.arange(E) if pattern == "random" else np.arange(0, E, 5)[: max(k, 8)]
+    return np.stack([rng.choice(pool, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("case", PERM_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_permute_parity(case):
+    T, d, E, k, dt, pattern = case
+    rng = np.random.default_rng(T + E + k)
+    idx = _idx(rng, T, E, k, pattern)
+    w = rng.random((T, k)).astype(np.float32)
+    inp = mw.make_small_layer_inputs(5, T=T, d=d, E=1, F=8, dtype=dt)
+    ref = mo.permute(inp.x, idx, w, E)
+    x = gh.to_gpu(inp.x)
+    gi, gw = gh.to_gpu(idx), gh.to_gpu(w)
+    N = T * k
+    res = []
+    for _ in range(2):
+        out = (gh.poison((E + 1,), torch.int32), gh.poison((T, k), torch.int32),
+               gh.poison((N,), torch.int32), gh.poison((N,), torch.float32),
+               gh.poison((N, d), x.dtype))
+        moe.permute(x, gi, gw, E, out=out)
+        torch.cuda.synchronize()
+        res.append(out)
+    for a, c in zip(res[0], res[1]):
+        assert gh.bits_equal(a, c)
+    off, slot, rtok, rw, xp = res[0]
+    assert off.cpu().numpy().tolist() == ref.offsets.tolist()
+    assert np.array_equal(slot.cpu().numpy(), ref.slot_of)
+    assert np.array_equal(rtok.cpu().numpy(), ref.row_token)
+    assert np.array_equal(rw.cpu().numpy().view(np.uint32), ref.row_w.view(np.uint32))
+    xp_ref = gh.to_gpu(ref.x_perm)
+    assert gh.bits_equal(xp, xp_ref)
+    # unpermute(permute(x)) == x for every copy
+    for j in range(k):
+        assert gh.bits_equal(xp[slot[:, j].long()], x)
+
+
+def test_permute_drops_out_of_range_experts():
+    T, d, E, k = 50, 64, 8, 2
+    rng = np.random.default_rng(1)
+    idx = _idx(rng, T, E, k, "random")
+    idx[3, 1] = -1
+    idx[7, 0] = E
+    x = gh.to_gpu(mw.make_small_layer_inputs(2, T=T, d=d, E=1, F=8, dtype="bf16").x)
+    off, slot, rtok, _, xp = moe.permute(x, gh.to_gpu(idx), None, E)
+    slot = slot.cpu().numpy()
+    assert slot[3, 1] == -1 and slot[7, 0] == -1
+    assert off.cpu().numpy()[-1] == T * k - 2
+    valid = slot >= 0
+    assert sorted(slot[valid].tolist()) == list(range(T * k - 2))
+
+
+def _segments(rng, E, pattern, scale):
+    if pattern == "ragged":
+        c = rng.integers(0, scale, E)
+        c[::3] = 0                              # empty experts
+        c[1] = 1                                # a one-row expert
+        return c
+    if pattern == "one_hot":
+        c = np.zeros(E, dtype=np.int64)
+        c[E // 2] = scale
+        return c
+    raise ValueError(pattern)
+
+
+FFN_CASES = [
+    # E, d, F, dtype, pattern, scale
+    (5, 64, 64, "f32", "ragged", 150),
+    (4, 128, 256, "f32", "ragged", 90),
+    (6, 64, 64, "bf16", "ragged", 300),
+    (7, 136, 72, "bf16", "ragged", 200),       # K and N tails
+    (3, 256, 192, "bf16", "one_hot", 517),
+    (9, 192, 136, "bf16", "ragged", 140),
+]
+
+
+@pytest.mark.parametrize("case", FFN_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_grouped_fwd_parity(case):
+    E, d, F, dt, pattern, scale = case
+    rng = np.random.default_rng(E * 1000 + d + F)
+    counts = _segments(rng, E, pattern, scale)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    N = int(off[-1])
+    inp = mw.make_small_layer_inputs(E + d + F, T=N, d=d, E=E, F=F, dtype=dt, w_std=0.05)
+    rs = (rng.random(N) + 0.5).astype(np.float32)
+    y_ref, gu_ref = mo.grouped_swiglu_fwd(inp.as_f32("x"), inp.as_f32("w1"), inp.as_f32("w2"),
+                                          off, rs, return_gu=True)
+    x, w1, w2 = gh.to_gpu(inp.x), gh.to_gpu(inp.w1), gh.to_gpu(inp.w2)
+    go, grs = gh.to_gpu(off), gh.to_gpu(rs)
+    res = []
+    for _ in range(2):
+        y = gh.poison((N, d), x.dtype)
+        gu = gh.poison((N, 2 * F), x.dtype)
+        moe.grouped_swiglu_fwd(x, w1, w2, go, grs, save_gu=True, out=y, gu_out=gu)
+        torch.cuda.synchronize()
+        res.append((y, gu))
+    assert gh.bits_equal(res[0][0], res[1][0]) and gh.bits_equal(res[0][1], res[1][1])
+    tol = gh.TOL_F32 if dt == "f32" else gh.TOL_BF16
+    y, gu = (gh.to_f64(t) for t in res[0])
+    assert np.isfinite(y).all()
+    assert gh.normwise(y, y_ref) <= tol
+    assert gh.normwise(gu, gu_ref) <= tol
+
+
+BWD_CASES = [
+    # E, d, F, pattern, scale, save_gu, row_scale, accumulate
+    (5, 64, 64, "ragged", 200, True, False, False),
+    (7, 136, 72, "ragged", 200, True, True, False),
+    (4, 128, 128, "ragged", 300, False, True, True),
+    (3, 256, 192, "one_hot", 517, True, False, True),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_grouped_bwd_parity(case):
+    E, d, F, pattern, scale, save_gu, use_rs, acc = case
+    rng = np.random.default_rng(E * 7 + d + F)
+    counts = _segments(rng, E, pattern, scale)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    N = int(off[-1])
+    inp = mw.make_small_layer_inputs(3 * E + d, T=N, d=d, E=E, F=F, dtype="bf16", w_std=0.05)
+    dy = mw.round_to_bf16_bits(rng.standard_normal((N, d)).astype(np.float32))
+    rs = (rng.random(N) + 0.5).astype(np.float32) if use_rs else None
+    f = inp.as_f32
+    dx_ref, dw1_ref, dw2_ref = mo.grouped_swiglu_bwd(mw.bf16_bits_to_f32(dy), f("x"), f("w1"),
+                                                     f("w2"), off, rs)
+    x, w1, w2 = gh.to_gpu(inp.x), gh.to_gpu(inp.w1), gh.to_gpu(inp.w2)
+    go = gh.to_gpu(off)
+    grs = gh.to_gpu(rs) if use_rs else None
+    gdy = gh.to_gpu(dy)
+    gu = None
+    if save_gu:
+        _, gu = moe.grouped_swiglu_fwd(x, w1, w2, go, grs, save_gu=True)
+    base1 = torch.full((E, 2 * F, d), 0.25, dtype=torch.float32, device=gh.dev())
+    base2 = torch.full((E, d, F), -0.5, dtype=torch.float32, device=gh.dev())
+    res = []
+    for _ in range(2):
+        dw1 = base1.clone() if acc else gh.poison((E, 2 * F, d), torch.float32)
+        dw2 = base2.clone() if acc else gh.poison((E, d, F), torch.float32)
+        dx = gh.poison((N, d), x.dtype)
+        moe.grouped_swiglu_bwd(gdy, x, w1, w2, go, gu, grs, acc, dw1, dw2, dx_out=dx)
+        torch.cuda.synchronize()
+        res.append((dx, dw1, dw2))
+    for a, c in zip(res[0], res[1]):
+        assert gh.bits_equal(a, c)
+    dx, dw1, dw2 = (gh.to_f64(t) for t in res[0])
+    if acc:
+        dw1 = dw1 - 0.25
+        dw2 = dw2 + 0.5
+    assert gh.normwise(dx, dx_ref) <= gh.TOL_BF16_GRAD
+    for e in range(E):
+        if counts[e] == 0:
+            assert np.abs(dw1[e]).max() <= (1e-6 if acc else 0.0)
+            assert np.abs(dw2[e]).max() <= (1e-6 if acc else 0.0)
+            continue
+        assert gh.normwise(dw1[e], dw1_ref[e]) <= gh.TOL_BF16_GRAD, e
+        assert gh.normwise(dw2[e], dw2_ref[e]) <= gh.TOL_BF16_GRAD, e
+
+
+COMB_CASES = [(1, 64, 1, "bf16", False), (300, 136, 6, "bf16", True),
+              (257, 128, 2, "f32", True), (100, 64, 8, "bf16", False)]
+
+
+@pytest.mark.parametrize("case", COMB_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_combine_parity(case):
+    T, d, k, dt, shared = case
+    rng = np.random.default_rng(T + d + k)
+    N = T * k
+    ypf = rng.standard_normal((N, d)).astype(np.float32)
+    yp = ypf if dt == "f32" else mw.round_to_bf16_bits(ypf)
+    slot = rng.permutation(N).reshape(T, k).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    ysh = None
+    if shared:
+        s = rng.standard_normal((T, d)).astype(np.float32)
+        ysh = s if dt == "f32" else mw.round_to_bf16_bits(s)
+    as32 = (lambda a: a) if dt == "f32" else mw.bf16_bits_to_f32
+    ref = mo.unpermute_combine(as32(yp), slot, w, None if ysh is None else as32(ysh))
+    g = [moe.unpermute_combine(gh.to_gpu(yp), gh.to_gpu(slot), gh.to_gpu(w),
+                               None if ysh is None else gh.to_gpu(ysh)) for _ in range(2)]
+    torch.cuda.synchronize()
+    assert gh.bits_equal(g[0], g[1])
+    tol = gh.TOL_F32 if dt == "f32" else gh.TOL_BF16
+    assert gh.normwise(gh.to_f64(g[0]), ref) <= tol
