@@ -1,0 +1,225 @@
+"""Benchmark of the MoE-layer hot path on one MI355X.
+
+One step = one forward pass of the whole layer over one batch of the
+128-expert top-8 workload (T=4096 tokens, d=2048, E=128, k=8, ffn 768,
+bf16 storage, fp32 accumulation and router math):
+    route -> permute -> grouped SwiGLU (fc1 + fc2, routing weight as the fc2
+    row scale) -> combine
+Inputs are seeded synthetic tensors already resident in HBM; every launch
+goes through the C ABI (libmoe_mi355x.so).
+
+Prints ONE JSON line.  `value` is layer tokens/s; the grouped-GEMM TFLOP/s
+and its fraction of the bf16 MFMA peak are reported beside it.  `roofline`
+describes the grouped-GEMM forward call (its fc1 and fc2 launches on one
+stream), timed with HIP events around that call inside the timed region.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same batch.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, AMD's published figure
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, AMD's published figure
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="qwen3_30b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
+    return ap.parse_args()
+
+
+def algorithmic(cfg):
+    """Per-call algorithmic work (what the method itself must move or do)."""
+    T, d, E, k, F = cfg.T, cfg.d, cfg.E, cfg.k, cfg.F
+    N = T * k
+    b = 2
+    gemm_flop = 6.0 * N * d * F
+    # expert weights read once + X_perm read + A written and read + Y_perm written
+    gemm_bytes = 3.0 * E * d * F * b + N * d * b + 2.0 * N * F * b + N * d * b
+    route_bytes = T * (2 * d + 8 * k + 4) + E * d * b
+    permute_bytes = T * (2 * d * (1 + k) + 20 * k)
+    combine_bytes = T * (2 * d * (k + 1) + 4 * k)
+    return dict(gemm_flop=gemm_flop, gemm_bytes=gemm_bytes, route_bytes=route_bytes,
+                permute_bytes=permute_bytes, combine_bytes=combine_bytes)
+
+
+def cpu_baseline(inp, cfg, ntok, min_seconds=10.0):
+    """The oracle as it stands, on the first `ntok` tokens of the batch."""
+    import numpy as np
+    from oracle import moe_oracle as mo
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=None)
+    except Exception:
+        pass
+    if threads is None:
+        threads = len(os.sched_getaffinity(0))
+    f = inp.as_f32
+    x = f("x")[:ntok]
+    wr, w1, w2 = f("w_router"), f("w1"), f("w2")
+    # repeat whole passes until about 10 s of CPU work has been timed
+    reps, dt = 0, 0.0
+    while dt < min_seconds or reps == 0:
+        t0 = time.perf_counter()
+        y, _, _ = mo.moe_layer_forward(x, wr, w1, w2, cfg.k, cfg.score, cfg.normalize)
+        dt += time.perf_counter() - t0
+        reps += 1
+        assert np.isfinite(y).all()
+    return {"value": reps * ntok / dt, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {ntok} of {cfg.T} tokens of the {cfg.name} batch, all {cfg.E} "
+                      f"experts, float64 oracle layer forward, {reps} passes in {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(expert-parallel sharding is described in the design notes, not built).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_workloads as mw
+    import mixture_experts_layer_05_amd as moe
+
+    cfg = mw.get(args.workload)
+    assert not cfg.backward, "bench steps are forward workloads"
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    inp = mw.make_layer_inputs(cfg)
+
+    def gpu(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    x = gpu(inp.x)
+    layer = moe.MoELayer(gpu(inp.w_router), gpu(inp.w1), gpu(inp.w2), cfg.k, cfg.T, cfg.score,
+                         cfg.normalize, gpu(inp.logit_bias), gpu(inp.w_gate), gpu(inp.ws1),
+                         gpu(inp.ws2))
+    stream = torch.cuda.current_stream()
+
+    stages = ["route", "permute", "grouped_gemm", "shared", "combine"]
+
+    def step(ev=None):
+        L = layer
+        if ev is not None:
+            ev[0].record(stream)
+        idx, w, cnt, gate = moe.route(x, L.w_router, L.k, L.score, L.normalize, L.logit_bias,
+                                      L.w_gate, out=L.route_out)
+        if ev is not None:
+            ev[1].record(stream)
+        off, slot, rtok, rw, xp = moe.permute(x, idx, w, L.E, out=L.perm_out, ws=L.perm_ws)
+        if ev is not None:
+            ev[2].record(stream)
+        moe.grouped_swiglu_fwd(xp, L.w1, L.w2, off, row_scale=rw, out=L.y_perm, ws=L.ffn_ws)
+        if ev is not None:
+            ev[3].record(stream)
+        ysh = None
+        if L.ws1 is not None:
+            moe.grouped_swiglu_fwd(x, L.ws1_e, L.ws2_e, L.shared_off, row_scale=gate,
+                                   out=L.y_shared, ws=L.ffn_ws)
+            ysh = L.y_shared
+        if ev is not None:
+            ev[4].record(stream)
+        moe.unpermute_combine(L.y_perm, slot, None, ysh, out=L.y)
+        if ev is not None:
+            ev[5].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per_stage = {s: 0.0 for s in stages}
+    total_ev = 0.0
+    for ev in evs:
+        for j, s in enumerate(stages):
+            per_stage[s] += ev[j].elapsed_time(ev[j + 1])
+        total_ev += ev[0].elapsed_time(ev[5])
+    per_stage = {s: v / args.steps for s, v in per_stage.items()}  # ms per call
+    ms_per_step = wall * 1e3 / args.steps
+    tokens_per_s = cfg.T / (wall / args.steps)
+
+    alg = algorithmic(cfg)
+    t_gemm = per_stage["grouped_gemm"] * 1e-3
+    gemm_tflops = alg["gemm_flop"] / t_gemm / 1e12
+    gemm_gbs = alg["gemm_bytes"] / t_gemm / 1e9
+    # the binding roof of the grouped GEMM: whichever of MFMA and HBM time is longer
+    t_mfma = alg["gemm_flop"] / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = alg["gemm_bytes"] / (PEAK_HBM_GBS * 1e9)
+    if t_hbm > t_mfma:
+        roof = {"bound": "hbm", "achieved": round(gemm_gbs, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(gemm_gbs / PEAK_HBM_GBS, 4), "traffic": None}
+    else:
+        roof = {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
+                "traffic": None}
+    roof["kernel"] = "moe_grouped_swiglu_fwd (fc1+SwiGLU, fc2+row-scale launches)"
+    roof["algorithmic_flop"] = alg["gemm_flop"]
+    roof["algorithmic_bytes"] = alg["gemm_bytes"]
+    roof["avg_launch_ms"] = round(per_stage["grouped_gemm"], 4)
+
+    def gbs(key, stage):
+        t = per_stage[stage] * 1e-3
+        return round(alg[key] / t / 1e9, 1) if t > 0 else None
+
+    out = {
+        "metric": "MoE layer tokens/sec + grouped-GEMM TFLOP/s (% bf16 MFMA peak), 1 MI355X",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded PCG64; x~N(0,1), router~N(0,1/d), experts~N(0,0.02^2))",
+        "config": {"workload": f"{cfg.name}: T={cfg.T} d={cfg.d} E={cfg.E} top-{cfg.k} "
+                               f"{cfg.score} ffn={cfg.F}", "T": cfg.T, "d": cfg.d, "E": cfg.E,
+                   "k": cfg.k, "F": cfg.F, "Fs": cfg.Fs, "score": cfg.score},
+        "grouped_gemm_tflops": round(gemm_tflops, 1),
+        "grouped_gemm_mfma_frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
+        "stage_ms": {s: round(v, 4) for s, v in per_stage.items()},
+        "stage_gbs": {"route": gbs("route_bytes", "route"),
+                      "permute": gbs("permute_bytes", "permute"),
+                      "combine": gbs("combine_bytes", "combine")},
+        "event_ms_per_step": round(total_ev / args.steps, 4),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, cfg, min(args.cpu_sample_tokens, cfg.T))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
