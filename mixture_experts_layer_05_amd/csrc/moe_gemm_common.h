@@ -1,0 +1,98 @@
+// Tile enumeration over ragged expert segments, shared by the grouped-GEMM
+// kernels.  Tiles are listed per expert (experts in order), column tiles
+// outer, row tiles inner, and found on the device from expert_offsets, so
+// no host synchronisation is needed.
+#pragma once
+
+#include "moe_internal.h"
+
+namespace moe {
+
+struct TileIdx {
+  int e, mt, nt, lo, hi;
+};
+
+// Block-wide exclusive scan over the experts' tile counts, into s_cum[0..E]
+// (s_cum[E] = total).  E <= 1024, blockDim.x == kThreads (a multiple of 64,
+// at most 1024).  Every thread of the block must call it.
+template <int kThreads>
+__device__ inline void tile_prefix(const int32_t* __restrict__ offsets, int E, int bm, int ntn,
+                                   int* s_cum, int* s_tmp) {
+  constexpr int kPer = (1024 + kThreads - 1) / kThreads;
+  const int tid = threadIdx.x;
+  int loc[kPer], sum = 0;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int e = tid * kPer + q;
+    int t = 0;
+    if (e < E) {
+      const int n = offsets[e + 1] - offsets[e];
+      t = (n > 0 ? (n + bm - 1) / bm : 0) * ntn;
+    }
+    loc[q] = t;
+    sum += t;
+  }
+  const int lane = tid & 63, wave = tid >> 6;
+  int v = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o, kWave);
+    if (lane >= o) v += u;
+  }
+  if (lane == 63) s_tmp[wave] = v;
+  __syncthreads();
+  int add = 0;
+  for (int w = 0; w < wave; ++w) add += s_tmp[w];
+  int run = v + add - sum;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int e = tid * kPer + q;
+    if (e < E) s_cum[e] = run;
+    run += loc[q];
+  }
+  if (tid == kThreads - 1) s_cum[E] = v + add;
+  __syncthreads();
+}
+
+// Workgroups are handed to the 8 XCDs round-robin (block b -> XCD b % 8).
+// Give each XCD a contiguous range of logical tiles instead, so the row
+// tiles that share one expert's weight panel run at the same time on the
+// same XCD and share its L2.  Bijective on [0, total).
+__device__ inline int xcd_remap(int b, int total) {
+  const int x = b & 7, pos = b >> 3;
+  const int q = total >> 3, r = total & 7;
+  return x * q + (x < r ? x : r) + pos;
+}
+
+// logical tile -> (expert, row tile, column tile) given s_cum from tile_prefix
+__device__ inline TileIdx tile_decode(const int32_t* __restrict__ offsets, int E, int bm, int L,
+                                      const int* s_cum) {
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {  // largest e with s_cum[e] <= L (that expert is non-empty)
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_cum[mid] <= L) lo = mid; else hi = mid - 1;
+  }
+  TileIdx t;
+  t.e = lo;
+  t.lo = offsets[lo];
+  t.hi = offsets[lo + 1];
+  const int mts = (t.hi - t.lo + bm - 1) / bm;
+  const int local = L - s_cum[lo];
+  t.nt = local / mts;
+  t.mt = local - t.nt * mts;
+  return t;
+}
+
+inline int tiles_bound(int64_t N, int E, int bm) {
+  return static_cast<int>((N + bm - 1) / bm + E);
+}
+
+// Forward launcher shared with the backward's recompute path.  bf16 only.
+// a_buf [N, F] receives silu(G) * U; gu_save (or NULL) receives [G | U];
+// when run_fc2, y_perm = (a_buf W2^T) * row_scale.
+hipError_t launch_grouped_fwd_bf16(hipStream_t stream, int64_t N, int64_t d, int64_t F, int32_t E,
+                                   const void* x_perm, const void* w1, const void* w2,
+                                   const int32_t* offsets, const float* row_scale, void* y_perm,
+                                   void* gu_save, uint16_t* a_buf, bool run_fc2);
+
+}  // namespace moe

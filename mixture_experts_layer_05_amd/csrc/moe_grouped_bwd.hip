@@ -1,12 +1,9 @@
-// Grouped SwiGLU expert FFN: forward (fc1 + SwiGLU, fc2 + row scale) and
-// backward (fc2 dgrad + SwiGLU backward, fc1 dgrad, fc2 / fc1 wgrad).
+// Grouped SwiGLU expert FFN, backward: fc2 dgrad + SwiGLU backward, fc1
+// dgrad, fc2 and fc1 wgrad.
 //
-// Passages: "Megatron-Bridge 深度剖析", section "计算融合 / Grouped GEMM" (all
-// experts' GEMMs in one launch over segments of different length, expert
-// weights stored back to back), section "权重映射策略" (GatedMLPMapping:
-// linear_fc1 = [gate_proj; up_proj], (2*ffn, hidden)), "Motivation" (SwiGLU
-// experts: gate_proj, up_proj, down_proj), "通信隐藏与混合精度 / TP 通信重叠"
-// (backward dgrad and wgrad GEMMs) and "其他融合优化"
+// Passages: "Megatron-Bridge 深度剖析", section "计算融合 / Grouped GEMM" (one
+// grouped launch over all experts' segments), "通信隐藏与混合精度 / TP 通信重叠"
+// (the backward's dgrad and wgrad GEMMs) and "其他融合优化"
 // (gradient_accumulation_fusion: fp32 weight-gradient accumulation).
 //
 // bf16 engine (gfx950):
@@ -17,21 +14,20 @@
 //     buffered through registers; the 8-byte k-groups are XOR-swizzled by
 //     row so both the 16-byte MFMA operand reads and the transposing
 //     8-byte writes spread over the banks;
-//   * an operand whose K runs along memory rows ("K-strided": weights in
-//     dgrad, activations in wgrad) is read as 4 (k) x 8 (row) blocks of
-//     16-byte loads and transposed in registers (v_perm) before the LDS
-//     write, so every GEMM of the forward and backward uses the same core;
-//   * tiles over ragged expert segments are enumerated on the device from
-//     expert_offsets (no host synchronisation): per expert its row tiles
-//     ceil(n_e / 128) x column tiles, row tiles fastest so tiles sharing a
-//     weight panel are issued back to back;
-//   * epilogues fuse SwiGLU (gate and up columns of the same f sit in the
-//     same lane: the B tile holds 64 gate rows then the 64 matching up rows),
-//     the routing-weight row scale, the SwiGLU backward and the fp32
-//     (optionally accumulating) weight-gradient store.
+//   * an operand whose K runs along memory rows ("K-strided": the weights
+//     in dgrad, the activations in wgrad) is read as 4 (k) x 8 (row) blocks
+//     of 16-byte loads and transposed in registers (v_perm) before the LDS
+//     write, so all four backward GEMMs use one core;
+//   * dgrad tiles over ragged expert segments are decoded on the device from
+//     expert_offsets (no host synchronisation) and handed to XCDs in
+//     contiguous ranges; wgrad tiles are per expert, K = the expert's rows
+//     (an empty expert yields zeros);
+//   * epilogues fuse the SwiGLU backward (dG = dA U silu'(G), dU = dA
+//     silu(G)) with the recomputed A * row_scale for the fc2 wgrad, and the
+//     fp32 (optionally accumulating) weight-gradient store.
 //   Deterministic: each output element is produced by one workgroup with a
 //   fixed K order; no atomics.
-#include "moe_internal.h"
+#include "moe_gemm_common.h"
 
 namespace moe {
 
@@ -40,7 +36,7 @@ constexpr int kBM = 128, kBN = 128, kBK = 64;
 constexpr int kLDK = 72;          // LDS row pitch in bf16 elements
 constexpr int kTileElems = 128 * kLDK;
 
-enum Epi { EPI_FC1 = 0, EPI_FC2 = 1, EPI_DGRAD2 = 2, EPI_DGRAD1 = 3, EPI_WGRAD = 4 };
+enum Epi { EPI_DGRAD2 = 2, EPI_DGRAD1 = 3, EPI_WGRAD = 4 };
 
 struct GGParams {
   int E, F, d;
@@ -56,8 +52,8 @@ struct GGParams {
   int K;                          // contraction length (token-tiled GEMMs)
   const float* scale;             // [N] row scale or NULL
   const uint16_t* gu_in;          // [N, 2F] (DGRAD2)
-  uint16_t* out;                  // FC1: A [N,F]; FC2: Y [N,d]; DGRAD2: dH [N,2F]; DGRAD1: dX
-  uint16_t* out2;                 // FC1: gu_save or NULL; DGRAD2: A*scale [N,F]
+  uint16_t* out;                  // DGRAD2: dH [N,2F]; DGRAD1: dX [N,d]
+  uint16_t* out2;                 // DGRAD2: A*scale [N,F]
   float* outf;                    // WGRAD: dW (expert 0)
   size_t outf_estride;
   int wg_m, wg_n;                 // WGRAD: output rows / cols per expert
@@ -142,67 +138,6 @@ __device__ __forceinline__ void mfma_tile(const uint16_t* As, const uint16_t* Bs
   }
 }
 
-// Token-tiled tile lookup: tile -> (expert, row tile, column tile).
-// Builds, in LDS, the cumulative tile count over experts.
-struct TileIdx { int e, mt, nt, lo, hi; bool valid; };
-
-__device__ TileIdx token_tile(const GGParams& p, int* s_cum /*[E+1]*/, int* s_tmp) {
-  const int tid = threadIdx.x;
-  // per thread up to 4 consecutive experts
-  int loc[4], sum = 0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = tid * 4 + q;
-    int t = 0;
-    if (e < p.E) {
-      const int n = p.offsets[e + 1] - p.offsets[e];
-      t = (n > 0 ? (n + kBM - 1) / kBM : 0) * p.ntn;
-    }
-    loc[q] = t;
-    sum += t;
-  }
-  // block exclusive scan
-  const int lane = tid & 63, wave = tid >> 6;
-  int v = sum;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(v, o, kWave);
-    if (lane >= o) v += u;
-  }
-  if (lane == 63) s_tmp[wave] = v;
-  __syncthreads();
-  int add = 0;
-  for (int w = 0; w < wave; ++w) add += s_tmp[w];
-  int run = v + add - sum;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = tid * 4 + q;
-    if (e < p.E) s_cum[e] = run;
-    run += loc[q];
-  }
-  if (tid == kGT - 1) s_cum[p.E] = v + add;
-  __syncthreads();
-  TileIdx ti;
-  const int tile = blockIdx.x;
-  ti.valid = tile < s_cum[p.E];
-  if (!ti.valid) return ti;
-  // largest e with s_cum[e] <= tile (and a non-empty expert)
-  int lo = 0, hi = p.E - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (s_cum[mid] <= tile) lo = mid; else hi = mid - 1;
-  }
-  const int e = lo;
-  const int local = tile - s_cum[e];
-  ti.e = e;
-  ti.lo = p.offsets[e];
-  ti.hi = p.offsets[e + 1];
-  const int mts = (ti.hi - ti.lo + kBM - 1) / kBM;
-  ti.nt = local / mts;
-  ti.mt = local - ti.nt * mts;
-  return ti;
-}
-
 template <int kEpi>
 __global__ __launch_bounds__(kGT, 2) void gg_kernel(GGParams p) {
   extern __shared__ __align__(16) uint16_t lds[];
@@ -229,35 +164,23 @@ __global__ __launch_bounds__(kGT, 2) void gg_kernel(GGParams p) {
     seg_hi = p.offsets[e + 1];
     klen = seg_hi - seg_lo;
   } else {
-    const TileIdx ti = token_tile(p, s_cum, s_tmp);
-    if (!ti.valid) return;
+    tile_prefix<kGT>(p.offsets, p.E, kBM, p.ntn, s_cum, s_tmp);
+    const int total = s_cum[p.E];
+    if (static_cast<int>(blockIdx.x) >= total) return;
+    const TileIdx ti = tile_decode(p.offsets, p.E, kBM, xcd_remap(blockIdx.x, total), s_cum);
     e = ti.e;
     seg_lo = ti.lo;
     seg_hi = ti.hi;
     m0 = seg_lo + ti.mt * kBM;
-    n0 = ti.nt * (kEpi == EPI_FC1 ? 64 : kBN);
+    n0 = ti.nt * kBN;
     klen = p.K;
   }
 
   const uint16_t* bexp = p.b + static_cast<size_t>(e) * p.b_estride;
   const int last_row = seg_hi - 1;
   auto arow = [&](int r) { const int g = m0 + r; return g <= last_row ? g : last_row; };
-  auto brow_fc1 = [&](int r) {
-    // rows 0..63: gate rows n0+r; rows 64..127: up rows F+n0+r-64
-    const int f = n0 + (r & 63);
-    const int fc = f < p.F ? f : p.F - 1;
-    return (r < 64) ? fc : p.F + fc;
-  };
-  auto brow_fc2 = [&](int r) { const int n = n0 + r; return n < p.d ? n : p.d - 1; };
-
   auto load = [&](RegsK& ra, RegsK& rb, int k0) {
-    if constexpr (kEpi == EPI_FC1) {
-      load_kcontig(ra, p.a, p.lda, arow, k0, klen);
-      load_kcontig(rb, bexp, p.ldb, brow_fc1, k0, klen);
-    } else if constexpr (kEpi == EPI_FC2) {
-      load_kcontig(ra, p.a, p.lda, arow, k0, klen);
-      load_kcontig(rb, bexp, p.ldb, brow_fc2, k0, klen);
-    } else if constexpr (kEpi == EPI_DGRAD2) {
+    if constexpr (kEpi == EPI_DGRAD2) {
       // A = dY rows (K = d contiguous); B = W2[e] (d x F): element (k=n, r=f)
       load_kcontig(ra, p.a, p.lda, arow, k0, klen);
       load_kstrided(rb, bexp, p.ldb, 0, klen, n0, p.F, k0);
@@ -273,10 +196,7 @@ __global__ __launch_bounds__(kGT, 2) void gg_kernel(GGParams p) {
   };
   auto store = [&](const RegsK& ra, const RegsK& rb, uint16_t* As, uint16_t* Bs) {
     if constexpr (kEpi == EPI_WGRAD) store_kstrided(ra, As); else store_kcontig(ra, As);
-    if constexpr (kEpi == EPI_DGRAD2 || kEpi == EPI_DGRAD1 || kEpi == EPI_WGRAD)
-      store_kstrided(rb, Bs);
-    else
-      store_kcontig(rb, Bs);
+    store_kstrided(rb, Bs);
   };
 
   f32x16 acc[2][2];
@@ -326,24 +246,7 @@ __global__ __launch_bounds__(kGT, 2) void gg_kernel(GGParams p) {
         const int row = m0 + trow;
         if (row >= seg_hi) continue;
         const size_t rowz = static_cast<size_t>(row);
-        if constexpr (kEpi == EPI_FC1) {
-          const int f = n0 + wn * 32 + r32;
-          if (f < p.F) {
-            const float g = acc[mi][0][r], u = acc[mi][1][r];
-            p.out[rowz * p.F + f] = f32_to_bf16(siluf_(g) * u);
-            if (p.out2) {
-              p.out2[rowz * 2 * p.F + f] = f32_to_bf16(g);
-              p.out2[rowz * 2 * p.F + p.F + f] = f32_to_bf16(u);
-            }
-          }
-        } else if constexpr (kEpi == EPI_FC2) {
-          const float s = p.scale ? p.scale[row] : 1.0f;
-#pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const int n = n0 + c * 64 + wn * 32 + r32;
-            if (n < p.d) p.out[rowz * p.d + n] = f32_to_bf16(acc[mi][c][r] * s);
-          }
-        } else if constexpr (kEpi == EPI_DGRAD2) {
+        if constexpr (kEpi == EPI_DGRAD2) {
           const float s = p.scale ? p.scale[row] : 1.0f;
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
@@ -373,163 +276,17 @@ __global__ __launch_bounds__(kGT, 2) void gg_kernel(GGParams p) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// fp32 path (MOE_F32): LDS-tiled FMA, 64 x 64 x 16 tiles, 4 x 4 per thread.
-// Same tile enumeration and epilogue semantics as the bf16 engine.
-// ---------------------------------------------------------------------------
-constexpr int kFM = 64, kFN = 64, kFK = 16;
-
-template <int kEpi>
-__global__ __launch_bounds__(256) void gg_f32_kernel(int E, int F, int d, int K, int ntn,
-                                                     const int32_t* __restrict__ offsets,
-                                                     const float* __restrict__ a, int lda,
-                                                     const float* __restrict__ b, int ldb,
-                                                     size_t b_estride, const float* __restrict__ scale,
-                                                     float* __restrict__ out, float* __restrict__ out2) {
-  __shared__ float As[kFK][kFM + 4];
-  __shared__ float Bs[kFK][kFN + 4];
-  __shared__ int s_cum[1025];
-  __shared__ int s_tmp[4];
-  const int tid = threadIdx.x;
-  // tile lookup (row tiles of 64)
-  {
-    int loc[4], sum = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = tid * 4 + q;
-      int t = 0;
-      if (e < E) {
-        const int n = offsets[e + 1] - offsets[e];
-        t = (n > 0 ? (n + kFM - 1) / kFM : 0) * ntn;
-      }
-      loc[q] = t;
-      sum += t;
-    }
-    const int lane = tid & 63, wave = tid >> 6;
-    int v = sum;
-    for (int o = 1; o < 64; o <<= 1) {
-      const int u = __shfl_up(v, o, kWave);
-      if (lane >= o) v += u;
-    }
-    if (lane == 63) s_tmp[wave] = v;
-    __syncthreads();
-    int add = 0;
-    for (int w = 0; w < wave; ++w) add += s_tmp[w];
-    int run = v + add - sum;
-    for (int q = 0; q < 4; ++q) {
-      const int e = tid * 4 + q;
-      if (e < E) s_cum[e] = run;
-      run += loc[q];
-    }
-    if (tid == 255) s_cum[E] = v + add;
-    __syncthreads();
-  }
-  const int tile = blockIdx.x;
-  if (tile >= s_cum[E]) return;
-  int lo = 0, hi = E - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (s_cum[mid] <= tile) lo = mid; else hi = mid - 1;
-  }
-  const int e = lo;
-  const int seg_lo = offsets[e], seg_hi = offsets[e + 1];
-  const int mts = (seg_hi - seg_lo + kFM - 1) / kFM;
-  const int local = tile - s_cum[e];
-  const int nt = local / mts, mt = local - nt * mts;
-  const int m0 = seg_lo + mt * kFM;
-  const float* bexp = b + static_cast<size_t>(e) * b_estride;
-
-  const int ty = tid >> 4, tx = tid & 15;
-  // B-tile rows held by this thread: FC1 {2tx, 2tx+1, 32+2tx, 33+2tx}; FC2 4tx..4tx+3
-  int bcol[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    bcol[j] = (kEpi == EPI_FC1) ? ((j >> 1) * 32 + 2 * tx + (j & 1)) : (4 * tx + j);
-  float acc[4][4] = {};
-  for (int k0 = 0; k0 < K; k0 += kFK) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;          // 0..1023
-      const int r = c >> 4, kk = c & 15;    // 64 rows x 16 k
-      const int k = k0 + kk;
-      int ar = m0 + r;
-      if (ar > seg_hi - 1) ar = seg_hi - 1;
-      As[kk][r] = k < K ? a[static_cast<size_t>(ar) * lda + k] : 0.0f;
-      int br;
-      if constexpr (kEpi == EPI_FC1) {
-        int f = nt * 32 + (r & 31);
-        if (f > F - 1) f = F - 1;
-        br = r < 32 ? f : F + f;
-      } else {
-        br = nt * kFN + r;
-        if (br > d - 1) br = d - 1;
-      }
-      Bs[kk][r] = k < K ? bexp[static_cast<size_t>(br) * ldb + k] : 0.0f;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < kFK; ++kk) {
-      float av[4], bv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) av[i] = As[kk][ty * 4 + i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bv[j] = Bs[kk][bcol[j]];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = m0 + ty * 4 + i;
-    if (row >= seg_hi) continue;
-    const size_t rowz = static_cast<size_t>(row);
-    if constexpr (kEpi == EPI_FC1) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int f = nt * 32 + 2 * tx + j;
-        if (f < F) {
-          const float g = acc[i][j], u = acc[i][j + 2];
-          out[rowz * F + f] = siluf_(g) * u;
-          if (out2) {
-            out2[rowz * 2 * F + f] = g;
-            out2[rowz * 2 * F + F + f] = u;
-          }
-        }
-      }
-    } else {
-      const float s = scale ? scale[row] : 1.0f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = nt * kFN + 4 * tx + j;
-        if (n < d) out[rowz * d + n] = acc[i][j] * s;
-      }
-    }
-  }
-}
-
-inline int tiles_bound(int64_t N, int E, int bm) {
-  return static_cast<int>((N + bm - 1) / bm + E);
-}
-
 }  // namespace moe
 
 using namespace moe;
 
-static moe_status check_common(moe_dtype dt, int64_t N, int64_t d, int64_t F, int32_t E) {
+moe_status moe_grouped_check(moe_dtype dt, int64_t N, int64_t d, int64_t F, int32_t E) {
   if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_DTYPE;
   if (N < 0 || d < 1 || F < 1 || E < 1 || E > 1024) return MOE_ERR_SHAPE;
   if (N >= (int64_t(1) << 31) || d >= (int64_t(1) << 24) || F >= (int64_t(1) << 24))
     return MOE_ERR_SHAPE;
   if (d % 8 || F % 8) return MOE_ERR_ALIGNMENT;
   return MOE_OK;
-}
-
-extern "C" size_t moe_grouped_swiglu_fwd_workspace_size(int64_t N, int64_t F, moe_dtype dt) {
-  if (N < 0 || F < 1) return 0;
-  return static_cast<size_t>(N) * F * elt_size(dt) + 256;
 }
 
 extern "C" size_t moe_grouped_swiglu_bwd_workspace_size(int64_t N, int64_t F, moe_dtype dt,
@@ -542,73 +299,6 @@ extern "C" size_t moe_grouped_swiglu_bwd_workspace_size(int64_t N, int64_t F, mo
 
 static size_t round_up256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
-static hipError_t launch_fwd_bf16(hipStream_t stream, int64_t N, int64_t d, int64_t F, int32_t E,
-                                  const void* x_perm, const void* w1, const void* w2,
-                                  const int32_t* offsets, const float* row_scale, void* y_perm,
-                                  void* gu_save, uint16_t* a_buf, bool run_fc2) {
-  const size_t lds = 4 * kTileElems * sizeof(uint16_t);
-  hipError_t err = allow_lds(gg_kernel<EPI_FC1>, lds);
-  if (err != hipSuccess) return err;
-  GGParams p{};
-  p.E = E; p.F = (int)F; p.d = (int)d; p.offsets = offsets;
-  // fc1: C[N, (gate,up) F] = X W1^T, fused SwiGLU
-  p.ntn = (int)((F + 63) / 64);
-  p.a = static_cast<const uint16_t*>(x_perm); p.lda = (int)d;
-  p.b = static_cast<const uint16_t*>(w1); p.ldb = (int)d; p.b_estride = static_cast<size_t>(2 * F) * d;
-  p.K = (int)d;
-  p.out = a_buf; p.out2 = static_cast<uint16_t*>(gu_save);
-  err = launch(gg_kernel<EPI_FC1>, dim3(tiles_bound(N, E, kBM) * p.ntn), dim3(kGT), lds, stream, p);
-  if (err != hipSuccess || !run_fc2) return err;
-  // fc2: Y[N, d] = A W2^T * row_scale
-  err = allow_lds(gg_kernel<EPI_FC2>, lds);
-  if (err != hipSuccess) return err;
-  GGParams q{};
-  q.E = E; q.F = (int)F; q.d = (int)d; q.offsets = offsets;
-  q.ntn = (int)((d + kBN - 1) / kBN);
-  q.a = a_buf; q.lda = (int)F;
-  q.b = static_cast<const uint16_t*>(w2); q.ldb = (int)F; q.b_estride = static_cast<size_t>(d) * F;
-  q.K = (int)F;
-  q.scale = row_scale;
-  q.out = static_cast<uint16_t*>(y_perm);
-  return launch(gg_kernel<EPI_FC2>, dim3(tiles_bound(N, E, kBM) * q.ntn), dim3(kGT), lds, stream, q);
-}
-
-extern "C" moe_status moe_grouped_swiglu_fwd(hipStream_t stream, moe_dtype dt, int64_t N,
-                                             int64_t d, int64_t F, int32_t E,
-                                             const void* x_perm, const void* w1, const void* w2,
-                                             const int32_t* expert_offsets,
-                                             const float* row_scale, void* y_perm,
-                                             void* gu_save, void* ws, size_t ws_bytes) {
-  moe_status st = check_common(dt, N, d, F, E);
-  if (st != MOE_OK) return st;
-  if (!x_perm || !w1 || !w2 || !expert_offsets || !y_perm) return MOE_ERR_INVALID_ARG;
-  if (!aligned16(x_perm) || !aligned16(w1) || !aligned16(w2) || !aligned16(expert_offsets) ||
-      !aligned16(row_scale) || !aligned16(y_perm) || !aligned16(gu_save) || !aligned16(ws))
-    return MOE_ERR_ALIGNMENT;
-  if (!ws || ws_bytes < moe_grouped_swiglu_fwd_workspace_size(N, F, dt)) return MOE_ERR_WORKSPACE;
-  if (N == 0) return MOE_OK;
-  if (dt == MOE_BF16) {
-    return hip_status(launch_fwd_bf16(stream, N, d, F, E, x_perm, w1, w2, expert_offsets,
-                                      row_scale, y_perm, gu_save, static_cast<uint16_t*>(ws),
-                                      true));
-  }
-  float* a_buf = static_cast<float*>(ws);
-  const int ntn1 = (int)((F + 31) / 32);
-  hipError_t err = launch(gg_f32_kernel<EPI_FC1>, dim3(tiles_bound(N, E, kFM) * ntn1), dim3(256), 0,
-                          stream, E, (int)F, (int)d, (int)d, ntn1, expert_offsets,
-                          static_cast<const float*>(x_perm), (int)d, static_cast<const float*>(w1),
-                          (int)d, static_cast<size_t>(2 * F) * d, (const float*)nullptr, a_buf,
-                          static_cast<float*>(gu_save));
-  if (err == hipSuccess) {
-    const int ntn2 = (int)((d + kFN - 1) / kFN);
-    err = launch(gg_f32_kernel<EPI_FC2>, dim3(tiles_bound(N, E, kFM) * ntn2), dim3(256), 0, stream,
-                 E, (int)F, (int)d, (int)F, ntn2, expert_offsets, (const float*)a_buf, (int)F,
-                 static_cast<const float*>(w2), (int)F, static_cast<size_t>(d) * F, row_scale,
-                 static_cast<float*>(y_perm), (float*)nullptr);
-  }
-  return hip_status(err);
-}
-
 extern "C" moe_status moe_grouped_swiglu_bwd(hipStream_t stream, moe_dtype dt, int64_t N,
                                              int64_t d, int64_t F, int32_t E,
                                              const void* dy_perm, const void* x_perm,
@@ -617,7 +307,7 @@ extern "C" moe_status moe_grouped_swiglu_bwd(hipStream_t stream, moe_dtype dt, i
                                              const float* row_scale, int32_t accumulate,
                                              void* dx_perm, float* dw1, float* dw2, void* ws,
                                              size_t ws_bytes) {
-  moe_status st = check_common(dt, N, d, F, E);
+  moe_status st = moe_grouped_check(dt, N, d, F, E);
   if (st != MOE_OK) return st;
   if (dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (!dy_perm || !x_perm || !w1 || !w2 || !expert_offsets || !dx_perm || !dw1 || !dw2)
@@ -640,8 +330,8 @@ extern "C" moe_status moe_grouped_swiglu_bwd(hipStream_t stream, moe_dtype dt, i
   if (recompute && N > 0) {
     uint16_t* gu_r = reinterpret_cast<uint16_t*>(wsb + off);
     // fc1 again: its SwiGLU output goes to As (overwritten below), G,U to gu_r
-    err = launch_fwd_bf16(stream, N, d, F, E, x_perm, w1, w2, expert_offsets, nullptr, nullptr,
-                          gu_r, As, false);
+    err = launch_grouped_fwd_bf16(stream, N, d, F, E, x_perm, w1, w2, expert_offsets, nullptr,
+                                  nullptr, gu_r, As, false);
     gu = gu_r;
   }
   const size_t lds = 4 * kTileElems * sizeof(uint16_t);

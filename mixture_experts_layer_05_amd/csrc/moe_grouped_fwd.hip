@@ -1,0 +1,417 @@
+// Grouped SwiGLU expert FFN, forward: fc1 + SwiGLU, then fc2 + row scale.
+//
+// Passages: "Megatron-Bridge 深度剖析", section "计算融合 / Grouped GEMM" (all
+// experts' GEMMs in one launch over segments of different length, expert
+// weights stored back to back), section "权重映射策略" (GatedMLPMapping:
+// linear_fc1 = [gate_proj; up_proj], (2*ffn, hidden)) and "Motivation"
+// (SwiGLU experts with gate_proj, up_proj, down_proj).
+//
+// bf16 kernel (gfx950): one workgroup = 8 wavefronts (2 x 4) = one output
+// tile of 128 token rows x 256 weight rows (fc1: 128 gate rows + the 128
+// matching up rows; fc2: 256 output columns); each wave computes 64 x 64
+// with 2 x 2 v_mfma_f32_32x32x16_bf16 accumulators, two waves per SIMD.
+//   * operand tiles go global -> LDS directly (buffer_load_dwordx4 ... lds):
+//     no staging registers, so a 4-deep ring of K tiles (32 wide) is in
+//     flight per workgroup; each wave fills one 1 KB block of the A tile and
+//     two of the B tile per K tile (16 rows x 64 bytes each);
+//   * the LDS layout is [row][4 x 16-byte chunks] with chunk index XOR f(r),
+//     f = (r1 ^ r3) | r2 << 1 (r_i = bit i of the row): lane l of a block
+//     fetches the chunk that lands at position l, and the MFMA operand reads
+//     (16 consecutive rows, one chunk) are free of bank conflicts with 32 or
+//     64 banks;
+//   * addresses are a buffer descriptor, a loop-invariant per-lane offset
+//     and a scalar K offset; a chunk past K gets an offset past the end of
+//     the buffer, which reads as zero, so K tails need no branches;
+//   * a wave whose 32-row blocks lie past the end of the expert's segment
+//     skips their MFMAs;
+//   * tiles are decoded on the device from expert_offsets and handed to
+//     XCDs in contiguous ranges (the row tiles sharing a weight panel run
+//     together on one XCD and share its L2);
+//   * fc1's epilogue computes silu(G) * U in registers (gate and up of the
+//     same f land in the same lane); fc2's multiplies by the row's routing
+//     weight.
+#include "moe_gemm_common.h"
+
+namespace moe {
+
+constexpr int kFwdThreads = 512;
+constexpr int kFwdBM = 128;                   // token rows per tile
+constexpr int kFwdBN = 256;                   // weight rows per tile
+constexpr int kFwdBK = 32;
+constexpr int kStages = 4;                    // LDS ring depth (K tiles)
+constexpr int kATileE = kFwdBM * kFwdBK;      // bf16 per stage
+constexpr int kBTileE = kFwdBN * kFwdBK;
+constexpr int kStageE = kATileE + kBTileE;
+constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format
+constexpr int kOob = 0x7fff0000;              // offset past any buffer: reads zero
+
+enum FwdEpi { FWD_FC1 = 0, FWD_FC2 = 1 };
+
+struct FwdParams {
+  int E, F, d, K, ntn;
+  const int32_t* offsets;
+  const uint16_t* a;                          // token rows [N, K]
+  int lda;
+  const uint16_t* b;                          // weights, expert-major
+  int ldb;
+  size_t b_estride;
+  const float* scale;                         // [N] or NULL
+  uint16_t* out;                              // FC1: A [N, F]; FC2: Y [N, d]
+  uint16_t* out2;                             // FC1: [G | U] [N, 2F] or NULL
+};
+
+__device__ __forceinline__ int swz_f(int r) {
+  return (((r >> 1) ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1);
+}
+// staged tile element offset (bf16 units) of row r, 16-byte chunk kc
+__device__ __forceinline__ int swz(int r, int kc) { return r * kFwdBK + ((kc ^ swz_f(r)) << 3); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One output tile.  kNRB = live 32-row blocks of this wave (0..2).
+template <int kEpi, int kNRB>
+__device__ __forceinline__ void ggf_tile(const FwdParams& p, const TileIdx& ti, uint16_t* s_lds) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int r32 = lane & 31, h = lane >> 5;
+  const int nbn = kEpi == FWD_FC1 ? kFwdBN / 2 : kFwdBN;   // output columns per tile
+  const int m0 = ti.lo + ti.mt * kFwdBM;
+  const int n0 = ti.nt * nbn;
+  const int K = p.K;
+
+  // buffer descriptors: this tile's token rows, this expert's weights
+  const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(p.a + static_cast<size_t>(m0) * p.lda), 0,
+      (ti.hi - m0) * p.lda * 2, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(p.b + static_cast<size_t>(ti.e) * p.b_estride), 0,
+      static_cast<int>(p.b_estride * 2), kRsrcWord3);
+
+  // This wave fills A block `wave` (tile rows 16 wave .. +15) and B blocks
+  // `wave` and `wave + 8`.  Lane l of a block writes LDS position l, i.e. row
+  // 16 blk + l / 4, physical chunk l % 4, so it fetches logical chunk
+  // (l % 4) ^ f(row).
+  const int lr = lane >> 2, pc = lane & 3;
+  const int last = ti.hi - 1 - m0;
+  int vo[3], kcl[3];
+  {
+    const int r = wave * 16 + lr;
+    const int kc = pc ^ swz_f(r);
+    kcl[0] = kc;
+    vo[0] = (min(r, last) * p.lda + kc * 8) * 2;   // rows past the segment: computed, dropped
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = (wave + 8 * j) * 16 + lr;
+    const int kc = pc ^ swz_f(r);
+    int wr;
+    if constexpr (kEpi == FWD_FC1) {          // B rows 0..127 gate, 128..255 up
+      int f = n0 + (r & 127);
+      f = f < p.F ? f : p.F - 1;
+      wr = r < 128 ? f : p.F + f;
+    } else {
+      wr = n0 + r;
+      wr = wr < p.d ? wr : p.d - 1;
+    }
+    kcl[1 + j] = kc;
+    vo[1 + j] = (wr * p.ldb + kc * 8) * 2;
+  }
+  const int nk = (K + kFwdBK - 1) / kFwdBK;
+
+  // fetch K tile kt (clamped to the last one) into ring slot kt % kStages
+  auto issue = [&](int kt) {
+    const int t = min(kt, nk - 1);
+    const int k0 = t * kFwdBK;
+    uint16_t* st = s_lds + (kt % kStages) * kStageE;
+    const int so = k0 * 2;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const int v = (k0 + kcl[j] * 8 < K) ? vo[j] : kOob;
+      uint16_t* dst = (j == 0) ? st + wave * 16 * kFwdBK
+                               : st + kATileE + (wave + 8 * (j - 1)) * 16 * kFwdBK;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(j == 0 ? rs_a : rs_b,
+                                               (lds_void*)(dst), 16, v, so, 0, 0);
+    }
+  };
+
+  // this wave's operand rows in the staged tiles
+  int a_rd[2], b_rd[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) a_rd[i] = wm * 64 + i * 32 + r32;
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+    b_rd[c] = (kEpi == FWD_FC1) ? (c * 128 + wn * 32 + r32)      // gate, then up
+                                : (wn * 64 + c * 32 + r32);
+
+  f32x16 acc[kNRB > 0 ? kNRB : 1][2];
+#pragma unroll
+  for (int i = 0; i < (kNRB > 0 ? kNRB : 1); ++i) acc[i][0] = acc[i][1] = f32x16{};
+
+  auto compute = [&](int slot) {
+    if constexpr (kNRB > 0) {
+      const uint16_t* As = s_lds + slot * kStageE;
+      const uint16_t* Bs = As + kATileE;
+#pragma unroll
+      for (int kk = 0; kk < kFwdBK / 16; ++kk) {
+        const int ck = 2 * kk + h;
+        bf16x8 bv[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) bv[c] = *reinterpret_cast<const bf16x8*>(Bs + swz(b_rd[c], ck));
+#pragma unroll
+        for (int rb = 0; rb < kNRB; ++rb) {
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(As + swz(a_rd[rb], ck));
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+            acc[rb][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv[c], acc[rb][c], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // ring: tiles kt+1 .. kt+3 stay in flight while tile kt is multiplied.
+  // Every wave issues 3 loads per tile; "vmcnt(6)" = this wave's loads of
+  // tile kt have landed, the barrier extends that to all waves and also
+  // guarantees that slot (kt+3) % 4 (= tile kt-1) is no longer being read.
+  // The barrier is the bare s_barrier (LDS is coherent inside the CU): a
+  // __syncthreads fence would wait for every load in flight.
+#pragma unroll
+  for (int t = 0; t < kStages - 1; ++t) issue(t);
+#pragma unroll 1
+  for (int kt = 0; kt < nk; ++kt) {
+    asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
+    issue(kt + kStages - 1);
+    compute(kt % kStages);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain the clamped extra loads
+
+  // ---------------- epilogue ------------------------------------------------
+  if constexpr (kNRB > 0) {
+#pragma unroll
+    for (int rb = 0; rb < kNRB; ++rb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * 64 + rb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (row >= ti.hi) continue;
+        const size_t rowz = static_cast<size_t>(row);
+        if constexpr (kEpi == FWD_FC1) {
+          const int f = n0 + wn * 32 + r32;
+          if (f < p.F) {
+            const float g = acc[rb][0][r], u = acc[rb][1][r];
+            p.out[rowz * p.F + f] = f32_to_bf16(siluf_(g) * u);
+            if (p.out2) {
+              p.out2[rowz * 2 * p.F + f] = f32_to_bf16(g);
+              p.out2[rowz * 2 * p.F + p.F + f] = f32_to_bf16(u);
+            }
+          }
+        } else {
+          const float sc = p.scale ? p.scale[row] : 1.0f;
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const int n = n0 + wn * 64 + c * 32 + r32;
+            if (n < p.d) p.out[rowz * p.d + n] = f32_to_bf16(acc[rb][c][r] * sc);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int kEpi>
+__global__ __launch_bounds__(kFwdThreads) void ggf_kernel(FwdParams p) {
+  extern __shared__ __align__(16) uint16_t s_lds[];   // kStages x (A tile + B tile)
+  __shared__ int s_cum[1025];
+  __shared__ int s_tmp[kFwdThreads / 64];
+  tile_prefix<kFwdThreads>(p.offsets, p.E, kFwdBM, p.ntn, s_cum, s_tmp);
+  const int total = s_cum[p.E];
+  if (static_cast<int>(blockIdx.x) >= total) return;
+  const TileIdx ti = tile_decode(p.offsets, p.E, kFwdBM, xcd_remap(blockIdx.x, total), s_cum);
+  // live 32-row blocks of this wave's 64-row half
+  const int rows = ti.hi - (ti.lo + ti.mt * kFwdBM) - (threadIdx.x >> 8) * 64;
+  const int nrb = rows > 32 ? 2 : (rows > 0 ? 1 : 0);
+  switch (nrb) {
+    case 0: ggf_tile<kEpi, 0>(p, ti, s_lds); break;
+    case 1: ggf_tile<kEpi, 1>(p, ti, s_lds); break;
+    default: ggf_tile<kEpi, 2>(p, ti, s_lds); break;
+  }
+}
+
+constexpr size_t kFwdLds = kStages * kStageE * sizeof(uint16_t);
+
+// ---------------------------------------------------------------------------
+// fp32 path (MOE_F32): LDS-tiled FMA, 64 x 64 x 16 tiles, 4 x 4 outputs per
+// thread, same tile enumeration and epilogue semantics.
+// ---------------------------------------------------------------------------
+constexpr int kFM = 64, kFN = 64, kFK = 16;
+
+template <int kEpi>
+__global__ __launch_bounds__(256) void ggf_f32_kernel(int E, int F, int d, int K, int ntn,
+                                                      const int32_t* __restrict__ offsets,
+                                                      const float* __restrict__ a, int lda,
+                                                      const float* __restrict__ b, int ldb,
+                                                      size_t b_estride,
+                                                      const float* __restrict__ scale,
+                                                      float* __restrict__ out,
+                                                      float* __restrict__ out2) {
+  __shared__ float As[kFK][kFM + 4];
+  __shared__ float Bs[kFK][kFN + 4];
+  __shared__ int s_cum[1025];
+  __shared__ int s_tmp[4];
+  const int tid = threadIdx.x;
+  tile_prefix<256>(offsets, E, kFM, ntn, s_cum, s_tmp);
+  const int total = s_cum[E];
+  if (static_cast<int>(blockIdx.x) >= total) return;
+  const TileIdx ti = tile_decode(offsets, E, kFM, blockIdx.x, s_cum);
+  const int m0 = ti.lo + ti.mt * kFM;
+  const int nt = ti.nt;
+  const float* bexp = b + static_cast<size_t>(ti.e) * b_estride;
+
+  const int ty = tid >> 4, tx = tid & 15;
+  // B-tile rows of this thread: FC1 {2tx, 2tx+1, 32+2tx, 33+2tx}; FC2 4tx..4tx+3
+  int bcol[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    bcol[j] = (kEpi == FWD_FC1) ? ((j >> 1) * 32 + 2 * tx + (j & 1)) : (4 * tx + j);
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += kFK) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i;          // 64 rows x 16 k
+      const int r = c >> 4, kk = c & 15;
+      const int k = k0 + kk;
+      int ar = m0 + r;
+      if (ar > ti.hi - 1) ar = ti.hi - 1;
+      As[kk][r] = k < K ? a[static_cast<size_t>(ar) * lda + k] : 0.0f;
+      int br;
+      if constexpr (kEpi == FWD_FC1) {
+        int f = nt * 32 + (r & 31);
+        if (f > F - 1) f = F - 1;
+        br = r < 32 ? f : F + f;
+      } else {
+        br = nt * kFN + r;
+        if (br > d - 1) br = d - 1;
+      }
+      Bs[kk][r] = k < K ? bexp[static_cast<size_t>(br) * ldb + k] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kFK; ++kk) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) av[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bv[j] = Bs[kk][bcol[j]];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = m0 + ty * 4 + i;
+    if (row >= ti.hi) continue;
+    const size_t rowz = static_cast<size_t>(row);
+    if constexpr (kEpi == FWD_FC1) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int f = nt * 32 + 2 * tx + j;
+        if (f < F) {
+          const float g = acc[i][j], u = acc[i][j + 2];
+          out[rowz * F + f] = siluf_(g) * u;
+          if (out2) {
+            out2[rowz * 2 * F + f] = g;
+            out2[rowz * 2 * F + F + f] = u;
+          }
+        }
+      }
+    } else {
+      const float s = scale ? scale[row] : 1.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = nt * kFN + 4 * tx + j;
+        if (n < d) out[rowz * d + n] = acc[i][j] * s;
+      }
+    }
+  }
+}
+
+hipError_t launch_grouped_fwd_bf16(hipStream_t stream, int64_t N, int64_t d, int64_t F, int32_t E,
+                                   const void* x_perm, const void* w1, const void* w2,
+                                   const int32_t* offsets, const float* row_scale, void* y_perm,
+                                   void* gu_save, uint16_t* a_buf, bool run_fc2) {
+  FwdParams p{};
+  p.E = E; p.F = (int)F; p.d = (int)d; p.offsets = offsets;
+  // fc1: [G | U] = X W1^T with the SwiGLU epilogue; 128 f per tile
+  p.ntn = (int)((F + kFwdBN / 2 - 1) / (kFwdBN / 2));
+  p.a = static_cast<const uint16_t*>(x_perm); p.lda = (int)d;
+  p.b = static_cast<const uint16_t*>(w1); p.ldb = (int)d;
+  p.b_estride = static_cast<size_t>(2 * F) * d;
+  p.K = (int)d;
+  p.out = a_buf; p.out2 = static_cast<uint16_t*>(gu_save);
+  hipError_t err = allow_lds(ggf_kernel<FWD_FC1>, kFwdLds);
+  if (err == hipSuccess) err = allow_lds(ggf_kernel<FWD_FC2>, kFwdLds);
+  if (err == hipSuccess)
+    err = launch(ggf_kernel<FWD_FC1>, dim3(tiles_bound(N, E, kFwdBM) * p.ntn), dim3(kFwdThreads),
+                 kFwdLds, stream, p);
+  if (err != hipSuccess || !run_fc2) return err;
+  // fc2: Y = (A W2^T) * row_scale; 256 output columns per tile
+  FwdParams q{};
+  q.E = E; q.F = (int)F; q.d = (int)d; q.offsets = offsets;
+  q.ntn = (int)((d + kFwdBN - 1) / kFwdBN);
+  q.a = a_buf; q.lda = (int)F;
+  q.b = static_cast<const uint16_t*>(w2); q.ldb = (int)F;
+  q.b_estride = static_cast<size_t>(d) * F;
+  q.K = (int)F;
+  q.scale = row_scale;
+  q.out = static_cast<uint16_t*>(y_perm);
+  return launch(ggf_kernel<FWD_FC2>, dim3(tiles_bound(N, E, kFwdBM) * q.ntn), dim3(kFwdThreads),
+                kFwdLds, stream, q);
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+moe_status moe_grouped_check(moe_dtype dt, int64_t N, int64_t d, int64_t F, int32_t E);
+
+extern "C" size_t moe_grouped_swiglu_fwd_workspace_size(int64_t N, int64_t F, moe_dtype dt) {
+  if (N < 0 || F < 1) return 0;
+  return static_cast<size_t>(N) * F * elt_size(dt) + 256;
+}
+
+extern "C" moe_status moe_grouped_swiglu_fwd(hipStream_t stream, moe_dtype dt, int64_t N,
+                                             int64_t d, int64_t F, int32_t E,
+                                             const void* x_perm, const void* w1, const void* w2,
+                                             const int32_t* expert_offsets,
+                                             const float* row_scale, void* y_perm,
+                                             void* gu_save, void* ws, size_t ws_bytes) {
+  moe_status st = moe_grouped_check(dt, N, d, F, E);
+  if (st != MOE_OK) return st;
+  if (!x_perm || !w1 || !w2 || !expert_offsets || !y_perm) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x_perm) || !aligned16(w1) || !aligned16(w2) || !aligned16(expert_offsets) ||
+      !aligned16(row_scale) || !aligned16(y_perm) || !aligned16(gu_save) || !aligned16(ws))
+    return MOE_ERR_ALIGNMENT;
+  if (!ws || ws_bytes < moe_grouped_swiglu_fwd_workspace_size(N, F, dt)) return MOE_ERR_WORKSPACE;
+  if (N == 0) return MOE_OK;
+  if (dt == MOE_BF16) {
+    return hip_status(launch_grouped_fwd_bf16(stream, N, d, F, E, x_perm, w1, w2, expert_offsets,
+                                              row_scale, y_perm, gu_save,
+                                              static_cast<uint16_t*>(ws), true));
+  }
+  float* a_buf = static_cast<float*>(ws);
+  const int ntn1 = (int)((F + 31) / 32);
+  hipError_t err = launch(ggf_f32_kernel<FWD_FC1>, dim3(tiles_bound(N, E, kFM) * ntn1), dim3(256),
+                          0, stream, E, (int)F, (int)d, (int)d, ntn1, expert_offsets,
+                          static_cast<const float*>(x_perm), (int)d, static_cast<const float*>(w1),
+                          (int)d, static_cast<size_t>(2 * F) * d, (const float*)nullptr, a_buf,
+                          static_cast<float*>(gu_save));
+  if (err == hipSuccess) {
+    const int ntn2 = (int)((d + kFN - 1) / kFN);
+    err = launch(ggf_f32_kernel<FWD_FC2>, dim3(tiles_bound(N, E, kFM) * ntn2), dim3(256), 0,
+                 stream, E, (int)F, (int)d, (int)F, ntn2, expert_offsets, (const float*)a_buf,
+                 (int)F, static_cast<const float*>(w2), (int)F, static_cast<size_t>(d) * F,
+                 row_scale, static_cast<float*>(y_perm), (float*)nullptr);
+  }
+  return hip_status(err);
+}
