@@ -126,7 +126,7 @@ def main():
         if ev is not None:
             ev[0].record(stream)
         idx, w, cnt, gate = moe.route(x, L.w_router, L.k, L.score, L.normalize, L.logit_bias,
-                                      L.w_gate, out=L.route_out)
+                                      L.w_gate, out=L.route_out, ws=L.route_ws)
         if ev is not None:
             ev[1].record(stream)
         off, slot, rtok, rw, xp = moe.permute(x, idx, w, L.E, out=L.perm_out, ws=L.perm_ws)

@@ -94,15 +94,18 @@ MOE_API const char* moe_status_string(moe_status s);
  *   topk_w     [T, k]  fp32      out
  *   expert_counts [E]  int32     out: tokens routed to each expert
  *   gate       [T]     fp32      out, or NULL
- * Limits: 1 <= k <= min(E, 32); 1 <= E <= 1024; d % 8 == 0; T >= 1.
- * No workspace.
+ * Limits: 1 <= k <= min(E, 32); 1 <= E <= 1024; d % 8 == 0; T >= 1;
+ * 16*T*E < 2^31.  Workspace: moe_route_workspace_size(T, d, E, dt) bytes (the
+ * fp32 logits, up to 16 K slabs).  A NaN score is never chosen; a token with fewer than k
+ * selectable scores gets index E (out of range) for the missing slots.
  * --------------------------------------------------------------------- */
+MOE_API size_t moe_route_workspace_size(int64_t T, int64_t d, int32_t E, moe_dtype dt);
 MOE_API moe_status moe_route(hipStream_t stream, moe_dtype dt, int64_t T, int64_t d,
                      int32_t E, int32_t k, moe_score_fn fn, int32_t normalize,
                      const void* x, const void* w_router,
                      const float* logit_bias, const void* w_gate,
                      int32_t* topk_idx, float* topk_w,
-                     int32_t* expert_counts, float* gate);
+                     int32_t* expert_counts, float* gate, void* ws, size_t ws_bytes);
 
 /* ------------------------------------------------------------------------
  * moe_permute -- regroup token copies into per-expert contiguous segments.
@@ -160,7 +163,8 @@ MOE_API moe_status moe_permute(hipStream_t stream, moe_dtype dt, int64_t T, int6
  *   gu_save    [N, 2F]     dt    out, or NULL: G in cols 0..F-1, U in F..2F-1
  *                                (saved for the backward)
  * Workspace: moe_grouped_swiglu_fwd_workspace_size(N, F, dt) bytes.
- * Limits: E <= 1024, d % 8 == 0, F % 8 == 0, N >= 0.
+ * Limits: E <= 1024, d % 8 == 0, F % 8 == 0, N >= 0, 4*F*d < 2^31 (one
+ * expert's fc1 weights addressable with 32-bit byte offsets).
  * --------------------------------------------------------------------- */
 MOE_API size_t moe_grouped_swiglu_fwd_workspace_size(int64_t N, int64_t F, moe_dtype dt);
 MOE_API moe_status moe_grouped_swiglu_fwd(hipStream_t stream, moe_dtype dt, int64_t N,

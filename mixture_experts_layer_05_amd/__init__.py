@@ -38,8 +38,9 @@ _sz = ctypes.c_size_t
 EXPORTED = {
     "moe_abi_version": (_i32, []),
     "moe_status_string": (ctypes.c_char_p, [_i32]),
+    "moe_route_workspace_size": (_sz, [_i64, _i64, _i32, _i32]),
     "moe_route": (_i32, [_vp, _i32, _i64, _i64, _i32, _i32, _i32, _i32,
-                         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+                         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz]),
     "moe_permute_workspace_size": (_sz, [_i64, _i32, _i32]),
     "moe_permute": (_i32, [_vp, _i32, _i64, _i64, _i32, _i32, _vp, _vp, _vp,
                            _vp, _vp, _vp, _vp, _vp, _vp, _sz]),
@@ -112,8 +113,12 @@ def _ws(nbytes: int, device) -> torch.Tensor:
 
 
 # ---------------------------------------------------------------------------
+def route_workspace_size(T, d, E, dtype):
+    return lib().moe_route_workspace_size(T, d, E, MOE_BF16 if dtype == torch.bfloat16 else MOE_F32)
+
+
 def route(x, w_router, k, score="softmax", normalize=True, logit_bias=None,
-          w_gate=None, out=None):
+          w_gate=None, out=None, ws=None):
     """-> (topk_idx [T,k] int32, topk_w [T,k] fp32, counts [E] int32, gate [T] or None)"""
     T, d = x.shape
     E = w_router.shape[0]
@@ -124,9 +129,11 @@ def route(x, w_router, k, score="softmax", normalize=True, logit_bias=None,
                torch.empty((E,), dtype=torch.int32, device=dev),
                torch.empty((T,), dtype=torch.float32, device=dev) if w_gate is not None else None)
     idx, w, cnt, gate = out
+    if ws is None:
+        ws = _ws(route_workspace_size(T, d, E, x.dtype), dev)
     _check(lib().moe_route(_stream(), _dt(x), T, d, E, k, SCORE[score], int(bool(normalize)),
                            _p(x), _p(w_router), _p(logit_bias), _p(w_gate), _p(idx), _p(w),
-                           _p(cnt), _p(gate)), "moe_route")
+                           _p(cnt), _p(gate), _p(ws), ws.numel()), "moe_route")
     return idx, w, cnt, gate
 
 
@@ -249,6 +256,7 @@ class MoELayer:
                          torch.empty((N,), dtype=f32, device=dev),
                          torch.empty((N, d), dtype=dt, device=dev))
         self.perm_ws = _ws(permute_workspace_size(T, E, k), dev)
+        self.route_ws = _ws(route_workspace_size(T, d, E, dt), dev)
         self.y_perm = torch.empty((N, d), dtype=dt, device=dev)
         self.gu = torch.empty((N, 2 * self.F), dtype=dt, device=dev) if save_gu else None
         ws_f = fwd_workspace_size(N, self.F, dt)
@@ -264,7 +272,8 @@ class MoELayer:
 
     def forward(self, x):
         idx, w, cnt, gate = route(x, self.w_router, self.k, self.score, self.normalize,
-                                  self.logit_bias, self.w_gate, out=self.route_out)
+                                  self.logit_bias, self.w_gate, out=self.route_out,
+                                  ws=self.route_ws)
         off, slot, rtok, rw, xp = permute(x, idx, w, self.E, out=self.perm_out, ws=self.perm_ws)
         grouped_swiglu_fwd(xp, self.w1, self.w2, off, row_scale=rw, out=self.y_perm,
                            gu_out=self.gu, save_gu=self.gu is not None, ws=self.ffn_ws)

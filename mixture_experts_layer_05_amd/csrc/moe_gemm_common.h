@@ -95,4 +95,12 @@ hipError_t launch_grouped_fwd_bf16(hipStream_t stream, int64_t N, int64_t d, int
                                    const int32_t* offsets, const float* row_scale, void* y_perm,
                                    void* gu_save, uint16_t* a_buf, bool run_fc2);
 
+// Router logits with the forward kernel as a one-group GEMM, K split into
+// `ksplit` slabs: logits[s][T][E] = x[:, slab s] W_r[:, slab s]^T (+ bias
+// on slab 0), fp32; offsets01 = device array {0, T}.  bf16 only.
+int router_ksplit(int64_t T, int64_t d, int32_t E);
+hipError_t launch_router_logits_bf16(hipStream_t stream, int64_t T, int64_t d, int32_t E,
+                                    const void* x, const void* w_router, const float* bias,
+                                    const int32_t* offsets01, float* logits, int ksplit);
+
 }  // namespace moe

@@ -283,8 +283,10 @@ using namespace moe;
 moe_status moe_grouped_check(moe_dtype dt, int64_t N, int64_t d, int64_t F, int32_t E) {
   if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_DTYPE;
   if (N < 0 || d < 1 || F < 1 || E < 1 || E > 1024) return MOE_ERR_SHAPE;
-  if (N >= (int64_t(1) << 31) || d >= (int64_t(1) << 24) || F >= (int64_t(1) << 24))
+  if (N >= (int64_t(1) << 31) || d >= (int64_t(1) << 20) || F >= (int64_t(1) << 20))
     return MOE_ERR_SHAPE;
+  // buffer descriptors address one expert's weights with 32-bit byte offsets
+  if (2 * F * d * 2 >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
   if (d % 8 || F % 8) return MOE_ERR_ALIGNMENT;
   return MOE_OK;
 }

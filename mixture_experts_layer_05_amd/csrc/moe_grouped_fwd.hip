@@ -9,11 +9,12 @@
 // bf16 kernel (gfx950): one workgroup = 8 wavefronts (2 x 4) = one output
 // tile of 128 token rows x 256 weight rows (fc1: 128 gate rows + the 128
 // matching up rows; fc2: 256 output columns); each wave computes 64 x 64
-// with 2 x 2 v_mfma_f32_32x32x16_bf16 accumulators, two waves per SIMD.
+// with 2 x 2 v_mfma_f32_32x32x16_bf16 accumulators, four waves per SIMD.
 //   * operand tiles go global -> LDS directly (buffer_load_dwordx4 ... lds):
-//     no staging registers, so a 4-deep ring of K tiles (32 wide) is in
-//     flight per workgroup; each wave fills one 1 KB block of the A tile and
-//     two of the B tile per K tile (16 rows x 64 bytes each);
+//     no staging registers, so a 3-deep ring of K tiles (32 wide, 72 KB)
+//     is in flight per workgroup and two workgroups share a CU (16 waves);
+//     each wave fills one 1 KB block of the A tile and two of the B tile per
+//     K tile (16 rows x 64 bytes each);
 //   * the LDS layout is [row][4 x 16-byte chunks] with chunk index XOR f(r),
 //     f = (r1 ^ r3) | r2 << 1 (r_i = bit i of the row): lane l of a block
 //     fetches the chunk that lands at position l, and the MFMA operand reads
@@ -30,6 +31,8 @@
 //   * fc1's epilogue computes silu(G) * U in registers (gate and up of the
 //     same f land in the same lane); fc2's multiplies by the row's routing
 //     weight.
+#include <algorithm>
+
 #include "moe_gemm_common.h"
 
 namespace moe {
@@ -38,14 +41,14 @@ constexpr int kFwdThreads = 512;
 constexpr int kFwdBM = 128;                   // token rows per tile
 constexpr int kFwdBN = 256;                   // weight rows per tile
 constexpr int kFwdBK = 32;
-constexpr int kStages = 4;                    // LDS ring depth (K tiles)
+constexpr int kStages = 3;                    // LDS ring depth (K tiles)
 constexpr int kATileE = kFwdBM * kFwdBK;      // bf16 per stage
 constexpr int kBTileE = kFwdBN * kFwdBK;
 constexpr int kStageE = kATileE + kBTileE;
 constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format
 constexpr int kOob = 0x7fff0000;              // offset past any buffer: reads zero
 
-enum FwdEpi { FWD_FC1 = 0, FWD_FC2 = 1 };
+enum FwdEpi { FWD_FC1 = 0, FWD_FC2 = 1, FWD_LOGITS = 2 };
 
 struct FwdParams {
   int E, F, d, K, ntn;
@@ -55,9 +58,12 @@ struct FwdParams {
   const uint16_t* b;                          // weights, expert-major
   int ldb;
   size_t b_estride;
-  const float* scale;                         // [N] or NULL
+  const float* scale;                         // FC2: [N] row scale; LOGITS: [d] column bias (or NULL)
   uint16_t* out;                              // FC1: A [N, F]; FC2: Y [N, d]
   uint16_t* out2;                             // FC1: [G | U] [N, 2F] or NULL
+  float* outf;                                // LOGITS: z [N, d] fp32 (d = output columns)
+  int ksplit;                                 // K split into gridDim.y slabs (LOGITS)
+  size_t outf_split;                          // LOGITS: elements between slabs
 };
 
 __device__ __forceinline__ int swz_f(int r) {
@@ -82,7 +88,7 @@ __device__ __forceinline__ void ggf_tile(const FwdParams& p, const TileIdx& ti, 
   // buffer descriptors: this tile's token rows, this expert's weights
   const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(p.a + static_cast<size_t>(m0) * p.lda), 0,
-      (ti.hi - m0) * p.lda * 2, kRsrcWord3);
+      min(ti.hi - m0, kFwdBM) * p.lda * 2, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(p.b + static_cast<size_t>(ti.e) * p.b_estride), 0,
       static_cast<int>(p.b_estride * 2), kRsrcWord3);
@@ -116,13 +122,17 @@ __device__ __forceinline__ void ggf_tile(const FwdParams& p, const TileIdx& ti, 
     kcl[1 + j] = kc;
     vo[1 + j] = (wr * p.ldb + kc * 8) * 2;
   }
-  const int nk = (K + kFwdBK - 1) / kFwdBK;
+  // K tiles [kt_lo, kt_hi) of this workgroup (all of them unless K is split)
+  const int nk_all = (K + kFwdBK - 1) / kFwdBK;
+  const int kchunk = (nk_all + p.ksplit - 1) / p.ksplit;
+  const int kt_lo = min(nk_all, static_cast<int>(blockIdx.y) * kchunk);
+  const int kt_hi = min(nk_all, kt_lo + kchunk);
 
-  // fetch K tile kt (clamped to the last one) into ring slot kt % kStages
+  // fetch K tile kt (clamped to the last one) into ring slot (kt - kt_lo) % kStages
   auto issue = [&](int kt) {
-    const int t = min(kt, nk - 1);
+    const int t = min(kt, kt_hi - 1);
     const int k0 = t * kFwdBK;
-    uint16_t* st = s_lds + (kt % kStages) * kStageE;
+    uint16_t* st = s_lds + ((kt - kt_lo) % kStages) * kStageE;
     const int so = k0 * 2;
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
@@ -168,19 +178,21 @@ __device__ __forceinline__ void ggf_tile(const FwdParams& p, const TileIdx& ti, 
     }
   };
 
-  // ring: tiles kt+1 .. kt+3 stay in flight while tile kt is multiplied.
-  // Every wave issues 3 loads per tile; "vmcnt(6)" = this wave's loads of
+  // ring: tiles kt+1 .. kt+2 stay in flight while tile kt is multiplied.
+  // Every wave issues 3 loads per tile; "vmcnt(3)" = this wave's loads of
   // tile kt have landed, the barrier extends that to all waves and also
-  // guarantees that slot (kt+3) % 4 (= tile kt-1) is no longer being read.
+  // guarantees that slot (kt+2) % 3 (= tile kt-1) is no longer being read.
   // The barrier is the bare s_barrier (LDS is coherent inside the CU): a
   // __syncthreads fence would wait for every load in flight.
+  if (kt_lo < kt_hi) {
 #pragma unroll
-  for (int t = 0; t < kStages - 1; ++t) issue(t);
+    for (int t = 0; t < kStages - 1; ++t) issue(kt_lo + t);
 #pragma unroll 1
-  for (int kt = 0; kt < nk; ++kt) {
-    asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
-    issue(kt + kStages - 1);
-    compute(kt % kStages);
+    for (int kt = kt_lo; kt < kt_hi; ++kt) {
+      asm volatile("s_waitcnt vmcnt(3)\n\ts_barrier" ::: "memory");
+      issue(kt + kStages - 1);
+      compute((kt - kt_lo) % kStages);
+    }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain the clamped extra loads
 
@@ -203,12 +215,21 @@ __device__ __forceinline__ void ggf_tile(const FwdParams& p, const TileIdx& ti, 
               p.out2[rowz * 2 * p.F + p.F + f] = f32_to_bf16(u);
             }
           }
-        } else {
+        } else if constexpr (kEpi == FWD_FC2) {
           const float sc = p.scale ? p.scale[row] : 1.0f;
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
             const int n = n0 + wn * 64 + c * 32 + r32;
             if (n < p.d) p.out[rowz * p.d + n] = f32_to_bf16(acc[rb][c][r] * sc);
+          }
+        } else {  // FWD_LOGITS: this K slab's fp32 partial logits (bias on slab 0)
+          float* dst = p.outf + blockIdx.y * p.outf_split;
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const int n = n0 + wn * 64 + c * 32 + r32;
+            if (n < p.d)
+              dst[rowz * p.d + n] =
+                  acc[rb][c][r] + ((p.scale && blockIdx.y == 0) ? p.scale[n] : 0.0f);
           }
         }
       }
@@ -217,7 +238,7 @@ __device__ __forceinline__ void ggf_tile(const FwdParams& p, const TileIdx& ti, 
 }
 
 template <int kEpi>
-__global__ __launch_bounds__(kFwdThreads) void ggf_kernel(FwdParams p) {
+__global__ __launch_bounds__(kFwdThreads, 2) void ggf_kernel(FwdParams p) {
   extern __shared__ __align__(16) uint16_t s_lds[];   // kStages x (A tile + B tile)
   __shared__ int s_cum[1025];
   __shared__ int s_tmp[kFwdThreads / 64];
@@ -349,6 +370,7 @@ hipError_t launch_grouped_fwd_bf16(hipStream_t stream, int64_t N, int64_t d, int
   p.b_estride = static_cast<size_t>(2 * F) * d;
   p.K = (int)d;
   p.out = a_buf; p.out2 = static_cast<uint16_t*>(gu_save);
+  p.ksplit = 1;
   hipError_t err = allow_lds(ggf_kernel<FWD_FC1>, kFwdLds);
   if (err == hipSuccess) err = allow_lds(ggf_kernel<FWD_FC2>, kFwdLds);
   if (err == hipSuccess)
@@ -365,8 +387,38 @@ hipError_t launch_grouped_fwd_bf16(hipStream_t stream, int64_t N, int64_t d, int
   q.K = (int)F;
   q.scale = row_scale;
   q.out = static_cast<uint16_t*>(y_perm);
+  q.ksplit = 1;
   return launch(ggf_kernel<FWD_FC2>, dim3(tiles_bound(N, E, kFwdBM) * q.ntn), dim3(kFwdThreads),
                 kFwdLds, stream, q);
+}
+
+int router_ksplit(int64_t T, int64_t d, int32_t E) {
+  // enough K slabs for ~2 workgroups per CU, each slab at least 8 K tiles
+  const int64_t tiles = ((T + kFwdBM - 1) / kFwdBM) * ((E + kFwdBN - 1) / kFwdBN);
+  const int64_t nk = (d + kFwdBK - 1) / kFwdBK;
+  int64_t s = (512 + tiles - 1) / tiles;
+  s = std::min<int64_t>(s, std::max<int64_t>(1, nk / 8));
+  return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(s, 16)));
+}
+
+hipError_t launch_router_logits_bf16(hipStream_t stream, int64_t T, int64_t d, int32_t E,
+                                    const void* x, const void* w_router, const float* bias,
+                                    const int32_t* offsets01, float* logits, int ksplit) {
+  FwdParams p{};
+  p.E = 1; p.F = 1; p.d = E; p.offsets = offsets01;
+  p.ntn = (E + kFwdBN - 1) / kFwdBN;
+  p.a = static_cast<const uint16_t*>(x); p.lda = (int)d;
+  p.b = static_cast<const uint16_t*>(w_router); p.ldb = (int)d;
+  p.b_estride = static_cast<size_t>(E) * d;
+  p.K = (int)d;
+  p.scale = bias;
+  p.outf = logits;
+  p.ksplit = ksplit;
+  p.outf_split = static_cast<size_t>(T) * E;
+  hipError_t err = allow_lds(ggf_kernel<FWD_LOGITS>, kFwdLds);
+  if (err != hipSuccess) return err;
+  return launch(ggf_kernel<FWD_LOGITS>, dim3(tiles_bound(T, 1, kFwdBM) * p.ntn, ksplit),
+                dim3(kFwdThreads), kFwdLds, stream, p);
 }
 
 }  // namespace moe

@@ -1,242 +1,238 @@
-// moe_route: router logits (bf16 MFMA or fp32 FMA), score function,
-// wavefront top-k, weight normalisation, per-expert counts, shared gate.
+// moe_route: router logits, score function, wavefront top-k, weight
+// normalisation, per-expert counts and the shared-expert gate.
 //
 // Passage: "Megatron-Bridge 深度剖析", section "MoE 加速深度剖析 / Expert
 // Parallel 基础", step 1 of the diagram: the router turns each token into
 // its top-k experts with scores (top-6 sigmoid in the example); the score
 // function is a TransformerConfig choice (section "Megatron-Core 架构速览").
 //
-// One workgroup = 4 wavefronts = kRouteTM tokens.
-//   phase 1: logits tile z[kRouteTM][E] into LDS.  bf16: each wave owns
-//            32-expert column blocks and runs v_mfma_f32_32x32x16_bf16 over d
-//            with operands loaded straight from global memory (64 contiguous
-//            bytes per lane per step).  fp32: one dot product per thread.
-//   phase 2: each wave takes tokens in turn; lane l holds the scores of
-//            experts l, l+64, ...; k rounds of a wave-wide arg-max (ties to
-//            the lower expert index) pick the experts in descending order.
-//   phase 3: the block's LDS histogram is added to the global counts with
-//            integer atomics (order-independent, so deterministic).
-#include "moe_internal.h"
+//   1. route_init: write the one-group offsets {0, T} for the GEMM;
+//   2. logits z[T, E] (fp32, in the workspace): bf16 runs the grouped-GEMM
+//      forward kernel as a one-group GEMM with a bias epilogue (MFMA, LDS
+//      ring); fp32 runs a plain FMA dot product per (token, expert);
+//   3. route_topk: one wavefront per token; lane l holds the scores of
+//      experts l, l+64, ...; k rounds of a wave-wide arg-max (ties to the
+//      lower expert index) pick the experts in descending score order; the
+//      workgroup's choices are counted in LDS and written as one histogram
+//      row; the gate is a wave-wide dot product x[t] . w_gate;
+//   4. route_count: counts[e] = sum of the histogram rows (one workgroup per
+//      expert; no global atomics, so a hot expert costs nothing extra).
+#include "moe_gemm_common.h"
 
 namespace moe {
 
-constexpr int kRouteTM = 32;
-constexpr int kRouteThreads = 256;
+constexpr int kTopkThreads = 1024;  // 16 tokens per workgroup, one per wave
+constexpr int kTopkTokens = kTopkThreads / 64;
 
-__global__ void zero_i32_kernel(int32_t* p, int n) {
-  int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0;
+__global__ void route_init_kernel(int32_t* offsets01, int T) {
+  if (threadIdx.x == 0) { offsets01[0] = 0; offsets01[1] = T; }
+}
+
+__global__ __launch_bounds__(256) void route_logits_f32_kernel(
+    int T, int d, int E, const float* __restrict__ x, const float* __restrict__ wr,
+    const float* __restrict__ bias, float* __restrict__ z) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= static_cast<int64_t>(T) * E) return;
+  const int t = static_cast<int>(idx / E), e = static_cast<int>(idx - static_cast<int64_t>(t) * E);
+  const float4* xr = reinterpret_cast<const float4*>(x + static_cast<size_t>(t) * d);
+  const float4* wrr = reinterpret_cast<const float4*>(wr + static_cast<size_t>(e) * d);
+  float acc = 0.0f;
+  for (int i = 0; i < d / 4; ++i) {
+    const float4 a = xr[i], b = wrr[i];
+    acc = fmaf(a.x, b.x, acc);
+    acc = fmaf(a.y, b.y, acc);
+    acc = fmaf(a.z, b.z, acc);
+    acc = fmaf(a.w, b.w, acc);
+  }
+  z[idx] = acc + (bias ? bias[e] : 0.0f);
+}
+
+// One wavefront per token.  kPer = scores held per lane (E <= 64 kPer).
+template <bool kBF16, int kPer>
+__global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
+    int T, int d, int E, int k, int score_fn, int normalize, int nslab, const float* __restrict__ z,
+    const void* __restrict__ xv, const void* __restrict__ wgv, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w, int32_t* __restrict__ hist, float* __restrict__ gate) {
+  extern __shared__ int s_cnt[];     // [E] histogram of this workgroup's choices
+  for (int e = threadIdx.x; e < E; e += kTopkThreads) s_cnt[e] = 0;
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kTopkTokens + (threadIdx.x >> 6);
+  if (t < T) {
+  // logits = sum of the K slabs, in slab order
+  const size_t slab = static_cast<size_t>(T) * E;
+  const float* zrow = z + static_cast<size_t>(t) * E;
+  float p[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = lane + 64 * i;
+    float v = 0.0f;
+    if (e < E)
+      for (int sl = 0; sl < nslab; ++sl) v += zrow[sl * slab + e];
+    p[i] = v;
+  }
+  if (score_fn == MOE_SCORE_SOFTMAX) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      if (lane + 64 * i < E) m = fmaxf(m, p[i]);
+    m = wave_max(m);
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      p[i] = (lane + 64 * i < E) ? expf(p[i] - m) : 0.0f;
+      s += p[i];
+    }
+    s = wave_sum(s);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) p[i] = (lane + 64 * i < E) ? p[i] / s : -INFINITY;
+  } else {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) p[i] = (lane + 64 * i < E) ? sigmoidf_(p[i]) : -INFINITY;
+  }
+  uint32_t taken = 0;
+  int my_e = E;
+  float my_p = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int bi = E;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      // strict '>' keeps the lower expert index among equal scores
+      if (!((taken >> i) & 1u) && p[i] > bv) { bv = p[i]; bi = lane + 64 * i; }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, kWave);
+      const int oi = __shfl_xor(bi, o, kWave);
+      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+    }
+    if (bi < E && (bi & 63) == lane) taken |= 1u << (bi >> 6);
+    if (lane == j) { my_e = bi; my_p = bv; }
+  }
+  float denom = 1.0f;
+  if (normalize) denom = wave_sum(lane < k ? my_p : 0.0f);
+  if (lane < k) {
+    topk_idx[static_cast<size_t>(t) * k + lane] = my_e;
+    topk_w[static_cast<size_t>(t) * k + lane] = normalize ? my_p / denom : my_p;
+    if (my_e < E) atomicAdd(&s_cnt[my_e], 1);   // LDS integer atomics: order-free
+  }
+  if (gate) {
+    float g = 0.0f;
+    if constexpr (kBF16) {
+      const uint16_t* xr = static_cast<const uint16_t*>(xv) + static_cast<size_t>(t) * d;
+      const uint16_t* wg = static_cast<const uint16_t*>(wgv);
+      for (int k8 = lane * 8; k8 < d; k8 += 512) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(xr + k8);
+        const u32x4 b = *reinterpret_cast<const u32x4*>(wg + k8);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          g = fmaf(bf16lo(a[q]), bf16lo(b[q]), g);
+          g = fmaf(bf16hi(a[q]), bf16hi(b[q]), g);
+        }
+      }
+    } else {
+      const float* xr = static_cast<const float*>(xv) + static_cast<size_t>(t) * d;
+      const float* wg = static_cast<const float*>(wgv);
+      for (int i = lane; i < d; i += 64) g = fmaf(xr[i], wg[i], g);
+    }
+    g = wave_sum(g);
+    if (lane == 0) gate[t] = sigmoidf_(g);
+  }
+  }
+  __syncthreads();
+  int32_t* hrow = hist + static_cast<size_t>(blockIdx.x) * E;
+  for (int e = threadIdx.x; e < E; e += kTopkThreads) hrow[e] = s_cnt[e];
+}
+
+// counts[e] = sum over workgroups of hist[b][e] (one workgroup per expert)
+__global__ __launch_bounds__(256) void route_count_kernel(int nblk, int E,
+                                                          const int32_t* __restrict__ hist,
+                                                          int32_t* __restrict__ counts) {
+  __shared__ int s_part[4];
+  const int e = blockIdx.x;
+  int v = 0;
+  for (int b = threadIdx.x; b < nblk; b += 256) v += hist[static_cast<size_t>(b) * E + e];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) counts[e] = s_part[0] + s_part[1] + s_part[2] + s_part[3];
 }
 
 template <bool kBF16>
-__global__ __launch_bounds__(kRouteThreads) void route_kernel(
-    int T, int d, int E, int k, int score_fn, int normalize,
-    const void* __restrict__ xv, const void* __restrict__ wrv,
-    const float* __restrict__ bias, const void* __restrict__ wgv,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    int32_t* __restrict__ counts, float* __restrict__ gate) {
-  extern __shared__ float smem[];
-  const int ldz = E + 1;
-  float* s_z = smem;                                  // [kRouteTM][E+1]
-  int* s_cnt = reinterpret_cast<int*>(smem + kRouteTM * ldz);  // [E]
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int t0 = blockIdx.x * kRouteTM;
-
-  for (int e = tid; e < E; e += kRouteThreads) s_cnt[e] = 0;
-
-  // ---------------- phase 1: logits -------------------------------------
-  if constexpr (kBF16) {
-    const uint16_t* x = static_cast<const uint16_t*>(xv);
-    const uint16_t* wr = static_cast<const uint16_t*>(wrv);
-    const int h = lane >> 5;          // which half of the 16-wide k step
-    const int r32 = lane & 31;
-    int trow = t0 + r32;
-    if (trow >= T) trow = T - 1;      // clamped rows are computed, not stored
-    const uint16_t* xrow = x + static_cast<size_t>(trow) * d;
-    const int ncb = (E + 31) / 32;
-    for (int cb = wave; cb < ncb; cb += 4) {
-      int erow = cb * 32 + r32;
-      const bool evalid = erow < E;
-      const uint16_t* wrow = wr + static_cast<size_t>(evalid ? erow : 0) * d;
-      f32x16 acc = {};
-      for (int kc = 0; kc < d; kc += 64) {
-        bf16x8 a[4], b[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int k8 = kc + 32 * h + 8 * i;
-          if (k8 < d) {
-            a[i] = *reinterpret_cast<const bf16x8*>(xrow + k8);
-            b[i] = evalid ? *reinterpret_cast<const bf16x8*>(wrow + k8) : bf16x8{};
-          } else {
-            a[i] = bf16x8{};
-            b[i] = bf16x8{};
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[i], acc, 0, 0, 0);
-      }
-      // accumulator r of lane l holds C[row][col], col = l % 32,
-      // row = 8*(r/4) + 4*(l/32) + r%4
-      if (evalid) {
-        const float bb = bias ? bias[erow] : 0.0f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = 8 * (r >> 2) + 4 * h + (r & 3);
-          s_z[row * ldz + erow] = acc[r] + bb;
-        }
-      }
-    }
-  } else {
-    const float* x = static_cast<const float*>(xv);
-    const float* wr = static_cast<const float*>(wrv);
-    for (int idx = tid; idx < kRouteTM * E; idx += kRouteThreads) {
-      const int tl = idx / E, e = idx - tl * E;
-      int trow = t0 + tl;
-      if (trow >= T) trow = T - 1;
-      const float4* xr = reinterpret_cast<const float4*>(x + static_cast<size_t>(trow) * d);
-      const float4* wrr = reinterpret_cast<const float4*>(wr + static_cast<size_t>(e) * d);
-      float acc = 0.0f;
-      for (int i = 0; i < d / 4; ++i) {
-        const float4 a = xr[i], b = wrr[i];
-        acc = fmaf(a.x, b.x, acc);
-        acc = fmaf(a.y, b.y, acc);
-        acc = fmaf(a.z, b.z, acc);
-        acc = fmaf(a.w, b.w, acc);
-      }
-      s_z[tl * ldz + e] = acc + (bias ? bias[e] : 0.0f);
-    }
-  }
-  __syncthreads();
-
-  // ---------------- phase 2: scores and top-k per token ------------------
-  constexpr int kMaxPerLane = 16;     // E <= 1024
-  const int nper = (E + 63) / 64;
-  for (int tl = wave; tl < kRouteTM; tl += 4) {
-    const int t = t0 + tl;
-    if (t >= T) break;
-    float p[kMaxPerLane];
-    const float* zrow = s_z + tl * ldz;
-    if (score_fn == MOE_SCORE_SOFTMAX) {
-      float m = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < kMaxPerLane; ++i) {
-        const int e = lane + 64 * i;
-        p[i] = (i < nper && e < E) ? zrow[e] : -INFINITY;
-        m = fmaxf(m, p[i]);
-      }
-      m = wave_max(m);
-      float s = 0.0f;
-#pragma unroll
-      for (int i = 0; i < kMaxPerLane; ++i) {
-        const int e = lane + 64 * i;
-        p[i] = (i < nper && e < E) ? expf(p[i] - m) : 0.0f;
-        s += p[i];
-      }
-      s = wave_sum(s);
-#pragma unroll
-      for (int i = 0; i < kMaxPerLane; ++i) {
-        const int e = lane + 64 * i;
-        p[i] = (i < nper && e < E) ? p[i] / s : -INFINITY;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < kMaxPerLane; ++i) {
-        const int e = lane + 64 * i;
-        p[i] = (i < nper && e < E) ? sigmoidf_(zrow[e]) : -INFINITY;
-      }
-    }
-    uint32_t taken = 0;
-    int my_e = E;
-    float my_p = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      float bv = -INFINITY;
-      int bi = E;
-#pragma unroll
-      for (int i = 0; i < kMaxPerLane; ++i) {
-        const int e = lane + 64 * i;
-        // strict '>' keeps the lower expert index among equal scores
-        if (!((taken >> i) & 1u) && p[i] > bv) { bv = p[i]; bi = e; }
-      }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, kWave);
-        const int oi = __shfl_xor(bi, o, kWave);
-        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-      }
-      if (bi < E && (bi & 63) == lane) taken |= 1u << (bi >> 6);
-      if (lane == j) { my_e = bi; my_p = bv; }
-    }
-    float denom = 1.0f;
-    if (normalize) denom = wave_sum(lane < k ? my_p : 0.0f);
-    if (lane < k) {
-      topk_idx[static_cast<size_t>(t) * k + lane] = my_e;
-      topk_w[static_cast<size_t>(t) * k + lane] = normalize ? my_p / denom : my_p;
-      if (my_e < E) atomicAdd(&s_cnt[my_e], 1);
-    }
-    if (gate) {
-      float g = 0.0f;
-      if constexpr (kBF16) {
-        const uint16_t* xr = static_cast<const uint16_t*>(xv) + static_cast<size_t>(t) * d;
-        const uint16_t* wg = static_cast<const uint16_t*>(wgv);
-        for (int k8 = lane * 8; k8 < d; k8 += 512) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(xr + k8);
-          const u32x4 b = *reinterpret_cast<const u32x4*>(wg + k8);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            g = fmaf(bf16lo(a[q]), bf16lo(b[q]), g);
-            g = fmaf(bf16hi(a[q]), bf16hi(b[q]), g);
-          }
-        }
-      } else {
-        const float* xr = static_cast<const float*>(xv) + static_cast<size_t>(t) * d;
-        const float* wg = static_cast<const float*>(wgv);
-        for (int i = lane; i < d; i += 64) g = fmaf(xr[i], wg[i], g);
-      }
-      g = wave_sum(g);
-      if (lane == 0) gate[t] = sigmoidf_(g);
-    }
-  }
-  __syncthreads();
-  for (int e = tid; e < E; e += kRouteThreads)
-    if (s_cnt[e]) atomicAdd(&counts[e], s_cnt[e]);
+static auto pick_topk(int E) {
+  if (E <= 64) return route_topk_kernel<kBF16, 1>;
+  if (E <= 128) return route_topk_kernel<kBF16, 2>;
+  if (E <= 256) return route_topk_kernel<kBF16, 4>;
+  if (E <= 512) return route_topk_kernel<kBF16, 8>;
+  return route_topk_kernel<kBF16, 16>;
 }
 
 }  // namespace moe
 
 using namespace moe;
 
-extern "C" moe_status moe_route(hipStream_t stream, moe_dtype dt, int64_t T,
-                                int64_t d, int32_t E, int32_t k,
-                                moe_score_fn fn, int32_t normalize,
+static int route_slabs(moe_dtype dt, int64_t T, int64_t d, int32_t E) {
+  return dt == MOE_BF16 ? router_ksplit(T, d, E) : 1;
+}
+
+static size_t route_hist_bytes(int64_t T, int32_t E) {
+  const int64_t nblk = (T + kTopkTokens - 1) / kTopkTokens;
+  return (static_cast<size_t>(nblk) * E * sizeof(int32_t) + 255) & ~static_cast<size_t>(255);
+}
+
+extern "C" size_t moe_route_workspace_size(int64_t T, int64_t d, int32_t E, moe_dtype dt) {
+  if (T < 1 || d < 1 || E < 1 || (dt != MOE_F32 && dt != MOE_BF16)) return 0;
+  // {0, T}; per-workgroup histograms; fp32 logits, one slab per K split
+  return 256 + route_hist_bytes(T, E) +
+         static_cast<size_t>(route_slabs(dt, T, d, E)) * T * E * sizeof(float);
+}
+
+extern "C" moe_status moe_route(hipStream_t stream, moe_dtype dt, int64_t T, int64_t d,
+                                int32_t E, int32_t k, moe_score_fn fn, int32_t normalize,
                                 const void* x, const void* w_router,
                                 const float* logit_bias, const void* w_gate,
                                 int32_t* topk_idx, float* topk_w,
-                                int32_t* expert_counts, float* gate) {
+                                int32_t* expert_counts, float* gate, void* ws, size_t ws_bytes) {
   if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_DTYPE;
   if (fn != MOE_SCORE_SOFTMAX && fn != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
   if (!x || !w_router || !topk_idx || !topk_w || !expert_counts) return MOE_ERR_INVALID_ARG;
   if ((w_gate == nullptr) != (gate == nullptr)) return MOE_ERR_INVALID_ARG;
   if (T < 1 || d < 1 || E < 1 || E > 1024 || k < 1 || k > 32 || k > E) return MOE_ERR_SHAPE;
-  if (T * static_cast<int64_t>(k) >= (int64_t(1) << 31) || d >= (int64_t(1) << 30)) return MOE_ERR_SHAPE;
+  if (T * static_cast<int64_t>(k) >= (int64_t(1) << 31) || d >= (int64_t(1) << 20) ||
+      16 * T * static_cast<int64_t>(E) >= (int64_t(1) << 31) ||
+      static_cast<int64_t>(E) * d * 2 >= (int64_t(1) << 31))
+    return MOE_ERR_SHAPE;
   if (d % 8) return MOE_ERR_ALIGNMENT;
   if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || !aligned16(topk_idx) ||
-      !aligned16(topk_w) || !aligned16(expert_counts) || !aligned16(gate) || !aligned16(logit_bias))
+      !aligned16(topk_w) || !aligned16(expert_counts) || !aligned16(gate) ||
+      !aligned16(logit_bias) || !aligned16(ws))
     return MOE_ERR_ALIGNMENT;
+  if (!ws || ws_bytes < moe_route_workspace_size(T, d, E, dt)) return MOE_ERR_WORKSPACE;
 
-  hipError_t err = launch(zero_i32_kernel, dim3((E + 255) / 256), dim3(256), 0, stream,
-                          expert_counts, E);
+  int32_t* offsets01 = static_cast<int32_t*>(ws);
+  int32_t* hist = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + 256);
+  float* z = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + 256 + route_hist_bytes(T, E));
+  hipError_t err = launch(route_init_kernel, dim3(1), dim3(64), 0, stream, offsets01, (int)T);
   if (err != hipSuccess) return MOE_ERR_HIP;
-  const int nblk = static_cast<int>((T + kRouteTM - 1) / kRouteTM);
-  const size_t lds = (static_cast<size_t>(kRouteTM) * (E + 1) + E) * sizeof(float);
-  auto kern = dt == MOE_BF16 ? route_kernel<true> : route_kernel<false>;
-  err = allow_lds(kern, lds);
+  const int nslab = route_slabs(dt, T, d, E);
+  if (dt == MOE_BF16) {
+    err = launch_router_logits_bf16(stream, T, d, E, x, w_router, logit_bias, offsets01, z, nslab);
+  } else {
+    const int64_t n = T * E;
+    err = launch(route_logits_f32_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
+                 stream, (int)T, (int)d, E, static_cast<const float*>(x),
+                 static_cast<const float*>(w_router), logit_bias, z);
+  }
+  if (err != hipSuccess) return MOE_ERR_HIP;
+  auto kern = dt == MOE_BF16 ? pick_topk<true>(E) : pick_topk<false>(E);
+  const int nblk = static_cast<int>((T + kTopkTokens - 1) / kTopkTokens);
+  err = launch(kern, dim3(nblk), dim3(kTopkThreads), E * sizeof(int), stream, (int)T, (int)d, E, k,
+               (int)fn, normalize, nslab, (const float*)z, x, w_gate, topk_idx, topk_w, hist,
+               gate);
   if (err == hipSuccess)
-    err = launch(kern, dim3(nblk), dim3(kRouteThreads), lds, stream, (int)T, (int)d, E, k,
-                 (int)fn, normalize, x, w_router, logit_bias, w_gate, topk_idx, topk_w,
-                 expert_counts, gate);
+    err = launch(route_count_kernel, dim3(E), dim3(256), 0, stream, nblk, E, (const int32_t*)hist,
+                 expert_counts);
   return hip_status(err);
 }
