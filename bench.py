@@ -101,9 +101,10 @@ def main():
     import mixture_experts_layer_05_amd as moe
 
     cfg = mw.get(args.workload)
-    assert not cfg.backward, "bench steps are forward workloads"
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if cfg.backward:
+        return bench_ep_share(args, cfg, dev)
     inp = mw.make_layer_inputs(cfg)
 
     def gpu(a):
@@ -218,6 +219,69 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, cfg, min(args.cpu_sample_tokens, cfg.T))
+    print(json.dumps(out), flush=True)
+
+
+def bench_ep_share(args, cfg, dev):
+    """One expert-parallel rank's share: grouped SwiGLU forward (saving G, U)
+    plus the grouped-GEMM backward (dgrad and fp32 wgrad) per step."""
+    import numpy as np
+    import torch
+
+    import moe_workloads as mw
+    import mixture_experts_layer_05_amd as moe
+
+    inp = mw.make_ep_share_inputs(cfg)
+
+    def gpu(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    x, w1, w2, dy, off = gpu(inp.x_perm), gpu(inp.w1), gpu(inp.w2), gpu(inp.dy), gpu(inp.offsets)
+    N, d, E, F = cfg.N, cfg.d, cfg.E, cfg.F
+    y = torch.empty((N, d), dtype=torch.bfloat16, device=dev)
+    gu = torch.empty((N, 2 * F), dtype=torch.bfloat16, device=dev)
+    dx = torch.empty_like(x)
+    dw1 = torch.empty((E, 2 * F, d), dtype=torch.float32, device=dev)
+    dw2 = torch.empty((E, d, F), dtype=torch.float32, device=dev)
+    ws_f = moe._ws(moe.fwd_workspace_size(N, F, torch.bfloat16), dev)
+    ws_b = moe._ws(moe.bwd_workspace_size(N, F, torch.bfloat16, False), dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        moe.grouped_swiglu_fwd(x, w1, w2, off, None, True, out=y, gu_out=gu, ws=ws_f)
+        if ev is not None:
+            ev[1].record(stream)
+        moe.grouped_swiglu_bwd(dy, x, w1, w2, off, gu, None, False, dw1, dw2, dx_out=dx, ws=ws_b)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_f = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    t_b = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    flop_f = 6.0 * N * d * F
+    flop_b = 12.0 * N * d * F
+    out = {
+        "metric": "grouped-GEMM fwd+bwd TFLOP/s on one expert-parallel share, 1 MI355X",
+        "value": round((flop_f + flop_b) / (wall / args.steps) / 1e12, 1),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {E} local experts, {N} token-slots, d={d} ffn={F}"},
+        "fwd_ms": round(t_f, 4), "bwd_ms": round(t_b, 4),
+        "fwd_tflops": round(flop_f / t_f / 1e9, 1), "bwd_tflops": round(flop_b / t_b / 1e9, 1),
+    }
     print(json.dumps(out), flush=True)
 
 

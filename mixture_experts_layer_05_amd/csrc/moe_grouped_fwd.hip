@@ -37,16 +37,49 @@
 
 namespace moe {
 
-constexpr int kFwdThreads = 512;
-constexpr int kFwdBM = 128;                   // token rows per tile
-constexpr int kFwdBN = 256;                   // weight rows per tile
+// Tile configuration: kWM x kWN wavefronts; each wave owns kRB x kCB blocks of
+// 32 x 32 outputs.  (Overridable at build time for tuning sweeps.)
+// Default: 2 x 4 waves of 64 x 64 (tile 128 x 256), a 3-deep ring of 32-wide
+// K tiles (72 KB) and two workgroups per CU.  Measured on MI355X against
+// 256 x 256 tiles (4 x 2 waves of 64 x 128), 128 x 512 tiles, and 4- to
+// 6-deep rings with one workgroup per CU: this was the fastest on the
+// 128-expert and 256-expert workloads; more waves per CU beat deeper rings.
+#ifndef MOE_FWD_WM
+#define MOE_FWD_WM 2
+#define MOE_FWD_WN 4
+#define MOE_FWD_RB 2
+#define MOE_FWD_CB 2
+#define MOE_FWD_STAGES 3
+#define MOE_FWD_WG_PER_CU 2
+#endif
+constexpr int kWM = MOE_FWD_WM, kWN = MOE_FWD_WN, kRB = MOE_FWD_RB, kCB = MOE_FWD_CB;
+constexpr int kFwdThreads = 64 * kWM * kWN;
+constexpr int kWaves = kWM * kWN;
+constexpr int kFwdBM = kWM * kRB * 32;        // token rows per tile
+constexpr int kFwdBN = kWN * kCB * 32;        // weight rows per tile
 constexpr int kFwdBK = 32;
-constexpr int kStages = 3;                    // LDS ring depth (K tiles)
+constexpr int kStages = MOE_FWD_STAGES;       // LDS ring depth (K tiles)
 constexpr int kATileE = kFwdBM * kFwdBK;      // bf16 per stage
 constexpr int kBTileE = kFwdBN * kFwdBK;
 constexpr int kStageE = kATileE + kBTileE;
+constexpr int kABlocks = kFwdBM / 16;         // 1 KB blocks (16 rows x 64 B) per stage
+constexpr int kBBlocks = kFwdBN / 16;
+constexpr int kALoads = kABlocks / kWaves;    // per wave per K tile
+constexpr int kBLoads = kBBlocks / kWaves;
+constexpr int kLoads = kALoads + kBLoads;
+static_assert(kABlocks % kWaves == 0 && kBBlocks % kWaves == 0, "blocks per wave");
+static_assert(kCB % 2 == 0, "fc1 pairs gate and up column blocks");
 constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format
 constexpr int kOob = 0x7fff0000;              // offset past any buffer: reads zero
+
+#ifndef MOE_FWD_VMCNT
+// loads per wave per K tile x (kStages - 2) tiles left in flight: must equal
+// kLoads * (kStages - 2) (checked below)
+#define MOE_FWD_VMCNT 3
+#endif
+static_assert(MOE_FWD_VMCNT == kLoads * (kStages - 2), "ring wait count");
+#define MOE_STR2(x) #x
+#define MOE_STR(x) MOE_STR2(x)
 
 enum FwdEpi { FWD_FC1 = 0, FWD_FC2 = 1, FWD_LOGITS = 2 };
 
@@ -74,13 +107,13 @@ __device__ __forceinline__ int swz(int r, int kc) { return r * kFwdBK + ((kc ^ s
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// One output tile.  kNRB = live 32-row blocks of this wave (0..2).
+// One output tile.  kNRB = live 32-row blocks of this wave (0..kRB).
 template <int kEpi, int kNRB>
 __device__ __forceinline__ void ggf_tile(const FwdParams& p, const TileIdx& ti, uint16_t* s_lds) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave / kWN, wn = wave % kWN;
   const int r32 = lane & 31, h = lane >> 5;
-  const int nbn = kEpi == FWD_FC1 ? kFwdBN / 2 : kFwdBN;   // output columns per tile
+  constexpr int nbn = kEpi == FWD_FC1 ? kFwdBN / 2 : kFwdBN;   // output columns per tile
   const int m0 = ti.lo + ti.mt * kFwdBM;
   const int n0 = ti.nt * nbn;
   const int K = p.K;
@@ -93,34 +126,35 @@ __device__ __forceinline__ void ggf_tile(const FwdParams& p, const TileIdx& ti, 
       const_cast<uint16_t*>(p.b + static_cast<size_t>(ti.e) * p.b_estride), 0,
       static_cast<int>(p.b_estride * 2), kRsrcWord3);
 
-  // This wave fills A block `wave` (tile rows 16 wave .. +15) and B blocks
-  // `wave` and `wave + 8`.  Lane l of a block writes LDS position l, i.e. row
-  // 16 blk + l / 4, physical chunk l % 4, so it fetches logical chunk
-  // (l % 4) ^ f(row).
+  // This wave fills A blocks wave + kWaves j and B blocks wave + kWaves j
+  // (16 tile rows x 64 bytes each).  Lane l of a block writes LDS position l,
+  // i.e. row 16 blk + l / 4, physical chunk l % 4, so it fetches logical
+  // chunk (l % 4) ^ f(row).
   const int lr = lane >> 2, pc = lane & 3;
   const int last = ti.hi - 1 - m0;
-  int vo[3], kcl[3];
-  {
-    const int r = wave * 16 + lr;
+  int vo[kLoads], kcl[kLoads];
+#pragma unroll
+  for (int j = 0; j < kALoads; ++j) {
+    const int r = (wave + kWaves * j) * 16 + lr;
     const int kc = pc ^ swz_f(r);
-    kcl[0] = kc;
-    vo[0] = (min(r, last) * p.lda + kc * 8) * 2;   // rows past the segment: computed, dropped
+    kcl[j] = kc;
+    vo[j] = (min(r, last) * p.lda + kc * 8) * 2;   // rows past the segment: computed, dropped
   }
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int r = (wave + 8 * j) * 16 + lr;
+  for (int j = 0; j < kBLoads; ++j) {
+    const int r = (wave + kWaves * j) * 16 + lr;
     const int kc = pc ^ swz_f(r);
     int wr;
-    if constexpr (kEpi == FWD_FC1) {          // B rows 0..127 gate, 128..255 up
-      int f = n0 + (r & 127);
+    if constexpr (kEpi == FWD_FC1) {          // B rows: gate half, then the matching up half
+      int f = n0 + (r % (kFwdBN / 2));
       f = f < p.F ? f : p.F - 1;
-      wr = r < 128 ? f : p.F + f;
+      wr = r < kFwdBN / 2 ? f : p.F + f;
     } else {
       wr = n0 + r;
       wr = wr < p.d ? wr : p.d - 1;
     }
-    kcl[1 + j] = kc;
-    vo[1 + j] = (wr * p.ldb + kc * 8) * 2;
+    kcl[kALoads + j] = kc;
+    vo[kALoads + j] = (wr * p.ldb + kc * 8) * 2;
   }
   // K tiles [kt_lo, kt_hi) of this workgroup (all of them unless K is split)
   const int nk_all = (K + kFwdBK - 1) / kFwdBK;
@@ -135,27 +169,36 @@ __device__ __forceinline__ void ggf_tile(const FwdParams& p, const TileIdx& ti, 
     uint16_t* st = s_lds + ((kt - kt_lo) % kStages) * kStageE;
     const int so = k0 * 2;
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
+    for (int j = 0; j < kLoads; ++j) {
       const int v = (k0 + kcl[j] * 8 < K) ? vo[j] : kOob;
-      uint16_t* dst = (j == 0) ? st + wave * 16 * kFwdBK
-                               : st + kATileE + (wave + 8 * (j - 1)) * 16 * kFwdBK;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(j == 0 ? rs_a : rs_b,
-                                               (lds_void*)(dst), 16, v, so, 0, 0);
+      uint16_t* dst = (j < kALoads)
+                          ? st + (wave + kWaves * j) * 16 * kFwdBK
+                          : st + kATileE + (wave + kWaves * (j - kALoads)) * 16 * kFwdBK;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(j < kALoads ? rs_a : rs_b, (lds_void*)(dst), 16, v,
+                                               so, 0, 0);
     }
   };
 
   // this wave's operand rows in the staged tiles
-  int a_rd[2], b_rd[2];
+  int a_rd[kRB], b_rd[kCB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) a_rd[i] = wm * 64 + i * 32 + r32;
+  for (int i = 0; i < kRB; ++i) a_rd[i] = wm * kRB * 32 + i * 32 + r32;
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
-    b_rd[c] = (kEpi == FWD_FC1) ? (c * 128 + wn * 32 + r32)      // gate, then up
-                                : (wn * 64 + c * 32 + r32);
+  for (int c = 0; c < kCB; ++c) {
+    if constexpr (kEpi == FWD_FC1) {          // gate blocks, then the matching up blocks
+      const int cc = c % (kCB / 2);
+      b_rd[c] = (c < kCB / 2 ? 0 : kFwdBN / 2) + wn * (kCB / 2) * 32 + cc * 32 + r32;
+    } else {
+      b_rd[c] = wn * kCB * 32 + c * 32 + r32;
+    }
+  }
 
-  f32x16 acc[kNRB > 0 ? kNRB : 1][2];
+  constexpr int kAccRB = kNRB > 0 ? kNRB : 1;
+  f32x16 acc[kAccRB][kCB];
 #pragma unroll
-  for (int i = 0; i < (kNRB > 0 ? kNRB : 1); ++i) acc[i][0] = acc[i][1] = f32x16{};
+  for (int i = 0; i < kAccRB; ++i)
+#pragma unroll
+    for (int c = 0; c < kCB; ++c) acc[i][c] = f32x16{};
 
   auto compute = [&](int slot) {
     if constexpr (kNRB > 0) {
@@ -164,32 +207,32 @@ __device__ __forceinline__ void ggf_tile(const FwdParams& p, const TileIdx& ti, 
 #pragma unroll
       for (int kk = 0; kk < kFwdBK / 16; ++kk) {
         const int ck = 2 * kk + h;
-        bf16x8 bv[2];
+        bf16x8 bv[kCB];
 #pragma unroll
-        for (int c = 0; c < 2; ++c) bv[c] = *reinterpret_cast<const bf16x8*>(Bs + swz(b_rd[c], ck));
+        for (int c = 0; c < kCB; ++c) bv[c] = *reinterpret_cast<const bf16x8*>(Bs + swz(b_rd[c], ck));
 #pragma unroll
         for (int rb = 0; rb < kNRB; ++rb) {
           const bf16x8 av = *reinterpret_cast<const bf16x8*>(As + swz(a_rd[rb], ck));
 #pragma unroll
-          for (int c = 0; c < 2; ++c)
+          for (int c = 0; c < kCB; ++c)
             acc[rb][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv[c], acc[rb][c], 0, 0, 0);
         }
       }
     }
   };
 
-  // ring: tiles kt+1 .. kt+2 stay in flight while tile kt is multiplied.
-  // Every wave issues 3 loads per tile; "vmcnt(3)" = this wave's loads of
-  // tile kt have landed, the barrier extends that to all waves and also
-  // guarantees that slot (kt+2) % 3 (= tile kt-1) is no longer being read.
-  // The barrier is the bare s_barrier (LDS is coherent inside the CU): a
-  // __syncthreads fence would wait for every load in flight.
+  // Ring: tiles kt+1 .. kt+kStages-1 stay in flight while tile kt is
+  // multiplied.  Each wave issues kLoads loads per tile; the wait leaves the
+  // later tiles' loads in flight, the barrier extends "tile kt landed" to all
+  // waves and guarantees the slot about to be refilled (tile kt-1) is no
+  // longer read.  The barrier is the bare s_barrier (LDS is coherent inside
+  // the CU): a __syncthreads fence would wait for every load in flight.
   if (kt_lo < kt_hi) {
 #pragma unroll
     for (int t = 0; t < kStages - 1; ++t) issue(kt_lo + t);
 #pragma unroll 1
     for (int kt = kt_lo; kt < kt_hi; ++kt) {
-      asm volatile("s_waitcnt vmcnt(3)\n\ts_barrier" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(" MOE_STR(MOE_FWD_VMCNT) ")\n\ts_barrier" ::: "memory");
       issue(kt + kStages - 1);
       compute((kt - kt_lo) % kStages);
     }
@@ -202,31 +245,34 @@ __device__ __forceinline__ void ggf_tile(const FwdParams& p, const TileIdx& ti, 
     for (int rb = 0; rb < kNRB; ++rb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * 64 + rb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int row = m0 + wm * kRB * 32 + rb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
         if (row >= ti.hi) continue;
         const size_t rowz = static_cast<size_t>(row);
         if constexpr (kEpi == FWD_FC1) {
-          const int f = n0 + wn * 32 + r32;
-          if (f < p.F) {
-            const float g = acc[rb][0][r], u = acc[rb][1][r];
-            p.out[rowz * p.F + f] = f32_to_bf16(siluf_(g) * u);
-            if (p.out2) {
-              p.out2[rowz * 2 * p.F + f] = f32_to_bf16(g);
-              p.out2[rowz * 2 * p.F + p.F + f] = f32_to_bf16(u);
+#pragma unroll
+          for (int c = 0; c < kCB / 2; ++c) {
+            const int f = n0 + wn * (kCB / 2) * 32 + c * 32 + r32;
+            if (f < p.F) {
+              const float g = acc[rb][c][r], u = acc[rb][c + kCB / 2][r];
+              p.out[rowz * p.F + f] = f32_to_bf16(siluf_(g) * u);
+              if (p.out2) {
+                p.out2[rowz * 2 * p.F + f] = f32_to_bf16(g);
+                p.out2[rowz * 2 * p.F + p.F + f] = f32_to_bf16(u);
+              }
             }
           }
         } else if constexpr (kEpi == FWD_FC2) {
           const float sc = p.scale ? p.scale[row] : 1.0f;
 #pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const int n = n0 + wn * 64 + c * 32 + r32;
+          for (int c = 0; c < kCB; ++c) {
+            const int n = n0 + wn * kCB * 32 + c * 32 + r32;
             if (n < p.d) p.out[rowz * p.d + n] = f32_to_bf16(acc[rb][c][r] * sc);
           }
         } else {  // FWD_LOGITS: this K slab's fp32 partial logits (bias on slab 0)
           float* dst = p.outf + blockIdx.y * p.outf_split;
 #pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const int n = n0 + wn * 64 + c * 32 + r32;
+          for (int c = 0; c < kCB; ++c) {
+            const int n = n0 + wn * kCB * 32 + c * 32 + r32;
             if (n < p.d)
               dst[rowz * p.d + n] =
                   acc[rb][c][r] + ((p.scale && blockIdx.y == 0) ? p.scale[n] : 0.0f);
@@ -238,21 +284,31 @@ __device__ __forceinline__ void ggf_tile(const FwdParams& p, const TileIdx& ti, 
 }
 
 template <int kEpi>
-__global__ __launch_bounds__(kFwdThreads, 2) void ggf_kernel(FwdParams p) {
+__global__ __launch_bounds__(kFwdThreads, MOE_FWD_WG_PER_CU) void ggf_kernel(FwdParams p) {
   extern __shared__ __align__(16) uint16_t s_lds[];   // kStages x (A tile + B tile)
   __shared__ int s_cum[1025];
-  __shared__ int s_tmp[kFwdThreads / 64];
+  __shared__ int s_tmp[kWaves];
   tile_prefix<kFwdThreads>(p.offsets, p.E, kFwdBM, p.ntn, s_cum, s_tmp);
   const int total = s_cum[p.E];
   if (static_cast<int>(blockIdx.x) >= total) return;
   const TileIdx ti = tile_decode(p.offsets, p.E, kFwdBM, xcd_remap(blockIdx.x, total), s_cum);
-  // live 32-row blocks of this wave's 64-row half
-  const int rows = ti.hi - (ti.lo + ti.mt * kFwdBM) - (threadIdx.x >> 8) * 64;
-  const int nrb = rows > 32 ? 2 : (rows > 0 ? 1 : 0);
-  switch (nrb) {
-    case 0: ggf_tile<kEpi, 0>(p, ti, s_lds); break;
-    case 1: ggf_tile<kEpi, 1>(p, ti, s_lds); break;
-    default: ggf_tile<kEpi, 2>(p, ti, s_lds); break;
+  // live 32-row blocks of this wave's rows
+  const int rows = ti.hi - (ti.lo + ti.mt * kFwdBM) - (static_cast<int>(threadIdx.x >> 6) / kWN) * kRB * 32;
+  const int nrb = rows <= 0 ? 0 : min(kRB, (rows + 31) >> 5);
+  if constexpr (kRB == 2) {
+    switch (nrb) {
+      case 0: ggf_tile<kEpi, 0>(p, ti, s_lds); break;
+      case 1: ggf_tile<kEpi, 1>(p, ti, s_lds); break;
+      default: ggf_tile<kEpi, 2>(p, ti, s_lds); break;
+    }
+  } else {
+    switch (nrb) {
+      case 0: ggf_tile<kEpi, 0>(p, ti, s_lds); break;
+      case 1: ggf_tile<kEpi, 1>(p, ti, s_lds); break;
+      case 2: ggf_tile<kEpi, 2>(p, ti, s_lds); break;
+      case 3: ggf_tile<kEpi, 3>(p, ti, s_lds); break;
+      default: ggf_tile<kEpi, 4>(p, ti, s_lds); break;
+    }
   }
 }
 
