@@ -39,7 +39,26 @@ def parse():
     ap.add_argument("--workload", default="qwen3_30b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (scales the HBM "
+                         "byte counters FETCH_SIZE / WRITE_SIZE) and exit")
     return ap.parse_args()
+
+
+COPY_CAL_BYTES = 1 << 30
+
+
+def copy_calibration():
+    """A plain 1 GiB device-to-device copy, five times; under `rocprofv3 --pmc`
+    each dispatch should read and write COPY_CAL_BYTES."""
+    import torch
+    dev = torch.device("cuda", 0)
+    src = torch.ones(COPY_CAL_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": COPY_CAL_BYTES, "dispatches": 5}), flush=True)
 
 
 def algorithmic(cfg):
@@ -89,10 +108,11 @@ def cpu_baseline(inp, cfg, ntok, min_seconds=10.0):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(expert-parallel sharding is described in the design notes, not built).",
-              file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(expert-parallel sharding is not implemented).", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        return copy_calibration()
 
     import numpy as np
     import torch

@@ -83,6 +83,19 @@ __device__ inline TileIdx tile_decode(const int32_t* __restrict__ offsets, int E
   return t;
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format
+constexpr int kOob = 0x7fff0000;              // offset past any buffer: reads zero
+
+// Row-layout staging (K contiguous): a staged row holds 32 k = 4 chunks of
+// 16 bytes; chunk kc of row r sits at position kc ^ swz_f(r).  The MFMA
+// operand read (16 consecutive rows, one chunk per lane) and the 1 KB
+// direct-to-LDS block writes are then free of bank conflicts.
+__device__ __forceinline__ int swz_f(int r) {
+  return (((r >> 1) ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1);
+}
+
 inline int tiles_bound(int64_t N, int E, int bm) {
   return static_cast<int>((N + bm - 1) / bm + E);
 }

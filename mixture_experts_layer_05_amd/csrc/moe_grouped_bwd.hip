@@ -6,253 +6,291 @@
 // (the backward's dgrad and wgrad GEMMs) and "其他融合优化"
 // (gradient_accumulation_fusion: fp32 weight-gradient accumulation).
 //
-// bf16 engine (gfx950):
-//   * workgroup = 256 threads = 4 wavefronts in a 2 x 2 grid; block tile
-//     128 (rows of the A operand) x 128 (rows of the B operand) x 64 (K);
-//     wave tile 64 x 64 = 2 x 2 v_mfma_f32_32x32x16_bf16 accumulators;
-//   * both operands are staged in LDS as [row][k] (k contiguous), double
-//     buffered through registers; the 8-byte k-groups are XOR-swizzled by
-//     row so both the 16-byte MFMA operand reads and the transposing
-//     8-byte writes spread over the banks;
-//   * an operand whose K runs along memory rows ("K-strided": the weights
-//     in dgrad, the activations in wgrad) is read as 4 (k) x 8 (row) blocks
-//     of 16-byte loads and transposed in registers (v_perm) before the LDS
-//     write, so all four backward GEMMs use one core;
+// bf16 engine (gfx950), the forward's pipeline with a second operand layout:
+//   * workgroup = 8 wavefronts (2 x 4), output tile 128 x 256, wave tile
+//     64 x 64 = 2 x 2 v_mfma_f32_32x32x16_bf16 accumulators; a 3-deep ring
+//     of 32-wide K tiles filled global -> LDS directly (no staging
+//     registers), two workgroups per CU;
+//   * a K-contiguous operand (dY and dH rows in dgrad) is staged as in the
+//     forward: [row][32 k] with XOR-swizzled 16-byte chunks, read with
+//     ds_read_b128;
+//   * a K-strided operand (the weights in dgrad; both operands in wgrad,
+//     whose K is the expert's token rows) is staged as it lies in memory,
+//     [k][columns], and read with ds_read_b64_tr_b16, which transposes
+//     4 x 4 blocks of 16-bit elements across each 16-lane group: lane p of
+//     a group addresses k row p / 4, columns 4 (p % 4) .. +3, and receives
+//     column p at 4 consecutive k.  Two such reads give one MFMA operand
+//     (8 k for one row/column).  Chunk c of k row k sits at position
+//     c ^ 4 (k % 4), so the 4 k rows x 64 bytes of each half-wave's read
+//     fall on 64 distinct banks;
+//   * K tails: a K-contiguous chunk past K gets an offset past the buffer
+//     (reads zero); a K-strided operand's buffer descriptor is rebuilt per K
+//     tile to cover exactly the K rows left, so rows past K (the next
+//     expert's tokens in wgrad) read zero;
 //   * dgrad tiles over ragged expert segments are decoded on the device from
-//     expert_offsets (no host synchronisation) and handed to XCDs in
-//     contiguous ranges; wgrad tiles are per expert, K = the expert's rows
-//     (an empty expert yields zeros);
+//     expert_offsets and handed to XCDs in contiguous ranges; a wave whose
+//     32-row blocks lie past the segment skips their MFMAs.  wgrad tiles are
+//     per expert (an empty expert yields zeros), listed expert-major so that
+//     the tiles reading one expert's token panels share an XCD;
 //   * epilogues fuse the SwiGLU backward (dG = dA U silu'(G), dU = dA
-//     silu(G)) with the recomputed A * row_scale for the fc2 wgrad, and the
-//     fp32 (optionally accumulating) weight-gradient store.
+//     silu(G)) with A * row_scale for the fc2 wgrad, and the fp32
+//     (optionally accumulating) weight-gradient store.
 //   Deterministic: each output element is produced by one workgroup with a
 //   fixed K order; no atomics.
 #include "moe_gemm_common.h"
 
 namespace moe {
 
-constexpr int kGT = 256;          // threads per workgroup
-constexpr int kBM = 128, kBN = 128, kBK = 64;
-constexpr int kLDK = 72;          // LDS row pitch in bf16 elements
-constexpr int kTileElems = 128 * kLDK;
+constexpr int kWM = 2, kWN = 4, kRB = 2, kCB = 2;
+constexpr int kGT = 64 * kWM * kWN;           // threads per workgroup
+constexpr int kWaves = kWM * kWN;
+constexpr int kBM = kWM * kRB * 32;           // 128: rows of the A operand
+constexpr int kBN = kWN * kCB * 32;           // 256: rows of the B operand
+constexpr int kBK = 32;
+constexpr int kStages = 3;
+constexpr int kATileE = kBM * kBK;            // bf16 per stage
+constexpr int kBTileE = kBN * kBK;
+constexpr int kStageE = kATileE + kBTileE;
+constexpr int kALoads = kATileE / 512 / kWaves;   // 1 KB blocks per wave per K tile
+constexpr int kBLoads = kBTileE / 512 / kWaves;
+constexpr int kLoads = kALoads + kBLoads;
+static_assert(kALoads == 1 && kBLoads == 2, "block split");
+// loads per wave per K tile x (kStages - 2) tiles left in flight
+#define MOE_BWD_VMCNT 3
+static_assert(MOE_BWD_VMCNT == kLoads * (kStages - 2), "ring wait count");
+#define MOE_STR2(x) #x
+#define MOE_STR(x) MOE_STR2(x)
+constexpr size_t kBwdLds = kStages * kStageE * sizeof(uint16_t);
 
 enum Epi { EPI_DGRAD2 = 2, EPI_DGRAD1 = 3, EPI_WGRAD = 4 };
 
 struct GGParams {
   int E, F, d;
-  int ntn;                        // column tiles per row tile
+  int K;                          // dgrad: contraction length
+  int ntn;                        // dgrad: column tiles per row tile
+  int mts, nts;                   // wgrad: tiles per expert along rows / columns
   const int32_t* offsets;         // [E+1]
-  // A operand (rows of C)
+  // A operand (rows of C): dgrad: token rows [N, K]; wgrad: [N, out_m]
   const uint16_t* a;
   int lda;
-  // B operand (columns of C), expert 0; expert e at b + e * b_estride
+  // B operand (columns of C): dgrad: weights [E][K, ldb]; wgrad: [N, out_n]
   const uint16_t* b;
   int ldb;
   size_t b_estride;
-  int K;                          // contraction length (token-tiled GEMMs)
-  const float* scale;             // [N] row scale or NULL
+  const float* scale;             // [N] row scale or NULL (DGRAD2)
   const uint16_t* gu_in;          // [N, 2F] (DGRAD2)
   uint16_t* out;                  // DGRAD2: dH [N,2F]; DGRAD1: dX [N,d]
   uint16_t* out2;                 // DGRAD2: A*scale [N,F]
   float* outf;                    // WGRAD: dW (expert 0)
   size_t outf_estride;
-  int wg_m, wg_n;                 // WGRAD: output rows / cols per expert
+  int out_m, out_n;               // WGRAD: output rows / cols per expert
   int accumulate;
 };
 
-// element (r, k) of a staged operand; k a multiple of 4
-__device__ __forceinline__ int lds_off(int r, int k) {
-  return r * kLDK + ((((k >> 2) ^ ((r >> 2) & 14))) << 2) + (k & 3);
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((ext_vector_type(8))) short i16x8;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+
+// Raw buffer descriptor words: base address, num_records bytes, 32-bit data
+// format; offsets at or past num_records read zero.
+__device__ __forceinline__ i32x4 buf_desc(const void* base, int num_records) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4{static_cast<int>(a), static_cast<int>((a >> 32) & 0xffff), num_records,
+               static_cast<int>(kRsrcWord3)};
 }
 
-// ---- K-contiguous operand: 128 rows x 64 k; 4 x 16 B per thread ---------
-struct RegsK { u32x4 v[4]; };
-
-template <typename RowFn>
-__device__ __forceinline__ void load_kcontig(RegsK& s, const uint16_t* base, int ld, RowFn rowfn,
-                                             int k0, int K) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = threadIdx.x + kGT * i;
-    const int r = c >> 3, kk = (c & 7) * 8;
-    if (k0 + kk < K) {
-      s.v[i] = *reinterpret_cast<const u32x4*>(base + static_cast<size_t>(rowfn(r)) * ld + k0 + kk);
-    } else {
-      s.v[i] = u32x4{0, 0, 0, 0};
-    }
-  }
-}
-__device__ __forceinline__ void store_kcontig(const RegsK& s, uint16_t* lds) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = threadIdx.x + kGT * i;
-    const int r = c >> 3, kk = (c & 7) * 8;
-    *reinterpret_cast<u32x4*>(lds + lds_off(r, kk)) = s.v[i];
-  }
+// 16 bytes per lane from buffer offset voff + soff into LDS at dst + 16 lane
+// (dst uniform).  Written as inline asm so that the compiler does not track
+// it as an LDS write: it would otherwise drain every load in flight before
+// each transposed LDS read (which it cannot tell apart from the ring slot
+// being filled).  Ordering is the ring's own wait + barrier, which clobber
+// memory.
+__device__ __forceinline__ void dma16(const i32x4& desc, uint16_t* dst, int voff, int soff) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(dst))));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(m0), "v"(voff), "s"(desc), "s"(soff)
+               : "memory", "m0");
 }
 
-// ---- K-strided operand: element (k, r) at base + krow(k) * ld + col0 + r -
-// thread covers k = 4*kb .. 4*kb+3 and rows r = 8*rb .. 8*rb+7
-__device__ __forceinline__ void load_kstrided(RegsK& s, const uint16_t* base, int ld, int krow0,
-                                              int kvalid, int col0, int ncols, int k0) {
-  const int rb = threadIdx.x & 15, kb = threadIdx.x >> 4;
-  const int c = col0 + rb * 8;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int k = k0 + kb * 4 + q;
-    if (k < kvalid && c < ncols) {
-      s.v[q] = *reinterpret_cast<const u32x4*>(base + static_cast<size_t>(krow0 + k) * ld + c);
-    } else {
-      s.v[q] = u32x4{0, 0, 0, 0};
-    }
-  }
-}
-__device__ __forceinline__ void store_kstrided(const RegsK& s, uint16_t* lds) {
-  const int rb = threadIdx.x & 15, kb = threadIdx.x >> 4;
-#pragma unroll
-  for (int rr = 0; rr < 8; ++rr) {
-    const uint32_t sel = (rr & 1) ? 0x07060302u : 0x05040100u;
-    const int w = rr >> 1;
-    u32x2 o;
-    o[0] = __builtin_amdgcn_perm(s.v[1][w], s.v[0][w], sel);
-    o[1] = __builtin_amdgcn_perm(s.v[3][w], s.v[2][w], sel);
-    *reinterpret_cast<u32x2*>(lds + lds_off(rb * 8 + rr, kb * 4)) = o;
-  }
+// row-layout staged element offset of row r, 16-byte chunk kc
+__device__ __forceinline__ int swz(int r, int kc) { return r * kBK + ((kc ^ swz_f(r)) << 3); }
+
+// MFMA operand (lane l: row R + l % 32, k = 16 kk + 8 (l / 32) .. +7) from a
+// row-layout staged tile
+__device__ __forceinline__ bf16x8 frag_row(const uint16_t* T, int R, int kk, int lane) {
+  return *reinterpret_cast<const bf16x8*>(T + swz(R + (lane & 31), 2 * kk + (lane >> 5)));
 }
 
-// ---- one staged K tile through the MFMAs ----------------------------------
-__device__ __forceinline__ void mfma_tile(const uint16_t* As, const uint16_t* Bs, f32x16 (&acc)[2][2],
-                                          int wm, int wn, int lane) {
-  const int r32 = lane & 31, h = lane >> 5;
-#pragma unroll
-  for (int kk = 0; kk < kBK / 16; ++kk) {
-    const int ko = kk * 16 + 8 * h;
-    bf16x8 a0 = *reinterpret_cast<const bf16x8*>(As + lds_off(wm * 64 + r32, ko));
-    bf16x8 a1 = *reinterpret_cast<const bf16x8*>(As + lds_off(wm * 64 + 32 + r32, ko));
-    bf16x8 b0 = *reinterpret_cast<const bf16x8*>(Bs + lds_off(wn * 32 + r32, ko));
-    bf16x8 b1 = *reinterpret_cast<const bf16x8*>(Bs + lds_off(64 + wn * 32 + r32, ko));
-    acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0][0], 0, 0, 0);
-    acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[0][1], 0, 0, 0);
-    acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1][0], 0, 0, 0);
-    acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[1][1], 0, 0, 0);
-  }
+// Per-lane part of a transposed read's LDS offset for the operand rows
+// starting at R (a multiple of 32) of a [kBK][kW] staged tile: k row
+// 8 (l / 32) + (l % 16) / 4, column R + 16 ((l / 16) % 2) + 4 (l % 4),
+// chunk XOR 4 (k % 4) with k % 4 = (l % 16) / 4.
+template <int kW>
+__device__ __forceinline__ int tr_base(int R, int lane) {
+  const int q = lane & 15, g = lane >> 4;
+  const int krow = 8 * (g >> 1) + (q >> 2);
+  const int col = R + 16 * (g & 1) + 4 * (q & 3);
+  return krow * kW + ((((col >> 3) ^ ((q >> 2) << 2))) << 3) + (col & 7);
+}
+// the same operand as frag_row, from a [kBK][kW] staged tile
+template <int kW>
+__device__ __forceinline__ bf16x8 frag_tr(const uint16_t* T, int base, int kk) {
+  const uint16_t* p0 = T + base + 16 * kk * kW;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 4 * kW));
+  const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
 }
 
-template <int kEpi>
-__global__ __launch_bounds__(kGT, 2) void gg_kernel(GGParams p) {
-  extern __shared__ __align__(16) uint16_t lds[];
-  uint16_t* As0 = lds;
-  uint16_t* Bs0 = lds + kTileElems;
-  uint16_t* As1 = lds + 2 * kTileElems;
-  uint16_t* Bs1 = lds + 3 * kTileElems;
-  __shared__ int s_cum[1025];
-  __shared__ int s_tmp[4];
-
+// One output tile.  dgrad: rows [m0, min(m0 + kBM, hi)) of expert e's
+// segment [lo, hi), output columns from n0.  wgrad: output rows from m0 and
+// columns from n0 of dW[e], K = the segment's token rows.  kNRB = live
+// 32-row blocks of this wave (dgrad; wgrad passes kRB).
+template <int kEpi, int kNRB>
+__device__ __forceinline__ void ggb_tile(const GGParams& p, int e, int lo, int hi, int m0, int n0,
+                                         uint16_t* s_lds) {
+  constexpr bool kATr = kEpi == EPI_WGRAD;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / kWN, wn = wave % kWN;
+  const int r32 = lane & 31, h = lane >> 5;
+  const int K = kATr ? hi - lo : p.K;
 
-  int e, m0, n0, seg_lo, seg_hi, klen;
-  if constexpr (kEpi == EPI_WGRAD) {
-    const int tm = (p.wg_m + kBM - 1) / kBM, tn = (p.wg_n + kBN - 1) / kBN;
-    const int per_e = tm * tn;
-    e = blockIdx.x / per_e;
-    if (e >= p.E) return;
-    const int local = blockIdx.x - e * per_e;
-    m0 = (local / tn) * kBM;
-    n0 = (local % tn) * kBN;
-    seg_lo = p.offsets[e];
-    seg_hi = p.offsets[e + 1];
-    klen = seg_hi - seg_lo;
+  // --- A operand loads: block `wave` of the A tile --------------------------
+  // K-contiguous: one descriptor over the tile's rows (unused when K-strided)
+  const i32x4 rs_a = buf_desc(p.a + static_cast<size_t>(m0) * p.lda, min(hi - m0, kBM) * p.lda * 2);
+  const uint16_t* a_kbase = nullptr;          // K-strided: element (k, col) at a_kbase + k lda + col
+  int vo_a, kcl_a = 0;
+  if constexpr (kATr) {
+    // [32 k][128 columns]: 256-byte k rows, 4 per block
+    const int krow = wave * 4 + (lane >> 4);
+    const int lc = (lane & 15) ^ ((krow & 3) << 2);
+    vo_a = (krow * p.lda + m0 + 8 * lc) * 2;
+    a_kbase = p.a + static_cast<size_t>(lo) * p.lda;
   } else {
-    tile_prefix<kGT>(p.offsets, p.E, kBM, p.ntn, s_cum, s_tmp);
-    const int total = s_cum[p.E];
-    if (static_cast<int>(blockIdx.x) >= total) return;
-    const TileIdx ti = tile_decode(p.offsets, p.E, kBM, xcd_remap(blockIdx.x, total), s_cum);
-    e = ti.e;
-    seg_lo = ti.lo;
-    seg_hi = ti.hi;
-    m0 = seg_lo + ti.mt * kBM;
-    n0 = ti.nt * kBN;
-    klen = p.K;
+    // [128 rows][32 k], 16 rows per block
+    const int r = wave * 16 + (lane >> 2);
+    kcl_a = (lane & 3) ^ swz_f(r);
+    vo_a = (min(r, hi - 1 - m0) * p.lda + kcl_a * 8) * 2;   // rows past the segment: dropped
+  }
+  // --- B operand loads: blocks wave, wave + 8 of the [32 k][256 columns] tile
+  const uint16_t* b_kbase = kATr ? p.b + static_cast<size_t>(lo) * p.ldb
+                                 : p.b + static_cast<size_t>(e) * p.b_estride;
+  int vo_b[kBLoads];
+#pragma unroll
+  for (int j = 0; j < kBLoads; ++j) {
+    const int krow = (wave + kWaves * j) * 2 + (lane >> 5);   // 512-byte k rows, 2 per block
+    const int lc = (lane & 31) ^ ((krow & 3) << 2);
+    vo_b[j] = (krow * p.ldb + n0 + 8 * lc) * 2;
   }
 
-  const uint16_t* bexp = p.b + static_cast<size_t>(e) * p.b_estride;
-  const int last_row = seg_hi - 1;
-  auto arow = [&](int r) { const int g = m0 + r; return g <= last_row ? g : last_row; };
-  auto load = [&](RegsK& ra, RegsK& rb, int k0) {
-    if constexpr (kEpi == EPI_DGRAD2) {
-      // A = dY rows (K = d contiguous); B = W2[e] (d x F): element (k=n, r=f)
-      load_kcontig(ra, p.a, p.lda, arow, k0, klen);
-      load_kstrided(rb, bexp, p.ldb, 0, klen, n0, p.F, k0);
-    } else if constexpr (kEpi == EPI_DGRAD1) {
-      // A = dH rows (K = 2F contiguous); B = W1[e] (2F x d): element (k=j, r=col)
-      load_kcontig(ra, p.a, p.lda, arow, k0, klen);
-      load_kstrided(rb, bexp, p.ldb, 0, klen, n0, p.d, k0);
+  const int nk = (K + kBK - 1) / kBK;
+  auto issue = [&](int kt) {
+    const int t = min(kt, nk - 1);
+    const int k0 = t * kBK;
+    const int krows = min(kBK, K - k0);
+    uint16_t* st = s_lds + (kt % kStages) * kStageE;
+    if constexpr (kATr) {
+      dma16(buf_desc(a_kbase + static_cast<size_t>(k0) * p.lda, krows * p.lda * 2),
+            st + wave * 512, vo_a, 0);
     } else {
-      // WGRAD: both operands K-strided over the expert's token rows
-      load_kstrided(ra, p.a, p.lda, seg_lo, klen, m0, p.wg_m, k0);
-      load_kstrided(rb, p.b, p.ldb, seg_lo, klen, n0, p.wg_n, k0);
+      dma16(rs_a, st + wave * 512, (k0 + kcl_a * 8 < K) ? vo_a : kOob, k0 * 2);
+    }
+    const i32x4 rb = buf_desc(b_kbase + static_cast<size_t>(k0) * p.ldb, krows * p.ldb * 2);
+#pragma unroll
+    for (int j = 0; j < kBLoads; ++j)
+      dma16(rb, st + kATileE + (wave + kWaves * j) * 512, vo_b[j], 0);
+  };
+
+  // this wave's operand read offsets
+  int a_tr[kRB], b_tr[kCB];
+#pragma unroll
+  for (int i = 0; i < kRB; ++i) a_tr[i] = tr_base<kBM>(wm * kRB * 32 + i * 32, lane);
+#pragma unroll
+  for (int c = 0; c < kCB; ++c) b_tr[c] = tr_base<kBN>(wn * kCB * 32 + c * 32, lane);
+
+  constexpr int kAccRB = kNRB > 0 ? kNRB : 1;
+  f32x16 acc[kAccRB][kCB];
+#pragma unroll
+  for (int i = 0; i < kAccRB; ++i)
+#pragma unroll
+    for (int c = 0; c < kCB; ++c) acc[i][c] = f32x16{};
+
+  auto compute = [&](int slot) {
+    if constexpr (kNRB > 0) {
+      const uint16_t* As = s_lds + slot * kStageE;
+      const uint16_t* Bs = As + kATileE;
+#pragma unroll
+      for (int kk = 0; kk < kBK / 16; ++kk) {
+        bf16x8 bv[kCB];
+#pragma unroll
+        for (int c = 0; c < kCB; ++c) bv[c] = frag_tr<kBN>(Bs, b_tr[c], kk);
+#pragma unroll
+        for (int rb = 0; rb < kNRB; ++rb) {
+          const bf16x8 av = kATr ? frag_tr<kBM>(As, a_tr[rb], kk)
+                                 : frag_row(As, wm * kRB * 32 + rb * 32, kk, lane);
+#pragma unroll
+          for (int c = 0; c < kCB; ++c)
+            acc[rb][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv[c], acc[rb][c], 0, 0, 0);
+        }
+      }
     }
   };
-  auto store = [&](const RegsK& ra, const RegsK& rb, uint16_t* As, uint16_t* Bs) {
-    if constexpr (kEpi == EPI_WGRAD) store_kstrided(ra, As); else store_kcontig(ra, As);
-    store_kstrided(rb, Bs);
-  };
 
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-
-  const int nk = (klen + kBK - 1) / kBK;
+  // Ring as in the forward: tiles kt+1 .. kt+kStages-1 stay in flight while
+  // tile kt is multiplied; the wait leaves the later tiles' loads in flight,
+  // the bare barrier extends "tile kt landed" to all waves and frees the
+  // slot about to be refilled.
   if (nk > 0) {
-    RegsK ra, rb;
-    load(ra, rb, 0);
-    store(ra, rb, As0, Bs0);
-    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < kStages - 1; ++t) issue(t);
+#pragma unroll 1
     for (int kt = 0; kt < nk; ++kt) {
-      const bool odd = kt & 1;
-      uint16_t* Ac = odd ? As1 : As0;
-      uint16_t* Bc = odd ? Bs1 : Bs0;
-      const bool more = kt + 1 < nk;
-      if (more) load(ra, rb, (kt + 1) * kBK);
-      mfma_tile(Ac, Bc, acc, wm, wn, lane);
-      if (more) store(ra, rb, odd ? As0 : As1, odd ? Bs0 : Bs1);
-      __syncthreads();
+      asm volatile("s_waitcnt vmcnt(" MOE_STR(MOE_BWD_VMCNT) ")\n\ts_barrier" ::: "memory");
+      issue(kt + kStages - 1);
+      compute(kt % kStages);
     }
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain the clamped extra loads
 
   // ---------------- epilogue ------------------------------------------------
-  const int r32 = lane & 31, h = lane >> 5;
+  if constexpr (kEpi == EPI_WGRAD) {
+    float* dw = p.outf + static_cast<size_t>(e) * p.outf_estride;
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
+    for (int rb = 0; rb < kRB; ++rb) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int trow = wm * 64 + mi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-      if constexpr (kEpi == EPI_WGRAD) {
-        const int row = m0 + trow;
-        if (row >= p.wg_m) continue;
-        float* dst = p.outf + static_cast<size_t>(e) * p.outf_estride + static_cast<size_t>(row) * p.wg_n;
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * kRB * 32 + rb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (row >= p.out_m) continue;
+        float* dst = dw + static_cast<size_t>(row) * p.out_n;
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const int col = n0 + c * 64 + wn * 32 + r32;
-          if (col < p.wg_n) {
-            const float v = acc[mi][c][r];
+        for (int c = 0; c < kCB; ++c) {
+          const int col = n0 + wn * kCB * 32 + c * 32 + r32;
+          if (col < p.out_n) {
+            const float v = acc[rb][c][r];
             dst[col] = p.accumulate ? dst[col] + v : v;
           }
         }
-      } else {
-        const int row = m0 + trow;
-        if (row >= seg_hi) continue;
+      }
+    }
+  } else if constexpr (kNRB > 0) {
+#pragma unroll
+    for (int rb = 0; rb < kNRB; ++rb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * kRB * 32 + rb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (row >= hi) continue;
         const size_t rowz = static_cast<size_t>(row);
         if constexpr (kEpi == EPI_DGRAD2) {
           const float s = p.scale ? p.scale[row] : 1.0f;
 #pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const int f = n0 + c * 64 + wn * 32 + r32;
+          for (int c = 0; c < kCB; ++c) {
+            const int f = n0 + wn * kCB * 32 + c * 32 + r32;
             if (f < p.F) {
-              const float da = acc[mi][c][r] * s;
+              const float da = acc[rb][c][r] * s;
               const float g = bf16_to_f32(p.gu_in[rowz * 2 * p.F + f]);
               const float u = bf16_to_f32(p.gu_in[rowz * 2 * p.F + p.F + f]);
               const float sg = sigmoidf_(g);
@@ -266,12 +304,41 @@ __global__ __launch_bounds__(kGT, 2) void gg_kernel(GGParams p) {
           }
         } else {  // EPI_DGRAD1
 #pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const int n = n0 + c * 64 + wn * 32 + r32;
-            if (n < p.d) p.out[rowz * p.d + n] = f32_to_bf16(acc[mi][c][r]);
+          for (int c = 0; c < kCB; ++c) {
+            const int n = n0 + wn * kCB * 32 + c * 32 + r32;
+            if (n < p.d) p.out[rowz * p.d + n] = f32_to_bf16(acc[rb][c][r]);
           }
         }
       }
+    }
+  }
+}
+
+template <int kEpi>
+__global__ __launch_bounds__(kGT, 2) void ggb_kernel(GGParams p) {
+  extern __shared__ __align__(16) uint16_t s_lds[];   // kStages x (A tile + B tile)
+  if constexpr (kEpi == EPI_WGRAD) {
+    const int per_e = p.mts * p.nts;
+    const int total = per_e * p.E;
+    if (static_cast<int>(blockIdx.x) >= total) return;
+    const int L = xcd_remap(blockIdx.x, total);
+    const int e = L / per_e, local = L - e * per_e;
+    const int nt = local / p.mts, mt = local - nt * p.mts;
+    ggb_tile<kEpi, kRB>(p, e, p.offsets[e], p.offsets[e + 1], mt * kBM, nt * kBN, s_lds);
+  } else {
+    __shared__ int s_cum[1025];
+    __shared__ int s_tmp[kWaves];
+    tile_prefix<kGT>(p.offsets, p.E, kBM, p.ntn, s_cum, s_tmp);
+    const int total = s_cum[p.E];
+    if (static_cast<int>(blockIdx.x) >= total) return;
+    const TileIdx ti = tile_decode(p.offsets, p.E, kBM, xcd_remap(blockIdx.x, total), s_cum);
+    const int m0 = ti.lo + ti.mt * kBM;
+    const int rows = ti.hi - m0 - (static_cast<int>(threadIdx.x >> 6) / kWN) * kRB * 32;
+    const int nrb = rows <= 0 ? 0 : min(kRB, (rows + 31) >> 5);
+    switch (nrb) {
+      case 0: ggb_tile<kEpi, 0>(p, ti.e, ti.lo, ti.hi, m0, ti.nt * kBN, s_lds); break;
+      case 1: ggb_tile<kEpi, 1>(p, ti.e, ti.lo, ti.hi, m0, ti.nt * kBN, s_lds); break;
+      default: ggb_tile<kEpi, 2>(p, ti.e, ti.lo, ti.hi, m0, ti.nt * kBN, s_lds); break;
     }
   }
 }
@@ -336,10 +403,10 @@ extern "C" moe_status moe_grouped_swiglu_bwd(hipStream_t stream, moe_dtype dt, i
                                   nullptr, gu_r, As, false);
     gu = gu_r;
   }
-  const size_t lds = 4 * kTileElems * sizeof(uint16_t);
-  if (err == hipSuccess) err = allow_lds(gg_kernel<EPI_DGRAD2>, lds);
-  if (err == hipSuccess) err = allow_lds(gg_kernel<EPI_DGRAD1>, lds);
-  if (err == hipSuccess) err = allow_lds(gg_kernel<EPI_WGRAD>, lds);
+  const size_t lds = kBwdLds;
+  if (err == hipSuccess) err = allow_lds(ggb_kernel<EPI_DGRAD2>, lds);
+  if (err == hipSuccess) err = allow_lds(ggb_kernel<EPI_DGRAD1>, lds);
+  if (err == hipSuccess) err = allow_lds(ggb_kernel<EPI_WGRAD>, lds);
   if (err == hipSuccess && N > 0) {
     // fc2 dgrad + SwiGLU backward: dH, A*scale
     GGParams p{};
@@ -348,7 +415,7 @@ extern "C" moe_status moe_grouped_swiglu_bwd(hipStream_t stream, moe_dtype dt, i
     p.a = static_cast<const uint16_t*>(dy_perm); p.lda = (int)d;
     p.b = static_cast<const uint16_t*>(w2); p.ldb = (int)F; p.b_estride = static_cast<size_t>(d) * F;
     p.K = (int)d; p.scale = row_scale; p.gu_in = gu; p.out = dH; p.out2 = As;
-    err = launch(gg_kernel<EPI_DGRAD2>, dim3(tiles_bound(N, E, kBM) * p.ntn), dim3(kGT), lds,
+    err = launch(ggb_kernel<EPI_DGRAD2>, dim3(tiles_bound(N, E, kBM) * p.ntn), dim3(kGT), lds,
                  stream, p);
   }
   if (err == hipSuccess && N > 0) {
@@ -359,7 +426,7 @@ extern "C" moe_status moe_grouped_swiglu_bwd(hipStream_t stream, moe_dtype dt, i
     p.a = dH; p.lda = (int)(2 * F);
     p.b = static_cast<const uint16_t*>(w1); p.ldb = (int)d; p.b_estride = static_cast<size_t>(2 * F) * d;
     p.K = (int)(2 * F); p.out = static_cast<uint16_t*>(dx_perm);
-    err = launch(gg_kernel<EPI_DGRAD1>, dim3(tiles_bound(N, E, kBM) * p.ntn), dim3(kGT), lds,
+    err = launch(ggb_kernel<EPI_DGRAD1>, dim3(tiles_bound(N, E, kBM) * p.ntn), dim3(kGT), lds,
                  stream, p);
   }
   if (err == hipSuccess) {
@@ -368,10 +435,10 @@ extern "C" moe_status moe_grouped_swiglu_bwd(hipStream_t stream, moe_dtype dt, i
     p.E = E; p.F = (int)F; p.d = (int)d; p.offsets = expert_offsets;
     p.a = static_cast<const uint16_t*>(dy_perm); p.lda = (int)d;
     p.b = As; p.ldb = (int)F;
-    p.wg_m = (int)d; p.wg_n = (int)F; p.outf = dw2; p.outf_estride = static_cast<size_t>(d) * F;
+    p.out_m = (int)d; p.out_n = (int)F; p.outf = dw2; p.outf_estride = static_cast<size_t>(d) * F;
+    p.mts = (int)((d + kBM - 1) / kBM); p.nts = (int)((F + kBN - 1) / kBN);
     p.accumulate = accumulate;
-    const int tiles = (int)(((d + kBM - 1) / kBM) * ((F + kBN - 1) / kBN)) * E;
-    err = launch(gg_kernel<EPI_WGRAD>, dim3(tiles), dim3(kGT), lds, stream, p);
+    err = launch(ggb_kernel<EPI_WGRAD>, dim3(p.mts * p.nts * E), dim3(kGT), lds, stream, p);
   }
   if (err == hipSuccess) {
     // fc1 wgrad: dW1[e] (2F x d) = dH^T X
@@ -379,10 +446,11 @@ extern "C" moe_status moe_grouped_swiglu_bwd(hipStream_t stream, moe_dtype dt, i
     p.E = E; p.F = (int)F; p.d = (int)d; p.offsets = expert_offsets;
     p.a = dH; p.lda = (int)(2 * F);
     p.b = static_cast<const uint16_t*>(x_perm); p.ldb = (int)d;
-    p.wg_m = (int)(2 * F); p.wg_n = (int)d; p.outf = dw1; p.outf_estride = static_cast<size_t>(2 * F) * d;
+    p.out_m = (int)(2 * F); p.out_n = (int)d; p.outf = dw1;
+    p.outf_estride = static_cast<size_t>(2 * F) * d;
+    p.mts = (int)((2 * F + kBM - 1) / kBM); p.nts = (int)((d + kBN - 1) / kBN);
     p.accumulate = accumulate;
-    const int tiles = (int)(((2 * F + kBM - 1) / kBM) * ((d + kBN - 1) / kBN)) * E;
-    err = launch(gg_kernel<EPI_WGRAD>, dim3(tiles), dim3(kGT), lds, stream, p);
+    err = launch(ggb_kernel<EPI_WGRAD>, dim3(p.mts * p.nts * E), dim3(kGT), lds, stream, p);
   }
   return hip_status(err);
 }

@@ -69,8 +69,6 @@ constexpr int kBLoads = kBBlocks / kWaves;
 constexpr int kLoads = kALoads + kBLoads;
 static_assert(kABlocks % kWaves == 0 && kBBlocks % kWaves == 0, "blocks per wave");
 static_assert(kCB % 2 == 0, "fc1 pairs gate and up column blocks");
-constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format
-constexpr int kOob = 0x7fff0000;              // offset past any buffer: reads zero
 
 #ifndef MOE_FWD_VMCNT
 // loads per wave per K tile x (kStages - 2) tiles left in flight: must equal
@@ -99,13 +97,8 @@ struct FwdParams {
   size_t outf_split;                          // LOGITS: elements between slabs
 };
 
-__device__ __forceinline__ int swz_f(int r) {
-  return (((r >> 1) ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1);
-}
 // staged tile element offset (bf16 units) of row r, 16-byte chunk kc
 __device__ __forceinline__ int swz(int r, int kc) { return r * kFwdBK + ((kc ^ swz_f(r)) << 3); }
-
-typedef __attribute__((address_space(3))) void lds_void;
 
 // One output tile.  kNRB = live 32-row blocks of this wave (0..kRB).
 template <int kEpi, int kNRB>
