@@ -96,6 +96,43 @@ __device__ __forceinline__ int swz_f(int r) {
   return (((r >> 1) ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1);
 }
 
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+
+// Raw buffer descriptor words: base address, num_records bytes, 32-bit data
+// format; offsets at or past num_records read zero.
+__device__ __forceinline__ i32x4 buf_desc(const void* base, int num_records) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4{static_cast<int>(a), static_cast<int>((a >> 32) & 0xffff), num_records,
+               static_cast<int>(kRsrcWord3)};
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(const_cast<void*>(p)))));
+}
+
+// 16 bytes per lane from buffer offset voff + soff into LDS at dst + 16 lane
+// (dst uniform).  Inline asm, so the compiler does not track it as an LDS
+// write (it would otherwise wait for every load in flight before LDS reads
+// it cannot tell apart from the slot being filled); callers order it with
+// their own s_waitcnt vmcnt + s_barrier, which clobber memory.
+__device__ __forceinline__ void dma16(const i32x4& desc, const void* dst, int voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_addr(dst)), "v"(voff), "s"(desc), "s"(soff)
+               : "memory", "m0");
+}
+
+// 4 bytes per lane into LDS at dst + 4 lane: one cache line per lane, used
+// to pull operand lines into L2 ahead of the 16-byte-per-lane loads (the
+// LDS bytes written are never read).
+__device__ __forceinline__ void dma4(const i32x4& desc, const void* dst, int voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :
+               : "s"(lds_addr(dst)), "v"(voff), "s"(desc), "s"(soff)
+               : "memory", "m0");
+}
+
 inline int tiles_bound(int64_t N, int E, int bm) {
   return static_cast<int>((N + bm - 1) / bm + E);
 }

@@ -91,31 +91,6 @@ typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
 typedef __attribute__((ext_vector_type(8))) short i16x8;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-typedef __attribute__((ext_vector_type(4))) int i32x4;
-
-// Raw buffer descriptor words: base address, num_records bytes, 32-bit data
-// format; offsets at or past num_records read zero.
-__device__ __forceinline__ i32x4 buf_desc(const void* base, int num_records) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  return i32x4{static_cast<int>(a), static_cast<int>((a >> 32) & 0xffff), num_records,
-               static_cast<int>(kRsrcWord3)};
-}
-
-// 16 bytes per lane from buffer offset voff + soff into LDS at dst + 16 lane
-// (dst uniform).  Written as inline asm so that the compiler does not track
-// it as an LDS write: it would otherwise drain every load in flight before
-// each transposed LDS read (which it cannot tell apart from the ring slot
-// being filled).  Ordering is the ring's own wait + barrier, which clobber
-// memory.
-__device__ __forceinline__ void dma16(const i32x4& desc, uint16_t* dst, int voff, int soff) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(dst))));
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :
-               : "s"(m0), "v"(voff), "s"(desc), "s"(soff)
-               : "memory", "m0");
-}
-
 // row-layout staged element offset of row r, 16-byte chunk kc
 __device__ __forceinline__ int swz(int r, int kc) { return r * kBK + ((kc ^ swz_f(r)) << 3); }
 

@@ -6,20 +6,27 @@
 // linear_fc1 = [gate_proj; up_proj], (2*ffn, hidden)) and "Motivation"
 // (SwiGLU experts with gate_proj, up_proj, down_proj).
 //
-// bf16 kernel (gfx950): one workgroup = 8 wavefronts (2 x 4) = one output
-// tile of 128 token rows x 256 weight rows (fc1: 128 gate rows + the 128
-// matching up rows; fc2: 256 output columns); each wave computes 64 x 64
-// with 2 x 2 v_mfma_f32_32x32x16_bf16 accumulators, four waves per SIMD.
+// bf16 kernel (gfx950), one tile shape per use (compile-time FwdCfg):
+//   * expert GEMMs: one workgroup of 16 wavefronts (4 x 4) per CU = one
+//     output tile of 256 token rows x 256 weight rows (fc1: 128 gate rows +
+//     the 128 matching up rows; fc2: 256 output columns); each wave computes
+//     64 x 64 with 2 x 2 v_mfma_f32_32x32x16_bf16 accumulators; K tiles are
+//     64 wide, so every staged row segment is one whole 128-byte cache line
+//     (a 32-wide K tile fetches half lines, which measured 1.5x slower from
+//     L2 into LDS), in a 2-deep ring (128 KB);
+//   * router logits (few output columns, many K slabs): two workgroups of
+//     8 wavefronts (2 x 4) per CU, tiles of 128 x 256, a 3-deep ring of
+//     32-wide K tiles (72 KB each), so that the small GEMM still fills the
+//     chip;
 //   * operand tiles go global -> LDS directly (buffer_load_dwordx4 ... lds):
-//     no staging registers, so a 3-deep ring of K tiles (32 wide, 72 KB)
-//     is in flight per workgroup and two workgroups share a CU (16 waves);
-//     each wave fills one 1 KB block of the A tile and two of the B tile per
-//     K tile (16 rows x 64 bytes each);
-//   * the LDS layout is [row][4 x 16-byte chunks] with chunk index XOR f(r),
-//     f = (r1 ^ r3) | r2 << 1 (r_i = bit i of the row): lane l of a block
-//     fetches the chunk that lands at position l, and the MFMA operand reads
-//     (16 consecutive rows, one chunk) are free of bank conflicts with 32 or
-//     64 banks;
+//     no staging registers; each 1 KB block is 16 rows x 64 bytes (32-wide
+//     K) or 8 rows x 128 bytes (64-wide K);
+//   * the LDS layout is [row][16-byte chunks] with the chunk index XOR a
+//     function of the row (f = (r1 ^ r3) | r2 << 1 for 4 chunks, (r mod 8)
+//     ^ r3 for 8 chunks; r_i = bit i of the row): lane l of a block fetches
+//     the chunk that lands at position l, and the MFMA operand reads (32
+//     consecutive rows, one chunk) and the block writes are free of bank
+//     conflicts with 32 or 64 banks;
 //   * addresses are a buffer descriptor, a loop-invariant per-lane offset
 //     and a scalar K offset; a chunk past K gets an offset past the end of
 //     the buffer, which reads as zero, so K tails need no branches;
@@ -37,47 +44,54 @@
 
 namespace moe {
 
-// Tile configuration: kWM x kWN wavefronts; each wave owns kRB x kCB blocks of
-// 32 x 32 outputs.  (Overridable at build time for tuning sweeps.)
-// Default: 2 x 4 waves of 64 x 64 (tile 128 x 256), a 3-deep ring of 32-wide
-// K tiles (72 KB) and two workgroups per CU.  Measured on MI355X against
-// 256 x 256 tiles (4 x 2 waves of 64 x 128), 128 x 512 tiles, and 4- to
-// 6-deep rings with one workgroup per CU: this was the fastest on the
-// 128-expert and 256-expert workloads; more waves per CU beat deeper rings.
+// Tile configuration: WM x WN wavefronts, each owning RB x CB blocks of
+// 32 x 32 outputs; S-deep LDS ring of BK-wide K tiles; WG workgroups per CU.
+template <int WM, int WN, int RB, int CB, int S, int BK, int WG>
+struct FwdCfg {
+  static constexpr int kWM = WM, kWN = WN, kRB = RB, kCB = CB, kStages = S, kBK = BK, kWgPerCu = WG;
+  static constexpr int kThreads = 64 * WM * WN;
+  static constexpr int kWaves = WM * WN;
+  static constexpr int kBM = WM * RB * 32;            // token rows per tile
+  static constexpr int kBN = WN * CB * 32;            // weight rows per tile
+  static constexpr int kChunks = BK / 8;              // 16-byte chunks per staged row
+  static constexpr int kRowsPerBlk = 64 / kChunks;    // staged rows per 1 KB block
+  static constexpr int kATileE = kBM * BK;            // bf16 per ring slot
+  static constexpr int kBTileE = kBN * BK;
+  static constexpr int kStageE = kATileE + kBTileE;
+  static constexpr int kALoads = kBM / kRowsPerBlk / kWaves;   // 1 KB blocks per wave per K tile
+  static constexpr int kBLoads = kBN / kRowsPerBlk / kWaves;
+  static constexpr int kLoads = kALoads + kBLoads;
+  // loads a wave may leave in flight when K tile kt must have landed
+  static constexpr int kRingWait = kLoads * (S - 2);
+  static constexpr size_t kLdsBytes = static_cast<size_t>(S) * kStageE * sizeof(uint16_t);
+  static_assert(BK == 32 || BK == 64, "K tile");
+  static_assert(S >= 2, "ring depth");
+  static_assert((kBM / kRowsPerBlk) % kWaves == 0 && (kBN / kRowsPerBlk) % kWaves == 0,
+                "blocks per wave");
+  static_assert(CB % 2 == 0, "fc1 pairs gate and up column blocks");
+  static_assert(kLdsBytes >= (1040 + 64) * sizeof(int), "tile-decode scratch fits the ring");
+  static_assert(RB == 2 || RB == 4, "live-row dispatch");
+};
+
+// Expert GEMMs.  Measured on MI355X (fc1 + fc2, bf16) against 128 x 256
+// tiles with two workgroups per CU and a 3-deep ring of 32-wide K tiles:
+// 2 to 9% faster on the 128- and 32-expert shapes with 256 to 1024 rows per
+// expert, equal on the 128-expert shape with ragged segments.  A deeper ring
+// for the weights (160 KB) and software L2 prefetch of the weight rows were
+// no faster.  (Overridable at build time for tuning sweeps.)
 #ifndef MOE_FWD_WM
-#define MOE_FWD_WM 2
+#define MOE_FWD_WM 4
 #define MOE_FWD_WN 4
 #define MOE_FWD_RB 2
 #define MOE_FWD_CB 2
-#define MOE_FWD_STAGES 3
-#define MOE_FWD_WG_PER_CU 2
+#define MOE_FWD_STAGES 2
+#define MOE_FWD_BK 64
+#define MOE_FWD_WG_PER_CU 1
 #endif
-constexpr int kWM = MOE_FWD_WM, kWN = MOE_FWD_WN, kRB = MOE_FWD_RB, kCB = MOE_FWD_CB;
-constexpr int kFwdThreads = 64 * kWM * kWN;
-constexpr int kWaves = kWM * kWN;
-constexpr int kFwdBM = kWM * kRB * 32;        // token rows per tile
-constexpr int kFwdBN = kWN * kCB * 32;        // weight rows per tile
-constexpr int kFwdBK = 32;
-constexpr int kStages = MOE_FWD_STAGES;       // LDS ring depth (K tiles)
-constexpr int kATileE = kFwdBM * kFwdBK;      // bf16 per stage
-constexpr int kBTileE = kFwdBN * kFwdBK;
-constexpr int kStageE = kATileE + kBTileE;
-constexpr int kABlocks = kFwdBM / 16;         // 1 KB blocks (16 rows x 64 B) per stage
-constexpr int kBBlocks = kFwdBN / 16;
-constexpr int kALoads = kABlocks / kWaves;    // per wave per K tile
-constexpr int kBLoads = kBBlocks / kWaves;
-constexpr int kLoads = kALoads + kBLoads;
-static_assert(kABlocks % kWaves == 0 && kBBlocks % kWaves == 0, "blocks per wave");
-static_assert(kCB % 2 == 0, "fc1 pairs gate and up column blocks");
-
-#ifndef MOE_FWD_VMCNT
-// loads per wave per K tile x (kStages - 2) tiles left in flight: must equal
-// kLoads * (kStages - 2) (checked below)
-#define MOE_FWD_VMCNT 3
-#endif
-static_assert(MOE_FWD_VMCNT == kLoads * (kStages - 2), "ring wait count");
-#define MOE_STR2(x) #x
-#define MOE_STR(x) MOE_STR2(x)
+using GemmCfg = FwdCfg<MOE_FWD_WM, MOE_FWD_WN, MOE_FWD_RB, MOE_FWD_CB, MOE_FWD_STAGES, MOE_FWD_BK,
+                       MOE_FWD_WG_PER_CU>;
+// Router logits: many small tiles (see router_ksplit).
+using RouterCfg = FwdCfg<2, 4, 2, 2, 3, 32, 2>;
 
 enum FwdEpi { FWD_FC1 = 0, FWD_FC2 = 1, FWD_LOGITS = 2 };
 
@@ -97,51 +111,58 @@ struct FwdParams {
   size_t outf_split;                          // LOGITS: elements between slabs
 };
 
-// staged tile element offset (bf16 units) of row r, 16-byte chunk kc
-__device__ __forceinline__ int swz(int r, int kc) { return r * kFwdBK + ((kc ^ swz_f(r)) << 3); }
+// chunk permutation of staged row r (see the file comment)
+template <int kChunks>
+__device__ __forceinline__ int swz_row(int r) {
+  return kChunks == 4 ? swz_f(r) : ((r & 7) ^ ((r >> 3) & 1));
+}
 
-// One output tile.  kNRB = live 32-row blocks of this wave (0..kRB).
-template <int kEpi, int kNRB>
+// One output tile.  kNRB = live 32-row blocks of this wave (0..RB).
+template <class C, int kEpi, int kNRB>
 __device__ __forceinline__ void ggf_tile(const FwdParams& p, const TileIdx& ti, uint16_t* s_lds) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int kWN = C::kWN, kRB = C::kRB, kCB = C::kCB, kWaves = C::kWaves;
+  constexpr int kBM = C::kBM, kBN = C::kBN, kBK = C::kBK, kChunks = C::kChunks;
+  constexpr int kStages = C::kStages, kALoads = C::kALoads, kLoads = C::kLoads;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / kWN, wn = wave % kWN;
   const int r32 = lane & 31, h = lane >> 5;
-  constexpr int nbn = kEpi == FWD_FC1 ? kFwdBN / 2 : kFwdBN;   // output columns per tile
-  const int m0 = ti.lo + ti.mt * kFwdBM;
+  constexpr int nbn = kEpi == FWD_FC1 ? kBN / 2 : kBN;   // output columns per tile
+  const int m0 = ti.lo + ti.mt * kBM;
   const int n0 = ti.nt * nbn;
   const int K = p.K;
 
   // buffer descriptors: this tile's token rows, this expert's weights
   const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(p.a + static_cast<size_t>(m0) * p.lda), 0,
-      min(ti.hi - m0, kFwdBM) * p.lda * 2, kRsrcWord3);
+      min(ti.hi - m0, kBM) * p.lda * 2, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(p.b + static_cast<size_t>(ti.e) * p.b_estride), 0,
       static_cast<int>(p.b_estride * 2), kRsrcWord3);
 
-  // This wave fills A blocks wave + kWaves j and B blocks wave + kWaves j
-  // (16 tile rows x 64 bytes each).  Lane l of a block writes LDS position l,
-  // i.e. row 16 blk + l / 4, physical chunk l % 4, so it fetches logical
-  // chunk (l % 4) ^ f(row).
-  const int lr = lane >> 2, pc = lane & 3;
+  // This wave fills A blocks wave + kWaves j and B blocks wave + kWaves j.
+  // Lane l of a block writes LDS position l, i.e. row kRowsPerBlk blk +
+  // l / kChunks, physical chunk l % kChunks, so it fetches logical chunk
+  // (l % kChunks) ^ swz_row(row).
+  const int lr = lane / kChunks, pc = lane % kChunks;
   const int last = ti.hi - 1 - m0;
   int vo[kLoads], kcl[kLoads];
 #pragma unroll
   for (int j = 0; j < kALoads; ++j) {
-    const int r = (wave + kWaves * j) * 16 + lr;
-    const int kc = pc ^ swz_f(r);
+    const int r = (wave + kWaves * j) * C::kRowsPerBlk + lr;
+    const int kc = pc ^ swz_row<kChunks>(r);
     kcl[j] = kc;
-    vo[j] = (min(r, last) * p.lda + kc * 8) * 2;   // rows past the segment: computed, dropped
+    vo[j] = r <= last ? (r * p.lda + kc * 8) * 2 : kOob;   // rows past the segment read zero
   }
 #pragma unroll
-  for (int j = 0; j < kBLoads; ++j) {
-    const int r = (wave + kWaves * j) * 16 + lr;
-    const int kc = pc ^ swz_f(r);
+  for (int j = 0; j < C::kBLoads; ++j) {
+    const int r = (wave + kWaves * j) * C::kRowsPerBlk + lr;
+    const int kc = pc ^ swz_row<kChunks>(r);
     int wr;
     if constexpr (kEpi == FWD_FC1) {          // B rows: gate half, then the matching up half
-      int f = n0 + (r % (kFwdBN / 2));
+      int f = n0 + (r % (kBN / 2));
       f = f < p.F ? f : p.F - 1;
-      wr = r < kFwdBN / 2 ? f : p.F + f;
+      wr = r < kBN / 2 ? f : p.F + f;
     } else {
       wr = n0 + r;
       wr = wr < p.d ? wr : p.d - 1;
@@ -150,7 +171,7 @@ __device__ __forceinline__ void ggf_tile(const FwdParams& p, const TileIdx& ti, 
     vo[kALoads + j] = (wr * p.ldb + kc * 8) * 2;
   }
   // K tiles [kt_lo, kt_hi) of this workgroup (all of them unless K is split)
-  const int nk_all = (K + kFwdBK - 1) / kFwdBK;
+  const int nk_all = (K + kBK - 1) / kBK;
   const int kchunk = (nk_all + p.ksplit - 1) / p.ksplit;
   const int kt_lo = min(nk_all, static_cast<int>(blockIdx.y) * kchunk);
   const int kt_hi = min(nk_all, kt_lo + kchunk);
@@ -158,17 +179,15 @@ __device__ __forceinline__ void ggf_tile(const FwdParams& p, const TileIdx& ti, 
   // fetch K tile kt (clamped to the last one) into ring slot (kt - kt_lo) % kStages
   auto issue = [&](int kt) {
     const int t = min(kt, kt_hi - 1);
-    const int k0 = t * kFwdBK;
-    uint16_t* st = s_lds + ((kt - kt_lo) % kStages) * kStageE;
-    const int so = k0 * 2;
+    const int k0 = t * kBK;
+    uint16_t* st = s_lds + ((kt - kt_lo) % kStages) * C::kStageE;
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) {
       const int v = (k0 + kcl[j] * 8 < K) ? vo[j] : kOob;
-      uint16_t* dst = (j < kALoads)
-                          ? st + (wave + kWaves * j) * 16 * kFwdBK
-                          : st + kATileE + (wave + kWaves * (j - kALoads)) * 16 * kFwdBK;
+      uint16_t* dst = (j < kALoads) ? st + (wave + kWaves * j) * 512
+                                    : st + C::kATileE + (wave + kWaves * (j - kALoads)) * 512;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(j < kALoads ? rs_a : rs_b, (lds_void*)(dst), 16, v,
-                                               so, 0, 0);
+                                               k0 * 2, 0, 0);
     }
   };
 
@@ -180,11 +199,13 @@ __device__ __forceinline__ void ggf_tile(const FwdParams& p, const TileIdx& ti, 
   for (int c = 0; c < kCB; ++c) {
     if constexpr (kEpi == FWD_FC1) {          // gate blocks, then the matching up blocks
       const int cc = c % (kCB / 2);
-      b_rd[c] = (c < kCB / 2 ? 0 : kFwdBN / 2) + wn * (kCB / 2) * 32 + cc * 32 + r32;
+      b_rd[c] = (c < kCB / 2 ? 0 : kBN / 2) + wn * (kCB / 2) * 32 + cc * 32 + r32;
     } else {
       b_rd[c] = wn * kCB * 32 + c * 32 + r32;
     }
   }
+  // staged element offset of row r, 16-byte chunk kc
+  auto swz = [](int r, int kc) { return r * kBK + ((kc ^ swz_row<kChunks>(r)) << 3); };
 
   constexpr int kAccRB = kNRB > 0 ? kNRB : 1;
   f32x16 acc[kAccRB][kCB];
@@ -195,10 +216,10 @@ __device__ __forceinline__ void ggf_tile(const FwdParams& p, const TileIdx& ti, 
 
   auto compute = [&](int slot) {
     if constexpr (kNRB > 0) {
-      const uint16_t* As = s_lds + slot * kStageE;
-      const uint16_t* Bs = As + kATileE;
+      const uint16_t* As = s_lds + slot * C::kStageE;
+      const uint16_t* Bs = As + C::kATileE;
 #pragma unroll
-      for (int kk = 0; kk < kFwdBK / 16; ++kk) {
+      for (int kk = 0; kk < kBK / 16; ++kk) {
         const int ck = 2 * kk + h;
         bf16x8 bv[kCB];
 #pragma unroll
@@ -225,7 +246,7 @@ __device__ __forceinline__ void ggf_tile(const FwdParams& p, const TileIdx& ti, 
     for (int t = 0; t < kStages - 1; ++t) issue(kt_lo + t);
 #pragma unroll 1
     for (int kt = kt_lo; kt < kt_hi; ++kt) {
-      asm volatile("s_waitcnt vmcnt(" MOE_STR(MOE_FWD_VMCNT) ")\n\ts_barrier" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(C::kRingWait) : "memory");
       issue(kt + kStages - 1);
       compute((kt - kt_lo) % kStages);
     }
@@ -276,36 +297,38 @@ __device__ __forceinline__ void ggf_tile(const FwdParams& p, const TileIdx& ti, 
   }
 }
 
-template <int kEpi>
-__global__ __launch_bounds__(kFwdThreads, MOE_FWD_WG_PER_CU) void ggf_kernel(FwdParams p) {
-  extern __shared__ __align__(16) uint16_t s_lds[];   // kStages x (A tile + B tile)
-  __shared__ int s_cum[1025];
-  __shared__ int s_tmp[kWaves];
-  tile_prefix<kFwdThreads>(p.offsets, p.E, kFwdBM, p.ntn, s_cum, s_tmp);
+template <class C, int kEpi>
+__global__ __launch_bounds__(C::kThreads, C::kWgPerCu) void ggf_kernel(FwdParams p) {
+  // kStages x (A tile + B tile); the tile-decode scratch lives in the same
+  // memory before the ring starts
+  extern __shared__ __align__(16) uint16_t s_lds[];
+  int* s_cum = reinterpret_cast<int*>(s_lds);
+  int* s_tmp = s_cum + 1040;
+  tile_prefix<C::kThreads>(p.offsets, p.E, C::kBM, p.ntn, s_cum, s_tmp);
   const int total = s_cum[p.E];
   if (static_cast<int>(blockIdx.x) >= total) return;
-  const TileIdx ti = tile_decode(p.offsets, p.E, kFwdBM, xcd_remap(blockIdx.x, total), s_cum);
+  const TileIdx ti = tile_decode(p.offsets, p.E, C::kBM, xcd_remap(blockIdx.x, total), s_cum);
+  __syncthreads();   // every wave has decoded its tile before the ring overwrites s_cum
   // live 32-row blocks of this wave's rows
-  const int rows = ti.hi - (ti.lo + ti.mt * kFwdBM) - (static_cast<int>(threadIdx.x >> 6) / kWN) * kRB * 32;
-  const int nrb = rows <= 0 ? 0 : min(kRB, (rows + 31) >> 5);
-  if constexpr (kRB == 2) {
+  const int rows = ti.hi - (ti.lo + ti.mt * C::kBM) -
+                   (static_cast<int>(threadIdx.x >> 6) / C::kWN) * C::kRB * 32;
+  const int nrb = rows <= 0 ? 0 : min(C::kRB, (rows + 31) >> 5);
+  if constexpr (C::kRB == 2) {
     switch (nrb) {
-      case 0: ggf_tile<kEpi, 0>(p, ti, s_lds); break;
-      case 1: ggf_tile<kEpi, 1>(p, ti, s_lds); break;
-      default: ggf_tile<kEpi, 2>(p, ti, s_lds); break;
+      case 0: ggf_tile<C, kEpi, 0>(p, ti, s_lds); break;
+      case 1: ggf_tile<C, kEpi, 1>(p, ti, s_lds); break;
+      default: ggf_tile<C, kEpi, 2>(p, ti, s_lds); break;
     }
   } else {
     switch (nrb) {
-      case 0: ggf_tile<kEpi, 0>(p, ti, s_lds); break;
-      case 1: ggf_tile<kEpi, 1>(p, ti, s_lds); break;
-      case 2: ggf_tile<kEpi, 2>(p, ti, s_lds); break;
-      case 3: ggf_tile<kEpi, 3>(p, ti, s_lds); break;
-      default: ggf_tile<kEpi, 4>(p, ti, s_lds); break;
+      case 0: ggf_tile<C, kEpi, 0>(p, ti, s_lds); break;
+      case 1: ggf_tile<C, kEpi, 1>(p, ti, s_lds); break;
+      case 2: ggf_tile<C, kEpi, 2>(p, ti, s_lds); break;
+      case 3: ggf_tile<C, kEpi, 3>(p, ti, s_lds); break;
+      default: ggf_tile<C, kEpi, 4>(p, ti, s_lds); break;
     }
   }
 }
-
-constexpr size_t kFwdLds = kStages * kStageE * sizeof(uint16_t);
 
 // ---------------------------------------------------------------------------
 // fp32 path (MOE_F32): LDS-tiled FMA, 64 x 64 x 16 tiles, 4 x 4 outputs per
@@ -410,26 +433,27 @@ hipError_t launch_grouped_fwd_bf16(hipStream_t stream, int64_t N, int64_t d, int
                                    const void* x_perm, const void* w1, const void* w2,
                                    const int32_t* offsets, const float* row_scale, void* y_perm,
                                    void* gu_save, uint16_t* a_buf, bool run_fc2) {
+  using C = GemmCfg;
   FwdParams p{};
   p.E = E; p.F = (int)F; p.d = (int)d; p.offsets = offsets;
-  // fc1: [G | U] = X W1^T with the SwiGLU epilogue; 128 f per tile
-  p.ntn = (int)((F + kFwdBN / 2 - 1) / (kFwdBN / 2));
+  // fc1: [G | U] = X W1^T with the SwiGLU epilogue; kBN / 2 f per tile
+  p.ntn = (int)((F + C::kBN / 2 - 1) / (C::kBN / 2));
   p.a = static_cast<const uint16_t*>(x_perm); p.lda = (int)d;
   p.b = static_cast<const uint16_t*>(w1); p.ldb = (int)d;
   p.b_estride = static_cast<size_t>(2 * F) * d;
   p.K = (int)d;
   p.out = a_buf; p.out2 = static_cast<uint16_t*>(gu_save);
   p.ksplit = 1;
-  hipError_t err = allow_lds(ggf_kernel<FWD_FC1>, kFwdLds);
-  if (err == hipSuccess) err = allow_lds(ggf_kernel<FWD_FC2>, kFwdLds);
+  hipError_t err = allow_lds(ggf_kernel<C, FWD_FC1>, C::kLdsBytes);
+  if (err == hipSuccess) err = allow_lds(ggf_kernel<C, FWD_FC2>, C::kLdsBytes);
   if (err == hipSuccess)
-    err = launch(ggf_kernel<FWD_FC1>, dim3(tiles_bound(N, E, kFwdBM) * p.ntn), dim3(kFwdThreads),
-                 kFwdLds, stream, p);
+    err = launch(ggf_kernel<C, FWD_FC1>, dim3(tiles_bound(N, E, C::kBM) * p.ntn),
+                 dim3(C::kThreads), C::kLdsBytes, stream, p);
   if (err != hipSuccess || !run_fc2) return err;
-  // fc2: Y = (A W2^T) * row_scale; 256 output columns per tile
+  // fc2: Y = (A W2^T) * row_scale; kBN output columns per tile
   FwdParams q{};
   q.E = E; q.F = (int)F; q.d = (int)d; q.offsets = offsets;
-  q.ntn = (int)((d + kFwdBN - 1) / kFwdBN);
+  q.ntn = (int)((d + C::kBN - 1) / C::kBN);
   q.a = a_buf; q.lda = (int)F;
   q.b = static_cast<const uint16_t*>(w2); q.ldb = (int)F;
   q.b_estride = static_cast<size_t>(d) * F;
@@ -437,14 +461,15 @@ hipError_t launch_grouped_fwd_bf16(hipStream_t stream, int64_t N, int64_t d, int
   q.scale = row_scale;
   q.out = static_cast<uint16_t*>(y_perm);
   q.ksplit = 1;
-  return launch(ggf_kernel<FWD_FC2>, dim3(tiles_bound(N, E, kFwdBM) * q.ntn), dim3(kFwdThreads),
-                kFwdLds, stream, q);
+  return launch(ggf_kernel<C, FWD_FC2>, dim3(tiles_bound(N, E, C::kBM) * q.ntn),
+                dim3(C::kThreads), C::kLdsBytes, stream, q);
 }
 
 int router_ksplit(int64_t T, int64_t d, int32_t E) {
   // enough K slabs for ~2 workgroups per CU, each slab at least 8 K tiles
-  const int64_t tiles = ((T + kFwdBM - 1) / kFwdBM) * ((E + kFwdBN - 1) / kFwdBN);
-  const int64_t nk = (d + kFwdBK - 1) / kFwdBK;
+  using C = RouterCfg;
+  const int64_t tiles = ((T + C::kBM - 1) / C::kBM) * ((E + C::kBN - 1) / C::kBN);
+  const int64_t nk = (d + C::kBK - 1) / C::kBK;
   int64_t s = (512 + tiles - 1) / tiles;
   s = std::min<int64_t>(s, std::max<int64_t>(1, nk / 8));
   return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(s, 16)));
@@ -453,9 +478,10 @@ int router_ksplit(int64_t T, int64_t d, int32_t E) {
 hipError_t launch_router_logits_bf16(hipStream_t stream, int64_t T, int64_t d, int32_t E,
                                     const void* x, const void* w_router, const float* bias,
                                     const int32_t* offsets01, float* logits, int ksplit) {
+  using C = RouterCfg;
   FwdParams p{};
   p.E = 1; p.F = 1; p.d = E; p.offsets = offsets01;
-  p.ntn = (E + kFwdBN - 1) / kFwdBN;
+  p.ntn = (E + C::kBN - 1) / C::kBN;
   p.a = static_cast<const uint16_t*>(x); p.lda = (int)d;
   p.b = static_cast<const uint16_t*>(w_router); p.ldb = (int)d;
   p.b_estride = static_cast<size_t>(E) * d;
@@ -464,10 +490,10 @@ hipError_t launch_router_logits_bf16(hipStream_t stream, int64_t T, int64_t d, i
   p.outf = logits;
   p.ksplit = ksplit;
   p.outf_split = static_cast<size_t>(T) * E;
-  hipError_t err = allow_lds(ggf_kernel<FWD_LOGITS>, kFwdLds);
+  hipError_t err = allow_lds(ggf_kernel<C, FWD_LOGITS>, C::kLdsBytes);
   if (err != hipSuccess) return err;
-  return launch(ggf_kernel<FWD_LOGITS>, dim3(tiles_bound(T, 1, kFwdBM) * p.ntn, ksplit),
-                dim3(kFwdThreads), kFwdLds, stream, p);
+  return launch(ggf_kernel<C, FWD_LOGITS>, dim3(tiles_bound(T, 1, C::kBM) * p.ntn, ksplit),
+                dim3(C::kThreads), C::kLdsBytes, stream, p);
 }
 
 }  // namespace moe
