@@ -45,6 +45,21 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }
+
+// Epilogue forms: e^-z as 2^(-z log2 e) and the hardware reciprocal (about
+// one ulp each); z -> -inf gives 2^+inf = inf and a sigmoid of 0.
+__device__ __forceinline__ float sigmoid_fast(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
+}
+
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v;
+// four fp32 -> four bf16 in 8 bytes, hardware round-to-nearest-even
+__device__ __forceinline__ u32x2 pack4_bf16(float a, float b, float c, float d) {
+  const f32x2 lo = {a, b}, hi = {c, d};
+  return u32x2{__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2v)),
+               __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2v))};
+}
 // silu(z) = z * sigmoid(z); written as a quotient so that very negative z
 // (expf(-z) = +inf) gives -0 instead of NaN.
 __device__ __forceinline__ float siluf_(float z) { return z / (1.0f + expf(-z)); }

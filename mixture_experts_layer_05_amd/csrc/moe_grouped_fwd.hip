@@ -128,6 +128,9 @@ __device__ __forceinline__ void ggf_tile(const FwdParams& p, const TileIdx& ti, 
   const int wm = wave / kWN, wn = wave % kWN;
   const int r32 = lane & 31, h = lane >> 5;
   constexpr int nbn = kEpi == FWD_FC1 ? kBN / 2 : kBN;   // output columns per tile
+  // accumulator layout (see the epilogue): row per lane for the bf16
+  // outputs, column per lane for the fp32 logits
+  constexpr bool kSwap = kEpi != FWD_LOGITS;
   const int m0 = ti.lo + ti.mt * kBM;
   const int n0 = ti.nt * nbn;
   const int K = p.K;
@@ -229,7 +232,9 @@ __device__ __forceinline__ void ggf_tile(const FwdParams& p, const TileIdx& ti, 
           const bf16x8 av = *reinterpret_cast<const bf16x8*>(As + swz(a_rd[rb], ck));
 #pragma unroll
           for (int c = 0; c < kCB; ++c)
-            acc[rb][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv[c], acc[rb][c], 0, 0, 0);
+            acc[rb][c] = kSwap
+                             ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[c], av, acc[rb][c], 0, 0, 0)
+                             : __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv[c], acc[rb][c], 0, 0, 0);
         }
       }
     }
@@ -254,42 +259,72 @@ __device__ __forceinline__ void ggf_tile(const FwdParams& p, const TileIdx& ti, 
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain the clamped extra loads
 
   // ---------------- epilogue ------------------------------------------------
-  if constexpr (kNRB > 0) {
+  // fc1 / fc2: the MFMAs take the weight block as their first operand, so
+  // accumulator register 4q + i of lane l holds token row l % 32 of the
+  // block and output column 8q + 4(l / 32) + i: four consecutive columns per
+  // lane, stored as one 8-byte (bf16) write.  F and d are multiples of 8, so
+  // col < limit covers all four.  Logits: register r of lane l holds token
+  // row 8(r / 4) + 4(l / 32) + r % 4 and column l % 32 (32 lanes write 128
+  // contiguous bytes of fp32).
+  if constexpr (kEpi == FWD_LOGITS && kNRB > 0) {
+    float* dst = p.outf + blockIdx.y * p.outf_split;
 #pragma unroll
     for (int rb = 0; rb < kNRB; ++rb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = m0 + wm * kRB * 32 + rb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
         if (row >= ti.hi) continue;
-        const size_t rowz = static_cast<size_t>(row);
-        if constexpr (kEpi == FWD_FC1) {
 #pragma unroll
-          for (int c = 0; c < kCB / 2; ++c) {
-            const int f = n0 + wn * (kCB / 2) * 32 + c * 32 + r32;
-            if (f < p.F) {
-              const float g = acc[rb][c][r], u = acc[rb][c + kCB / 2][r];
-              p.out[rowz * p.F + f] = f32_to_bf16(siluf_(g) * u);
-              if (p.out2) {
-                p.out2[rowz * 2 * p.F + f] = f32_to_bf16(g);
-                p.out2[rowz * 2 * p.F + p.F + f] = f32_to_bf16(u);
-              }
+        for (int c = 0; c < kCB; ++c) {
+          const int n = n0 + wn * kCB * 32 + c * 32 + r32;
+          if (n < p.d)
+            dst[static_cast<size_t>(row) * p.d + n] =
+                acc[rb][c][r] + ((p.scale && blockIdx.y == 0) ? p.scale[n] : 0.0f);
+        }
+      }
+    }
+  } else if constexpr (kNRB > 0) {
+#pragma unroll
+    for (int rb = 0; rb < kNRB; ++rb) {
+      const int row = m0 + wm * kRB * 32 + rb * 32 + r32;
+      if (row >= ti.hi) continue;
+      const size_t rowz = static_cast<size_t>(row);
+      if constexpr (kEpi == FWD_FC1) {
+#pragma unroll
+        for (int c = 0; c < kCB / 2; ++c) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int f = n0 + wn * (kCB / 2) * 32 + c * 32 + 8 * q + 4 * h;
+            if (f >= p.F) continue;
+            const f32x16& G = acc[rb][c];
+            const f32x16& U = acc[rb][c + kCB / 2];
+            float a4[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float g = G[4 * q + i];
+              a4[i] = g * sigmoid_fast(g) * U[4 * q + i];
+            }
+            *reinterpret_cast<u32x2*>(p.out + rowz * p.F + f) = pack4_bf16(a4[0], a4[1], a4[2], a4[3]);
+            if (p.out2) {
+              uint16_t* gu = p.out2 + rowz * 2 * p.F;
+              *reinterpret_cast<u32x2*>(gu + f) =
+                  pack4_bf16(G[4 * q], G[4 * q + 1], G[4 * q + 2], G[4 * q + 3]);
+              *reinterpret_cast<u32x2*>(gu + p.F + f) =
+                  pack4_bf16(U[4 * q], U[4 * q + 1], U[4 * q + 2], U[4 * q + 3]);
             }
           }
-        } else if constexpr (kEpi == FWD_FC2) {
-          const float sc = p.scale ? p.scale[row] : 1.0f;
+        }
+      } else {  // FWD_FC2
+        const float sc = p.scale ? p.scale[row] : 1.0f;
 #pragma unroll
-          for (int c = 0; c < kCB; ++c) {
-            const int n = n0 + wn * kCB * 32 + c * 32 + r32;
-            if (n < p.d) p.out[rowz * p.d + n] = f32_to_bf16(acc[rb][c][r] * sc);
-          }
-        } else {  // FWD_LOGITS: this K slab's fp32 partial logits (bias on slab 0)
-          float* dst = p.outf + blockIdx.y * p.outf_split;
+        for (int c = 0; c < kCB; ++c) {
 #pragma unroll
-          for (int c = 0; c < kCB; ++c) {
-            const int n = n0 + wn * kCB * 32 + c * 32 + r32;
-            if (n < p.d)
-              dst[rowz * p.d + n] =
-                  acc[rb][c][r] + ((p.scale && blockIdx.y == 0) ? p.scale[n] : 0.0f);
+          for (int q = 0; q < 4; ++q) {
+            const int n = n0 + wn * kCB * 32 + c * 32 + 8 * q + 4 * h;
+            if (n >= p.d) continue;
+            const f32x16& Y = acc[rb][c];
+            *reinterpret_cast<u32x2*>(p.out + rowz * p.d + n) =
+                pack4_bf16(Y[4 * q] * sc, Y[4 * q + 1] * sc, Y[4 * q + 2] * sc, Y[4 * q + 3] * sc);
           }
         }
       }
