@@ -30,6 +30,33 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, AMD's published figure
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, AMD's published figure
 
+# HBM bytes per grouped-GEMM forward call (fc1 + fc2 dispatches), from
+# `rocprofv3 --pmc FETCH_SIZE` and `--pmc WRITE_SIZE` runs of this script,
+# each counter scaled by what it reads for a 1 GiB device copy
+# (--copy-calibration: FETCH_SIZE x 2.0, WRITE_SIZE x 1.0); summary in
+# profiles/grouped_gemm_fwd_qwen3_30b_hbm_bytes.md.  Valid only for the
+# kernel sources the counters were taken on (sha256 over KERNEL_SOURCES):
+# reported as null once they change.
+KERNEL_SOURCES = ("mixture_experts_layer_05_amd/csrc/moe_grouped_fwd.hip",
+                  "mixture_experts_layer_05_amd/csrc/moe_gemm_common.h",
+                  "mixture_experts_layer_05_amd/csrc/moe_device.h")
+MEASURED_TRAFFIC = {
+    "qwen3_30b": {"bytes": 1628437833,
+                  "sources_sha256": "0cd0361ba1d41d94a78e99b8b6aad8894a3a09a02d7683b2e53283698263072b"},
+}
+
+
+def measured_traffic(workload):
+    import hashlib
+    rec = MEASURED_TRAFFIC.get(workload)
+    if rec is None:
+        return None
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return rec["bytes"] if h.hexdigest() == rec["sources_sha256"] else None
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -196,17 +223,19 @@ def main():
     # the binding roof of the grouped GEMM: whichever of MFMA and HBM time is longer
     t_mfma = alg["gemm_flop"] / (PEAK_BF16_TFLOPS * 1e12)
     t_hbm = alg["gemm_bytes"] / (PEAK_HBM_GBS * 1e9)
+    traffic = measured_traffic(cfg.name)
     if t_hbm > t_mfma:
         roof = {"bound": "hbm", "achieved": round(gemm_gbs, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(gemm_gbs / PEAK_HBM_GBS, 4), "traffic": None}
+                "unit": "GB/s", "frac": round(gemm_gbs / PEAK_HBM_GBS, 4), "traffic": traffic}
     else:
         roof = {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
-                "traffic": None}
+                "traffic": traffic}
     roof["kernel"] = "moe_grouped_swiglu_fwd (fc1+SwiGLU, fc2+row-scale launches)"
     roof["algorithmic_flop"] = alg["gemm_flop"]
     roof["algorithmic_bytes"] = alg["gemm_bytes"]
     roof["avg_launch_ms"] = round(per_stage["grouped_gemm"], 4)
+    roof["traffic_unit"] = "bytes per call (HBM, counter-measured)"
 
     def gbs(key, stage):
         t = per_stage[stage] * 1e-3
