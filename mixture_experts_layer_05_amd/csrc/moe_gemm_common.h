@@ -9,7 +9,9 @@
 namespace moe {
 
 struct TileIdx {
-  int e, mt, nt, lo, hi;
+  int e, mt, nt;
+  int lo, hi;      // the expert's segment
+  int m0, mend;    // this tile's rows
 };
 
 // Block-wide exclusive scan over the experts' tile counts, into s_cum[0..E]
@@ -64,7 +66,10 @@ __device__ inline int xcd_remap(int b, int total) {
   return x * q + (x < r ? x : r) + pos;
 }
 
-// logical tile -> (expert, row tile, column tile) given s_cum from tile_prefix
+// logical tile -> (expert, row tile, column tile) given s_cum from tile_prefix.
+// An expert's n rows are split over ceil(n / bm) row tiles of equal height
+// h = ceil(n / tiles) rounded up to 32 (h <= bm, every tile non-empty), e.g.
+// 260 rows at bm = 128 as 96 + 96 + 68 rather than 128 + 128 + 4.
 __device__ inline TileIdx tile_decode(const int32_t* __restrict__ offsets, int E, int bm, int L,
                                       const int* s_cum) {
   int lo = 0, hi = E - 1;
@@ -76,10 +81,14 @@ __device__ inline TileIdx tile_decode(const int32_t* __restrict__ offsets, int E
   t.e = lo;
   t.lo = offsets[lo];
   t.hi = offsets[lo + 1];
-  const int mts = (t.hi - t.lo + bm - 1) / bm;
+  const int n = t.hi - t.lo;
+  const int mts = (n + bm - 1) / bm;
   const int local = L - s_cum[lo];
   t.nt = local / mts;
   t.mt = local - t.nt * mts;
+  const int h = ((n + mts - 1) / mts + 31) & ~31;
+  t.m0 = t.lo + t.mt * h;
+  t.mend = min(t.m0 + h, t.hi);
   return t;
 }
 

@@ -312,13 +312,13 @@ __global__ __launch_bounds__(kGT, 2) void ggb_kernel(GGParams p) {
     const int total = s_cum[p.E];
     if (static_cast<int>(blockIdx.x) >= total) return;
     const TileIdx ti = tile_decode(p.offsets, p.E, kBM, xcd_remap(blockIdx.x, total), s_cum);
-    const int m0 = ti.lo + ti.mt * kBM;
-    const int rows = ti.hi - m0 - (static_cast<int>(threadIdx.x >> 6) / kWN) * kRB * 32;
+    const int m0 = ti.m0;
+    const int rows = ti.mend - m0 - (static_cast<int>(threadIdx.x >> 6) / kWN) * kRB * 32;
     const int nrb = rows <= 0 ? 0 : min(kRB, (rows + 31) >> 5);
     switch (nrb) {
-      case 0: ggb_tile<kEpi, 0>(p, ti.e, ti.lo, ti.hi, m0, ti.nt * kBN, s_lds); break;
-      case 1: ggb_tile<kEpi, 1>(p, ti.e, ti.lo, ti.hi, m0, ti.nt * kBN, s_lds); break;
-      default: ggb_tile<kEpi, 2>(p, ti.e, ti.lo, ti.hi, m0, ti.nt * kBN, s_lds); break;
+      case 0: ggb_tile<kEpi, 0>(p, ti.e, ti.lo, ti.mend, m0, ti.nt * kBN, s_lds); break;
+      case 1: ggb_tile<kEpi, 1>(p, ti.e, ti.lo, ti.mend, m0, ti.nt * kBN, s_lds); break;
+      default: ggb_tile<kEpi, 2>(p, ti.e, ti.lo, ti.mend, m0, ti.nt * kBN, s_lds); break;
     }
   }
 }

@@ -44,13 +44,14 @@
 
 namespace moe {
 
-// Tile configuration: WM x WN wavefronts, each owning RB x CB blocks of
-// 32 x 32 outputs; S-deep LDS ring of BK-wide K tiles; WG workgroups per CU.
-template <int WM, int WN, int RB, int CB, int S, int BK, int WG>
+// Tile configuration: WM x WN MFMA wavefronts, each owning RB x CB blocks of
+// 32 x 32 outputs, out of W wavefronts that all load (W >= WM * WN; the
+// others only load); S-deep LDS ring of BK-wide K tiles; WG workgroups per CU.
+template <int WM, int WN, int RB, int CB, int S, int BK, int WG, int W = WM * WN>
 struct FwdCfg {
   static constexpr int kWM = WM, kWN = WN, kRB = RB, kCB = CB, kStages = S, kBK = BK, kWgPerCu = WG;
-  static constexpr int kThreads = 64 * WM * WN;
-  static constexpr int kWaves = WM * WN;
+  static constexpr int kThreads = 64 * W;
+  static constexpr int kWaves = W;
   static constexpr int kBM = WM * RB * 32;            // token rows per tile
   static constexpr int kBN = WN * CB * 32;            // weight rows per tile
   static constexpr int kChunks = BK / 8;              // 16-byte chunks per staged row
@@ -58,16 +59,15 @@ struct FwdCfg {
   static constexpr int kATileE = kBM * BK;            // bf16 per ring slot
   static constexpr int kBTileE = kBN * BK;
   static constexpr int kStageE = kATileE + kBTileE;
-  static constexpr int kALoads = kBM / kRowsPerBlk / kWaves;   // 1 KB blocks per wave per K tile
-  static constexpr int kBLoads = kBN / kRowsPerBlk / kWaves;
-  static constexpr int kLoads = kALoads + kBLoads;
+  static constexpr int kABlocks = kBM / kRowsPerBlk;   // 1 KB blocks per ring slot
+  static constexpr int kBBlocks = kBN / kRowsPerBlk;
+  static constexpr int kLoads = (kABlocks + kBBlocks) / W;   // per wave per K tile
   // loads a wave may leave in flight when K tile kt must have landed
   static constexpr int kRingWait = kLoads * (S - 2);
   static constexpr size_t kLdsBytes = static_cast<size_t>(S) * kStageE * sizeof(uint16_t);
   static_assert(BK == 32 || BK == 64, "K tile");
   static_assert(S >= 2, "ring depth");
-  static_assert((kBM / kRowsPerBlk) % kWaves == 0 && (kBN / kRowsPerBlk) % kWaves == 0,
-                "blocks per wave");
+  static_assert((kABlocks + kBBlocks) % W == 0 && W >= WM * WN && W <= 16, "blocks per wave");
   static_assert(CB % 2 == 0, "fc1 pairs gate and up column blocks");
   static_assert(kLdsBytes >= (1040 + 64) * sizeof(int), "tile-decode scratch fits the ring");
   static_assert(RB == 2 || RB == 4, "live-row dispatch");
@@ -88,8 +88,11 @@ struct FwdCfg {
 #define MOE_FWD_BK 64
 #define MOE_FWD_WG_PER_CU 1
 #endif
+#ifndef MOE_FWD_W
+#define MOE_FWD_W (MOE_FWD_WM * MOE_FWD_WN)
+#endif
 using GemmCfg = FwdCfg<MOE_FWD_WM, MOE_FWD_WN, MOE_FWD_RB, MOE_FWD_CB, MOE_FWD_STAGES, MOE_FWD_BK,
-                       MOE_FWD_WG_PER_CU>;
+                       MOE_FWD_WG_PER_CU, MOE_FWD_W>;
 // Router logits: many small tiles (see router_ksplit).
 using RouterCfg = FwdCfg<2, 4, 2, 2, 3, 32, 2>;
 
@@ -122,7 +125,7 @@ template <class C, int kEpi, int kNRB>
 __device__ __forceinline__ void ggf_tile(const FwdParams& p, const TileIdx& ti, uint16_t* s_lds) {
   constexpr int kWN = C::kWN, kRB = C::kRB, kCB = C::kCB, kWaves = C::kWaves;
   constexpr int kBM = C::kBM, kBN = C::kBN, kBK = C::kBK, kChunks = C::kChunks;
-  constexpr int kStages = C::kStages, kALoads = C::kALoads, kLoads = C::kLoads;
+  constexpr int kStages = C::kStages, kLoads = C::kLoads;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / kWN, wn = wave % kWN;
@@ -131,47 +134,49 @@ __device__ __forceinline__ void ggf_tile(const FwdParams& p, const TileIdx& ti, 
   // accumulator layout (see the epilogue): row per lane for the bf16
   // outputs, column per lane for the fp32 logits
   constexpr bool kSwap = kEpi != FWD_LOGITS;
-  const int m0 = ti.lo + ti.mt * kBM;
+  const int m0 = ti.m0;
   const int n0 = ti.nt * nbn;
   const int K = p.K;
 
   // buffer descriptors: this tile's token rows, this expert's weights
   const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(p.a + static_cast<size_t>(m0) * p.lda), 0,
-      min(ti.hi - m0, kBM) * p.lda * 2, kRsrcWord3);
+      (ti.mend - m0) * p.lda * 2, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(p.b + static_cast<size_t>(ti.e) * p.b_estride), 0,
       static_cast<int>(p.b_estride * 2), kRsrcWord3);
 
-  // This wave fills A blocks wave + kWaves j and B blocks wave + kWaves j.
-  // Lane l of a block writes LDS position l, i.e. row kRowsPerBlk blk +
-  // l / kChunks, physical chunk l % kChunks, so it fetches logical chunk
-  // (l % kChunks) ^ swz_row(row).
+  // Load j of this wave fills block wave + kWaves j of the slot: A blocks
+  // first, then B blocks (which one is uniform per wave).  Lane l of a block
+  // writes LDS position l, i.e. row kRowsPerBlk blk + l / kChunks, physical
+  // chunk l % kChunks, so it fetches logical chunk (l % kChunks) ^ swz_row(row).
   const int lr = lane / kChunks, pc = lane % kChunks;
-  const int last = ti.hi - 1 - m0;
-  int vo[kLoads], kcl[kLoads];
+  const int last = ti.mend - 1 - m0;
+  int vo[kLoads], kcl[kLoads], dsto[kLoads];
+  bool isa[kLoads];
 #pragma unroll
-  for (int j = 0; j < kALoads; ++j) {
-    const int r = (wave + kWaves * j) * C::kRowsPerBlk + lr;
+  for (int j = 0; j < kLoads; ++j) {
+    const int blk = wave + kWaves * j;
+    isa[j] = blk < C::kABlocks;
+    const int bb = isa[j] ? blk : blk - C::kABlocks;
+    const int r = bb * C::kRowsPerBlk + lr;
     const int kc = pc ^ swz_row<kChunks>(r);
     kcl[j] = kc;
-    vo[j] = r <= last ? (r * p.lda + kc * 8) * 2 : kOob;   // rows past the segment read zero
-  }
-#pragma unroll
-  for (int j = 0; j < C::kBLoads; ++j) {
-    const int r = (wave + kWaves * j) * C::kRowsPerBlk + lr;
-    const int kc = pc ^ swz_row<kChunks>(r);
-    int wr;
-    if constexpr (kEpi == FWD_FC1) {          // B rows: gate half, then the matching up half
-      int f = n0 + (r % (kBN / 2));
-      f = f < p.F ? f : p.F - 1;
-      wr = r < kBN / 2 ? f : p.F + f;
+    dsto[j] = isa[j] ? blk * 512 : C::kATileE + bb * 512;
+    if (isa[j]) {
+      vo[j] = r <= last ? (r * p.lda + kc * 8) * 2 : kOob;   // rows past the tile read zero
     } else {
-      wr = n0 + r;
-      wr = wr < p.d ? wr : p.d - 1;
+      int wr;
+      if constexpr (kEpi == FWD_FC1) {        // B rows: gate half, then the matching up half
+        int f = n0 + (r % (kBN / 2));
+        f = f < p.F ? f : p.F - 1;
+        wr = r < kBN / 2 ? f : p.F + f;
+      } else {
+        wr = n0 + r;
+        wr = wr < p.d ? wr : p.d - 1;
+      }
+      vo[j] = (wr * p.ldb + kc * 8) * 2;
     }
-    kcl[kALoads + j] = kc;
-    vo[kALoads + j] = (wr * p.ldb + kc * 8) * 2;
   }
   // K tiles [kt_lo, kt_hi) of this workgroup (all of them unless K is split)
   const int nk_all = (K + kBK - 1) / kBK;
@@ -187,10 +192,8 @@ __device__ __forceinline__ void ggf_tile(const FwdParams& p, const TileIdx& ti, 
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) {
       const int v = (k0 + kcl[j] * 8 < K) ? vo[j] : kOob;
-      uint16_t* dst = (j < kALoads) ? st + (wave + kWaves * j) * 512
-                                    : st + C::kATileE + (wave + kWaves * (j - kALoads)) * 512;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(j < kALoads ? rs_a : rs_b, (lds_void*)(dst), 16, v,
-                                               k0 * 2, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isa[j] ? rs_a : rs_b, (lds_void*)(st + dsto[j]), 16,
+                                               v, k0 * 2, 0, 0);
     }
   };
 
@@ -273,7 +276,7 @@ __device__ __forceinline__ void ggf_tile(const FwdParams& p, const TileIdx& ti, 
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = m0 + wm * kRB * 32 + rb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (row >= ti.hi) continue;
+        if (row >= ti.mend) continue;
 #pragma unroll
         for (int c = 0; c < kCB; ++c) {
           const int n = n0 + wn * kCB * 32 + c * 32 + r32;
@@ -287,7 +290,7 @@ __device__ __forceinline__ void ggf_tile(const FwdParams& p, const TileIdx& ti, 
 #pragma unroll
     for (int rb = 0; rb < kNRB; ++rb) {
       const int row = m0 + wm * kRB * 32 + rb * 32 + r32;
-      if (row >= ti.hi) continue;
+      if (row >= ti.mend) continue;
       const size_t rowz = static_cast<size_t>(row);
       if constexpr (kEpi == FWD_FC1) {
 #pragma unroll
@@ -345,7 +348,7 @@ __global__ __launch_bounds__(C::kThreads, C::kWgPerCu) void ggf_kernel(FwdParams
   const TileIdx ti = tile_decode(p.offsets, p.E, C::kBM, xcd_remap(blockIdx.x, total), s_cum);
   __syncthreads();   // every wave has decoded its tile before the ring overwrites s_cum
   // live 32-row blocks of this wave's rows
-  const int rows = ti.hi - (ti.lo + ti.mt * C::kBM) -
+  const int rows = ti.mend - ti.m0 -
                    (static_cast<int>(threadIdx.x >> 6) / C::kWN) * C::kRB * 32;
   const int nrb = rows <= 0 ? 0 : min(C::kRB, (rows + 31) >> 5);
   if constexpr (C::kRB == 2) {
@@ -389,7 +392,7 @@ __global__ __launch_bounds__(256) void ggf_f32_kernel(int E, int F, int d, int K
   const int total = s_cum[E];
   if (static_cast<int>(blockIdx.x) >= total) return;
   const TileIdx ti = tile_decode(offsets, E, kFM, blockIdx.x, s_cum);
-  const int m0 = ti.lo + ti.mt * kFM;
+  const int m0 = ti.m0;
   const int nt = ti.nt;
   const float* bexp = b + static_cast<size_t>(ti.e) * b_estride;
 
@@ -407,7 +410,7 @@ __global__ __launch_bounds__(256) void ggf_f32_kernel(int E, int F, int d, int K
       const int r = c >> 4, kk = c & 15;
       const int k = k0 + kk;
       int ar = m0 + r;
-      if (ar > ti.hi - 1) ar = ti.hi - 1;
+      if (ar > ti.mend - 1) ar = ti.mend - 1;
       As[kk][r] = k < K ? a[static_cast<size_t>(ar) * lda + k] : 0.0f;
       int br;
       if constexpr (kEpi == FWD_FC1) {
@@ -438,7 +441,7 @@ __global__ __launch_bounds__(256) void ggf_f32_kernel(int E, int F, int d, int K
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = m0 + ty * 4 + i;
-    if (row >= ti.hi) continue;
+    if (row >= ti.mend) continue;
     const size_t rowz = static_cast<size_t>(row);
     if constexpr (kEpi == FWD_FC1) {
 #pragma unroll
