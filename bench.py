@@ -3,8 +3,9 @@
 One step = one forward pass of the whole layer over one batch of the
 128-expert top-8 workload (T=4096 tokens, d=2048, E=128, k=8, ffn 768,
 bf16 storage, fp32 accumulation and router math):
-    route -> permute -> grouped SwiGLU (fc1 + fc2, routing weight as the fc2
-    row scale) -> combine
+    route -> permute (index work only) -> grouped SwiGLU (fc1 gathers the
+    token rows from x by the permute's row map; fc2 applies the routing
+    weight as its row scale) -> combine
 Inputs are seeded synthetic tensors already resident in HBM; every launch
 goes through the C ABI (libmoe_mi355x.so).
 
@@ -40,10 +41,7 @@ PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, AMD's published figure
 KERNEL_SOURCES = ("mixture_experts_layer_05_amd/csrc/moe_grouped_fwd.hip",
                   "mixture_experts_layer_05_amd/csrc/moe_gemm_common.h",
                   "mixture_experts_layer_05_amd/csrc/moe_device.h")
-MEASURED_TRAFFIC = {
-    "qwen3_30b": {"bytes": 1628437833,
-                  "sources_sha256": "0cd0361ba1d41d94a78e99b8b6aad8894a3a09a02d7683b2e53283698263072b"},
-}
+MEASURED_TRAFFIC = {}
 
 
 def measured_traffic(workload):
@@ -94,10 +92,12 @@ def algorithmic(cfg):
     N = T * k
     b = 2
     gemm_flop = 6.0 * N * d * F
-    # expert weights read once + X_perm read + A written and read + Y_perm written
-    gemm_bytes = 3.0 * E * d * F * b + N * d * b + 2.0 * N * F * b + N * d * b
+    # expert weights read once + token rows read once (fc1 gathers them from x)
+    # + A written and read + Y_perm written
+    gemm_bytes = 3.0 * E * d * F * b + T * d * b + 2.0 * N * F * b + N * d * b
     route_bytes = T * (2 * d + 8 * k + 4) + E * d * b
-    permute_bytes = T * (2 * d * (1 + k) + 20 * k)
+    # permute without the row copy: topk_idx, topk_w read; slot_of, row_token, row_w written
+    permute_bytes = T * 20 * k
     combine_bytes = T * (2 * d * (k + 1) + 4 * k)
     return dict(gemm_flop=gemm_flop, gemm_bytes=gemm_bytes, route_bytes=route_bytes,
                 permute_bytes=permute_bytes, combine_bytes=combine_bytes)
@@ -177,10 +177,13 @@ def main():
                                       L.w_gate, out=L.route_out, ws=L.route_ws)
         if ev is not None:
             ev[1].record(stream)
-        off, slot, rtok, rw, xp = moe.permute(x, idx, w, L.E, out=L.perm_out, ws=L.perm_ws)
+        # permute folded into fc1: no row copy, fc1 gathers x rows by row_token
+        off, slot, rtok, rw, _ = moe.permute(x, idx, w, L.E, out=L.perm_out, ws=L.perm_ws,
+                                             copy_rows=False)
         if ev is not None:
             ev[2].record(stream)
-        moe.grouped_swiglu_fwd(xp, L.w1, L.w2, off, row_scale=rw, out=L.y_perm, ws=L.ffn_ws)
+        moe.grouped_swiglu_fwd_gather(x, rtok, L.w1, L.w2, off, row_scale=rw, out=L.y_perm,
+                                      ws=L.ffn_ws)
         if ev is not None:
             ev[3].record(stream)
         ysh = None
@@ -231,7 +234,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic}
-    roof["kernel"] = "moe_grouped_swiglu_fwd (fc1+SwiGLU, fc2+row-scale launches)"
+    roof["kernel"] = "moe_grouped_swiglu_fwd_gather (fc1 gather+SwiGLU, fc2+row-scale launches)"
     roof["algorithmic_flop"] = alg["gemm_flop"]
     roof["algorithmic_bytes"] = alg["gemm_bytes"]
     roof["avg_launch_ms"] = round(per_stage["grouped_gemm"], 4)

@@ -57,7 +57,7 @@ typedef enum moe_status {
   MOE_ERR_DTYPE = 3,        /* unknown moe_dtype                            */
   MOE_ERR_ALIGNMENT = 4,    /* pointer not 16-byte aligned / d, F not x8    */
   MOE_ERR_WORKSPACE = 5,    /* ws NULL or smaller than *_workspace_size()   */
-  MOE_ERR_UNSUPPORTED = 6,  /* valid request this build does not implement  */
+  MOE_ERR_UNSUPPORTED = 6,  /* valid request the library does not implement */
   MOE_ERR_HIP = 7           /* a HIP launch failed                          */
 } moe_status;
 
@@ -127,7 +127,10 @@ MOE_API moe_status moe_route(hipStream_t stream, moe_dtype dt, int64_t T, int64_
  *   slot_of    [T, k]  int32     out
  *   row_token  [T*k]   int32     out
  *   row_w      [T*k]   fp32      out, or NULL
- *   x_perm     [T*k, d] dt       out
+ *   x_perm     [T*k, d] dt       out, or NULL: no row copy is made (x may
+ *                                then be NULL); a consumer that gathers by
+ *                                row_token (moe_grouped_swiglu_fwd_gather)
+ *                                reads x directly
  * An entry of topk_idx outside [0, E) is dropped: its slot_of is -1 and it
  * takes no row (rows past the last kept one are left unwritten).
  * Workspace: moe_permute_workspace_size(T, E, k) bytes.
@@ -173,6 +176,33 @@ MOE_API moe_status moe_grouped_swiglu_fwd(hipStream_t stream, moe_dtype dt, int6
                                   const void* w2, const int32_t* expert_offsets,
                                   const float* row_scale, void* y_perm,
                                   void* gu_save, void* ws, size_t ws_bytes);
+
+/* ------------------------------------------------------------------------
+ * moe_grouped_swiglu_fwd_gather -- moe_grouped_swiglu_fwd with the permute
+ * folded into the first GEMM's operand load.
+ *
+ * Passage: "Megatron-Bridge 深度剖析", "Permute Fusion" (the standalone
+ * permute copy of the hidden states is replaced by reordering rows while
+ * they are loaded).  Computes exactly moe_grouped_swiglu_fwd with
+ *     x_perm[r, :] = x[row_token[r], :]
+ * but never materialises x_perm: fc1 reads row r of each expert segment
+ * from x[row_token[r]].
+ *
+ *   T          int64               rows of x, >= 1
+ *   x          [T, d]      dt    in
+ *   row_token  [N]         int32 in, device (moe_permute's row map); a value
+ *                                outside [0, T) reads as a zero row
+ *   the rest as in moe_grouped_swiglu_fwd (same workspace size)
+ * Limits: those of moe_grouped_swiglu_fwd, and T*d*elt < 2^31 (x addressed
+ * with 32-bit byte offsets).  Returns MOE_ERR_SHAPE beyond them.
+ * --------------------------------------------------------------------- */
+MOE_API moe_status moe_grouped_swiglu_fwd_gather(hipStream_t stream, moe_dtype dt, int64_t N,
+                                         int64_t d, int64_t F, int32_t E, int64_t T,
+                                         const void* x, const int32_t* row_token,
+                                         const void* w1, const void* w2,
+                                         const int32_t* expert_offsets,
+                                         const float* row_scale, void* y_perm,
+                                         void* gu_save, void* ws, size_t ws_bytes);
 
 /* ------------------------------------------------------------------------
  * moe_grouped_swiglu_bwd -- grouped-GEMM dgrad and wgrad of the forward.

@@ -19,7 +19,7 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "MoEError", "lib", "route", "permute", "grouped_swiglu_fwd",
+    "MoEError", "lib", "route", "permute", "grouped_swiglu_fwd", "grouped_swiglu_fwd_gather",
     "grouped_swiglu_bwd", "unpermute_combine", "moe_layer_forward",
     "MoELayer", "LIB_PATH", "EXPORTED",
 ]
@@ -47,6 +47,8 @@ EXPORTED = {
     "moe_grouped_swiglu_fwd_workspace_size": (_sz, [_i64, _i64, _i32]),
     "moe_grouped_swiglu_fwd": (_i32, [_vp, _i32, _i64, _i64, _i64, _i32,
                                       _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz]),
+    "moe_grouped_swiglu_fwd_gather": (_i32, [_vp, _i32, _i64, _i64, _i64, _i32, _i64,
+                                             _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz]),
     "moe_grouped_swiglu_bwd_workspace_size": (_sz, [_i64, _i64, _i32, _i32]),
     "moe_grouped_swiglu_bwd": (_i32, [_vp, _i32, _i64, _i64, _i64, _i32,
                                       _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
@@ -141,8 +143,10 @@ def permute_workspace_size(T, E, k):
     return lib().moe_permute_workspace_size(T, E, k)
 
 
-def permute(x, topk_idx, topk_w, E, out=None, ws=None):
-    """-> (expert_offsets [E+1], slot_of [T,k], row_token [N], row_w [N] or None, x_perm [N,d])"""
+def permute(x, topk_idx, topk_w, E, out=None, ws=None, copy_rows=True):
+    """-> (expert_offsets [E+1], slot_of [T,k], row_token [N], row_w [N] or None,
+    x_perm [N,d] or None).  copy_rows=False skips the row copy (for a consumer
+    that gathers rows by row_token)."""
     T, d = x.shape
     k = topk_idx.shape[1]
     N = T * k
@@ -152,11 +156,13 @@ def permute(x, topk_idx, topk_w, E, out=None, ws=None):
                torch.empty((T, k), dtype=torch.int32, device=dev),
                torch.empty((N,), dtype=torch.int32, device=dev),
                torch.empty((N,), dtype=torch.float32, device=dev) if topk_w is not None else None,
-               torch.empty((N, d), dtype=x.dtype, device=dev))
+               torch.empty((N, d), dtype=x.dtype, device=dev) if copy_rows else None)
     off, slot, rtok, rw, xp = out
     nbytes = permute_workspace_size(T, E, k)
     if ws is None:
         ws = _ws(nbytes, dev)
+    if not copy_rows:
+        xp = None
     _check(lib().moe_permute(_stream(), _dt(x), T, d, E, k, _p(x), _p(topk_idx), _p(topk_w),
                              _p(off), _p(slot), _p(rtok), _p(rw), _p(xp), _p(ws), ws.numel()),
            "moe_permute")
@@ -184,6 +190,29 @@ def grouped_swiglu_fwd(x_perm, w1, w2, expert_offsets, row_scale=None, save_gu=F
     _check(lib().moe_grouped_swiglu_fwd(_stream(), _dt(x_perm), N, d, F, E, _p(x_perm), _p(w1),
                                         _p(w2), _p(expert_offsets), _p(row_scale), _p(y), _p(gu),
                                         _p(ws), ws.numel()), "moe_grouped_swiglu_fwd")
+    return y, gu
+
+
+def grouped_swiglu_fwd_gather(x, row_token, w1, w2, expert_offsets, row_scale=None,
+                              save_gu=False, out=None, gu_out=None, ws=None):
+    """grouped_swiglu_fwd on x[row_token] without materialising it.
+    -> (y_perm [N,d], gu_save [N,2F] or None)"""
+    T, d = x.shape
+    N = row_token.shape[0]
+    E, twoF, _ = w1.shape
+    F = twoF // 2
+    dev = x.device
+    y = out if out is not None else torch.empty((N, d), dtype=x.dtype, device=dev)
+    gu = gu_out
+    if save_gu and gu is None:
+        gu = torch.empty((N, 2 * F), dtype=x.dtype, device=dev)
+    nbytes = fwd_workspace_size(N, F, x.dtype)
+    if ws is None:
+        ws = _ws(nbytes, dev)
+    _check(lib().moe_grouped_swiglu_fwd_gather(_stream(), _dt(x), N, d, F, E, T, _p(x),
+                                               _p(row_token), _p(w1), _p(w2), _p(expert_offsets),
+                                               _p(row_scale), _p(y), _p(gu), _p(ws), ws.numel()),
+           "moe_grouped_swiglu_fwd_gather")
     return y, gu
 
 
@@ -232,11 +261,15 @@ class MoELayer:
 
     route -> permute -> grouped SwiGLU (routing weight applied as the fc2
     row scale) -> [shared expert as a one-expert grouped call, row scale =
-    gate] -> combine.  Only kernel launches happen in ``forward``.
+    gate] -> combine.  Only kernel launches happen in ``forward``.  With
+    ``gather`` (default) the permute makes no row copy and fc1 reads the
+    token rows from x by row_token; otherwise x_perm is materialised.
     """
 
     def __init__(self, w_router, w1, w2, k, T, score="softmax", normalize=True,
-                 logit_bias=None, w_gate=None, ws1=None, ws2=None, save_gu=False):
+                 logit_bias=None, w_gate=None, ws1=None, ws2=None, save_gu=False,
+                 gather=True):
+        self.gather = gather
         self.w_router, self.w1, self.w2 = w_router, w1, w2
         self.k, self.T, self.score, self.normalize = k, T, score, normalize
         self.logit_bias, self.w_gate, self.ws1, self.ws2 = logit_bias, w_gate, ws1, ws2
@@ -254,7 +287,7 @@ class MoELayer:
                          torch.empty((T, k), dtype=i32, device=dev),
                          torch.empty((N,), dtype=i32, device=dev),
                          torch.empty((N,), dtype=f32, device=dev),
-                         torch.empty((N, d), dtype=dt, device=dev))
+                         None if gather else torch.empty((N, d), dtype=dt, device=dev))
         self.perm_ws = _ws(permute_workspace_size(T, E, k), dev)
         self.route_ws = _ws(route_workspace_size(T, d, E, dt), dev)
         self.y_perm = torch.empty((N, d), dtype=dt, device=dev)
@@ -274,9 +307,15 @@ class MoELayer:
         idx, w, cnt, gate = route(x, self.w_router, self.k, self.score, self.normalize,
                                   self.logit_bias, self.w_gate, out=self.route_out,
                                   ws=self.route_ws)
-        off, slot, rtok, rw, xp = permute(x, idx, w, self.E, out=self.perm_out, ws=self.perm_ws)
-        grouped_swiglu_fwd(xp, self.w1, self.w2, off, row_scale=rw, out=self.y_perm,
-                           gu_out=self.gu, save_gu=self.gu is not None, ws=self.ffn_ws)
+        off, slot, rtok, rw, xp = permute(x, idx, w, self.E, out=self.perm_out, ws=self.perm_ws,
+                                          copy_rows=not self.gather)
+        if self.gather:
+            grouped_swiglu_fwd_gather(x, rtok, self.w1, self.w2, off, row_scale=rw,
+                                      out=self.y_perm, gu_out=self.gu,
+                                      save_gu=self.gu is not None, ws=self.ffn_ws)
+        else:
+            grouped_swiglu_fwd(xp, self.w1, self.w2, off, row_scale=rw, out=self.y_perm,
+                               gu_out=self.gu, save_gu=self.gu is not None, ws=self.ffn_ws)
         ysh = None
         if self.ws1 is not None:
             grouped_swiglu_fwd(x, self.ws1_e, self.ws2_e, self.shared_off, row_scale=gate,
@@ -286,9 +325,9 @@ class MoELayer:
 
 
 def moe_layer_forward(x, w_router, w1, w2, k, score="softmax", normalize=True,
-                      logit_bias=None, w_gate=None, ws1=None, ws2=None):
+                      logit_bias=None, w_gate=None, ws1=None, ws2=None, gather=True):
     """Functional form of :class:`MoELayer` (allocates per call)."""
     layer = MoELayer(w_router, w1, w2, k, x.shape[0], score, normalize, logit_bias, w_gate,
-                     ws1, ws2)
+                     ws1, ws2, gather=gather)
     y = layer.forward(x)
     return y, layer

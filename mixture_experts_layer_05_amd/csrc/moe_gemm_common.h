@@ -148,11 +148,13 @@ inline int tiles_bound(int64_t N, int E, int bm) {
 
 // Forward launcher shared with the backward's recompute path.  bf16 only.
 // a_buf [N, F] receives silu(G) * U; gu_save (or NULL) receives [G | U];
-// when run_fc2, y_perm = (a_buf W2^T) * row_scale.
+// when run_fc2, y_perm = (a_buf W2^T) * row_scale.  With gather (or NULL),
+// row r of the first GEMM is row gather[r] of x_perm [a_rows, d].
 hipError_t launch_grouped_fwd_bf16(hipStream_t stream, int64_t N, int64_t d, int64_t F, int32_t E,
                                    const void* x_perm, const void* w1, const void* w2,
                                    const int32_t* offsets, const float* row_scale, void* y_perm,
-                                   void* gu_save, uint16_t* a_buf, bool run_fc2);
+                                   void* gu_save, uint16_t* a_buf, bool run_fc2,
+                                   const int32_t* gather = nullptr, int64_t a_rows = 0);
 
 // Router logits with the forward kernel as a one-group GEMM, K split into
 // `ksplit` slabs: logits[s][T][E] = x[:, slab s] W_r[:, slab s]^T (+ bias

@@ -101,8 +101,10 @@ enum FwdEpi { FWD_FC1 = 0, FWD_FC2 = 1, FWD_LOGITS = 2 };
 struct FwdParams {
   int E, F, d, K, ntn;
   const int32_t* offsets;
-  const uint16_t* a;                          // token rows [N, K]
+  const uint16_t* a;                          // token rows [N, K], or [a_rows, K] when gathering
   int lda;
+  const int32_t* gather;                      // [N]: source row of each row, or NULL (row r is a[r])
+  int a_rows;                                 // rows of a when gathering
   const uint16_t* b;                          // weights, expert-major
   int ldb;
   size_t b_estride;
@@ -138,10 +140,12 @@ __device__ __forceinline__ void ggf_tile(const FwdParams& p, const TileIdx& ti, 
   const int n0 = ti.nt * nbn;
   const int K = p.K;
 
-  // buffer descriptors: this tile's token rows, this expert's weights
+  // buffer descriptors: this tile's token rows (all of a when gathering),
+  // this expert's weights
+  const bool gath = p.gather != nullptr;
   const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(p.a + static_cast<size_t>(m0) * p.lda), 0,
-      (ti.mend - m0) * p.lda * 2, kRsrcWord3);
+      const_cast<uint16_t*>(gath ? p.a : p.a + static_cast<size_t>(m0) * p.lda), 0,
+      (gath ? p.a_rows : ti.mend - m0) * p.lda * 2, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(p.b + static_cast<size_t>(ti.e) * p.b_estride), 0,
       static_cast<int>(p.b_estride * 2), kRsrcWord3);
@@ -164,7 +168,9 @@ __device__ __forceinline__ void ggf_tile(const FwdParams& p, const TileIdx& ti, 
     kcl[j] = kc;
     dsto[j] = isa[j] ? blk * 512 : C::kATileE + bb * 512;
     if (isa[j]) {
-      vo[j] = r <= last ? (r * p.lda + kc * 8) * 2 : kOob;   // rows past the tile read zero
+      // rows past the tile, and gathered rows outside [0, a_rows), read zero
+      const int src = r > last ? -1 : gath ? p.gather[m0 + r] : r;
+      vo[j] = src >= 0 && (!gath || src < p.a_rows) ? (src * p.lda + kc * 8) * 2 : kOob;
     } else {
       int wr;
       if constexpr (kEpi == FWD_FC1) {        // B rows: gate half, then the matching up half
@@ -378,6 +384,8 @@ template <int kEpi>
 __global__ __launch_bounds__(256) void ggf_f32_kernel(int E, int F, int d, int K, int ntn,
                                                       const int32_t* __restrict__ offsets,
                                                       const float* __restrict__ a, int lda,
+                                                      const int32_t* __restrict__ gather,
+                                                      int a_rows,
                                                       const float* __restrict__ b, int ldb,
                                                       size_t b_estride,
                                                       const float* __restrict__ scale,
@@ -411,7 +419,9 @@ __global__ __launch_bounds__(256) void ggf_f32_kernel(int E, int F, int d, int K
       const int k = k0 + kk;
       int ar = m0 + r;
       if (ar > ti.mend - 1) ar = ti.mend - 1;
-      As[kk][r] = k < K ? a[static_cast<size_t>(ar) * lda + k] : 0.0f;
+      if (gather) ar = gather[ar];            // outside [0, a_rows): a zero row
+      As[kk][r] = k < K && ar >= 0 && (!gather || ar < a_rows)
+                      ? a[static_cast<size_t>(ar) * lda + k] : 0.0f;
       int br;
       if constexpr (kEpi == FWD_FC1) {
         int f = nt * 32 + (r & 31);
@@ -470,13 +480,15 @@ __global__ __launch_bounds__(256) void ggf_f32_kernel(int E, int F, int d, int K
 hipError_t launch_grouped_fwd_bf16(hipStream_t stream, int64_t N, int64_t d, int64_t F, int32_t E,
                                    const void* x_perm, const void* w1, const void* w2,
                                    const int32_t* offsets, const float* row_scale, void* y_perm,
-                                   void* gu_save, uint16_t* a_buf, bool run_fc2) {
+                                   void* gu_save, uint16_t* a_buf, bool run_fc2,
+                                   const int32_t* gather, int64_t a_rows) {
   using C = GemmCfg;
   FwdParams p{};
   p.E = E; p.F = (int)F; p.d = (int)d; p.offsets = offsets;
   // fc1: [G | U] = X W1^T with the SwiGLU epilogue; kBN / 2 f per tile
   p.ntn = (int)((F + C::kBN / 2 - 1) / (C::kBN / 2));
   p.a = static_cast<const uint16_t*>(x_perm); p.lda = (int)d;
+  p.gather = gather; p.a_rows = (int)a_rows;
   p.b = static_cast<const uint16_t*>(w1); p.ldb = (int)d;
   p.b_estride = static_cast<size_t>(2 * F) * d;
   p.K = (int)d;
@@ -545,38 +557,66 @@ extern "C" size_t moe_grouped_swiglu_fwd_workspace_size(int64_t N, int64_t F, mo
   return static_cast<size_t>(N) * F * elt_size(dt) + 256;
 }
 
+// The forward, with row r of the first GEMM read from x[gather[r]] when
+// gather is non-NULL (x then has T rows), else from x[r].
+static moe_status grouped_fwd(hipStream_t stream, moe_dtype dt, int64_t N, int64_t d, int64_t F,
+                              int32_t E, int64_t T, const void* x, const int32_t* gather,
+                              const void* w1, const void* w2, const int32_t* expert_offsets,
+                              const float* row_scale, void* y_perm, void* gu_save, void* ws,
+                              size_t ws_bytes) {
+  moe_status st = moe_grouped_check(dt, N, d, F, E);
+  if (st != MOE_OK) return st;
+  if (!x || !w1 || !w2 || !expert_offsets || !y_perm) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w1) || !aligned16(w2) || !aligned16(expert_offsets) ||
+      !aligned16(row_scale) || !aligned16(y_perm) || !aligned16(gu_save) || !aligned16(ws) ||
+      !aligned16(gather))
+    return MOE_ERR_ALIGNMENT;
+  if (!ws || ws_bytes < moe_grouped_swiglu_fwd_workspace_size(N, F, dt)) return MOE_ERR_WORKSPACE;
+  if (N == 0) return MOE_OK;
+  if (dt == MOE_BF16) {
+    return hip_status(launch_grouped_fwd_bf16(stream, N, d, F, E, x, w1, w2, expert_offsets,
+                                              row_scale, y_perm, gu_save,
+                                              static_cast<uint16_t*>(ws), true, gather, T));
+  }
+  float* a_buf = static_cast<float*>(ws);
+  const int ntn1 = (int)((F + 31) / 32);
+  hipError_t err = launch(ggf_f32_kernel<FWD_FC1>, dim3(tiles_bound(N, E, kFM) * ntn1), dim3(256),
+                          0, stream, E, (int)F, (int)d, (int)d, ntn1, expert_offsets,
+                          static_cast<const float*>(x), (int)d, gather, (int)T,
+                          static_cast<const float*>(w1), (int)d, static_cast<size_t>(2 * F) * d,
+                          (const float*)nullptr, a_buf, static_cast<float*>(gu_save));
+  if (err == hipSuccess) {
+    const int ntn2 = (int)((d + kFN - 1) / kFN);
+    err = launch(ggf_f32_kernel<FWD_FC2>, dim3(tiles_bound(N, E, kFM) * ntn2), dim3(256), 0,
+                 stream, E, (int)F, (int)d, (int)F, ntn2, expert_offsets, (const float*)a_buf,
+                 (int)F, (const int32_t*)nullptr, 0, static_cast<const float*>(w2), (int)F,
+                 static_cast<size_t>(d) * F, row_scale, static_cast<float*>(y_perm),
+                 (float*)nullptr);
+  }
+  return hip_status(err);
+}
+
 extern "C" moe_status moe_grouped_swiglu_fwd(hipStream_t stream, moe_dtype dt, int64_t N,
                                              int64_t d, int64_t F, int32_t E,
                                              const void* x_perm, const void* w1, const void* w2,
                                              const int32_t* expert_offsets,
                                              const float* row_scale, void* y_perm,
                                              void* gu_save, void* ws, size_t ws_bytes) {
-  moe_status st = moe_grouped_check(dt, N, d, F, E);
-  if (st != MOE_OK) return st;
-  if (!x_perm || !w1 || !w2 || !expert_offsets || !y_perm) return MOE_ERR_INVALID_ARG;
-  if (!aligned16(x_perm) || !aligned16(w1) || !aligned16(w2) || !aligned16(expert_offsets) ||
-      !aligned16(row_scale) || !aligned16(y_perm) || !aligned16(gu_save) || !aligned16(ws))
-    return MOE_ERR_ALIGNMENT;
-  if (!ws || ws_bytes < moe_grouped_swiglu_fwd_workspace_size(N, F, dt)) return MOE_ERR_WORKSPACE;
-  if (N == 0) return MOE_OK;
-  if (dt == MOE_BF16) {
-    return hip_status(launch_grouped_fwd_bf16(stream, N, d, F, E, x_perm, w1, w2, expert_offsets,
-                                              row_scale, y_perm, gu_save,
-                                              static_cast<uint16_t*>(ws), true));
-  }
-  float* a_buf = static_cast<float*>(ws);
-  const int ntn1 = (int)((F + 31) / 32);
-  hipError_t err = launch(ggf_f32_kernel<FWD_FC1>, dim3(tiles_bound(N, E, kFM) * ntn1), dim3(256),
-                          0, stream, E, (int)F, (int)d, (int)d, ntn1, expert_offsets,
-                          static_cast<const float*>(x_perm), (int)d, static_cast<const float*>(w1),
-                          (int)d, static_cast<size_t>(2 * F) * d, (const float*)nullptr, a_buf,
-                          static_cast<float*>(gu_save));
-  if (err == hipSuccess) {
-    const int ntn2 = (int)((d + kFN - 1) / kFN);
-    err = launch(ggf_f32_kernel<FWD_FC2>, dim3(tiles_bound(N, E, kFM) * ntn2), dim3(256), 0,
-                 stream, E, (int)F, (int)d, (int)F, ntn2, expert_offsets, (const float*)a_buf,
-                 (int)F, static_cast<const float*>(w2), (int)F, static_cast<size_t>(d) * F,
-                 row_scale, static_cast<float*>(y_perm), (float*)nullptr);
-  }
-  return hip_status(err);
+  return grouped_fwd(stream, dt, N, d, F, E, N, x_perm, nullptr, w1, w2, expert_offsets,
+                     row_scale, y_perm, gu_save, ws, ws_bytes);
+}
+
+extern "C" moe_status moe_grouped_swiglu_fwd_gather(hipStream_t stream, moe_dtype dt, int64_t N,
+                                                    int64_t d, int64_t F, int32_t E, int64_t T,
+                                                    const void* x, const int32_t* row_token,
+                                                    const void* w1, const void* w2,
+                                                    const int32_t* expert_offsets,
+                                                    const float* row_scale, void* y_perm,
+                                                    void* gu_save, void* ws, size_t ws_bytes) {
+  if (!row_token) return MOE_ERR_INVALID_ARG;
+  if (T < 1) return MOE_ERR_SHAPE;
+  // gathered rows are addressed from x's start with 32-bit byte offsets
+  if (T * d * static_cast<int64_t>(elt_size(dt)) >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
+  return grouped_fwd(stream, dt, N, d, F, E, T, x, row_token, w1, w2, expert_offsets, row_scale,
+                     y_perm, gu_save, ws, ws_bytes);
 }

@@ -183,7 +183,7 @@ extern "C" moe_status moe_permute(hipStream_t stream, moe_dtype dt, int64_t T, i
                                   int32_t* row_token, float* row_w, void* x_perm,
                                   void* ws, size_t ws_bytes) {
   if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_DTYPE;
-  if (!x || !topk_idx || !expert_offsets || !slot_of || !row_token || !x_perm)
+  if (!topk_idx || !expert_offsets || !slot_of || !row_token || (x_perm && !x))
     return MOE_ERR_INVALID_ARG;
   if ((topk_w == nullptr) != (row_w == nullptr)) return MOE_ERR_INVALID_ARG;
   if (T < 1 || d < 1 || E < 1 || E > 1024 || k < 1 || k > 32) return MOE_ERR_SHAPE;
@@ -209,7 +209,7 @@ extern "C" moe_status moe_permute(hipStream_t stream, moe_dtype dt, int64_t T, i
     err = launch(perm_rows_kernel, dim3(nblk), dim3(kPermThreads),
                  (E + 1 + kPermThreads) * sizeof(int), stream, (int)T, E, k, topk_idx, topk_w,
                  H, total, expert_offsets, slot_of, row_token, row_w);
-  if (err == hipSuccess)
+  if (err == hipSuccess && x_perm)   // NULL x_perm: the consumer gathers rows by row_token
     err = launch(perm_copy_kernel, dim3(static_cast<unsigned>((T + 3) / 4)), dim3(kPermThreads),
                  0, stream, (int)T, k, static_cast<int>(row_bytes / 16), slot_of,
                  static_cast<const u32x4*>(x), static_cast<u32x4*>(x_perm));

@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.moe_abi_version() == 2
+    assert L.moe_abi_version() == 3
     assert L.moe_status_string(0) == b"MOE_OK"
     assert L.moe_status_string(5) == b"MOE_ERR_WORKSPACE"
 
@@ -110,6 +110,11 @@ def test_grouped_validation(L):
     assert fwd(None, 1, 100, 64, 64, 4, P, P, P, P, None, P, None, P, 16) == 5       # workspace
     assert fwd(None, 1, 100, 64, 64, 4, None, P, P, P, None, P, None, P, 1 << 30) == 1
     assert fwd(None, 1, 100, 64, 64, 2000, P, P, P, P, None, P, None, P, 1 << 30) == 2
+    gat = L.moe_grouped_swiglu_fwd_gather
+    assert gat(None, 1, 100, 64, 64, 4, 50, P, None, P, P, P, None, P, None, P, 1 << 30) == 1  # no row map
+    assert gat(None, 1, 100, 64, 64, 4, 0, P, P, P, P, P, None, P, None, P, 1 << 30) == 2      # T = 0
+    assert gat(None, 1, 100, 64, 64, 4, 1 << 25, P, P, P, P, P, None, P, None, P, 1 << 30) == 2  # x > 2 GB
+    assert gat(None, 1, 100, 64, 64, 4, 50, P, MIS, P, P, P, None, P, None, P, 1 << 30) == 4
     bwd = L.moe_grouped_swiglu_bwd
     assert bwd(None, 0, 100, 64, 64, 4, P, P, P, P, P, P, None, 0, P, P, P, P, 1 << 30) == 6
     assert bwd(None, 1, 100, 64, 64, 4, P, P, P, P, P, P, None, 0, P, P, P, P, 16) == 5

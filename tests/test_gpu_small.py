@@ -182,6 +182,51 @@ def test_grouped_fwd_parity(case):
     assert gh.normwise(gu, gu_ref) <= tol
 
 
+GATHER_CASES = [
+    # E, d, F, dtype, T (rows of x), bad tokens
+    (6, 64, 64, "f32", 70, False),
+    (7, 136, 72, "bf16", 45, False),
+    (5, 192, 136, "bf16", 300, True),
+]
+
+
+@pytest.mark.parametrize("case", GATHER_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_grouped_fwd_gather_parity(case):
+    """fc1 reading x[row_token] directly equals the forward on the copied rows,
+    bit for bit, and the oracle to the usual tolerance; a row_token outside
+    [0, T) reads as a zero row."""
+    E, d, F, dt, T, bad = case
+    rng = np.random.default_rng(E * 31 + d + T)
+    counts = _segments(rng, E, "ragged", 200)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    N = int(off[-1])
+    inp = mw.make_small_layer_inputs(E + d + T, T=T, d=d, E=E, F=F, dtype=dt, w_std=0.05)
+    rtok = rng.integers(0, T, N).astype(np.int32)
+    if bad:
+        rtok[rng.choice(N, 5, replace=False)] = np.array([-1, T, T + 7, -100, 2 ** 30], np.int32)
+    rs = (rng.random(N) + 0.5).astype(np.float32)
+    xf = inp.as_f32("x")
+    ok = (rtok >= 0) & (rtok < T)
+    xp_ref = np.where(ok[:, None], xf[np.clip(rtok, 0, T - 1)], 0.0)
+    y_ref, gu_ref = mo.grouped_swiglu_fwd(xp_ref, inp.as_f32("w1"), inp.as_f32("w2"), off, rs,
+                                          return_gu=True)
+    x, w1, w2 = gh.to_gpu(inp.x), gh.to_gpu(inp.w1), gh.to_gpu(inp.w2)
+    go, grs, gtok = gh.to_gpu(off), gh.to_gpu(rs), gh.to_gpu(rtok)
+    y = gh.poison((N, d), x.dtype)
+    gu = gh.poison((N, 2 * F), x.dtype)
+    moe.grouped_swiglu_fwd_gather(x, gtok, w1, w2, go, grs, save_gu=True, out=y, gu_out=gu)
+    # the same rows materialised (zero rows where the token is out of range)
+    xp = torch.zeros((N, d), dtype=x.dtype, device=x.device)
+    okg = torch.from_numpy(ok).to(x.device)
+    xp[okg] = x[gtok[okg].long()]
+    y2, gu2 = moe.grouped_swiglu_fwd(xp, w1, w2, go, grs, save_gu=True)
+    torch.cuda.synchronize()
+    assert gh.bits_equal(y, y2) and gh.bits_equal(gu, gu2)
+    tol = gh.TOL_F32 if dt == "f32" else gh.TOL_BF16
+    assert gh.normwise(gh.to_f64(y), y_ref) <= tol
+    assert gh.normwise(gh.to_f64(gu), gu_ref) <= tol
+
+
 BWD_CASES = [
     # E, d, F, pattern, scale, save_gu, row_scale, accumulate
     (5, 64, 64, "ragged", 200, True, False, False),

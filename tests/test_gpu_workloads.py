@@ -26,10 +26,11 @@ pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 moe = pytest.importorskip("mixture_experts_layer_05_amd")
 
 
-def _layer(inp, cfg):
+def _layer(inp, cfg, gather=True):
     g = lambda a: None if a is None else gh.to_gpu(a)  # noqa: E731
     return moe.MoELayer(g(inp.w_router), g(inp.w1), g(inp.w2), cfg.k, cfg.T, cfg.score,
-                        cfg.normalize, g(inp.logit_bias), g(inp.w_gate), g(inp.ws1), g(inp.ws2))
+                        cfg.normalize, g(inp.logit_bias), g(inp.w_gate), g(inp.ws1), g(inp.ws2),
+                        gather=gather)
 
 
 @pytest.mark.parametrize("name", ["tiny", "qwen3_30b", "dsv_30b", "skew_shared"])
@@ -63,12 +64,20 @@ def test_layer_forward_full_size(name):
     # ---- permutation, all pairs, for the GPU's own choice
     pref = mo.permute(None, idx, w, cfg.E)
     off, slot, rtok, rw, xp = layer.perm_out
+    assert xp is None   # the layer gathers rows inside fc1
     assert np.array_equal(off.cpu().numpy(), pref.offsets)
     assert np.array_equal(slot.cpu().numpy(), pref.slot_of)
     assert np.array_equal(rtok.cpu().numpy(), pref.row_token)
     assert np.array_equal(rw.cpu().numpy().view(np.uint32), pref.row_w.view(np.uint32))
+
+    # ---- the same layer with the row copy materialised: x_perm exact, y bit-identical
+    layer_c = _layer(inp, cfg, gather=False)
+    y_c = layer_c.forward(x)
+    torch.cuda.synchronize()
+    xp = layer_c.perm_out[4]
     assert gh.bits_equal(xp, x[rtok.long()])
     assert gh.bits_equal(xp[slot[:, 0].long()], x)
+    assert gh.bits_equal(y_c, y)
 
     # ---- layer output on a seeded token sample (forced routing)
     rng = np.random.default_rng(cfg.index)
