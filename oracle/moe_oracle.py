@@ -26,7 +26,12 @@ What it computes, step by step, with the passage each step follows:
   (TorchSpec pull request "Add Megatron-Core MTP training for Qwen3.5 MoE",
   "What's in it": routed experts, shared expert and shared-expert gate);
 * backward -- the grouped GEMM's dgrad and wgrad ("通信隐藏与混合精度 / TP
-  通信重叠" names the backward's dgrad/wgrad GEMMs).
+  通信重叠" names the backward's dgrad/wgrad GEMMs); the rest of the layer's
+  backward runs through the router softmax and the dispatch permute, the
+  operations the backward recomputes ("Activation Recomputation": selective
+  recompute of the router softmax and the dispatch permute in MoE layers):
+  combine backward, permute backward, router backward (chain rule of the
+  forward's definition).
 
 Readings where the pages are silent (each listed in the design notes):
   * routing weights are renormalised over the selected k (softmax over all
@@ -54,6 +59,7 @@ __all__ = [
     "silu", "silu_grad", "swiglu_ffn", "grouped_swiglu_fwd",
     "grouped_swiglu_bwd", "unpermute_combine", "shared_expert",
     "moe_layer_forward", "RouteResult", "PermuteResult",
+    "combine_backward", "permute_backward", "route_backward", "moe_layer_backward",
 ]
 
 
@@ -326,3 +332,134 @@ def moe_layer_forward(x, w_router, w1, w2, k, score_fn="softmax",
         y_sh = shared_expert(x, ws1, ws2, r.gate, prec)
     y = unpermute_combine(y_perm, p.slot_of, w, y_sh, prec)
     return y, r, p
+
+
+# --------------------------------------------------------------------------
+# Full-layer backward: the chain rule of the forward above, for a fixed
+# expert selection (the selection itself is piecewise constant).
+# --------------------------------------------------------------------------
+def combine_backward(dy, y_perm, slot_of, topk_w, y_shared=None, gate=None,
+                     prec=np.float64):
+    """Gradients of L = sum(dy * y) for
+         y[t] = sum_j w[t, j] Y[slot_of[t, j]] + gate[t] Ysh[t]
+    (Y and Ysh unweighted):
+         dY[slot_of[t, j]] = w[t, j] dy[t]
+         dw[t, j]          = <dy[t], Y[slot_of[t, j]]>
+         dgate[t]          = <dy[t], Ysh[t]>
+    A slot of -1 (a dropped choice) contributes nothing and gets dw = 0.
+    Returns (dY [N, d], dw [T, k], dgate [T] or None)."""
+    dy = _as(dy, prec)
+    y_perm = _as(y_perm, prec)
+    w = _as(topk_w, prec)
+    T, k = slot_of.shape
+    dY = np.zeros_like(y_perm)
+    dw = np.zeros((T, k), dtype=prec)
+    for j in range(k):
+        ok = slot_of[:, j] >= 0
+        rows = slot_of[ok, j]
+        dY[rows] = w[ok, j:j + 1] * dy[ok]
+        dw[ok, j] = np.einsum("td,td->t", dy[ok], y_perm[rows])
+    dgate = None
+    if y_shared is not None and gate is not None:
+        dgate = np.einsum("td,td->t", dy, _as(y_shared, prec))
+    return dY, dw, dgate
+
+
+def permute_backward(dx_perm, slot_of, prec=np.float64):
+    """dx[t] = sum_j dX[slot_of[t, j]]: each row of x went to k rows."""
+    dx_perm = _as(dx_perm, prec)
+    T, k = slot_of.shape
+    dx = np.zeros((T, dx_perm.shape[1]), dtype=prec)
+    for j in range(k):
+        ok = slot_of[:, j] >= 0
+        dx[ok] += dx_perm[slot_of[ok, j]]
+    return dx
+
+
+def route_backward(x, w_router, topk_idx, d_topk_w, score_fn="softmax",
+                   normalize=True, logit_bias=None, w_gate=None, d_gate=None,
+                   prec=np.float64):
+    """Back through the routing weights of the selection topk_idx to the
+    logits, then to x and the router weights (the bias is a constant).
+
+      s = score(z)                  softmax over E, or sigmoid
+      w[t, j] = s[t, e_j] / S_t     S_t = sum_j s[t, e_j]   (normalize)
+              = s[t, e_j]                                   (otherwise)
+      ds[t, e_i] = (dw[t, i] - sum_j dw[t, j] w[t, j]) / S_t   (normalize)
+                 = dw[t, i]                                    (otherwise)
+      dz = s * (ds - <ds, s>)  (softmax)   or   ds * s * (1 - s)  (sigmoid)
+      dW_r = dz^T x,   dx = dz W_r
+    Shared gate g = sigmoid(x . w_gate): dgl = d_gate * g (1 - g),
+      dw_gate = dgl^T x,  dx += dgl w_gate.
+    Returns (dx [T, d], dw_router [E, d], dz [T, E], dw_gate [d] or None)."""
+    x = _as(x, prec)
+    wr = _as(w_router, prec)
+    z = logits(x, w_router, logit_bias, prec)
+    s = scores(z, score_fn)
+    T, E = s.shape
+    rows = np.arange(T)[:, None]
+    idx = np.asarray(topk_idx)
+    dw = _as(d_topk_w, prec)
+    sel = s[rows, idx]
+    ds = np.zeros((T, E), dtype=prec)
+    if normalize:
+        S = sel.sum(axis=1, keepdims=True)
+        w = sel / S
+        ds_sel = (dw - (dw * w).sum(axis=1, keepdims=True)) / S
+    else:
+        ds_sel = dw
+    ds[rows, idx] = ds_sel
+    if score_fn == "softmax":
+        dz = s * (ds - (ds * s).sum(axis=1, keepdims=True))
+    elif score_fn == "sigmoid":
+        dz = ds * s * (1.0 - s)
+    else:
+        raise ValueError(score_fn)
+    dx = dz @ wr
+    dw_router = dz.T @ x
+    dw_gate = None
+    if w_gate is not None and d_gate is not None:
+        g = x @ _as(w_gate, prec)
+        with np.errstate(over="ignore"):
+            gs = 1.0 / (1.0 + np.exp(-g))
+        dgl = _as(d_gate, prec) * gs * (1.0 - gs)
+        dw_gate = dgl @ x
+        dx = dx + dgl[:, None] * _as(w_gate, prec)[None, :]
+    return dx, dw_router, dz, dw_gate
+
+
+def moe_layer_backward(x, w_router, w1, w2, k, dy, score_fn="softmax",
+                       normalize=True, logit_bias=None, w_gate=None, ws1=None,
+                       ws2=None, prec=np.float64, topk_idx=None):
+    """Gradients of L = sum(dy * y) for y from :func:`moe_layer_forward`
+    with the selection held fixed (``topk_idx``, or the oracle's own):
+    combine backward -> grouped-GEMM backward (and the shared expert's, row
+    scale = gate) -> permute backward -> router backward.  Returns a dict
+    with dx, dw_router, dw1, dw2 (and dws1, dws2, dw_gate with a shared
+    expert) plus the intermediates d_topk_w, d_gate, dz, dx_perm."""
+    E = w_router.shape[0]
+    T = x.shape[0]
+    r = route(x, w_router, k, score_fn, normalize, logit_bias, w_gate, prec)
+    idx = r.topk_idx if topk_idx is None else np.asarray(topk_idx)
+    w = r.topk_w if topk_idx is None else route_weights_for(
+        x, w_router, idx, score_fn, normalize, logit_bias, prec)
+    p = permute(x, idx, w, E)
+    y_perm = grouped_swiglu_fwd(p.x_perm, w1, w2, p.offsets, None, prec)
+    ysh = swiglu_ffn(x, ws1, ws2, prec)[0] if ws1 is not None else None
+    dY, dw, dgate = combine_backward(dy, y_perm, p.slot_of, w, ysh, r.gate, prec)
+    dx_perm, dw1, dw2 = grouped_swiglu_bwd(dY, p.x_perm, w1, w2, p.offsets, None, prec)
+    dx = permute_backward(dx_perm, p.slot_of, prec)
+    dxr, dw_router, dz, dw_gate = route_backward(x, w_router, idx, dw, score_fn, normalize,
+                                                 logit_bias, w_gate, dgate, prec)
+    out = dict(dx_perm=dx_perm, d_topk_w=dw, d_gate=dgate, dz=dz, dw1=dw1, dw2=dw2,
+               dw_router=dw_router, topk_idx=idx, topk_w=w, offsets=p.offsets,
+               slot_of=p.slot_of, row_token=p.row_token)
+    dx = dx + dxr
+    if ws1 is not None:
+        off = np.array([0, T])
+        dxs, dws1, dws2 = grouped_swiglu_bwd(dy, x, _as(ws1, prec)[None], _as(ws2, prec)[None],
+                                             off, r.gate, prec)
+        dx = dx + dxs
+        out.update(dws1=dws1[0], dws2=dws2[0], dw_gate=dw_gate)
+    out["dx"] = dx
+    return out
