@@ -64,6 +64,9 @@ def parse():
     ap.add_argument("--workload", default="qwen3_30b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
+    ap.add_argument("--train", action="store_true",
+                    help="time a training step of the layer (forward keeping what the "
+                         "backward needs + the full backward) instead of the forward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (scales the HBM "
                          "byte counters FETCH_SIZE / WRITE_SIZE) and exit")
@@ -152,6 +155,8 @@ def main():
     torch.cuda.set_device(dev)
     if cfg.backward:
         return bench_ep_share(args, cfg, dev)
+    if args.train:
+        return bench_train(args, cfg, dev)
     inp = mw.make_layer_inputs(cfg)
 
     def gpu(a):
@@ -271,6 +276,71 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, cfg, min(args.cpu_sample_tokens, cfg.T))
+    print(json.dumps(out), flush=True)
+
+
+def bench_train(args, cfg, dev):
+    """One training step of the whole layer: forward in training mode (x_perm,
+    G/U and unweighted expert outputs kept) + backward (combine backward,
+    grouped-GEMM dgrad/wgrad, shared expert, permute + router backward)."""
+    import numpy as np
+    import torch
+
+    import moe_workloads as mw
+    import mixture_experts_layer_05_amd as moe
+
+    inp = mw.make_layer_inputs(cfg)
+
+    def gpu(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    x = gpu(inp.x)
+    rng = np.random.default_rng(cfg.index + 500)
+    dy = gpu(mw.round_to_bf16_bits(rng.standard_normal((cfg.T, cfg.d)).astype(np.float32)))
+    layer = moe.MoELayer(gpu(inp.w_router), gpu(inp.w1), gpu(inp.w2), cfg.k, cfg.T, cfg.score,
+                         cfg.normalize, gpu(inp.logit_bias), gpu(inp.w_gate), gpu(inp.ws1),
+                         gpu(inp.ws2), train=True)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        layer.forward(x)
+        if ev is not None:
+            ev[1].record(stream)
+        layer.backward(dy)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_f = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    t_b = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    N = cfg.T * cfg.k
+    flop = 18.0 * N * cfg.d * cfg.F + 18.0 * cfg.T * cfg.d * cfg.Fs
+    out = {
+        "metric": "MoE layer training step (fwd+bwd) tokens/s, 1 MI355X",
+        "value": round(cfg.T / (wall / args.steps), 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded PCG64, same recipe as the forward bench; dy ~ N(0,1))",
+        "config": {"workload": f"{cfg.name}: T={cfg.T} d={cfg.d} E={cfg.E} top-{cfg.k} "
+                               f"{cfg.score} ffn={cfg.F} shared={cfg.Fs}"},
+        "fwd_ms": round(t_f, 4), "bwd_ms": round(t_b, 4),
+        "expert_gemm_tflops_fwd_bwd": round(flop / ((t_f + t_b) * 1e-3) / 1e12, 1),
+    }
     print(json.dumps(out), flush=True)
 
 

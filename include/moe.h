@@ -246,13 +246,18 @@ MOE_API moe_status moe_grouped_swiglu_bwd(hipStream_t stream, moe_dtype dt, int6
  * Passage: "Megatron-Bridge 深度剖析", "Expert Parallel 基础" step 3 (the
  * results go back to the tokens' original layout) and "Shared Expert
  * Overlap" (the shared expert's output joins the routed result):
- *     y[t] = sum_j topk_w[t,j] * y_perm[slot_of[t,j]]  (+ y_shared[t])
+ *     y[t] = sum_j topk_w[t,j] * y_perm[slot_of[t,j]]
+ *            (+ shared_gate[t] * y_shared[t], gate 1 when NULL)
  * summed in fp32 in slot order j = 0..k-1, rounded once to dt.  With
  * topk_w = NULL the rows are taken as already weighted (the forward can
- * apply the weight through row_scale).  slot_of < 0 entries are skipped.
+ * apply the weight through row_scale, and the gate likewise).  slot_of < 0
+ * entries are skipped.  A training forward keeps y_perm and y_shared
+ * unweighted and passes topk_w and shared_gate here, so that
+ * moe_combine_backward can form the weight and gate gradients.
  *
  *   y_perm   [N, d] dt   in        slot_of [T, k] int32  in
  *   topk_w   [T, k] fp32 in/NULL   y_shared [T, d] dt in/NULL
+ *   shared_gate [T] fp32 in/NULL (requires y_shared)
  *   y        [T, d] dt   out
  * No workspace.  Limits: 1 <= k <= 32, d*elt % 16 == 0.
  * --------------------------------------------------------------------- */
@@ -260,7 +265,77 @@ MOE_API moe_status moe_unpermute_combine(hipStream_t stream, moe_dtype dt, int64
                                  int64_t d, int32_t k, int64_t N,
                                  const void* y_perm, const int32_t* slot_of,
                                  const float* topk_w, const void* y_shared,
-                                 void* y);
+                                 const float* shared_gate, void* y);
+
+/* ------------------------------------------------------------------------
+ * moe_combine_backward -- backward of the weighted combine.
+ *
+ * Passage: "Megatron-Bridge 深度剖析", "Expert Parallel 基础" step 3 and
+ * "Shared Expert Overlap" (the forward being differentiated), "Activation
+ * Recomputation" (the layer's backward).  For
+ *     y[t] = sum_j w[t,j] Y[s(t,j)] + gate[t] Ysh[t],   s = slot_of,
+ * with Y = y_perm and Ysh = y_shared unweighted:
+ *     dy_perm[s(t,j)] = w[t,j] dy[t]
+ *     d_topk_w[t,j]   = <dy[t], Y[s(t,j)]>        (0 for slot_of < 0)
+ *     d_gate[t]       = <dy[t], Ysh[t]>
+ * Dot products in fp32 (fixed order), dy_perm rounded once to dt.  Rows of
+ * dy_perm that no (t, j) maps to are left unwritten.
+ *
+ *   dy       [T, d] dt    in       y_perm [N, d] dt  in (unweighted)
+ *   slot_of  [T, k] int32 in       topk_w [T, k] fp32 in
+ *   y_shared [T, d] dt    in/NULL (unweighted; then d_gate is required)
+ *   dy_perm  [N, d] dt    out      d_topk_w [T, k] fp32 out
+ *   d_gate   [T]    fp32  out/NULL
+ * No workspace.  Limits: 1 <= k <= 32, d % 8 == 0.
+ * --------------------------------------------------------------------- */
+MOE_API moe_status moe_combine_backward(hipStream_t stream, moe_dtype dt, int64_t T,
+                                int64_t d, int32_t k, int64_t N, const void* dy,
+                                const void* y_perm, const int32_t* slot_of,
+                                const float* topk_w, const void* y_shared,
+                                void* dy_perm, float* d_topk_w, float* d_gate);
+
+/* ------------------------------------------------------------------------
+ * moe_route_backward -- permute backward + router backward (+ shared gate).
+ *
+ * Passage: "Megatron-Bridge 深度剖析", "Activation Recomputation" (the
+ * backward recomputes the router softmax and the dispatch permute), with
+ * the forward of moe_route / moe_permute.  For the selection topk_idx held
+ * fixed, w = normalise(score(z)) (z = x W_r^T + b, score softmax or
+ * sigmoid), c[t] = sum_j d_topk_w[t,j] w[t,j]:
+ *     softmax, normalised:  dz[t,e_j] = w[t,j] (d_topk_w[t,j] - c[t])
+ *     sigmoid, normalised:  dz[t,e_j] = (d_topk_w[t,j] - c[t]) / S[t] s (1 - s)
+ *     sigmoid:              dz[t,e_j] = d_topk_w[t,j] s (1 - s)
+ * (s = sigmoid(z[t,e_j]) recomputed in fp32, S[t] = sum_j s); dz = 0 off
+ * the selection.  Shared gate g = sigmoid(x . w_gate): dgl = d_gate g (1-g).
+ *     dx[t]        = sum_j dx_perm[slot_of[t,j]] + sum_j dz[t,e_j] W_r[e_j]
+ *                    + dgl[t] w_gate + dx_add[t]          (rounded once)
+ *     dw_router[e] (+)= sum over expert e's rows r of dz[r] x[row_token[r]]
+ *     dw_gate      (+)= sum_t dgl[t] x[t]
+ * All sums fp32 in a fixed order.  Softmax without normalisation (a dense
+ * dz) returns MOE_ERR_UNSUPPORTED.
+ *
+ *   x [T, d], w_router [E, d], w_gate [d] or NULL: dt, as in the forward
+ *   logit_bias [E] fp32 or NULL
+ *   topk_idx, topk_w [T, k]: moe_route's outputs;  d_topk_w [T, k] fp32
+ *   d_gate [T] fp32 (with w_gate, else NULL)
+ *   expert_offsets [E+1], slot_of [T, k], row_token [T*k]: moe_permute's
+ *   dx_perm [T*k, d] dt or NULL (the grouped backward's dx)
+ *   dx_add  [T, d] dt or NULL (added to dx, e.g. the shared expert's dx)
+ *   dx [T, d] dt out;  dw_router [E, d] fp32;  dw_gate [d] fp32 (with w_gate)
+ *   accumulate int32: 0 dw = grad, 1 dw += grad (dx is always written)
+ * Workspace: moe_route_backward_workspace_size(T, d, k) bytes.
+ * Limits: 1 <= k <= min(E, 32), E <= 1024, d % 8 == 0.
+ * --------------------------------------------------------------------- */
+MOE_API size_t moe_route_backward_workspace_size(int64_t T, int64_t d, int32_t k);
+MOE_API moe_status moe_route_backward(hipStream_t stream, moe_dtype dt, int64_t T, int64_t d,
+                              int32_t E, int32_t k, moe_score_fn fn, int32_t normalize,
+                              const void* x, const void* w_router, const float* logit_bias,
+                              const void* w_gate, const int32_t* topk_idx,
+                              const float* topk_w, const float* d_topk_w, const float* d_gate,
+                              const int32_t* expert_offsets, const int32_t* slot_of,
+                              const int32_t* row_token, const void* dx_perm,
+                              const void* dx_add, void* dx, float* dw_router, float* dw_gate,
+                              int32_t accumulate, void* ws, size_t ws_bytes);
 
 #ifdef __cplusplus
 }

@@ -20,7 +20,8 @@ import torch
 
 __all__ = [
     "MoEError", "lib", "route", "permute", "grouped_swiglu_fwd", "grouped_swiglu_fwd_gather",
-    "grouped_swiglu_bwd", "unpermute_combine", "moe_layer_forward",
+    "grouped_swiglu_bwd", "unpermute_combine", "combine_backward", "route_backward",
+    "moe_layer_forward",
     "MoELayer", "LIB_PATH", "EXPORTED",
 ]
 
@@ -54,7 +55,13 @@ EXPORTED = {
                                       _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                                       _vp, _vp, _vp, _vp, _sz]),
     "moe_unpermute_combine": (_i32, [_vp, _i32, _i64, _i64, _i32, _i64,
-                                     _vp, _vp, _vp, _vp, _vp]),
+                                     _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_combine_backward": (_i32, [_vp, _i32, _i64, _i64, _i32, _i64,
+                                    _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_route_backward_workspace_size": (_sz, [_i64, _i64, _i32]),
+    "moe_route_backward": (_i32, [_vp, _i32, _i64, _i64, _i32, _i32, _i32, _i32,
+                                  _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                  _vp, _vp, _vp, _vp, _vp, _i32, _vp, _sz]),
 }
 
 
@@ -244,15 +251,67 @@ def grouped_swiglu_bwd(dy_perm, x_perm, w1, w2, expert_offsets, gu_save=None, ro
     return dx, dw1, dw2
 
 
-def unpermute_combine(y_perm, slot_of, topk_w=None, y_shared=None, out=None):
+def unpermute_combine(y_perm, slot_of, topk_w=None, y_shared=None, out=None, shared_gate=None):
     """-> y [T, d]"""
     T, k = slot_of.shape
     N, d = y_perm.shape
     y = out if out is not None else torch.empty((T, d), dtype=y_perm.dtype, device=y_perm.device)
     _check(lib().moe_unpermute_combine(_stream(), _dt(y_perm), T, d, k, N, _p(y_perm),
-                                       _p(slot_of), _p(topk_w), _p(y_shared), _p(y)),
+                                       _p(slot_of), _p(topk_w), _p(y_shared), _p(shared_gate),
+                                       _p(y)),
            "moe_unpermute_combine")
     return y
+
+
+def combine_backward(dy, y_perm, slot_of, topk_w, y_shared=None, dy_perm=None, d_topk_w=None,
+                     d_gate=None):
+    """-> (dy_perm [N,d], d_topk_w [T,k] fp32, d_gate [T] fp32 or None)"""
+    T, d = dy.shape
+    k = slot_of.shape[1]
+    N = y_perm.shape[0]
+    dev = dy.device
+    if dy_perm is None:
+        dy_perm = torch.empty((N, d), dtype=dy.dtype, device=dev)
+    if d_topk_w is None:
+        d_topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    if y_shared is not None and d_gate is None:
+        d_gate = torch.empty((T,), dtype=torch.float32, device=dev)
+    _check(lib().moe_combine_backward(_stream(), _dt(dy), T, d, k, N, _p(dy), _p(y_perm),
+                                      _p(slot_of), _p(topk_w), _p(y_shared), _p(dy_perm),
+                                      _p(d_topk_w), _p(d_gate if y_shared is not None else None)),
+           "moe_combine_backward")
+    return dy_perm, d_topk_w, d_gate if y_shared is not None else None
+
+
+def route_backward_workspace_size(T, d, k):
+    return lib().moe_route_backward_workspace_size(T, d, k)
+
+
+def route_backward(x, w_router, topk_idx, topk_w, d_topk_w, expert_offsets, slot_of, row_token,
+                   score="softmax", normalize=True, logit_bias=None, w_gate=None, d_gate=None,
+                   dx_perm=None, dx_add=None, accumulate=False, dx=None, dw_router=None,
+                   dw_gate=None, ws=None):
+    """-> (dx [T,d], dw_router [E,d] fp32, dw_gate [d] fp32 or None)"""
+    T, d = x.shape
+    E = w_router.shape[0]
+    k = topk_idx.shape[1]
+    dev = x.device
+    if dx is None:
+        dx = torch.empty((T, d), dtype=x.dtype, device=dev)
+    if dw_router is None:
+        dw_router = torch.zeros((E, d), dtype=torch.float32, device=dev)
+    if w_gate is not None and dw_gate is None:
+        dw_gate = torch.zeros((d,), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = _ws(route_backward_workspace_size(T, d, k), dev)
+    _check(lib().moe_route_backward(_stream(), _dt(x), T, d, E, k, SCORE[score], int(bool(normalize)),
+                                    _p(x), _p(w_router), _p(logit_bias), _p(w_gate), _p(topk_idx),
+                                    _p(topk_w), _p(d_topk_w), _p(d_gate), _p(expert_offsets),
+                                    _p(slot_of), _p(row_token), _p(dx_perm), _p(dx_add), _p(dx),
+                                    _p(dw_router), _p(dw_gate if w_gate is not None else None),
+                                    int(bool(accumulate)), _p(ws), ws.numel()),
+           "moe_route_backward")
+    return dx, dw_router, dw_gate if w_gate is not None else None
 
 
 # ---------------------------------------------------------------------------
@@ -264,11 +323,18 @@ class MoELayer:
     gate] -> combine.  Only kernel launches happen in ``forward``.  With
     ``gather`` (default) the permute makes no row copy and fc1 reads the
     token rows from x by row_token; otherwise x_perm is materialised.
+
+    ``train=True`` keeps what :meth:`backward` needs: x_perm, G and U (of the
+    routed and the shared expert), and the expert outputs unweighted (fc2
+    without a row scale; combine applies the routing weights and the gate).
     """
 
     def __init__(self, w_router, w1, w2, k, T, score="softmax", normalize=True,
                  logit_bias=None, w_gate=None, ws1=None, ws2=None, save_gu=False,
-                 gather=True):
+                 gather=True, train=False):
+        self.train = train
+        if train:
+            save_gu, gather = True, False
         self.gather = gather
         self.w_router, self.w1, self.w2 = w_router, w1, w2
         self.k, self.T, self.score, self.normalize = k, T, score, normalize
@@ -300,8 +366,33 @@ class MoELayer:
             self.y_shared = torch.empty((T, d), dtype=dt, device=dev)
             self.ws1_e = ws1.unsqueeze(0)
             self.ws2_e = ws2.unsqueeze(0)
+            self.gu_sh = torch.empty((T, 2 * Fs), dtype=dt, device=dev) if train else None
         self.ffn_ws = _ws(ws_f, dev)
         self.y = torch.empty((T, d), dtype=dt, device=dev)
+        if train:
+            self._alloc_backward(dev, dt)
+
+    def _alloc_backward(self, dev, dt):
+        T, N, d, E, F, k = self.T, self.N, self.d, self.E, self.F, self.k
+        f32 = torch.float32
+        self.dy_perm = torch.empty((N, d), dtype=dt, device=dev)
+        self.d_topk_w = torch.empty((T, k), dtype=f32, device=dev)
+        self.dx_perm = torch.empty((N, d), dtype=dt, device=dev)
+        self.dx = torch.empty((T, d), dtype=dt, device=dev)
+        self.dw1 = torch.zeros((E, 2 * F, d), dtype=f32, device=dev)
+        self.dw2 = torch.zeros((E, d, F), dtype=f32, device=dev)
+        self.dw_router = torch.zeros((E, d), dtype=f32, device=dev)
+        bwd_ws = bwd_workspace_size(N, F, dt, False)
+        if self.ws1 is not None:
+            Fs = self.ws1.shape[0] // 2
+            bwd_ws = max(bwd_ws, bwd_workspace_size(T, Fs, dt, False))
+            self.d_gate = torch.empty((T,), dtype=f32, device=dev)
+            self.dx_shared = torch.empty((T, d), dtype=dt, device=dev)
+            self.dws1 = torch.zeros((1, 2 * Fs, d), dtype=f32, device=dev)
+            self.dws2 = torch.zeros((1, d, Fs), dtype=f32, device=dev)
+            self.dw_gate = torch.zeros((d,), dtype=f32, device=dev)
+        self.bwd_ws = _ws(bwd_ws, dev)
+        self.rbwd_ws = _ws(route_backward_workspace_size(T, d, k), dev)
 
     def forward(self, x):
         idx, w, cnt, gate = route(x, self.w_router, self.k, self.score, self.normalize,
@@ -309,19 +400,58 @@ class MoELayer:
                                   ws=self.route_ws)
         off, slot, rtok, rw, xp = permute(x, idx, w, self.E, out=self.perm_out, ws=self.perm_ws,
                                           copy_rows=not self.gather)
+        rs = None if self.train else rw      # training: weights applied in combine
         if self.gather:
-            grouped_swiglu_fwd_gather(x, rtok, self.w1, self.w2, off, row_scale=rw,
+            grouped_swiglu_fwd_gather(x, rtok, self.w1, self.w2, off, row_scale=rs,
                                       out=self.y_perm, gu_out=self.gu,
                                       save_gu=self.gu is not None, ws=self.ffn_ws)
         else:
-            grouped_swiglu_fwd(xp, self.w1, self.w2, off, row_scale=rw, out=self.y_perm,
+            grouped_swiglu_fwd(xp, self.w1, self.w2, off, row_scale=rs, out=self.y_perm,
                                gu_out=self.gu, save_gu=self.gu is not None, ws=self.ffn_ws)
         ysh = None
         if self.ws1 is not None:
-            grouped_swiglu_fwd(x, self.ws1_e, self.ws2_e, self.shared_off, row_scale=gate,
-                               out=self.y_shared, ws=self.ffn_ws)
+            grouped_swiglu_fwd(x, self.ws1_e, self.ws2_e, self.shared_off,
+                               row_scale=None if self.train else gate, out=self.y_shared,
+                               gu_out=self.gu_sh if self.train else None, save_gu=self.train,
+                               ws=self.ffn_ws)
             ysh = self.y_shared
+        if self.train:
+            self.x_saved = x
+            return unpermute_combine(self.y_perm, slot, w, ysh, out=self.y, shared_gate=gate)
         return unpermute_combine(self.y_perm, slot, None, ysh, out=self.y)
+
+    def backward(self, dy, accumulate=False):
+        """Gradients of sum(dy * y) for the last forward (``train=True``):
+        combine backward -> grouped-GEMM backward (and the shared expert's,
+        row scale = gate) -> permute + router backward.  Returns a dict with
+        dx, dw_router, dw1, dw2 (+ dws1, dws2, dw_gate with a shared expert);
+        weight gradients are fp32 and accumulate into the held buffers when
+        ``accumulate``.  Only kernel launches happen here."""
+        if not self.train:
+            raise MoEError("MoELayer.backward needs train=True")
+        x = self.x_saved
+        idx, w, _, gate = self.route_out
+        off, slot, rtok, _, xp = self.perm_out
+        shared = self.ws1 is not None
+        combine_backward(dy, self.y_perm, slot, w, self.y_shared if shared else None,
+                         dy_perm=self.dy_perm, d_topk_w=self.d_topk_w,
+                         d_gate=self.d_gate if shared else None)
+        grouped_swiglu_bwd(self.dy_perm, xp, self.w1, self.w2, off, self.gu, None, accumulate,
+                           self.dw1, self.dw2, dx_out=self.dx_perm, ws=self.bwd_ws)
+        if shared:
+            grouped_swiglu_bwd(dy, x, self.ws1_e, self.ws2_e, self.shared_off, self.gu_sh, gate,
+                               accumulate, self.dws1, self.dws2, dx_out=self.dx_shared,
+                               ws=self.bwd_ws)
+        route_backward(x, self.w_router, idx, w, self.d_topk_w, off, slot, rtok, self.score,
+                       self.normalize, self.logit_bias, self.w_gate,
+                       self.d_gate if shared else None, dx_perm=self.dx_perm,
+                       dx_add=self.dx_shared if shared else None, accumulate=accumulate,
+                       dx=self.dx, dw_router=self.dw_router,
+                       dw_gate=self.dw_gate if shared else None, ws=self.rbwd_ws)
+        g = dict(dx=self.dx, dw_router=self.dw_router, dw1=self.dw1, dw2=self.dw2)
+        if shared:
+            g.update(dws1=self.dws1[0], dws2=self.dws2[0], dw_gate=self.dw_gate)
+        return g
 
 
 def moe_layer_forward(x, w_router, w1, w2, k, score="softmax", normalize=True,

@@ -1,4 +1,4 @@
-// moe_unpermute_combine: y[t] = sum_j w[t,j] * y_perm[slot_of[t,j]] (+ y_shared[t])
+// moe_unpermute_combine: y[t] = sum_j w[t,j] * y_perm[slot_of[t,j]] (+ gate[t] * y_shared[t])
 //
 // Passage: "Megatron-Bridge 深度剖析", section "Expert Parallel 基础", step 3
 // (expert results return to the tokens' original layout) and section
@@ -18,7 +18,8 @@ template <bool kBF16>
 __global__ __launch_bounds__(kCombThreads) void combine_kernel(
     int T, int k, int N, int nchunk16, const u32x4* __restrict__ y_perm,
     const int32_t* __restrict__ slot_of, const float* __restrict__ topk_w,
-    const u32x4* __restrict__ y_shared, u32x4* __restrict__ y) {
+    const u32x4* __restrict__ y_shared, const float* __restrict__ shared_gate,
+    u32x4* __restrict__ y) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (kCombThreads / 64) + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -52,15 +53,16 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
     }
     if (y_shared) {
       const u32x4 v = y_shared[static_cast<size_t>(t) * nchunk16 + c];
+      const float g = shared_gate ? shared_gate[t] : 1.0f;
       if constexpr (kBF16) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          acc[2 * q] += bf16lo(v[q]);
-          acc[2 * q + 1] += bf16hi(v[q]);
+          acc[2 * q] = fmaf(g, bf16lo(v[q]), acc[2 * q]);
+          acc[2 * q + 1] = fmaf(g, bf16hi(v[q]), acc[2 * q + 1]);
         }
       } else {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[q] += __uint_as_float(v[q]);
+        for (int q = 0; q < 4; ++q) acc[q] = fmaf(g, __uint_as_float(v[q]), acc[q]);
       }
     }
     u32x4 o;
@@ -83,18 +85,19 @@ extern "C" moe_status moe_unpermute_combine(hipStream_t stream, moe_dtype dt, in
                                             int64_t d, int32_t k, int64_t N,
                                             const void* y_perm, const int32_t* slot_of,
                                             const float* topk_w, const void* y_shared,
-                                            void* y) {
+                                            const float* shared_gate, void* y) {
   if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_DTYPE;
-  if (!y_perm || !slot_of || !y) return MOE_ERR_INVALID_ARG;
+  if (!y_perm || !slot_of || !y || (shared_gate && !y_shared)) return MOE_ERR_INVALID_ARG;
   if (T < 1 || d < 1 || k < 1 || k > 32 || N < 0 || N >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
   const size_t row_bytes = static_cast<size_t>(d) * elt_size(dt);
   if (row_bytes % 16) return MOE_ERR_ALIGNMENT;
   if (!aligned16(y_perm) || !aligned16(slot_of) || !aligned16(topk_w) || !aligned16(y_shared) ||
-      !aligned16(y))
+      !aligned16(shared_gate) || !aligned16(y))
     return MOE_ERR_ALIGNMENT;
   auto kern = dt == MOE_BF16 ? combine_kernel<true> : combine_kernel<false>;
   return hip_status(launch(kern, dim3(static_cast<unsigned>((T + 3) / 4)), dim3(kCombThreads), 0,
                            stream, (int)T, k, (int)N, static_cast<int>(row_bytes / 16),
                            static_cast<const u32x4*>(y_perm), slot_of, topk_w,
-                           static_cast<const u32x4*>(y_shared), static_cast<u32x4*>(y)));
+                           static_cast<const u32x4*>(y_shared), shared_gate,
+                           static_cast<u32x4*>(y)));
 }

@@ -1,0 +1,393 @@
+// The layer's backward around the grouped GEMM: combine backward and
+// permute + router backward.
+//
+// Passages: "Megatron-Bridge 深度剖析", section "Activation Recomputation"
+// (the backward of an MoE layer recomputes the router softmax and the
+// dispatch permute), section "Expert Parallel 基础" step 3 (combine: the
+// expert results return to token order, weighted) and "Shared Expert
+// Overlap" (the gated shared expert joins the routed result).  The
+// derivatives are the chain rule of the forward:
+//   combine  y[t] = sum_j w[t,j] Y[s(t,j)] + gate[t] Ysh[t]
+//            dY[s(t,j)] = w[t,j] dy[t];  dw[t,j] = <dy[t], Y[s(t,j)]>;
+//            dgate[t] = <dy[t], Ysh[t]>
+//   permute  dx[t] += sum_j dX[s(t,j)]
+//   router   w = normalise(score(z)) on the selection; dz is non-zero on the
+//            selected experts only (see rbwd_token_kernel);
+//            dx[t] += sum_j dz[t,j] W_r[e_j];  dW_r[e] = sum_{t: e chosen} dz x[t]
+//   gate     g = sigmoid(x . w_gate): dgl = dgate g (1 - g);
+//            dx[t] += dgl[t] w_gate;  dw_gate = sum_t dgl[t] x[t]
+// All sums run in fp32 in a fixed order (deterministic, no atomics); every
+// output is rounded once.
+#include "moe_internal.h"
+
+namespace moe {
+
+constexpr int kLbThreads = 256;   // 4 wavefronts, one token each
+
+// 8 values of a 16-byte chunk as fp32
+template <bool kBF16>
+__device__ __forceinline__ void load8(const void* base, size_t chunk, float (&v)[8]) {
+  if constexpr (kBF16) {
+    const u32x4 c = static_cast<const u32x4*>(base)[chunk];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = bf16lo(c[q]);
+      v[2 * q + 1] = bf16hi(c[q]);
+    }
+  } else {
+    const u32x4 c0 = static_cast<const u32x4*>(base)[2 * chunk];
+    const u32x4 c1 = static_cast<const u32x4*>(base)[2 * chunk + 1];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[q] = __uint_as_float(c0[q]);
+      v[4 + q] = __uint_as_float(c1[q]);
+    }
+  }
+}
+template <bool kBF16>
+__device__ __forceinline__ void store8(void* base, size_t chunk, const float (&v)[8]) {
+  if constexpr (kBF16) {
+    u32x4 c;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) c[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
+    static_cast<u32x4*>(base)[chunk] = c;
+  } else {
+    u32x4 c0, c1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      c0[q] = __float_as_uint(v[q]);
+      c1[q] = __float_as_uint(v[4 + q]);
+    }
+    static_cast<u32x4*>(base)[2 * chunk] = c0;
+    static_cast<u32x4*>(base)[2 * chunk + 1] = c1;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Combine backward: one wavefront per token; a lane owns chunks of 8 columns.
+// ---------------------------------------------------------------------------
+template <bool kBF16>
+__global__ __launch_bounds__(kLbThreads) void combine_bwd_kernel(
+    int T, int k, int N, int nchunk, const void* __restrict__ dy, const void* __restrict__ y_perm,
+    const int32_t* __restrict__ slot_of, const float* __restrict__ topk_w,
+    const void* __restrict__ y_shared, void* __restrict__ dy_perm, float* __restrict__ d_topk_w,
+    float* __restrict__ d_gate) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kLbThreads / 64) + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const size_t trow = static_cast<size_t>(t) * nchunk;
+  for (int j = 0; j < k; ++j) {
+    int row = slot_of[static_cast<size_t>(t) * k + j];
+    if (row >= N) row = -1;
+    float dot = 0.0f;
+    if (row >= 0) {
+      const float w = topk_w[static_cast<size_t>(t) * k + j];
+      const size_t rrow = static_cast<size_t>(row) * nchunk;
+      for (int c = lane; c < nchunk; c += 64) {
+        float g[8], yv[8], o[8];
+        load8<kBF16>(dy, trow + c, g);
+        load8<kBF16>(y_perm, rrow + c, yv);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          dot = fmaf(g[q], yv[q], dot);
+          o[q] = w * g[q];
+        }
+        store8<kBF16>(dy_perm, rrow + c, o);
+      }
+    }
+    dot = wave_sum(dot);
+    if (lane == 0) d_topk_w[static_cast<size_t>(t) * k + j] = row >= 0 ? dot : 0.0f;
+  }
+  if (y_shared && d_gate) {
+    float dot = 0.0f;
+    for (int c = lane; c < nchunk; c += 64) {
+      float g[8], yv[8];
+      load8<kBF16>(dy, trow + c, g);
+      load8<kBF16>(y_shared, trow + c, yv);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) dot = fmaf(g[q], yv[q], dot);
+    }
+    dot = wave_sum(dot);
+    if (lane == 0) d_gate[t] = dot;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Router + permute backward, per token (one wavefront each).
+//
+// With the selection e_1..e_k fixed, w_j = s_j / S (normalise, S = sum_j s_j)
+// or w_j = s_j, s = score(z).  Writing c = sum_j dw_j w_j:
+//   softmax, normalised:  dz[e_j] = w_j (dw_j - c), dz = 0 off the selection
+//                         (the full-softmax denominator cancels in w);
+//   sigmoid, normalised:  dz[e_j] = (dw_j - c) / S * s_j (1 - s_j);
+//   sigmoid:              dz[e_j] = dw_j s_j (1 - s_j).
+// (Softmax without renormalisation has a dense dz; the entry point rejects it.)
+// The sigmoid forms need s_j = sigmoid(z_j): z_j = x[t] . W_r[e_j] (+ b) is
+// recomputed here in fp32.
+// ---------------------------------------------------------------------------
+template <bool kBF16>
+__global__ __launch_bounds__(kLbThreads) void rbwd_token_kernel(
+    int T, int k, int E, int N, int nchunk, int sigmoid, int normalize,
+    const void* __restrict__ x, const void* __restrict__ w_router,
+    const float* __restrict__ logit_bias, const void* __restrict__ w_gate,
+    const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_w,
+    const float* __restrict__ d_topk_w, const float* __restrict__ d_gate,
+    const int32_t* __restrict__ slot_of, const void* __restrict__ dx_perm,
+    const void* __restrict__ dx_add, void* __restrict__ dx, float* __restrict__ dz_slot,
+    float* __restrict__ dgl_tok) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kLbThreads / 64) + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const size_t trow = static_cast<size_t>(t) * nchunk;
+  // lane j < k holds choice j
+  int e = -1, row = -1;
+  float w = 0.0f, dw = 0.0f;
+  if (lane < k) {
+    e = topk_idx[static_cast<size_t>(t) * k + lane];
+    row = slot_of[static_cast<size_t>(t) * k + lane];
+    w = topk_w[static_cast<size_t>(t) * k + lane];
+    dw = d_topk_w[static_cast<size_t>(t) * k + lane];
+    if (e < 0 || e >= E) e = -1;
+    if (row >= N) row = -1;
+  }
+  float s = 0.0f;   // sigmoid score of choice `lane` (sigmoid only)
+  if (sigmoid) {
+    for (int j = 0; j < k; ++j) {
+      const int ej = __shfl(e, j, kWave);
+      float dot = 0.0f;
+      if (ej >= 0) {
+        const size_t erow = static_cast<size_t>(ej) * nchunk;
+        for (int c = lane; c < nchunk; c += 64) {
+          float xv[8], wv[8];
+          load8<kBF16>(x, trow + c, xv);
+          load8<kBF16>(w_router, erow + c, wv);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) dot = fmaf(xv[q], wv[q], dot);
+        }
+      }
+      dot = wave_sum(dot);
+      if (lane == j && ej >= 0) s = sigmoidf_(dot + (logit_bias ? logit_bias[ej] : 0.0f));
+    }
+  }
+  const bool mine = lane < k && e >= 0;
+  const float c = wave_sum(mine ? dw * w : 0.0f);
+  const float S = sigmoid && normalize ? wave_sum(mine ? s : 0.0f) : 1.0f;
+  float dz = 0.0f;
+  if (mine) {
+    if (!sigmoid) dz = w * (dw - c);                          // softmax, normalised
+    else if (normalize) dz = (dw - c) / S * s * (1.0f - s);
+    else dz = dw * s * (1.0f - s);
+  }
+  // every row of an expert segment is some token's valid choice, so the
+  // rows read by the dW_r pass are all written here
+  if (lane < k && row >= 0) dz_slot[row] = dz;
+  // shared gate
+  float dgl = 0.0f;
+  if (w_gate && d_gate) {
+    float dot = 0.0f;
+    for (int cc = lane; cc < nchunk; cc += 64) {
+      float xv[8], gv[8];
+      load8<kBF16>(x, trow + cc, xv);
+      load8<kBF16>(w_gate, cc, gv);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) dot = fmaf(xv[q], gv[q], dot);
+    }
+    dot = wave_sum(dot);
+    const float g = sigmoidf_(dot);
+    dgl = d_gate[t] * g * (1.0f - g);
+    if (lane == 0) dgl_tok[t] = dgl;
+  }
+  // dx[t] = sum_j dX[row_j] + sum_j dz_j W_r[e_j] + dgl w_gate + dx_add[t]
+  for (int cc = lane; cc < nchunk; cc += 64) {
+    float acc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const int rj = __shfl(row, j, kWave);
+      const int ej = __shfl(e, j, kWave);
+      const float dzj = __shfl(dz, j, kWave);
+      float v[8];
+      if (dx_perm && rj >= 0) {
+        load8<kBF16>(dx_perm, static_cast<size_t>(rj) * nchunk + cc, v);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] += v[q];
+      }
+      if (ej >= 0 && dzj != 0.0f) {
+        load8<kBF16>(w_router, static_cast<size_t>(ej) * nchunk + cc, v);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = fmaf(dzj, v[q], acc[q]);
+      }
+    }
+    if (w_gate && d_gate) {
+      float v[8];
+      load8<kBF16>(w_gate, cc, v);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = fmaf(dgl, v[q], acc[q]);
+    }
+    if (dx_add) {
+      float v[8];
+      load8<kBF16>(dx_add, trow + cc, v);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] += v[q];
+    }
+    store8<kBF16>(dx, trow + cc, acc);
+  }
+}
+
+// dW_r[e, cols] (+)= sum over expert e's rows r (in row order) of
+// dz_slot[r] * x[row_token[r], cols].  Grid (E, column blocks of 512); a
+// lane owns 8 columns.
+template <bool kBF16>
+__global__ __launch_bounds__(64) void rbwd_dwr_kernel(int d, int nchunk,
+                                                      const int32_t* __restrict__ offsets,
+                                                      const int32_t* __restrict__ row_token,
+                                                      const float* __restrict__ dz_slot,
+                                                      const void* __restrict__ x,
+                                                      float* __restrict__ dw_router,
+                                                      int accumulate) {
+  const int e = blockIdx.x;
+  const int c = blockIdx.y * 64 + threadIdx.x;
+  if (c >= nchunk) return;
+  const int lo = offsets[e], hi = offsets[e + 1];
+  float acc[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+  for (int r = lo; r < hi; ++r) {
+    const float g = dz_slot[r];
+    float v[8];
+    load8<kBF16>(x, static_cast<size_t>(row_token[r]) * nchunk + c, v);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = fmaf(g, v[q], acc[q]);
+  }
+  float* dst = dw_router + static_cast<size_t>(e) * d + 8 * c;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) dst[q] = accumulate ? dst[q] + acc[q] : acc[q];
+}
+
+// dw_gate = sum_t dgl[t] x[t]: partial sums over token blocks of 256 in
+// token order, then a fixed-order sum over the blocks.
+constexpr int kGateRows = 256;
+template <bool kBF16>
+__global__ __launch_bounds__(64) void rbwd_dwg_partial_kernel(int T, int nchunk,
+                                                              const float* __restrict__ dgl_tok,
+                                                              const void* __restrict__ x,
+                                                              float* __restrict__ part) {
+  const int c = blockIdx.x * 64 + threadIdx.x;
+  if (c >= nchunk) return;
+  const int t0 = blockIdx.y * kGateRows, t1 = min(T, t0 + kGateRows);
+  float acc[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+  for (int t = t0; t < t1; ++t) {
+    const float g = dgl_tok[t];
+    float v[8];
+    load8<kBF16>(x, static_cast<size_t>(t) * nchunk + c, v);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = fmaf(g, v[q], acc[q]);
+  }
+  float* dst = part + static_cast<size_t>(blockIdx.y) * nchunk * 8 + 8 * c;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) dst[q] = acc[q];
+}
+__global__ __launch_bounds__(256) void rbwd_dwg_sum_kernel(int d, int nblk,
+                                                           const float* __restrict__ part,
+                                                           float* __restrict__ dw_gate,
+                                                           int accumulate) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= d) return;
+  float s = 0.0f;
+  for (int b = 0; b < nblk; ++b) s += part[static_cast<size_t>(b) * d + i];
+  dw_gate[i] = accumulate ? dw_gate[i] + s : s;
+}
+
+inline size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" moe_status moe_combine_backward(hipStream_t stream, moe_dtype dt, int64_t T, int64_t d,
+                                           int32_t k, int64_t N, const void* dy,
+                                           const void* y_perm, const int32_t* slot_of,
+                                           const float* topk_w, const void* y_shared,
+                                           void* dy_perm, float* d_topk_w, float* d_gate) {
+  if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_DTYPE;
+  if (!dy || !y_perm || !slot_of || !topk_w || !dy_perm || !d_topk_w) return MOE_ERR_INVALID_ARG;
+  if ((y_shared == nullptr) != (d_gate == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (T < 1 || d < 1 || k < 1 || k > 32 || N < 0 || N >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
+  if (d % 8) return MOE_ERR_ALIGNMENT;
+  if (!aligned16(dy) || !aligned16(y_perm) || !aligned16(slot_of) || !aligned16(topk_w) ||
+      !aligned16(y_shared) || !aligned16(dy_perm) || !aligned16(d_topk_w) || !aligned16(d_gate))
+    return MOE_ERR_ALIGNMENT;
+  auto kern = dt == MOE_BF16 ? combine_bwd_kernel<true> : combine_bwd_kernel<false>;
+  return hip_status(launch(kern, dim3(static_cast<unsigned>((T + 3) / 4)), dim3(kLbThreads), 0,
+                           stream, (int)T, k, (int)N, (int)(d / 8), dy, y_perm, slot_of, topk_w,
+                           y_shared, dy_perm, d_topk_w, d_gate));
+}
+
+extern "C" size_t moe_route_backward_workspace_size(int64_t T, int64_t d, int32_t k) {
+  if (T < 1 || d < 1 || k < 1) return 0;
+  const int64_t nblk = (T + kGateRows - 1) / kGateRows;
+  return align256(static_cast<size_t>(T) * k * sizeof(float)) +
+         align256(static_cast<size_t>(T) * sizeof(float)) +
+         align256(static_cast<size_t>(nblk) * d * sizeof(float));
+}
+
+extern "C" moe_status moe_route_backward(
+    hipStream_t stream, moe_dtype dt, int64_t T, int64_t d, int32_t E, int32_t k, moe_score_fn fn,
+    int32_t normalize, const void* x, const void* w_router, const float* logit_bias,
+    const void* w_gate, const int32_t* topk_idx, const float* topk_w, const float* d_topk_w,
+    const float* d_gate, const int32_t* expert_offsets, const int32_t* slot_of,
+    const int32_t* row_token, const void* dx_perm, const void* dx_add, void* dx,
+    float* dw_router, float* dw_gate, int32_t accumulate, void* ws, size_t ws_bytes) {
+  if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_DTYPE;
+  if (fn != MOE_SCORE_SOFTMAX && fn != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
+  if (fn == MOE_SCORE_SOFTMAX && !normalize) return MOE_ERR_UNSUPPORTED;
+  if (!x || !w_router || !topk_idx || !topk_w || !d_topk_w || !expert_offsets || !slot_of ||
+      !row_token || !dx || !dw_router)
+    return MOE_ERR_INVALID_ARG;
+  if ((w_gate == nullptr) != (d_gate == nullptr) || (w_gate == nullptr) != (dw_gate == nullptr))
+    return MOE_ERR_INVALID_ARG;
+  if (T < 1 || d < 1 || E < 1 || E > 1024 || k < 1 || k > 32 || k > E) return MOE_ERR_SHAPE;
+  if (T * static_cast<int64_t>(k) >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
+  if (d % 8) return MOE_ERR_ALIGNMENT;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(logit_bias) || !aligned16(w_gate) ||
+      !aligned16(topk_idx) || !aligned16(topk_w) || !aligned16(d_topk_w) || !aligned16(d_gate) ||
+      !aligned16(expert_offsets) || !aligned16(slot_of) || !aligned16(row_token) ||
+      !aligned16(dx_perm) || !aligned16(dx_add) || !aligned16(dx) || !aligned16(dw_router) ||
+      !aligned16(dw_gate) || !aligned16(ws))
+    return MOE_ERR_ALIGNMENT;
+  if (!ws || ws_bytes < moe_route_backward_workspace_size(T, d, k)) return MOE_ERR_WORKSPACE;
+  const int N = static_cast<int>(T * k);
+  const int nchunk = static_cast<int>(d / 8);
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  float* dz_slot = reinterpret_cast<float*>(wsb);
+  size_t off = align256(static_cast<size_t>(N) * sizeof(float));
+  float* dgl = reinterpret_cast<float*>(wsb + off);
+  off += align256(static_cast<size_t>(T) * sizeof(float));
+  float* part = reinterpret_cast<float*>(wsb + off);
+  const int nblk = static_cast<int>((T + kGateRows - 1) / kGateRows);
+  const bool bf = dt == MOE_BF16;
+  hipError_t err;
+  {
+    auto kern = bf ? rbwd_token_kernel<true> : rbwd_token_kernel<false>;
+    err = launch(kern, dim3(static_cast<unsigned>((T + 3) / 4)), dim3(kLbThreads), 0, stream,
+                 (int)T, k, E, N, nchunk, fn == MOE_SCORE_SIGMOID ? 1 : 0, normalize ? 1 : 0, x,
+                 w_router, logit_bias, w_gate, topk_idx, topk_w, d_topk_w, d_gate, slot_of,
+                 dx_perm, dx_add, dx, dz_slot, dgl);
+  }
+  if (err == hipSuccess) {
+    auto kern = bf ? rbwd_dwr_kernel<true> : rbwd_dwr_kernel<false>;
+    err = launch(kern, dim3(E, (nchunk + 63) / 64), dim3(64), 0, stream, (int)d, nchunk,
+                 expert_offsets, row_token, dz_slot, x, dw_router, accumulate);
+  }
+  if (err == hipSuccess && w_gate) {
+    auto kern = bf ? rbwd_dwg_partial_kernel<true> : rbwd_dwg_partial_kernel<false>;
+    err = launch(kern, dim3((nchunk + 63) / 64, nblk), dim3(64), 0, stream, (int)T, nchunk, dgl, x,
+                 part);
+    if (err == hipSuccess)
+      err = launch(rbwd_dwg_sum_kernel, dim3(static_cast<unsigned>((d + 255) / 256)), dim3(256),
+                   0, stream, (int)d, nblk, part, dw_gate, accumulate);
+  }
+  return hip_status(err);
+}

@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.moe_abi_version() == 3
+    assert L.moe_abi_version() == 4
     assert L.moe_status_string(0) == b"MOE_OK"
     assert L.moe_status_string(5) == b"MOE_ERR_WORKSPACE"
 
@@ -119,5 +119,37 @@ def test_grouped_validation(L):
     assert bwd(None, 0, 100, 64, 64, 4, P, P, P, P, P, P, None, 0, P, P, P, P, 1 << 30) == 6
     assert bwd(None, 1, 100, 64, 64, 4, P, P, P, P, P, P, None, 0, P, P, P, P, 16) == 5
     comb = L.moe_unpermute_combine
-    assert comb(None, 1, 16, 64, 0, 32, P, P, None, None, P) == 2
-    assert comb(None, 1, 16, 64, 2, 32, P, P, None, None, MIS) == 4
+    assert comb(None, 1, 16, 64, 0, 32, P, P, None, None, None, P) == 2
+    assert comb(None, 1, 16, 64, 2, 32, P, P, None, None, None, MIS) == 4
+    assert comb(None, 1, 16, 64, 2, 32, P, P, None, None, P, P) == 1   # gate without y_shared
+
+
+def test_layer_backward_validation(L):
+    cb = L.moe_combine_backward
+    ok = [None, 1, 16, 64, 2, 32, P, P, P, P, None, P, P, None]
+    def c(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return cb(*a)
+    assert c(a1=5) == 3                        # dtype
+    assert c(a9=None) == 1                     # topk_w required
+    assert c(a10=P) == 1                       # y_shared without d_gate
+    assert c(a3=60) == 4                       # d % 8
+    assert c(a4=33) == 2                       # k > 32
+    rb = L.moe_route_backward
+    ws = L.moe_route_backward_workspace_size(16, 64, 2)
+    assert ws >= 16 * 2 * 4 + 16 * 4
+    base = [None, 1, 16, 64, 8, 2, 0, 1, P, P, None, None, P, P, P, None, P, P, P, None, None,
+            P, P, None, 0, P, ws]
+    def r(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return rb(*a)
+    assert r(a7=0) == 6                        # softmax without renormalisation: unsupported
+    assert r(a6=3) == 1                        # score function
+    assert r(a11=P) == 1                       # w_gate without d_gate / dw_gate
+    assert r(a5=9) == 2                        # k > E
+    assert r(a26=16) == 5                      # workspace
+    assert r(a8=MIS) == 4

@@ -1,0 +1,137 @@
+"""GPU parity of the full-layer backward (combine, grouped GEMM, permute and
+router backward, shared expert and gate) against the oracle's
+moe_layer_backward, with the GPU's own expert selection held fixed.
+
+* small bf16 layers: softmax / sigmoid scores, with and without
+  renormalisation (sigmoid), logit bias and gated shared expert;
+* the combine and route backward kernels alone in fp32 (tolerance 1e-5);
+* the qwen3_30b workload at full size: dx on sampled tokens, router and
+  expert weight gradients on sampled experts (the oracle runs on exactly
+  the tokens routed to those experts).
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import moe_workloads as mw  # noqa: E402
+import oracle.moe_oracle as mo  # noqa: E402
+import gpu_helpers as gh  # noqa: E402
+
+moe = pytest.importorskip("mixture_experts_layer_05_amd")
+
+
+def _g(a):
+    return None if a is None else gh.to_gpu(a)
+
+
+CASES = [
+    # seed, T, d, E, k, F, Fs, score, normalize, bias
+    (21, 96, 128, 12, 3, 64, 0, "softmax", True, False),
+    (22, 130, 136, 10, 4, 72, 64, "sigmoid", True, True),
+    (23, 77, 64, 8, 2, 64, 0, "sigmoid", False, False),
+    (24, 160, 128, 16, 2, 96, 64, "softmax", True, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
+def test_layer_backward_parity(case):
+    seed, T, d, E, k, F, Fs, score, normalize, bias = case
+    inp = mw.make_small_layer_inputs(seed, T=T, d=d, E=E, F=F, dtype="bf16", Fs=Fs,
+                                     bias=bias, w_std=0.05)
+    rng = np.random.default_rng(seed)
+    dy = mw.round_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    layer = moe.MoELayer(_g(inp.w_router), _g(inp.w1), _g(inp.w2), k, T, score, normalize,
+                         _g(inp.logit_bias), _g(inp.w_gate), _g(inp.ws1), _g(inp.ws2), train=True)
+    x = gh.to_gpu(inp.x)
+    y = layer.forward(x)
+    g1 = {kk: v.clone() for kk, v in layer.backward(gh.to_gpu(dy)).items()}
+    g2 = layer.backward(gh.to_gpu(dy))
+    torch.cuda.synchronize()
+    for kk in g1:
+        assert gh.bits_equal(g1[kk], g2[kk]), f"{kk} not deterministic"
+    idx = layer.route_out[0].cpu().numpy()
+    f = inp.as_f32
+    ref = mo.moe_layer_backward(f("x"), f("w_router"), f("w1"), f("w2"), k,
+                                mw.bf16_bits_to_f32(dy), score, normalize, inp.logit_bias,
+                                f("w_gate"), f("ws1"), f("ws2"), topk_idx=idx)
+    yref, _, _ = mo.moe_layer_forward(f("x"), f("w_router"), f("w1"), f("w2"), k, score,
+                                      normalize, inp.logit_bias, f("w_gate"), f("ws1"), f("ws2"),
+                                      topk_idx=idx)
+    assert gh.normwise(gh.to_f64(y), yref) <= gh.TOL_BF16
+    errs = {}
+    for kk in g1:
+        errs[kk] = gh.normwise(gh.to_f64(g1[kk]), np.asarray(ref[kk]))
+    print(f"\n[{case}] normwise errors: " + ", ".join(f"{a} {b:.2e}" for a, b in errs.items()))
+    for kk, e in errs.items():
+        assert e <= gh.TOL_BF16_GRAD, (kk, e)
+
+
+def test_combine_and_route_backward_fp32():
+    """The two kernels alone, fp32 storage, against the oracle's functions."""
+    rng = np.random.default_rng(5)
+    T, d, E, k = 70, 64, 9, 3
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    wr = (rng.standard_normal((E, d)) * 0.3).astype(np.float32)
+    wg = (rng.standard_normal(d) * 0.3).astype(np.float32)
+    bias = (rng.standard_normal(E) * 0.2).astype(np.float32)
+    for score, normalize in (("softmax", True), ("sigmoid", True), ("sigmoid", False)):
+        r = mo.route(x, wr, k, score, normalize, bias, wg)
+        idx = r.topk_idx
+        w = r.topk_w.astype(np.float32)
+        p = mo.permute(x, idx, w, E)
+        N = T * k
+        Y = rng.standard_normal((N, d)).astype(np.float32)
+        ysh = rng.standard_normal((T, d)).astype(np.float32)
+        gate = r.gate.astype(np.float32)
+        dy = rng.standard_normal((T, d)).astype(np.float32)
+        dXp = rng.standard_normal((N, d)).astype(np.float32)
+        dxa = rng.standard_normal((T, d)).astype(np.float32)
+        dYr, dwr_, dgr = mo.combine_backward(dy, Y, p.slot_of, w, ysh, gate)
+        dyp, dtw, dg = moe.combine_backward(_g(dy), _g(Y), _g(p.slot_of), _g(w), _g(ysh))
+        torch.cuda.synchronize()
+        assert gh.normwise(gh.to_f64(dyp), dYr) <= gh.TOL_F32
+        assert gh.normwise(gh.to_f64(dtw), dwr_) <= gh.TOL_F32
+        assert gh.normwise(gh.to_f64(dg), dgr) <= gh.TOL_F32
+        dx_ref, dwr_ref, _, dwg_ref = mo.route_backward(x, wr, idx, dwr_, score, normalize, bias,
+                                                        wg, dgr)
+        dx_ref = dx_ref + mo.permute_backward(dXp, p.slot_of) + dxa
+        dx, dwr_g, dwg_g = moe.route_backward(
+            _g(x), _g(wr), _g(idx), _g(w), dtw, _g(p.offsets), _g(p.slot_of), _g(p.row_token),
+            score, normalize, _g(bias), _g(wg), dg, dx_perm=_g(dXp), dx_add=_g(dxa))
+        torch.cuda.synchronize()
+        assert gh.normwise(gh.to_f64(dx), dx_ref) <= gh.TOL_F32, score
+        assert gh.normwise(gh.to_f64(dwr_g), dwr_ref) <= gh.TOL_F32, score
+        assert gh.normwise(gh.to_f64(dwg_g), dwg_ref) <= gh.TOL_F32, score
+
+
+def test_layer_backward_full_size_qwen3_30b():
+    cfg = mw.get("qwen3_30b")
+    inp = mw.make_layer_inputs(cfg)
+    f = inp.as_f32
+    rng = np.random.default_rng(77)
+    dy = mw.round_to_bf16_bits(rng.standard_normal((cfg.T, cfg.d)).astype(np.float32))
+    layer = moe.MoELayer(_g(inp.w_router), _g(inp.w1), _g(inp.w2), cfg.k, cfg.T, cfg.score,
+                         cfg.normalize, train=True)
+    layer.forward(gh.to_gpu(inp.x))
+    g = layer.backward(gh.to_gpu(dy))
+    torch.cuda.synchronize()
+    idx = layer.route_out[0].cpu().numpy()
+    # two sampled experts: the oracle on exactly the tokens routed to them
+    experts = [3, 77]
+    toks = np.nonzero(np.isin(idx, experts).any(axis=1))[0]
+    ref = mo.moe_layer_backward(f("x")[toks], f("w_router"), f("w1"), f("w2"), cfg.k,
+                                mw.bf16_bits_to_f32(dy)[toks], cfg.score, cfg.normalize,
+                                topk_idx=idx[toks])
+    tol = gh.TOL_BF16_GRAD
+    e_dx = gh.normwise(gh.to_f64(g["dx"][torch.from_numpy(toks).cuda()]), ref["dx"])
+    errs = {"dx": e_dx}
+    for e in experts:
+        errs[f"dw_router[{e}]"] = gh.normwise(gh.to_f64(g["dw_router"][e]), ref["dw_router"][e])
+        errs[f"dw1[{e}]"] = gh.normwise(gh.to_f64(g["dw1"][e]), ref["dw1"][e])
+        errs[f"dw2[{e}]"] = gh.normwise(gh.to_f64(g["dw2"][e]), ref["dw2"][e])
+    print("\n[qwen3_30b backward] " + ", ".join(f"{a} {b:.2e}" for a, b in errs.items())
+          + f" ({toks.size} tokens)")
+    for kk, e in errs.items():
+        assert e <= tol, (kk, e)
