@@ -175,11 +175,20 @@ def main():
     stages = ["route", "permute", "grouped_gemm", "shared", "combine"]
 
     def step(ev=None):
+        # the layer's forward, stage by stage (MoELayer.forward), with events
+        # on the main stream; the shared expert runs on a second stream
         L = layer
         if ev is not None:
             ev[0].record(stream)
+        if L.overlap_shared:
+            L.ev_x.record(stream)
+            L.side.wait_event(L.ev_x)
+            with torch.cuda.stream(L.side):
+                L._shared_unscaled(x)
+                L.ev_sh.record(L.side)
         idx, w, cnt, gate = moe.route(x, L.w_router, L.k, L.score, L.normalize, L.logit_bias,
-                                      L.w_gate, out=L.route_out, ws=L.route_ws)
+                                      L.w_gate, out=L.route_out, ws=L.route_ws,
+                                      selection_bias=L.selection_bias)
         if ev is not None:
             ev[1].record(stream)
         # permute folded into fc1: no row copy, fc1 gathers x rows by row_token
@@ -191,14 +200,18 @@ def main():
                                       ws=L.ffn_ws)
         if ev is not None:
             ev[3].record(stream)
-        ysh = None
+        ysh, sgate = None, None
         if L.ws1 is not None:
-            moe.grouped_swiglu_fwd(x, L.ws1_e, L.ws2_e, L.shared_off, row_scale=gate,
-                                   out=L.y_shared, ws=L.ffn_ws)
+            if L.overlap_shared:
+                stream.wait_event(L.ev_sh)     # "shared" = the part not hidden by the overlap
+                sgate = gate
+            else:                              # gate folded into the shared fc2 row scale
+                moe.grouped_swiglu_fwd(x, L.ws1_e, L.ws2_e, L.shared_off, row_scale=gate,
+                                       out=L.y_shared, ws=L.ffn_ws)
             ysh = L.y_shared
         if ev is not None:
             ev[4].record(stream)
-        moe.unpermute_combine(L.y_perm, slot, None, ysh, out=L.y)
+        moe.unpermute_combine(L.y_perm, slot, None, ysh, out=L.y, shared_gate=sgate)
         if ev is not None:
             ev[5].record(stream)
 

@@ -84,11 +84,16 @@ MOE_API const char* moe_status_string(moe_status s);
  * The k experts with the largest fp32 scores are chosen, in descending
  * score order (equal scores: lower expert index first).  With `normalize`
  * the weights are s / (sum of the k chosen s), else the raw scores.
+ * selection_bias (the expert-bias correction of the MoE-acceleration and
+ * recipe config listings, "moe_router_enable_expert_bias", DeepSeek-style)
+ * shifts only the choice: experts are ranked by the fp32 sum s + b[e],
+ * the weights still come from the unbiased s.
  * With w_gate, gate[t] = 1 / (1 + exp(-x[t] . w_gate)) (shared-expert gate).
  *
  *   x          [T, d]  dt        tokens
  *   w_router   [E, d]  dt        router weight (Megatron's router.weight)
- *   logit_bias [E]     fp32      or NULL
+ *   logit_bias [E]     fp32      or NULL (added to the logits: moves the weights too)
+ *   selection_bias [E] fp32      or NULL (ranking only; finite values)
  *   w_gate     [d]     dt        or NULL (then `gate` must be NULL too)
  *   topk_idx   [T, k]  int32     out
  *   topk_w     [T, k]  fp32      out
@@ -103,8 +108,8 @@ MOE_API size_t moe_route_workspace_size(int64_t T, int64_t d, int32_t E, moe_dty
 MOE_API moe_status moe_route(hipStream_t stream, moe_dtype dt, int64_t T, int64_t d,
                      int32_t E, int32_t k, moe_score_fn fn, int32_t normalize,
                      const void* x, const void* w_router,
-                     const float* logit_bias, const void* w_gate,
-                     int32_t* topk_idx, float* topk_w,
+                     const float* logit_bias, const float* selection_bias,
+                     const void* w_gate, int32_t* topk_idx, float* topk_w,
                      int32_t* expert_counts, float* gate, void* ws, size_t ws_bytes);
 
 /* ------------------------------------------------------------------------

@@ -12,7 +12,9 @@
 //      ring); fp32 runs a plain FMA dot product per (token, expert);
 //   3. route_topk: one wavefront per token; lane l holds the scores of
 //      experts l, l+64, ...; k rounds of a wave-wide arg-max (ties to the
-//      lower expert index) pick the experts in descending score order; the
+//      lower expert index) pick the experts in descending score order (or
+//      descending score + selection bias, when a selection-only expert bias
+//      is given: the weights still come from the unbiased scores); the
 //      workgroup's choices are counted in LDS and written as one histogram
 //      row; the gate is a wave-wide dot product x[t] . w_gate;
 //   4. route_count: counts[e] = sum of the histogram rows (one workgroup per
@@ -51,7 +53,8 @@ __global__ __launch_bounds__(256) void route_logits_f32_kernel(
 template <bool kBF16, int kPer>
 __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
     int T, int d, int E, int k, int score_fn, int normalize, int nslab, const float* __restrict__ z,
-    const void* __restrict__ xv, const void* __restrict__ wgv, int32_t* __restrict__ topk_idx,
+    const float* __restrict__ sel_bias, const void* __restrict__ xv, const void* __restrict__ wgv,
+    int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, int32_t* __restrict__ hist, float* __restrict__ gate) {
   extern __shared__ int s_cnt[];     // [E] histogram of this workgroup's choices
   for (int e = threadIdx.x; e < E; e += kTopkThreads) s_cnt[e] = 0;
@@ -90,6 +93,13 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
 #pragma unroll
     for (int i = 0; i < kPer; ++i) p[i] = (lane + 64 * i < E) ? sigmoidf_(p[i]) : -INFINITY;
   }
+  // ranking keys: the scores, or score + selection bias (fp32)
+  float key[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = (sel_bias && e < E) ? p[i] + sel_bias[e] : p[i];
+  }
   uint32_t taken = 0;
   int my_e = E;
   float my_p = 0.0f;
@@ -98,8 +108,8 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
     int bi = E;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      // strict '>' keeps the lower expert index among equal scores
-      if (!((taken >> i) & 1u) && p[i] > bv) { bv = p[i]; bi = lane + 64 * i; }
+      // strict '>' keeps the lower expert index among equal keys
+      if (!((taken >> i) & 1u) && key[i] > bv) { bv = key[i]; bi = lane + 64 * i; }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
@@ -107,8 +117,14 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
       const int oi = __shfl_xor(bi, o, kWave);
       if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
     }
+    // the winner's (unbiased) score, from the lane that holds it
+    float pw = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      if (i == (bi >> 6)) pw = p[i];
+    pw = __shfl(pw, bi & 63, kWave);
     if (bi < E && (bi & 63) == lane) taken |= 1u << (bi >> 6);
-    if (lane == j) { my_e = bi; my_p = bv; }
+    if (lane == j) { my_e = bi; my_p = pw; }
   }
   float denom = 1.0f;
   if (normalize) denom = wave_sum(lane < k ? my_p : 0.0f);
@@ -192,8 +208,8 @@ extern "C" size_t moe_route_workspace_size(int64_t T, int64_t d, int32_t E, moe_
 extern "C" moe_status moe_route(hipStream_t stream, moe_dtype dt, int64_t T, int64_t d,
                                 int32_t E, int32_t k, moe_score_fn fn, int32_t normalize,
                                 const void* x, const void* w_router,
-                                const float* logit_bias, const void* w_gate,
-                                int32_t* topk_idx, float* topk_w,
+                                const float* logit_bias, const float* selection_bias,
+                                const void* w_gate, int32_t* topk_idx, float* topk_w,
                                 int32_t* expert_counts, float* gate, void* ws, size_t ws_bytes) {
   if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_DTYPE;
   if (fn != MOE_SCORE_SOFTMAX && fn != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
@@ -207,7 +223,7 @@ extern "C" moe_status moe_route(hipStream_t stream, moe_dtype dt, int64_t T, int
   if (d % 8) return MOE_ERR_ALIGNMENT;
   if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || !aligned16(topk_idx) ||
       !aligned16(topk_w) || !aligned16(expert_counts) || !aligned16(gate) ||
-      !aligned16(logit_bias) || !aligned16(ws))
+      !aligned16(logit_bias) || !aligned16(selection_bias) || !aligned16(ws))
     return MOE_ERR_ALIGNMENT;
   if (!ws || ws_bytes < moe_route_workspace_size(T, d, E, dt)) return MOE_ERR_WORKSPACE;
 
@@ -229,8 +245,8 @@ extern "C" moe_status moe_route(hipStream_t stream, moe_dtype dt, int64_t T, int
   auto kern = dt == MOE_BF16 ? pick_topk<true>(E) : pick_topk<false>(E);
   const int nblk = static_cast<int>((T + kTopkTokens - 1) / kTopkTokens);
   err = launch(kern, dim3(nblk), dim3(kTopkThreads), E * sizeof(int), stream, (int)T, (int)d, E, k,
-               (int)fn, normalize, nslab, (const float*)z, x, w_gate, topk_idx, topk_w, hist,
-               gate);
+               (int)fn, normalize, nslab, (const float*)z, selection_bias, x, w_gate, topk_idx,
+               topk_w, hist, gate);
   if (err == hipSuccess)
     err = launch(route_count_kernel, dim3(E), dim3(256), 0, stream, nblk, E, (const int32_t*)hist,
                  expert_counts);

@@ -17,8 +17,11 @@ def f32(v: float) -> float:
     return struct.unpack("f", struct.pack("f", v))[0]
 
 
-def route(x, w_router, k, score_fn="softmax", normalize=True, bias=None):
-    """Per token: all E scores, fully sorted by (-fp32 score, index)."""
+def route(x, w_router, k, score_fn="softmax", normalize=True, bias=None,
+          selection_bias=None):
+    """Per token: all E scores, fully sorted by (-fp32 key, index); the key is
+    the fp32 score, plus the fp32 selection bias when given (the weights stay
+    the unbiased scores)."""
     T, d, E = len(x), len(x[0]), len(w_router)
     idx_out, w_out = [], []
     for t in range(T):
@@ -37,7 +40,10 @@ def route(x, w_router, k, score_fn="softmax", normalize=True, bias=None):
             s = [v / tot for v in ex]
         else:
             s = [1.0 / (1.0 + math.exp(-v)) for v in z]
-        ranked = sorted(range(E), key=lambda e: (-f32(s[e]), e))
+        if selection_bias is None:
+            ranked = sorted(range(E), key=lambda e: (-f32(s[e]), e))
+        else:
+            ranked = sorted(range(E), key=lambda e: (-f32(f32(s[e]) + f32(selection_bias[e])), e))
         chosen = ranked[:k]
         sel = [s[e] for e in chosen]
         tot = sum(sel)

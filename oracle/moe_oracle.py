@@ -98,7 +98,8 @@ class RouteResult:
     topk_w     [T, k]        routing weights (prec)
     counts     [E] int32     tokens per expert
     gate       [T] or None   sigmoid shared-expert gate
-    s32        [T, E] fp32   the scores the decision was taken on
+    s32        [T, E] fp32   the keys the decision was taken on (the fp32
+                             scores, plus the selection bias when given)
     margin     [T]           s_(k) - s_(k+1) in those fp32 scores (+inf if k=E)
     logit_margin [T]         z_(k) - z_(k+1) by the same order (+inf if k=E)
     """
@@ -111,16 +112,24 @@ class RouteResult:
 
 
 def route(x, w_router, k, score_fn="softmax", normalize=True,
-          logit_bias=None, w_gate=None, prec=np.float64):
-    """Router -> score -> top-k -> weight normalisation (+ shared gate)."""
+          logit_bias=None, w_gate=None, prec=np.float64, selection_bias=None):
+    """Router -> score -> top-k -> weight normalisation (+ shared gate).
+
+    ``selection_bias`` is the DeepSeek-style expert-bias correction named by
+    the pages' MoE config listings (moe_router_enable_expert_bias): it
+    shifts only the choice -- experts are ranked by the fp32 sum s + b --
+    while the weights come from the unbiased scores."""
     z = logits(x, w_router, logit_bias, prec)
     s = scores(z, score_fn)
     T, E = s.shape
     if not 1 <= k <= E:
         raise ValueError("k must be in [1, E]")
     s32 = s.astype(np.float32)
-    # descending fp32 score; a stable sort keeps the lower expert index first
-    # among equal scores
+    if selection_bias is not None:
+        # the ranking key, added in fp32 like the decision itself
+        s32 = (s32 + np.asarray(selection_bias, dtype=np.float32)[None, :]).astype(np.float32)
+    # descending fp32 key; a stable sort keeps the lower expert index first
+    # among equal keys
     order = np.argsort(-s32, axis=1, kind="stable")
     topk_idx = order[:, :k].astype(np.int32)
     rows = np.arange(T)[:, None]
@@ -316,12 +325,13 @@ def shared_expert(x, ws1, ws2, gate, prec=np.float64):
 
 def moe_layer_forward(x, w_router, w1, w2, k, score_fn="softmax",
                       normalize=True, logit_bias=None, w_gate=None,
-                      ws1=None, ws2=None, prec=np.float64, topk_idx=None):
+                      ws1=None, ws2=None, prec=np.float64, topk_idx=None,
+                      selection_bias=None):
     """The whole layer: route -> permute -> grouped SwiGLU -> combine
     (+ gated shared expert).  ``topk_idx`` forces a given expert choice
     (the weights are then the oracle's own for that choice)."""
     E = w_router.shape[0]
-    r = route(x, w_router, k, score_fn, normalize, logit_bias, w_gate, prec)
+    r = route(x, w_router, k, score_fn, normalize, logit_bias, w_gate, prec, selection_bias)
     idx = r.topk_idx if topk_idx is None else np.asarray(topk_idx)
     w = r.topk_w if topk_idx is None else route_weights_for(
         x, w_router, idx, score_fn, normalize, logit_bias, prec)

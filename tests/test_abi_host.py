@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.moe_abi_version() == 4
+    assert L.moe_abi_version() == 5
     assert L.moe_status_string(0) == b"MOE_OK"
     assert L.moe_status_string(5) == b"MOE_ERR_WORKSPACE"
 
@@ -71,13 +71,13 @@ MIS = 0x100004
 
 def test_route_validation(L):
     r = L.moe_route
-    args = dict(s=None, dt=1, T=16, d=64, E=8, k=2, fn=0, norm=1, x=P, w=P, b=None, g=None,
-                idx=P, tw=P, cnt=P, gate=None, ws=P, wsb=1 << 20)
+    args = dict(s=None, dt=1, T=16, d=64, E=8, k=2, fn=0, norm=1, x=P, w=P, b=None, sb=None,
+                g=None, idx=P, tw=P, cnt=P, gate=None, ws=P, wsb=1 << 20)
 
     def call(**kw):
         a = dict(args, **kw)
         return r(a["s"], a["dt"], a["T"], a["d"], a["E"], a["k"], a["fn"], a["norm"], a["x"],
-                 a["w"], a["b"], a["g"], a["idx"], a["tw"], a["cnt"], a["gate"], a["ws"],
+                 a["w"], a["b"], a["sb"], a["g"], a["idx"], a["tw"], a["cnt"], a["gate"], a["ws"],
                  a["wsb"])
 
     assert call(dt=7) == 3                 # MOE_ERR_DTYPE
@@ -91,6 +91,7 @@ def test_route_validation(L):
     assert call(d=60) == 4                 # d not a multiple of 8
     assert call(x=MIS) == 4                # misaligned pointer
     assert call(wsb=16) == 5               # workspace too small
+    assert call(sb=MIS) == 4               # misaligned selection bias
     assert L.moe_route_workspace_size(16, 64, 8, 0) >= 16 * 8 * 4
     assert L.moe_route_workspace_size(4096, 2048, 128, 1) >= 4096 * 128 * 4
 

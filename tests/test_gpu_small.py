@@ -63,6 +63,58 @@ def test_route_parity(case):
         assert np.abs(g - ref.gate).max() <= gh.TOL_ROUTE_W
 
 
+SELB_CASES = [
+    # T, d, E, k, score, dtype, bias std
+    (300, 64, 33, 5, "sigmoid", "f32", 0.1),
+    (513, 256, 130, 6, "sigmoid", "bf16", 0.1),
+    (700, 128, 128, 8, "softmax", "bf16", 0.01),
+]
+
+
+@pytest.mark.parametrize("case", SELB_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_route_selection_bias_parity(case):
+    """Selection-only expert bias: the choice ranks by score + bias, the
+    weights are the unbiased scores of the chosen experts."""
+    T, d, E, k, score, dt, std = case
+    inp = mw.make_small_layer_inputs(40 + T + E, T=T, d=d, E=E, F=8, dtype=dt)
+    sb = (np.random.default_rng(T + E).standard_normal(E) * std).astype(np.float32)
+    ref = mo.route(inp.as_f32("x"), inp.as_f32("w_router"), k, score, True,
+                   selection_bias=sb)
+    plain = mo.route(inp.as_f32("x"), inp.as_f32("w_router"), k, score, True)
+    moved = (np.sort(ref.topk_idx, 1) != np.sort(plain.topk_idx, 1)).any(1).mean()
+    assert moved > 0.05, f"bias changed only {moved:.1%} of the choices"
+    idx, w, cnt, _ = moe.route(gh.to_gpu(inp.x), gh.to_gpu(inp.w_router), k, score, True,
+                               selection_bias=gh.to_gpu(sb))
+    torch.cuda.synchronize()
+    idx, w, cnt = idx.cpu().numpy(), w.cpu().numpy(), cnt.cpu().numpy()
+    gh.check_routing(idx, w, ref, k)
+    assert (cnt == np.bincount(idx.reshape(-1), minlength=E)).all()
+
+
+def test_shared_overlap_matches_serial():
+    """The shared expert on a second stream (unscaled, gate applied in the
+    combine) equals the serial path up to where the gate is rounded."""
+    T, k = 160, 2
+    inp = mw.make_small_layer_inputs(8, T=T, d=128, E=16, F=96, dtype="bf16", Fs=64, bias=True,
+                                     w_std=0.05)
+    g = lambda a: None if a is None else gh.to_gpu(a)  # noqa: E731
+    args = (g(inp.w_router), g(inp.w1), g(inp.w2), k, T, "softmax", True, g(inp.logit_bias),
+            g(inp.w_gate), g(inp.ws1), g(inp.ws2))
+    x = gh.to_gpu(inp.x)
+    y1 = moe.MoELayer(*args, overlap_shared=True).forward(x).clone()
+    y2 = moe.MoELayer(*args, overlap_shared=False).forward(x).clone()
+    torch.cuda.synchronize()
+    f = inp.as_f32
+    layer = moe.MoELayer(*args)
+    layer.forward(x)
+    idx = layer.route_out[0].cpu().numpy()
+    ref, _, _ = mo.moe_layer_forward(f("x"), f("w_router"), f("w1"), f("w2"), k, "softmax", True,
+                                     inp.logit_bias, f("w_gate"), f("ws1"), f("ws2"), topk_idx=idx)
+    assert gh.normwise(gh.to_f64(y1), ref) <= gh.TOL_BF16
+    assert gh.normwise(gh.to_f64(y2), ref) <= gh.TOL_BF16
+    assert gh.normwise(gh.to_f64(y1), gh.to_f64(y2)) <= gh.TOL_BF16
+
+
 PERM_CASES = [
     # T, d, E, k, dtype, pattern
     (1, 64, 4, 1, "bf16", "random"),

@@ -159,3 +159,49 @@ def test_skew_bias_scale_reaches_ten_times_mean():
     ratio = r.counts.max() / (cfg.T * cfg.k / cfg.E)
     assert 9.5 <= ratio <= 10.5
     assert r.counts.min() > 0
+
+
+# --------------------------------------------------------------------------
+# Selection-only expert bias (DeepSeek-style correction): ranks by s + b,
+# weights from the unbiased s.
+# --------------------------------------------------------------------------
+def test_selection_bias_closed_form():
+    # softmax of ln 1..4 = [0.1, 0.2, 0.3, 0.4]; a +0.5 bias on expert 0 makes
+    # its key 0.6, so top-2 = [0, 3]; the weights stay 0.1 : 0.4
+    x = np.array([[1.0]])
+    wr = np.log(np.array([[1.0], [2.0], [3.0], [4.0]]))
+    b = np.array([0.5, 0.0, 0.0, 0.0], np.float32)
+    r = mo.route(x, wr, 2, "softmax", True, selection_bias=b)
+    assert r.topk_idx.tolist() == [[0, 3]]
+    assert np.allclose(r.topk_w, [[0.2, 0.8]], atol=1e-12)
+    r = mo.route(x, wr, 2, "softmax", False, selection_bias=b)
+    assert np.allclose(r.topk_w, [[0.1, 0.4]], atol=1e-12)
+    # without the bias the choice is [3, 2]
+    assert mo.route(x, wr, 2, "softmax", True).topk_idx.tolist() == [[3, 2]]
+
+
+@pytest.mark.parametrize("score", ["softmax", "sigmoid"])
+def test_selection_bias_against_brute_force(score):
+    import oracle.brute as br
+    rng = np.random.default_rng(31)
+    T, d, E, k = 9, 5, 7, 3
+    x = rng.standard_normal((T, d))
+    wr = rng.standard_normal((E, d))
+    b = (rng.standard_normal(E) * 0.3).astype(np.float32)
+    r = mo.route(x, wr, k, score, True, selection_bias=b)
+    bi, bw = br.route(x.tolist(), wr.tolist(), k, score, True, selection_bias=b.tolist())
+    assert r.topk_idx.tolist() == bi
+    assert np.allclose(r.topk_w, np.array(bw), atol=1e-12)
+
+
+def test_zero_selection_bias_is_the_plain_router():
+    rng = np.random.default_rng(32)
+    x, wr = rng.standard_normal((20, 6)), rng.standard_normal((9, 6))
+    a = mo.route(x, wr, 4, "sigmoid", True)
+    b = mo.route(x, wr, 4, "sigmoid", True, selection_bias=np.zeros(9, np.float32))
+    assert np.array_equal(a.topk_idx, b.topk_idx) and np.array_equal(a.topk_w, b.topk_w)
+    # a large negative bias removes an expert from every choice
+    nb = np.zeros(9, np.float32)
+    nb[int(a.topk_idx[0, 0])] = -10.0
+    c = mo.route(x, wr, 4, "sigmoid", True, selection_bias=nb)
+    assert not (c.topk_idx == a.topk_idx[0, 0]).any()
