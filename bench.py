@@ -196,8 +196,7 @@ def main():
                                              copy_rows=False)
         if ev is not None:
             ev[2].record(stream)
-        moe.grouped_swiglu_fwd_gather(x, rtok, L.w1, L.w2, off, row_scale=rw, out=L.y_perm,
-                                      ws=L.ffn_ws)
+        L._routed(x, None, rtok, off, rw)
         if ev is not None:
             ev[3].record(stream)
         ysh, sgate = None, None
@@ -206,8 +205,7 @@ def main():
                 stream.wait_event(L.ev_sh)     # "shared" = the part not hidden by the overlap
                 sgate = gate
             else:                              # gate folded into the shared fc2 row scale
-                moe.grouped_swiglu_fwd(x, L.ws1_e, L.ws2_e, L.shared_off, row_scale=gate,
-                                       out=L.y_shared, ws=L.ffn_ws)
+                L._shared(x, gate, L.ffn_ws)
             ysh = L.y_shared
         if ev is not None:
             ev[4].record(stream)

@@ -210,6 +210,54 @@ MOE_API moe_status moe_grouped_swiglu_fwd_gather(hipStream_t stream, moe_dtype d
                                          void* gu_save, void* ws, size_t ws_bytes);
 
 /* ------------------------------------------------------------------------
+ * moe_pack_weights -- expert weights in the tile-packed layout read by
+ * moe_grouped_swiglu_fwd_packed.
+ *
+ * Passage: "Megatron-Bridge 深度剖析", "计算融合 / Grouped GEMM" (the experts'
+ * weights are stored back to back and consumed by one grouped GEMM) and
+ * "权重映射策略" (linear_fc1 = [gate_proj; up_proj]).  The values are those
+ * of w; only their order in memory changes, so that each K tile of a weight
+ * panel is one contiguous block (a sequential HBM stream):
+ *     packed[e][t][kt][r][c] = w[e][row(t, r)][64 kt + c], zero past K or rows
+ * with 256-row panels t and 64-wide K tiles kt.  gated = 0 (W2 [E, d, F]):
+ * row(t, r) = 256 t + r.  gated = 1 (W1 [E, 2F, d], rows = 2F): panel t holds
+ * the gate rows 128 t .. 128 t + 127 and then the matching up rows F + 128 t
+ * .. F + 128 t + 127.
+ *
+ *   w          [E, rows, K] bf16   in
+ *   w_packed   moe_pack_weights_size(E, rows, K, gated) bytes, out
+ * Limits: bf16 only (MOE_ERR_DTYPE), K % 8 == 0, rows even when gated.
+ * The layout is a function of (rows, K, gated) only; repack after the
+ * weights change.
+ * --------------------------------------------------------------------- */
+MOE_API size_t moe_pack_weights_size(int32_t E, int64_t rows, int64_t K, int32_t gated);
+MOE_API moe_status moe_pack_weights(hipStream_t stream, moe_dtype dt, int32_t E, int64_t rows,
+                            int64_t K, int32_t gated, const void* w, void* w_packed);
+
+/* ------------------------------------------------------------------------
+ * moe_grouped_swiglu_fwd_packed -- moe_grouped_swiglu_fwd (row_token NULL,
+ * x = x_perm [N, d]) or moe_grouped_swiglu_fwd_gather (row_token given, x
+ * [T, d]) on tile-packed weights.
+ *
+ * Passages: those of the two calls it replaces.  Same results, bit for bit:
+ * the kernels stage identical tiles, only the weight reads differ.
+ *
+ *   w1_packed  moe_pack_weights(E, 2F, d, gated = 1) of W1
+ *   w2_packed  moe_pack_weights(E, d, F, gated = 0) of W2
+ *   T          rows of x when row_token is given (ignored otherwise)
+ *   the rest as in moe_grouped_swiglu_fwd / _gather (same workspace size)
+ * Limits: bf16 only (MOE_ERR_DTYPE); those of the call it replaces; one
+ * expert's packed weights below 2^31 bytes.
+ * --------------------------------------------------------------------- */
+MOE_API moe_status moe_grouped_swiglu_fwd_packed(hipStream_t stream, moe_dtype dt, int64_t N,
+                                         int64_t d, int64_t F, int32_t E, int64_t T,
+                                         const void* x, const int32_t* row_token,
+                                         const void* w1_packed, const void* w2_packed,
+                                         const int32_t* expert_offsets,
+                                         const float* row_scale, void* y_perm,
+                                         void* gu_save, void* ws, size_t ws_bytes);
+
+/* ------------------------------------------------------------------------
  * moe_grouped_swiglu_bwd -- grouped-GEMM dgrad and wgrad of the forward.
  *
  * Passage: "Megatron-Bridge 深度剖析", "通信隐藏与混合精度 / TP 通信重叠"

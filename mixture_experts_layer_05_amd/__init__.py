@@ -20,6 +20,7 @@ import torch
 
 __all__ = [
     "MoEError", "lib", "route", "permute", "grouped_swiglu_fwd", "grouped_swiglu_fwd_gather",
+    "PackedWeights", "pack_weights", "grouped_swiglu_fwd_packed",
     "grouped_swiglu_bwd", "unpermute_combine", "combine_backward", "route_backward",
     "moe_layer_forward",
     "MoELayer", "LIB_PATH", "EXPORTED",
@@ -49,6 +50,10 @@ EXPORTED = {
     "moe_grouped_swiglu_fwd": (_i32, [_vp, _i32, _i64, _i64, _i64, _i32,
                                       _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz]),
     "moe_grouped_swiglu_fwd_gather": (_i32, [_vp, _i32, _i64, _i64, _i64, _i32, _i64,
+                                             _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz]),
+    "moe_pack_weights_size": (_sz, [_i32, _i64, _i64, _i32]),
+    "moe_pack_weights": (_i32, [_vp, _i32, _i32, _i64, _i64, _i32, _vp, _vp]),
+    "moe_grouped_swiglu_fwd_packed": (_i32, [_vp, _i32, _i64, _i64, _i64, _i32, _i64,
                                              _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz]),
     "moe_grouped_swiglu_bwd_workspace_size": (_sz, [_i64, _i64, _i32, _i32]),
     "moe_grouped_swiglu_bwd": (_i32, [_vp, _i32, _i64, _i64, _i64, _i32,
@@ -223,6 +228,56 @@ def grouped_swiglu_fwd_gather(x, row_token, w1, w2, expert_offsets, row_scale=No
     return y, gu
 
 
+class PackedWeights:
+    """Expert weights [E, rows, K] in the tile-packed layout of moe_pack_weights
+    (a flat bf16 device buffer plus the logical shape)."""
+
+    def __init__(self, buf, E, rows, K, gated):
+        self.buf, self.E, self.rows, self.K, self.gated = buf, E, rows, K, bool(gated)
+
+
+def pack_weights(w, gated, out=None):
+    """w [E, rows, K] bf16 -> PackedWeights (gated: the fc1 [gate; up] layout)."""
+    E, rows, K = w.shape
+    nbytes = lib().moe_pack_weights_size(E, rows, K, int(bool(gated)))
+    if nbytes == 0:
+        raise MoEError(f"cannot pack weights of shape {tuple(w.shape)} (gated={gated})")
+    buf = out if out is not None else torch.empty(nbytes // 2, dtype=torch.bfloat16, device=w.device)
+    if buf.numel() * buf.element_size() < nbytes:
+        raise MoEError("packed-weight buffer too small")
+    _check(lib().moe_pack_weights(_stream(), _dt(w), E, rows, K, int(bool(gated)), _p(w), _p(buf)),
+           "moe_pack_weights")
+    return PackedWeights(buf, E, rows, K, gated)
+
+
+def grouped_swiglu_fwd_packed(x, row_token, w1p, w2p, expert_offsets, row_scale=None,
+                              save_gu=False, out=None, gu_out=None, ws=None):
+    """grouped_swiglu_fwd (row_token None: x is x_perm [N, d]) or
+    grouped_swiglu_fwd_gather (x [T, d], N = len(row_token)) on packed weights
+    (pack_weights(w1, True), pack_weights(w2, False)).
+    -> (y_perm [N,d], gu_save [N,2F] or None)"""
+    T, d = x.shape
+    N = row_token.shape[0] if row_token is not None else T
+    E, F = w1p.E, w1p.rows // 2
+    if not (w1p.gated and not w2p.gated and w1p.K == d and w2p.rows == d and w2p.K == F
+            and w2p.E == E):
+        raise MoEError("packed weights do not match x and each other")
+    dev = x.device
+    y = out if out is not None else torch.empty((N, d), dtype=x.dtype, device=dev)
+    gu = gu_out
+    if save_gu and gu is None:
+        gu = torch.empty((N, 2 * F), dtype=x.dtype, device=dev)
+    nbytes = fwd_workspace_size(N, F, x.dtype)
+    if ws is None:
+        ws = _ws(nbytes, dev)
+    _check(lib().moe_grouped_swiglu_fwd_packed(_stream(), _dt(x), N, d, F, E, T, _p(x),
+                                               _p(row_token), _p(w1p.buf), _p(w2p.buf),
+                                               _p(expert_offsets), _p(row_scale), _p(y), _p(gu),
+                                               _p(ws), ws.numel()),
+           "moe_grouped_swiglu_fwd_packed")
+    return y, gu
+
+
 def bwd_workspace_size(N, F, dtype, recompute):
     return lib().moe_grouped_swiglu_bwd_workspace_size(
         N, F, MOE_BF16 if dtype == torch.bfloat16 else MOE_F32, int(bool(recompute)))
@@ -328,6 +383,10 @@ class MoELayer:
     routed and the shared expert), and the expert outputs unweighted (fc2
     without a row scale; combine applies the routing weights and the gate).
 
+    ``packed`` (default: on for a bf16 inference layer) keeps the expert
+    weights also in the tile-packed layout (pack_weights) and runs the
+    grouped GEMMs on it; call :meth:`repack` after changing the weights.
+
     ``overlap_shared`` runs the shared expert, which depends only on x, on a
     second stream (default priority) concurrently with route, permute and
     the routed GEMM; its output stays unscaled and the combine applies the
@@ -340,8 +399,14 @@ class MoELayer:
 
     def __init__(self, w_router, w1, w2, k, T, score="softmax", normalize=True,
                  logit_bias=None, w_gate=None, ws1=None, ws2=None, save_gu=False,
-                 gather=True, train=False, overlap_shared=False, selection_bias=None):
+                 gather=True, train=False, overlap_shared=False, selection_bias=None,
+                 packed=None):
         self.train = train
+        if packed is None:
+            packed = not train and w1.dtype == torch.bfloat16
+        if packed and (train or w1.dtype != torch.bfloat16):
+            raise MoEError("packed weights serve the bf16 inference forward only")
+        self.packed = packed
         self.selection_bias = selection_bias
         self.overlap_shared = overlap_shared and ws1 is not None
         if train:
@@ -387,6 +452,16 @@ class MoELayer:
         self.y = torch.empty((T, d), dtype=dt, device=dev)
         if train:
             self._alloc_backward(dev, dt)
+        if packed:
+            self.repack()
+
+    def repack(self):
+        """(Re)build the tile-packed copies of the expert weights."""
+        self.w1p = pack_weights(self.w1, True)
+        self.w2p = pack_weights(self.w2, False)
+        if self.ws1 is not None:
+            self.ws1p = pack_weights(self.ws1_e, True)
+            self.ws2p = pack_weights(self.ws2_e, False)
 
     def _alloc_backward(self, dev, dt):
         T, N, d, E, F, k = self.T, self.N, self.d, self.E, self.F, self.k
@@ -410,11 +485,32 @@ class MoELayer:
         self.bwd_ws = _ws(bwd_ws, dev)
         self.rbwd_ws = _ws(route_backward_workspace_size(T, d, k), dev)
 
+    def _shared(self, x, scale, ws):
+        if self.packed:
+            grouped_swiglu_fwd_packed(x, None, self.ws1p, self.ws2p, self.shared_off,
+                                      row_scale=scale, out=self.y_shared, ws=ws)
+        else:
+            grouped_swiglu_fwd(x, self.ws1_e, self.ws2_e, self.shared_off, row_scale=scale,
+                               out=self.y_shared, gu_out=self.gu_sh if self.train else None,
+                               save_gu=self.train, ws=ws)
+
     def _shared_unscaled(self, x):
-        grouped_swiglu_fwd(x, self.ws1_e, self.ws2_e, self.shared_off, row_scale=None,
-                           out=self.y_shared, gu_out=self.gu_sh if self.train else None,
-                           save_gu=self.train,
-                           ws=self.shared_ws if self.overlap_shared else self.ffn_ws)
+        self._shared(x, None, self.shared_ws if self.overlap_shared else self.ffn_ws)
+
+    def _routed(self, x, xp, rtok, off, rs):
+        """The routed grouped GEMMs (fc1 gathers x rows by rtok when xp is None)."""
+        if self.packed:
+            grouped_swiglu_fwd_packed(x if xp is None else xp, rtok if xp is None else None,
+                                      self.w1p, self.w2p, off, row_scale=rs, out=self.y_perm,
+                                      gu_out=self.gu, save_gu=self.gu is not None,
+                                      ws=self.ffn_ws)
+        elif xp is None:
+            grouped_swiglu_fwd_gather(x, rtok, self.w1, self.w2, off, row_scale=rs,
+                                      out=self.y_perm, gu_out=self.gu,
+                                      save_gu=self.gu is not None, ws=self.ffn_ws)
+        else:
+            grouped_swiglu_fwd(xp, self.w1, self.w2, off, row_scale=rs, out=self.y_perm,
+                               gu_out=self.gu, save_gu=self.gu is not None, ws=self.ffn_ws)
 
     def forward(self, x):
         main = torch.cuda.current_stream()
@@ -431,13 +527,7 @@ class MoELayer:
         off, slot, rtok, rw, xp = permute(x, idx, w, self.E, out=self.perm_out, ws=self.perm_ws,
                                           copy_rows=not self.gather)
         rs = None if self.train else rw      # training: weights applied in combine
-        if self.gather:
-            grouped_swiglu_fwd_gather(x, rtok, self.w1, self.w2, off, row_scale=rs,
-                                      out=self.y_perm, gu_out=self.gu,
-                                      save_gu=self.gu is not None, ws=self.ffn_ws)
-        else:
-            grouped_swiglu_fwd(xp, self.w1, self.w2, off, row_scale=rs, out=self.y_perm,
-                               gu_out=self.gu, save_gu=self.gu is not None, ws=self.ffn_ws)
+        self._routed(x, None if self.gather else xp, rtok, off, rs)
         ysh, sgate = None, None
         if self.ws1 is not None:
             if self.overlap_shared:
@@ -447,8 +537,7 @@ class MoELayer:
                 self._shared_unscaled(x)
                 sgate = gate
             else:
-                grouped_swiglu_fwd(x, self.ws1_e, self.ws2_e, self.shared_off, row_scale=gate,
-                                   out=self.y_shared, ws=self.ffn_ws)
+                self._shared(x, gate, self.ffn_ws)
             ysh = self.y_shared
         if self.train:
             self.x_saved = x

@@ -1,7 +1,7 @@
 // Library identity: ABI version and status names.
 #include "moe_internal.h"
 
-extern "C" int32_t moe_abi_version(void) { return 5; }
+extern "C" int32_t moe_abi_version(void) { return 6; }
 
 extern "C" const char* moe_status_string(moe_status s) {
   switch (s) {

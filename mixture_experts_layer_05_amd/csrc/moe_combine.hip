@@ -14,7 +14,9 @@ namespace moe {
 
 constexpr int kCombThreads = 256;
 
-template <bool kBF16>
+// kMaxK >= k: the k row loads of one column chunk are issued together (no
+// round trip per row); the sum still runs in slot order.
+template <bool kBF16, int kMaxK>
 __global__ __launch_bounds__(kCombThreads) void combine_kernel(
     int T, int k, int N, int nchunk16, const u32x4* __restrict__ y_perm,
     const int32_t* __restrict__ slot_of, const float* __restrict__ topk_w,
@@ -30,39 +32,54 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
     if (my_row >= N) my_row = -1;
     if (topk_w) my_w = topk_w[static_cast<size_t>(t) * k + lane];
   }
+  // every lane holds all k rows and weights (wave-uniform)
+  const u32x4* src[kMaxK];
+  float wj[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    const int row = j < k ? __builtin_amdgcn_readfirstlane(__shfl(my_row, j, kWave)) : -1;
+    src[j] = row >= 0 ? y_perm + static_cast<size_t>(row) * nchunk16 : nullptr;
+    wj[j] = j < k ? __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                        __builtin_bit_cast(int, __shfl(my_w, j, kWave))))
+                  : 0.0f;
+  }
+  const float g = (y_shared && shared_gate) ? shared_gate[t] : 1.0f;
+  const u32x4* sh = y_shared ? y_shared + static_cast<size_t>(t) * nchunk16 : nullptr;
   constexpr int kVals = kBF16 ? 8 : 4;
   for (int c = lane; c < nchunk16; c += 64) {
+    u32x4 v[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      if (src[j]) v[j] = __builtin_nontemporal_load(src[j] + c);
+    u32x4 vs{};
+    if (sh) vs = __builtin_nontemporal_load(sh + c);
     float acc[kVals];
 #pragma unroll
     for (int q = 0; q < kVals; ++q) acc[q] = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      const int row = __shfl(my_row, j, kWave);
-      const float w = __shfl(my_w, j, kWave);
-      if (row < 0) continue;
-      const u32x4 v = y_perm[static_cast<size_t>(row) * nchunk16 + c];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (!src[j]) continue;
       if constexpr (kBF16) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          acc[2 * q] = fmaf(w, bf16lo(v[q]), acc[2 * q]);
-          acc[2 * q + 1] = fmaf(w, bf16hi(v[q]), acc[2 * q + 1]);
+          acc[2 * q] = fmaf(wj[j], bf16lo(v[j][q]), acc[2 * q]);
+          acc[2 * q + 1] = fmaf(wj[j], bf16hi(v[j][q]), acc[2 * q + 1]);
         }
       } else {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[q] = fmaf(w, __uint_as_float(v[q]), acc[q]);
+        for (int q = 0; q < 4; ++q) acc[q] = fmaf(wj[j], __uint_as_float(v[j][q]), acc[q]);
       }
     }
-    if (y_shared) {
-      const u32x4 v = y_shared[static_cast<size_t>(t) * nchunk16 + c];
-      const float g = shared_gate ? shared_gate[t] : 1.0f;
+    if (sh) {
       if constexpr (kBF16) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          acc[2 * q] = fmaf(g, bf16lo(v[q]), acc[2 * q]);
-          acc[2 * q + 1] = fmaf(g, bf16hi(v[q]), acc[2 * q + 1]);
+          acc[2 * q] = fmaf(g, bf16lo(vs[q]), acc[2 * q]);
+          acc[2 * q + 1] = fmaf(g, bf16hi(vs[q]), acc[2 * q + 1]);
         }
       } else {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[q] = fmaf(g, __uint_as_float(v[q]), acc[q]);
+        for (int q = 0; q < 4; ++q) acc[q] = fmaf(g, __uint_as_float(vs[q]), acc[q]);
       }
     }
     u32x4 o;
@@ -75,6 +92,15 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
     }
     y[static_cast<size_t>(t) * nchunk16 + c] = o;
   }
+}
+
+template <bool kBF16>
+static auto pick_combine(int k) {
+  if (k <= 2) return combine_kernel<kBF16, 2>;
+  if (k <= 4) return combine_kernel<kBF16, 4>;
+  if (k <= 8) return combine_kernel<kBF16, 8>;
+  if (k <= 16) return combine_kernel<kBF16, 16>;
+  return combine_kernel<kBF16, 32>;
 }
 
 }  // namespace moe
@@ -94,7 +120,7 @@ extern "C" moe_status moe_unpermute_combine(hipStream_t stream, moe_dtype dt, in
   if (!aligned16(y_perm) || !aligned16(slot_of) || !aligned16(topk_w) || !aligned16(y_shared) ||
       !aligned16(shared_gate) || !aligned16(y))
     return MOE_ERR_ALIGNMENT;
-  auto kern = dt == MOE_BF16 ? combine_kernel<true> : combine_kernel<false>;
+  auto kern = dt == MOE_BF16 ? pick_combine<true>(k) : pick_combine<false>(k);
   return hip_status(launch(kern, dim3(static_cast<unsigned>((T + 3) / 4)), dim3(kCombThreads), 0,
                            stream, (int)T, k, (int)N, static_cast<int>(row_bytes / 16),
                            static_cast<const u32x4*>(y_perm), slot_of, topk_w,

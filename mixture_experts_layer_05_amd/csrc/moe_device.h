@@ -44,6 +44,47 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// wave64 reductions without LDS: DPP within each 16-lane row (xor 1 and 2
+// by quad permutation, then the half-row and row mirrors), then the four
+// row results read as scalars.  The result is wave-uniform.
+template <int kCtrl>
+__device__ __forceinline__ int dpp_(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, kCtrl, 0xf, 0xf, false);
+}
+constexpr int kDppXor1 = 0xb1, kDppXor2 = 0x4e, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, __int_as_float(dpp_<kDppXor1>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_<kDppXor2>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_<kDppHalfMirror>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_<kDppMirror>(__float_as_int(v))));
+  const int b = __float_as_int(v);
+  return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 0)),
+                     __int_as_float(__builtin_amdgcn_readlane(b, 16))),
+               fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 32)),
+                     __int_as_float(__builtin_amdgcn_readlane(b, 48))));
+}
+__device__ __forceinline__ int wave_min_dpp(int v) {
+  v = min(v, dpp_<kDppXor1>(v));
+  v = min(v, dpp_<kDppXor2>(v));
+  v = min(v, dpp_<kDppHalfMirror>(v));
+  v = min(v, dpp_<kDppMirror>(v));
+  return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+// sum in a fixed order: pairs, quads, half rows, rows, then rows 0..3
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += __int_as_float(dpp_<kDppXor1>(__float_as_int(v)));
+  v += __int_as_float(dpp_<kDppXor2>(__float_as_int(v)));
+  v += __int_as_float(dpp_<kDppHalfMirror>(__float_as_int(v)));
+  v += __int_as_float(dpp_<kDppMirror>(__float_as_int(v)));
+  const int b = __float_as_int(v);
+  return (__int_as_float(__builtin_amdgcn_readlane(b, 0)) +
+          __int_as_float(__builtin_amdgcn_readlane(b, 16))) +
+         (__int_as_float(__builtin_amdgcn_readlane(b, 32)) +
+          __int_as_float(__builtin_amdgcn_readlane(b, 48)));
+}
+
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }
 
 // Epilogue forms: e^-z as 2^(-z log2 e) and the hardware reciprocal (about

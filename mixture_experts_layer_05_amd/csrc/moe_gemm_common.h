@@ -92,6 +92,21 @@ __device__ inline TileIdx tile_decode(const int32_t* __restrict__ offsets, int E
   return t;
 }
 
+// The same decode for a single group of n rows (no offsets array).
+__device__ inline TileIdx tile_decode_one(int n, int bm, int L) {
+  TileIdx t;
+  t.e = 0;
+  t.lo = 0;
+  t.hi = n;
+  const int mts = (n + bm - 1) / bm;
+  t.nt = L / mts;
+  t.mt = L - t.nt * mts;
+  const int h = ((n + mts - 1) / mts + 31) & ~31;
+  t.m0 = t.mt * h;
+  t.mend = min(t.m0 + h, n);
+  return t;
+}
+
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format
@@ -154,14 +169,15 @@ hipError_t launch_grouped_fwd_bf16(hipStream_t stream, int64_t N, int64_t d, int
                                    const void* x_perm, const void* w1, const void* w2,
                                    const int32_t* offsets, const float* row_scale, void* y_perm,
                                    void* gu_save, uint16_t* a_buf, bool run_fc2,
-                                   const int32_t* gather = nullptr, int64_t a_rows = 0);
+                                   const int32_t* gather = nullptr, int64_t a_rows = 0,
+                                   bool packed = false);
 
 // Router logits with the forward kernel as a one-group GEMM, K split into
 // `ksplit` slabs: logits[s][T][E] = x[:, slab s] W_r[:, slab s]^T (+ bias
-// on slab 0), fp32; offsets01 = device array {0, T}.  bf16 only.
+// on slab 0), fp32.  bf16 only.
 int router_ksplit(int64_t T, int64_t d, int32_t E);
 hipError_t launch_router_logits_bf16(hipStream_t stream, int64_t T, int64_t d, int32_t E,
                                     const void* x, const void* w_router, const float* bias,
-                                    const int32_t* offsets01, float* logits, int ksplit);
+                                    float* logits, int ksplit);
 
 }  // namespace moe

@@ -6,18 +6,18 @@
 // its top-k experts with scores (top-6 sigmoid in the example); the score
 // function is a TransformerConfig choice (section "Megatron-Core 架构速览").
 //
-//   1. route_init: write the one-group offsets {0, T} for the GEMM;
-//   2. logits z[T, E] (fp32, in the workspace): bf16 runs the grouped-GEMM
+//   1. logits z[T, E] (fp32, in the workspace): bf16 runs the grouped-GEMM
 //      forward kernel as a one-group GEMM with a bias epilogue (MFMA, LDS
-//      ring); fp32 runs a plain FMA dot product per (token, expert);
-//   3. route_topk: one wavefront per token; lane l holds the scores of
+//      ring), K split into slabs; fp32 runs a plain FMA dot product per
+//      (token, expert);
+//   2. route_topk: one wavefront per token; lane l holds the scores of
 //      experts l, l+64, ...; k rounds of a wave-wide arg-max (ties to the
 //      lower expert index) pick the experts in descending score order (or
 //      descending score + selection bias, when a selection-only expert bias
 //      is given: the weights still come from the unbiased scores); the
 //      workgroup's choices are counted in LDS and written as one histogram
 //      row; the gate is a wave-wide dot product x[t] . w_gate;
-//   4. route_count: counts[e] = sum of the histogram rows (one workgroup per
+//   3. route_count: counts[e] = sum of the histogram rows (one workgroup per
 //      expert; no global atomics, so a hot expert costs nothing extra).
 #include "moe_gemm_common.h"
 
@@ -25,10 +25,6 @@ namespace moe {
 
 constexpr int kTopkThreads = 1024;  // 16 tokens per workgroup, one per wave
 constexpr int kTopkTokens = kTopkThreads / 64;
-
-__global__ void route_init_kernel(int32_t* offsets01, int T) {
-  if (threadIdx.x == 0) { offsets01[0] = 0; offsets01[1] = T; }
-}
 
 __global__ __launch_bounds__(256) void route_logits_f32_kernel(
     int T, int d, int E, const float* __restrict__ x, const float* __restrict__ wr,
@@ -62,31 +58,41 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * kTopkTokens + (threadIdx.x >> 6);
   if (t < T) {
-  // logits = sum of the K slabs, in slab order
+  // logits = sum of the K slabs, in slab order (the loads of 8 slabs are
+  // issued before their sum, not one round trip per slab)
   const size_t slab = static_cast<size_t>(T) * E;
   const float* zrow = z + static_cast<size_t>(t) * E;
   float p[kPer];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int e = lane + 64 * i;
-    float v = 0.0f;
-    if (e < E)
-      for (int sl = 0; sl < nslab; ++sl) v += zrow[sl * slab + e];
-    p[i] = v;
+  for (int i = 0; i < kPer; ++i) p[i] = 0.0f;
+  for (int s0 = 0; s0 < nslab; s0 += 8) {
+    float v[8][kPer];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int e = lane + 64 * i;
+        v[q][i] = (s0 + q < nslab && e < E) ? zrow[(s0 + q) * slab + e] : 0.0f;
+      }
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        if (s0 + q < nslab) p[i] += v[q][i];
   }
   if (score_fn == MOE_SCORE_SOFTMAX) {
     float m = -INFINITY;
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
       if (lane + 64 * i < E) m = fmaxf(m, p[i]);
-    m = wave_max(m);
+    m = wave_max_dpp(m);
     float s = 0.0f;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       p[i] = (lane + 64 * i < E) ? expf(p[i] - m) : 0.0f;
       s += p[i];
     }
-    s = wave_sum(s);
+    s = wave_sum_dpp(s);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) p[i] = (lane + 64 * i < E) ? p[i] / s : -INFINITY;
   } else {
@@ -100,6 +106,8 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
     const int e = lane + 64 * i;
     key[i] = (sel_bias && e < E) ? p[i] + sel_bias[e] : p[i];
   }
+  // k rounds: the largest remaining key (wave max), then the lowest expert
+  // index holding it (wave min); both reductions stay in registers (DPP).
   uint32_t taken = 0;
   int my_e = E;
   float my_p = 0.0f;
@@ -111,23 +119,20 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
       // strict '>' keeps the lower expert index among equal keys
       if (!((taken >> i) & 1u) && key[i] > bv) { bv = key[i]; bi = lane + 64 * i; }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, kWave);
-      const int oi = __shfl_xor(bi, o, kWave);
-      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-    }
+    const float mv = wave_max_dpp(bv);
+    bi = wave_min_dpp(bv == mv ? bi : 0x7fffffff);
+    bi = bi < E ? bi : E;
     // the winner's (unbiased) score, from the lane that holds it
     float pw = 0.0f;
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
       if (i == (bi >> 6)) pw = p[i];
-    pw = __shfl(pw, bi & 63, kWave);
+    pw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pw), bi & 63));
     if (bi < E && (bi & 63) == lane) taken |= 1u << (bi >> 6);
     if (lane == j) { my_e = bi; my_p = pw; }
   }
   float denom = 1.0f;
-  if (normalize) denom = wave_sum(lane < k ? my_p : 0.0f);
+  if (normalize) denom = wave_sum_dpp(lane < k ? my_p : 0.0f);
   if (lane < k) {
     topk_idx[static_cast<size_t>(t) * k + lane] = my_e;
     topk_w[static_cast<size_t>(t) * k + lane] = normalize ? my_p / denom : my_p;
@@ -152,7 +157,7 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
       const float* wg = static_cast<const float*>(wgv);
       for (int i = lane; i < d; i += 64) g = fmaf(xr[i], wg[i], g);
     }
-    g = wave_sum(g);
+    g = wave_sum_dpp(g);
     if (lane == 0) gate[t] = sigmoidf_(g);
   }
   }
@@ -200,8 +205,8 @@ static size_t route_hist_bytes(int64_t T, int32_t E) {
 
 extern "C" size_t moe_route_workspace_size(int64_t T, int64_t d, int32_t E, moe_dtype dt) {
   if (T < 1 || d < 1 || E < 1 || (dt != MOE_F32 && dt != MOE_BF16)) return 0;
-  // {0, T}; per-workgroup histograms; fp32 logits, one slab per K split
-  return 256 + route_hist_bytes(T, E) +
+  // per-workgroup histograms; fp32 logits, one slab per K split
+  return route_hist_bytes(T, E) +
          static_cast<size_t>(route_slabs(dt, T, d, E)) * T * E * sizeof(float);
 }
 
@@ -227,14 +232,12 @@ extern "C" moe_status moe_route(hipStream_t stream, moe_dtype dt, int64_t T, int
     return MOE_ERR_ALIGNMENT;
   if (!ws || ws_bytes < moe_route_workspace_size(T, d, E, dt)) return MOE_ERR_WORKSPACE;
 
-  int32_t* offsets01 = static_cast<int32_t*>(ws);
-  int32_t* hist = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + 256);
-  float* z = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + 256 + route_hist_bytes(T, E));
-  hipError_t err = launch(route_init_kernel, dim3(1), dim3(64), 0, stream, offsets01, (int)T);
-  if (err != hipSuccess) return MOE_ERR_HIP;
+  int32_t* hist = static_cast<int32_t*>(ws);
+  float* z = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + route_hist_bytes(T, E));
+  hipError_t err;
   const int nslab = route_slabs(dt, T, d, E);
   if (dt == MOE_BF16) {
-    err = launch_router_logits_bf16(stream, T, d, E, x, w_router, logit_bias, offsets01, z, nslab);
+    err = launch_router_logits_bf16(stream, T, d, E, x, w_router, logit_bias, z, nslab);
   } else {
     const int64_t n = T * E;
     err = launch(route_logits_f32_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,

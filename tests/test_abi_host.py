@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.moe_abi_version() == 5
+    assert L.moe_abi_version() == 6
     assert L.moe_status_string(0) == b"MOE_OK"
     assert L.moe_status_string(5) == b"MOE_ERR_WORKSPACE"
 
@@ -116,6 +116,23 @@ def test_grouped_validation(L):
     assert gat(None, 1, 100, 64, 64, 4, 0, P, P, P, P, P, None, P, None, P, 1 << 30) == 2      # T = 0
     assert gat(None, 1, 100, 64, 64, 4, 1 << 25, P, P, P, P, P, None, P, None, P, 1 << 30) == 2  # x > 2 GB
     assert gat(None, 1, 100, 64, 64, 4, 50, P, MIS, P, P, P, None, P, None, P, 1 << 30) == 4
+    pk = L.moe_pack_weights
+    assert pk(None, 0, 4, 128, 64, 1, P, P) == 3          # fp32: bf16 only
+    assert pk(None, 1, 4, 128, 64, 1, None, P) == 1
+    assert pk(None, 1, 4, 127, 64, 1, P, P) == 2          # odd rows with gate/up halves
+    assert pk(None, 1, 4, 128, 60, 0, P, P) == 4          # K % 8
+    assert pk(None, 1, 4, 128, 64, 0, MIS, P) == 4
+    # F = 72 -> 1 panel of 128 gate + 128 up rows; d = 136 -> 3 K tiles of 64
+    assert L.moe_pack_weights_size(3, 144, 136, 1) == 3 * 1 * 3 * 256 * 64 * 2
+    # F = 200 -> 2 panels
+    assert L.moe_pack_weights_size(1, 400, 64, 1) == 1 * 2 * 1 * 256 * 64 * 2
+    assert L.moe_pack_weights_size(2, 200, 72, 0) == 2 * 1 * 2 * 256 * 64 * 2
+    assert L.moe_pack_weights_size(2, 201, 72, 1) == 0
+    fp = L.moe_grouped_swiglu_fwd_packed
+    assert fp(None, 0, 100, 64, 64, 4, 0, P, None, P, P, P, None, P, None, P, 1 << 30) == 3
+    assert fp(None, 1, 100, 64, 60, 4, 0, P, None, P, P, P, None, P, None, P, 1 << 30) == 4
+    assert fp(None, 1, 100, 64, 64, 4, 0, P, P, P, P, P, None, P, None, P, 1 << 30) == 2  # T = 0
+    assert fp(None, 1, 100, 64, 64, 4, 0, P, None, P, P, P, None, P, None, P, 16) == 5
     bwd = L.moe_grouped_swiglu_bwd
     assert bwd(None, 0, 100, 64, 64, 4, P, P, P, P, P, P, None, 0, P, P, P, P, 1 << 30) == 6
     assert bwd(None, 1, 100, 64, 64, 4, P, P, P, P, P, P, None, 0, P, P, P, P, 16) == 5

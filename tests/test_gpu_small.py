@@ -115,6 +115,29 @@ def test_shared_overlap_matches_serial():
     assert gh.normwise(gh.to_f64(y1), gh.to_f64(y2)) <= gh.TOL_BF16
 
 
+def test_layer_packed_matches_unpacked():
+    """The inference layer on tile-packed weights (its default) equals the layer
+    on the weights as stored, bit for bit; repack() follows a weight change."""
+    T, k = 300, 4
+    inp = mw.make_small_layer_inputs(9, T=T, d=192, E=12, F=136, dtype="bf16", Fs=72,
+                                     bias=True, w_std=0.05)
+    g = lambda a: None if a is None else gh.to_gpu(a)  # noqa: E731
+    args = (g(inp.w_router), g(inp.w1), g(inp.w2), k, T, "softmax", True, g(inp.logit_bias),
+            g(inp.w_gate), g(inp.ws1), g(inp.ws2))
+    x = gh.to_gpu(inp.x)
+    lp = moe.MoELayer(*args)
+    lu = moe.MoELayer(*args, packed=False)
+    assert lp.packed and not lu.packed
+    y1, y2 = lp.forward(x).clone(), lu.forward(x).clone()
+    torch.cuda.synchronize()
+    assert gh.bits_equal(y1, y2)
+    lp.w2.mul_(0.5)                     # shared storage: both layers see the change
+    lp.repack()
+    y3, y4 = lp.forward(x).clone(), lu.forward(x).clone()
+    torch.cuda.synchronize()
+    assert gh.bits_equal(y3, y4) and not gh.bits_equal(y1, y3)
+
+
 PERM_CASES = [
     # T, d, E, k, dtype, pattern
     (1, 64, 4, 1, "bf16", "random"),
@@ -277,6 +300,99 @@ def test_grouped_fwd_gather_parity(case):
     tol = gh.TOL_F32 if dt == "f32" else gh.TOL_BF16
     assert gh.normwise(gh.to_f64(y), y_ref) <= tol
     assert gh.normwise(gh.to_f64(gu), gu_ref) <= tol
+
+
+def _pack_reference(w, gated, bn=256, bk=64):
+    """The tile-packed layout written out from its definition in include/moe.h
+    (a data reordering only), for comparison with moe_pack_weights."""
+    E, rows, K = w.shape
+    if gated:
+        F = rows // 2
+        nt = -(-F // (bn // 2))
+    else:
+        nt = -(-rows // bn)
+    nkt = -(-K // bk)
+    out = np.zeros((E, nt, nkt, bn, bk), dtype=w.dtype)
+    for t in range(nt):
+        for r in range(bn):
+            if gated:
+                f = t * (bn // 2) + (r if r < bn // 2 else r - bn // 2)
+                row = (f if r < bn // 2 else F + f) if f < F else -1
+            else:
+                row = t * bn + r if t * bn + r < rows else -1
+            if row < 0:
+                continue
+            for kt in range(nkt):
+                k0, k1 = kt * bk, min(K, kt * bk + bk)
+                out[:, t, kt, r, :k1 - k0] = w[:, row, k0:k1]
+    return out
+
+
+@pytest.mark.parametrize("case", [(3, 2 * 72, 136, True), (2, 200, 72, False),
+                                  (1, 2 * 256, 64, True), (2, 520, 8, False)],
+                         ids=lambda c: "-".join(map(str, c)))
+def test_pack_weights_layout(case):
+    """moe_pack_weights places every weight where the layout says, zeros elsewhere."""
+    E, rows, K, gated = case
+    rng = np.random.default_rng(rows + K)
+    w = mw.round_to_bf16_bits(rng.standard_normal((E, rows, K)).astype(np.float32))
+    ref = _pack_reference(w, gated)
+    wp = moe.pack_weights(gh.to_gpu(w), gated)
+    torch.cuda.synchronize()
+    got = wp.buf.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert got.size == ref.size
+    assert (got == ref.reshape(-1)).all()
+
+
+PACKED_CASES = [
+    # E, d, F, T (rows of x; 0: no gather), pattern, scale
+    (6, 64, 64, 0, "ragged", 300),
+    (7, 136, 72, 45, "ragged", 200),          # K and N tails, gathered rows
+    (3, 256, 192, 0, "one_hot", 517),
+    (9, 200, 136, 300, "ragged", 140),        # d not a multiple of 64
+    (4, 512, 320, 0, "ragged", 600),          # several column tiles of both GEMMs
+]
+
+
+@pytest.mark.parametrize("case", PACKED_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_grouped_fwd_packed_parity(case):
+    """The forward on tile-packed weights equals the forward on the weights as
+    stored, bit for bit (with and without the gathered first operand), and
+    the oracle to the bf16 tolerance."""
+    E, d, F, T, pattern, scale = case
+    rng = np.random.default_rng(E * 7 + d + F + T)
+    counts = _segments(rng, E, pattern, scale)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    N = int(off[-1])
+    rows = T if T else N
+    inp = mw.make_small_layer_inputs(E + d + F + 5, T=rows, d=d, E=E, F=F, dtype="bf16",
+                                     w_std=0.05)
+    rs = (rng.random(N) + 0.5).astype(np.float32)
+    x, w1, w2 = gh.to_gpu(inp.x), gh.to_gpu(inp.w1), gh.to_gpu(inp.w2)
+    go, grs = gh.to_gpu(off), gh.to_gpu(rs)
+    w1p, w2p = moe.pack_weights(w1, True), moe.pack_weights(w2, False)
+    if T:
+        rtok = rng.integers(0, T, N).astype(np.int32)
+        gtok = gh.to_gpu(rtok)
+        y_u, gu_u = moe.grouped_swiglu_fwd_gather(x, gtok, w1, w2, go, grs, save_gu=True)
+        xp_ref = inp.as_f32("x")[rtok]
+    else:
+        gtok = None
+        y_u, gu_u = moe.grouped_swiglu_fwd(x, w1, w2, go, grs, save_gu=True)
+        xp_ref = inp.as_f32("x")
+    res = []
+    for _ in range(2):
+        y = gh.poison((N, d), x.dtype)
+        gu = gh.poison((N, 2 * F), x.dtype)
+        moe.grouped_swiglu_fwd_packed(x, gtok, w1p, w2p, go, grs, save_gu=True, out=y, gu_out=gu)
+        torch.cuda.synchronize()
+        res.append((y, gu))
+    assert gh.bits_equal(res[0][0], res[1][0]) and gh.bits_equal(res[0][1], res[1][1])
+    assert gh.bits_equal(res[0][0], y_u) and gh.bits_equal(res[0][1], gu_u)
+    y_ref, gu_ref = mo.grouped_swiglu_fwd(xp_ref, inp.as_f32("w1"), inp.as_f32("w2"), off, rs,
+                                          return_gu=True)
+    assert gh.normwise(gh.to_f64(res[0][0]), y_ref) <= gh.TOL_BF16
+    assert gh.normwise(gh.to_f64(res[0][1]), gu_ref) <= gh.TOL_BF16
 
 
 BWD_CASES = [
