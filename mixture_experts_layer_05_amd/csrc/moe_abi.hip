@@ -1,4 +1,6 @@
-// Library identity: ABI version and status names.
+// Library identity: ABI version and status names; the device-property cache.
+#include <atomic>
+
 #include "moe_internal.h"
 
 extern "C" int32_t moe_abi_version(void) { return 6; }
@@ -16,3 +18,22 @@ extern "C" const char* moe_status_string(moe_status s) {
   }
   return "MOE_ERR_UNKNOWN";
 }
+
+namespace moe {
+
+// Device-property cache: the CU count per device, queried on first use.
+int device_cu_count() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[kMaxDev];   // 0: not queried yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+}  // namespace moe

@@ -462,6 +462,292 @@ __global__ __launch_bounds__(C::kThreads, C::kWgPerCu) void ggf_kernel(FwdParams
 }
 
 // ---------------------------------------------------------------------------
+// Persistent expert GEMMs (fc1, fc2; bf16): one workgroup per CU walks its
+// share of the tiles with one 2-slot ring that runs across tile boundaries.
+// The next tile's first K tile is loaded while the current tile's last one
+// is multiplied, its decode and row gathers are done while the current tile
+// runs, and the current tile's epilogue overlaps those loads; the per-tile
+// prologue and the workgroup turnaround of the one-tile-per-workgroup launch
+// disappear.  Tiles, their staging and their epilogue math are those of
+// ggf_tile, so the results are bit-identical to it.
+//
+// Schedule: workgroup b sits on XCD b % 8 (round-robin dispatch); each XCD
+// owns a contiguous range of logical tiles (the row tiles that share a
+// weight panel are neighbours) and its workgroups take them round robin.
+// ---------------------------------------------------------------------------
+constexpr int kScanInts = 1040 + 64;    // tile_prefix scratch (E <= 1024)
+
+// One tile's addressing: its decode, buffer descriptors and per-lane offsets.
+template <int kLoads>
+struct PersistTile {
+  TileIdx ti;
+  __amdgpu_buffer_rsrc_t ra, rb;
+  int vo[kLoads];
+};
+
+template <class C, int kEpi>
+__device__ __forceinline__ void ggfp_body(const FwdParams& p) {
+  static_assert(kEpi == FWD_FC1 || kEpi == FWD_FC2, "expert GEMMs only");
+  static_assert(C::kStages == 2 && C::kStagesB == 2, "2-slot rings");
+  constexpr int kWN = C::kWN, kRB = C::kRB, kCB = C::kCB, kWaves = C::kWaves;
+  constexpr int kBM = C::kBM, kBN = C::kBN, kBK = C::kBK, kChunks = C::kChunks;
+  constexpr int kLoads = C::kLoads, kALoads = C::kALoads;
+  constexpr int nbn = kEpi == FWD_FC1 ? kBN / 2 : kBN;   // output columns per tile
+  extern __shared__ __align__(16) uint16_t s_lds[];
+  int* s_cum = reinterpret_cast<int*>(s_lds + C::kLdsBytes / 2);   // past the rings
+  int* s_tmp = s_cum + 1040;
+  uint16_t* const ring_a = s_lds;
+  uint16_t* const ring_b = s_lds + 2 * C::kATileE;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / kWN, wn = wave % kWN;
+  const int r32 = lane & 31, h = lane >> 5;
+  const int K = p.K;
+  const int nk = (K + kBK - 1) / kBK;
+
+  tile_prefix<C::kThreads>(p.offsets, p.E, kBM, p.ntn, s_cum, s_tmp);
+  const int total = s_cum[p.E];
+  const int g8 = static_cast<int>(gridDim.x >> 3);
+  const int xcd = static_cast<int>(blockIdx.x & 7), pos = static_cast<int>(blockIdx.x >> 3);
+  const int q = total >> 3, rq = total & 7;
+  const int xbeg = xcd * q + min(xcd, rq), xcnt = q + (xcd < rq ? 1 : 0);
+  const int ntiles = xcnt > pos ? (xcnt - pos + g8 - 1) / g8 : 0;
+  if (ntiles == 0) return;                       // uniform over the workgroup
+
+  // tile-invariant: the staged row, chunk and LDS block of each load
+  const int lr = lane / kChunks, pc = lane % kChunks;
+  int kcl[kLoads], dsto[kLoads], rowl[kLoads];
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) {
+    const bool isa = j < kALoads;
+    const int bb = isa ? wave + kWaves * j : wave + kWaves * (j - kALoads);
+    const int r = bb * C::kRowsPerBlk + lr;
+    rowl[j] = r;
+    kcl[j] = pc ^ swz_row<kChunks>(r);
+    dsto[j] = bb * 512;
+  }
+  const bool gath = p.gather != nullptr;
+
+  // per-tile addressing: decode, descriptors, per-lane source offsets
+  using TileState = PersistTile<kLoads>;
+  auto setup = [&](int j, TileState& st) {
+    st.ti = tile_decode(p.offsets, p.E, kBM, xbeg + pos + j * g8, s_cum);
+    const TileIdx& ti = st.ti;
+    const int m0 = ti.m0, n0 = ti.nt * nbn, last = ti.mend - 1 - m0;
+    st.ra = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(gath ? p.a : p.a + static_cast<size_t>(m0) * p.lda), 0,
+        (gath ? p.a_rows : ti.mend - m0) * p.lda * 2, kRsrcWord3);
+    st.rb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(p.b + static_cast<size_t>(ti.e) * p.b_estride), 0,
+        static_cast<int>(p.b_estride * 2), kRsrcWord3);
+#pragma unroll
+    for (int j2 = 0; j2 < kLoads; ++j2) {
+      const int r = rowl[j2], kc = kcl[j2];
+      if (j2 < kALoads) {
+        const int src = r > last ? -1 : gath ? p.gather[m0 + r] : r;
+        st.vo[j2] = src >= 0 && (!gath || src < p.a_rows) ? (src * p.lda + kc * 8) * 2 : kOob;
+      } else if (p.packed_b) {
+        st.vo[j2] = ((ti.nt * p.nkt * kBN + r) * kBK + kc * 8) * 2;
+      } else {
+        int wr;
+        if constexpr (kEpi == FWD_FC1) {
+          int f = n0 + (r % (kBN / 2));
+          f = f < p.F ? f : p.F - 1;
+          wr = r < kBN / 2 ? f : p.F + f;
+        } else {
+          wr = n0 + r;
+          wr = wr < p.d ? wr : p.d - 1;
+        }
+        st.vo[j2] = (wr * p.ldb + kc * 8) * 2;
+      }
+    }
+  };
+  // K tile kt of tile st into ring slot `slot`
+  auto issue = [&](const TileState& st, int kt, int slot) {
+    const int k0 = kt * kBK;
+    const int sb = p.packed_b ? kt * (kBN * kBK * 2) : k0 * 2;
+    uint16_t* da = ring_a + slot * C::kATileE;
+    uint16_t* db = ring_b + slot * C::kBTileE;
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      const int v = (k0 + kcl[j] * 8 < K) ? st.vo[j] : kOob;
+      if (j < kALoads)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(st.ra, (lds_void*)(da + dsto[j]), 16, v, k0 * 2,
+                                                 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(st.rb, (lds_void*)(db + dsto[j]), 16, v, sb, 0, 0);
+    }
+  };
+
+  // this wave's operand rows in the staged tiles
+  int a_rd[kRB], b_rd[kCB];
+#pragma unroll
+  for (int i = 0; i < kRB; ++i) a_rd[i] = wm * kRB * 32 + i * 32 + r32;
+#pragma unroll
+  for (int c = 0; c < kCB; ++c) {
+    if constexpr (kEpi == FWD_FC1) {
+      const int cc = c % (kCB / 2);
+      b_rd[c] = (c < kCB / 2 ? 0 : kBN / 2) + wn * (kCB / 2) * 32 + cc * 32 + r32;
+    } else {
+      b_rd[c] = wn * kCB * 32 + c * 32 + r32;
+    }
+  }
+  auto swz = [](int r, int kc) { return r * kBK + ((kc ^ swz_row<kChunks>(r)) << 3); };
+
+  f32x16 acc[kRB][kCB];
+  auto compute = [&](int slot, int nrb) {
+    const uint16_t* As = ring_a + slot * C::kATileE;
+    const uint16_t* Bs = ring_b + slot * C::kBTileE;
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      const int ck = 2 * kk + h;
+      bf16x8 bv[kCB];
+#pragma unroll
+      for (int c = 0; c < kCB; ++c) bv[c] = *reinterpret_cast<const bf16x8*>(Bs + swz(b_rd[c], ck));
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) {
+        if (rb < nrb) {
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(As + swz(a_rd[rb], ck));
+#pragma unroll
+          for (int c = 0; c < kCB; ++c)
+            acc[rb][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[c], av, acc[rb][c], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // Epilogue staging without padding: a staged row is kCols bf16, its
+  // 16-byte chunk c stored at c ^ (row mod 16); rows go to the two ring
+  // slots not being filled (region 0: A slot, region 1: B slot, 32 KB each).
+  constexpr int kCols = nbn;
+  constexpr int kRowB = kCols * 2;                     // staged row bytes
+  constexpr int kRR = 32768 / kRowB;                   // rows per region
+  constexpr int kPassRows = 2 * kRR;
+  constexpr int kPass = (kBM + kPassRows - 1) / kPassRows;
+  constexpr int kChunksRow = kCols / 8;
+  static_assert(C::kATileE * 2 == 32768 && C::kBTileE * 2 == 32768, "32 KB ring slots");
+  static_assert(kRR % (kRB * 32) == 0 && kBM % kPassRows == 0, "waves stage whole regions");
+  const int limit = kEpi == FWD_FC1 ? p.F : p.d;
+  auto epilogue = [&](const TileIdx& ti, int nrb, int free_slot) {
+    const int m0 = ti.m0, n0 = ti.nt * nbn;
+    uint8_t* reg0 = reinterpret_cast<uint8_t*>(ring_a + free_slot * C::kATileE);
+    uint8_t* reg1 = reinterpret_cast<uint8_t*>(ring_b + free_slot * C::kBTileE);
+    auto staged = [&](int lp, int byte) -> uint8_t* {   // row lp of the pass, byte offset
+      const int rr = lp % kRR;
+      uint8_t* base = lp < kRR ? reg0 : reg1;
+      return base + rr * kRowB + ((((byte >> 4) ^ (rr & 15))) << 4) + (byte & 15);
+    };
+    const int wrow0 = wm * kRB * 32;
+#pragma unroll
+    for (int ps = 0; ps < kPass; ++ps) {
+      if (wrow0 / kPassRows == ps) {
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) {
+          if (rb >= nrb) continue;
+          const int lp = wrow0 - ps * kPassRows + rb * 32 + r32;
+          const int row = m0 + wrow0 + rb * 32 + r32;
+          if constexpr (kEpi == FWD_FC1) {
+            const size_t rowz = static_cast<size_t>(row);
+#pragma unroll
+            for (int c = 0; c < kCB / 2; ++c) {
+#pragma unroll
+              for (int qq = 0; qq < 4; ++qq) {
+                const int fl = wn * (kCB / 2) * 32 + c * 32 + 8 * qq + 4 * h;
+                const f32x16& G = acc[rb][c];
+                const f32x16& U = acc[rb][c + kCB / 2];
+                float a4[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  const float g = G[4 * qq + i];
+                  a4[i] = g * sigmoid_fast(g) * U[4 * qq + i];
+                }
+                *reinterpret_cast<u32x2*>(staged(lp, fl * 2)) =
+                    pack4_bf16(a4[0], a4[1], a4[2], a4[3]);
+                const int f = n0 + fl;
+                if (p.out2 && row < ti.mend && f < p.F) {
+                  uint16_t* gu = p.out2 + rowz * 2 * p.F;
+                  *reinterpret_cast<u32x2*>(gu + f) =
+                      pack4_bf16(G[4 * qq], G[4 * qq + 1], G[4 * qq + 2], G[4 * qq + 3]);
+                  *reinterpret_cast<u32x2*>(gu + p.F + f) =
+                      pack4_bf16(U[4 * qq], U[4 * qq + 1], U[4 * qq + 2], U[4 * qq + 3]);
+                }
+              }
+            }
+          } else {
+            const float sc = (p.scale && row < ti.mend) ? p.scale[row] : 1.0f;
+#pragma unroll
+            for (int c = 0; c < kCB; ++c) {
+#pragma unroll
+              for (int qq = 0; qq < 4; ++qq) {
+                const int nl = wn * kCB * 32 + c * 32 + 8 * qq + 4 * h;
+                const f32x16& Y = acc[rb][c];
+                *reinterpret_cast<u32x2*>(staged(lp, nl * 2)) =
+                    pack4_bf16(Y[4 * qq] * sc, Y[4 * qq + 1] * sc, Y[4 * qq + 2] * sc,
+                               Y[4 * qq + 3] * sc);
+              }
+            }
+          }
+        }
+      }
+      // LDS only: a __syncthreads fence would also wait for the next tile's loads
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+      for (int i = tid; i < kPassRows * kChunksRow; i += C::kThreads) {
+        const int lp = i / kChunksRow, ch = i - lp * kChunksRow;
+        const int row = m0 + ps * kPassRows + lp;
+        const int col = n0 + ch * 8;
+        if (row < ti.mend && col < limit)
+          *reinterpret_cast<u32x4*>(p.out + static_cast<size_t>(row) * limit + col) =
+              *reinterpret_cast<const u32x4*>(staged(lp, ch * 16));
+      }
+      if (ps + 1 < kPass) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+  };
+
+  auto live_blocks = [&](const TileIdx& ti) {
+    const int rows = ti.mend - ti.m0 - wm * kRB * 32;
+    return rows <= 0 ? 0 : min(kRB, (rows + 31) >> 5);
+  };
+
+  TileState cur, nxt;
+  setup(0, cur);
+  __syncthreads();              // s_cum (read by setup) is never overwritten; the ring is free
+  issue(cur, 0, 0);
+  if (ntiles > 1) setup(1, nxt);
+  int g = 0;                    // global K step: ring slot g & 1
+#pragma unroll 1
+  for (int j = 0; j < ntiles; ++j) {
+    const int nrb = live_blocks(cur.ti);
+#pragma unroll
+    for (int i = 0; i < kRB; ++i)
+#pragma unroll
+      for (int c = 0; c < kCB; ++c) acc[i][c] = f32x16{};
+#pragma unroll 1
+    for (int kt = 0; kt < nk; ++kt, ++g) {
+      // everything this wave issued has landed (the ring's loads, the gathers
+      // of the next tile's setup, the last epilogue's stores); the barrier
+      // makes tile g visible and frees slot (g + 1) & 1
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      if (kt + 1 < nk) issue(cur, kt + 1, (g + 1) & 1);
+      else if (j + 1 < ntiles) issue(nxt, 0, (g + 1) & 1);
+      compute(g & 1, nrb);
+    }
+    asm volatile("s_barrier" ::: "memory");   // every wave is done reading slot (g - 1) & 1
+    epilogue(cur.ti, nrb, (g - 1) & 1);
+    if (j + 1 < ntiles) {
+      cur = nxt;
+      if (j + 2 < ntiles) setup(j + 2, nxt);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+template <class C, int kEpi>
+__global__ __launch_bounds__(C::kThreads, 1) void ggfp_kernel(FwdParams p) {
+  ggfp_body<C, kEpi>(p);
+}
+
+// ---------------------------------------------------------------------------
 // fp32 path (MOE_F32): LDS-tiled FMA, 64 x 64 x 16 tiles, 4 x 4 outputs per
 // thread, same tile enumeration and epilogue semantics.
 // ---------------------------------------------------------------------------
@@ -615,6 +901,13 @@ __global__ __launch_bounds__(256) void pack_b_kernel(int64_t total, int rows, in
   out[i] = v;
 }
 
+// One workgroup per CU (at most one per tile), a multiple of the 8 XCDs.
+static unsigned persistent_grid(int64_t tiles) {
+  const int64_t cus = device_cu_count();
+  const int64_t g = std::min<int64_t>(cus, (tiles + 7) / 8 * 8);
+  return static_cast<unsigned>(std::max<int64_t>(8, g / 8 * 8));
+}
+
 hipError_t launch_grouped_fwd_bf16(hipStream_t stream, int64_t N, int64_t d, int64_t F, int32_t E,
                                    const void* x_perm, const void* w1, const void* w2,
                                    const int32_t* offsets, const float* row_scale, void* y_perm,
@@ -634,11 +927,12 @@ hipError_t launch_grouped_fwd_bf16(hipStream_t stream, int64_t N, int64_t d, int
   p.K = (int)d;
   p.out = a_buf; p.out2 = static_cast<uint16_t*>(gu_save);
   p.ksplit = 1;
-  hipError_t err = allow_lds(ggf_kernel<C, FWD_FC1>, C::kLdsBytes);
-  if (err == hipSuccess) err = allow_lds(ggf_kernel<C, FWD_FC2>, C::kLdsBytes);
+  const size_t lds = C::kLdsBytes + kScanInts * sizeof(int);
+  hipError_t err = allow_lds(ggfp_kernel<C, FWD_FC1>, lds);
+  if (err == hipSuccess) err = allow_lds(ggfp_kernel<C, FWD_FC2>, lds);
   if (err == hipSuccess)
-    err = launch(ggf_kernel<C, FWD_FC1>, dim3(tiles_bound(N, E, C::kBM) * p.ntn),
-                 dim3(C::kThreads), C::kLdsBytes, stream, p);
+    err = launch(ggfp_kernel<C, FWD_FC1>, dim3(persistent_grid(tiles_bound(N, E, C::kBM) * p.ntn)),
+                 dim3(C::kThreads), lds, stream, p);
   if (err != hipSuccess || !run_fc2) return err;
   // fc2: Y = (A W2^T) * row_scale; kBN output columns per tile
   FwdParams q{};
@@ -653,8 +947,8 @@ hipError_t launch_grouped_fwd_bf16(hipStream_t stream, int64_t N, int64_t d, int
   q.scale = row_scale;
   q.out = static_cast<uint16_t*>(y_perm);
   q.ksplit = 1;
-  return launch(ggf_kernel<C, FWD_FC2>, dim3(tiles_bound(N, E, C::kBM) * q.ntn),
-                dim3(C::kThreads), C::kLdsBytes, stream, q);
+  return launch(ggfp_kernel<C, FWD_FC2>, dim3(persistent_grid(tiles_bound(N, E, C::kBM) * q.ntn)),
+                dim3(C::kThreads), lds, stream, q);
 }
 
 int router_ksplit(int64_t T, int64_t d, int32_t E) {

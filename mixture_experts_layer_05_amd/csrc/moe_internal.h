@@ -44,6 +44,10 @@ inline hipError_t allow_lds(void (*kernel)(KArgs...), size_t bytes) {
 
 inline moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// Compute units of the current device, queried once per device and cached
+// (256 on MI355X); 256 if the query fails.
+int device_cu_count();
+
 inline size_t elt_size(moe_dtype dt) { return dt == MOE_BF16 ? 2 : 4; }
 
 }  // namespace moe
