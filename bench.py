@@ -3,9 +3,9 @@
 One step = one forward pass of the whole layer over one batch of the
 128-expert top-8 workload (T=4096 tokens, d=2048, E=128, k=8, ffn 768,
 bf16 storage, fp32 accumulation and router math):
-    route -> permute (index work only) -> grouped SwiGLU (fc1 gathers the
-    token rows from x by the permute's row map; fc2 applies the routing
-    weight as its row scale) -> combine
+    route -> permute (index work only) -> grouped SwiGLU on tile-packed
+    weights (fc1 gathers the token rows from x by the permute's row map; fc2
+    applies the routing weight as its row scale) -> combine
 Inputs are seeded synthetic tensors already resident in HBM; every launch
 goes through the C ABI (libmoe_mi355x.so).
 
@@ -41,7 +41,10 @@ PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, AMD's published figure
 KERNEL_SOURCES = ("mixture_experts_layer_05_amd/csrc/moe_grouped_fwd.hip",
                   "mixture_experts_layer_05_amd/csrc/moe_gemm_common.h",
                   "mixture_experts_layer_05_amd/csrc/moe_device.h")
-MEASURED_TRAFFIC = {}
+MEASURED_TRAFFIC = {
+    "qwen3_30b": {"bytes": 1621016641,
+                  "sources_sha256": "23d1403b57799ac4246afa201c1eb501929cd1c6de142dad0a3b30b04303e5f4"},
+}
 
 
 def measured_traffic(workload):
@@ -250,7 +253,8 @@ def main():
         roof = {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic}
-    roof["kernel"] = "moe_grouped_swiglu_fwd_gather (fc1 gather+SwiGLU, fc2+row-scale launches)"
+    roof["kernel"] = ("moe_grouped_swiglu_fwd_packed (persistent fc1 gather+SwiGLU and fc2+row-scale "
+                      "launches on tile-packed weights)")
     roof["algorithmic_flop"] = alg["gemm_flop"]
     roof["algorithmic_bytes"] = alg["gemm_bytes"]
     roof["avg_launch_ms"] = round(per_stage["grouped_gemm"], 4)
