@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, AMD's published figure
+PEAK_FP8_TFLOPS = 5000.0         # MI355X dense fp8 MFMA, AMD's published figure
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, AMD's published figure
 
 # HBM bytes per grouped-GEMM forward call (fc1 + fc2 dispatches), from
@@ -41,19 +42,22 @@ PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, AMD's published figure
 KERNEL_SOURCES = ("mixture_experts_layer_05_amd/csrc/moe_grouped_fwd.hip",
                   "mixture_experts_layer_05_amd/csrc/moe_gemm_common.h",
                   "mixture_experts_layer_05_amd/csrc/moe_device.h")
+KERNEL_SOURCES_FP8 = ("mixture_experts_layer_05_amd/csrc/moe_grouped_mx.hip",
+                      "mixture_experts_layer_05_amd/csrc/moe_gemm_common.h",
+                      "mixture_experts_layer_05_amd/csrc/moe_device.h")
 MEASURED_TRAFFIC = {
     "qwen3_30b": {"bytes": 1621016641,
                   "sources_sha256": "23d1403b57799ac4246afa201c1eb501929cd1c6de142dad0a3b30b04303e5f4"},
 }
 
 
-def measured_traffic(workload):
+def measured_traffic(workload, fp8=False):
     import hashlib
-    rec = MEASURED_TRAFFIC.get(workload)
+    rec = MEASURED_TRAFFIC.get(workload + (":fp8" if fp8 else ""))
     if rec is None:
         return None
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in (KERNEL_SOURCES_FP8 if fp8 else KERNEL_SOURCES):
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return rec["bytes"] if h.hexdigest() == rec["sources_sha256"] else None
@@ -66,6 +70,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen3_30b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fp8", action="store_true",
+                    help="expert GEMMs in MXFP8 (E4M3, 32-value E8M0 block scales)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--train", action="store_true",
                     help="time a training step of the layer (forward keeping what the "
@@ -92,15 +98,23 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": COPY_CAL_BYTES, "dispatches": 5}), flush=True)
 
 
-def algorithmic(cfg):
+def algorithmic(cfg, fp8=False):
     """Per-call algorithmic work (what the method itself must move or do)."""
     T, d, E, k, F = cfg.T, cfg.d, cfg.E, cfg.k, cfg.F
     N = T * k
     b = 2
     gemm_flop = 6.0 * N * d * F
-    # expert weights read once + token rows read once (fc1 gathers them from x)
-    # + A written and read + Y_perm written
-    gemm_bytes = 3.0 * E * d * F * b + T * d * b + 2.0 * N * F * b + N * d * b
+    if fp8:
+        # MX operands: a byte per value plus a scale byte per 32.  x read (bf16)
+        # and its codes written by the quantiser, then read once by fc1; expert
+        # weight codes read once; A's codes written and read; Y_perm written (bf16)
+        q = 1.0 + 1.0 / 32
+        gemm_bytes = (T * d * (b + q) + T * d * q + 3.0 * E * d * F * q + 2.0 * N * F * q
+                      + N * d * b)
+    else:
+        # expert weights read once + token rows read once (fc1 gathers them from x)
+        # + A written and read + Y_perm written
+        gemm_bytes = 3.0 * E * d * F * b + T * d * b + 2.0 * N * F * b + N * d * b
     route_bytes = T * (2 * d + 8 * k + 4) + E * d * b
     # permute without the row copy: topk_idx, topk_w read; slot_of, row_token, row_w written
     permute_bytes = T * 20 * k
@@ -172,7 +186,7 @@ def main():
     x = gpu(inp.x)
     layer = moe.MoELayer(gpu(inp.w_router), gpu(inp.w1), gpu(inp.w2), cfg.k, cfg.T, cfg.score,
                          cfg.normalize, gpu(inp.logit_bias), gpu(inp.w_gate), gpu(inp.ws1),
-                         gpu(inp.ws2))
+                         gpu(inp.ws2), fp8=args.fp8)
     stream = torch.cuda.current_stream()
 
     stages = ["route", "permute", "grouped_gemm", "shared", "combine"]
@@ -238,23 +252,28 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     tokens_per_s = cfg.T / (wall / args.steps)
 
-    alg = algorithmic(cfg)
+    alg = algorithmic(cfg, args.fp8)
+    peak_mfma = PEAK_FP8_TFLOPS if args.fp8 else PEAK_BF16_TFLOPS
     t_gemm = per_stage["grouped_gemm"] * 1e-3
     gemm_tflops = alg["gemm_flop"] / t_gemm / 1e12
     gemm_gbs = alg["gemm_bytes"] / t_gemm / 1e9
     # the binding roof of the grouped GEMM: whichever of MFMA and HBM time is longer
-    t_mfma = alg["gemm_flop"] / (PEAK_BF16_TFLOPS * 1e12)
+    t_mfma = alg["gemm_flop"] / (peak_mfma * 1e12)
     t_hbm = alg["gemm_bytes"] / (PEAK_HBM_GBS * 1e9)
-    traffic = measured_traffic(cfg.name)
+    traffic = measured_traffic(cfg.name, args.fp8)
     if t_hbm > t_mfma:
         roof = {"bound": "hbm", "achieved": round(gemm_gbs, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(gemm_gbs / PEAK_HBM_GBS, 4), "traffic": traffic}
     else:
-        roof = {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
+        roof = {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": peak_mfma,
+                "unit": "TFLOP/s", "frac": round(gemm_tflops / peak_mfma, 4),
                 "traffic": traffic}
-    roof["kernel"] = ("moe_grouped_swiglu_fwd_packed (persistent fc1 gather+SwiGLU and fc2+row-scale "
-                      "launches on tile-packed weights)")
+    if args.fp8:
+        roof["kernel"] = ("moe_quantize_mx of x + moe_grouped_swiglu_fwd_mx (persistent MXFP8 fc1 "
+                          "gather+SwiGLU+A quantisation and fc2+row-scale launches)")
+    else:
+        roof["kernel"] = ("moe_grouped_swiglu_fwd_packed (persistent fc1 gather+SwiGLU and "
+                          "fc2+row-scale launches on tile-packed weights)")
     roof["algorithmic_flop"] = alg["gemm_flop"]
     roof["algorithmic_bytes"] = alg["gemm_bytes"]
     roof["avg_launch_ms"] = round(per_stage["grouped_gemm"], 4)
@@ -275,13 +294,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8_e4m3_mx" if args.fp8 else "bf16",
         "data": "synthetic (seeded PCG64; x~N(0,1), router~N(0,1/d), experts~N(0,0.02^2))",
         "config": {"workload": f"{cfg.name}: T={cfg.T} d={cfg.d} E={cfg.E} top-{cfg.k} "
                                f"{cfg.score} ffn={cfg.F}", "T": cfg.T, "d": cfg.d, "E": cfg.E,
-                   "k": cfg.k, "F": cfg.F, "Fs": cfg.Fs, "score": cfg.score},
+                   "k": cfg.k, "F": cfg.F, "Fs": cfg.Fs, "score": cfg.score,
+                   "expert_gemms": ("MXFP8: E4M3 values, E8M0 scale per 32 along K, fp32 "
+                                    "accumulation; routing bf16/fp32") if args.fp8 else "bf16"},
         "grouped_gemm_tflops": round(gemm_tflops, 1),
-        "grouped_gemm_mfma_frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
+        "grouped_gemm_mfma_frac": round(gemm_tflops / peak_mfma, 4),
+        "mfma_peak_tflops": peak_mfma,
         "stage_ms": {s: round(v, 4) for s, v in per_stage.items()},
         "stage_gbs": {"route": gbs("route_bytes", "route"),
                       "permute": gbs("permute_bytes", "permute"),

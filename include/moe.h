@@ -258,6 +258,54 @@ MOE_API moe_status moe_grouped_swiglu_fwd_packed(hipStream_t stream, moe_dtype d
                                          void* gu_save, void* ws, size_t ws_bytes);
 
 /* ------------------------------------------------------------------------
+ * MXFP8 forward: the grouped SwiGLU with microscaled FP8 E4M3 operands.
+ *
+ * Passages: "Megatron-Bridge 深度剖析", section "FP8 训练" (E4M3 and its scale
+ * factors; FP8 doubles the matrix rate and halves the traffic of the grouped
+ * GEMM that BF16 leaves memory-bound) and the section on future directions
+ * (MXFP8: finer-grained scale factors).  Format (OCP microscaling): E4M3
+ * codes (largest finite 448), one E8M0 scale byte (2^(code - 127)) per 32
+ * consecutive values along the reduction dimension,
+ *     scale = 2^(floor(log2 max|v|) - 8),  code = RNE(clamp(v / scale, +-448));
+ * an all-zero block gets scale byte 0.  Quantised: the token rows (along d),
+ * W1 and W2 rows (along d and F), and A = silu(G) U per row along F (taken
+ * from its fp32 value inside fc1's epilogue).  Accumulation is fp32 (the MFMA
+ * adds each 64-value product at reduced internal precision, ~2^-14 relative).
+ *
+ * moe_quantize_mx: rows [R, K] bf16 -> codes [R, K] u8 and scales laid out
+ *   [ceil(K/128)][R][4] u8 (the 4 scale bytes of a row for one 128-wide K
+ *   tile are adjacent; slots past K / 32 are 0).  K % 32 == 0.
+ * moe_pack_weights_mx: W [E, rows, K] bf16 -> codes in the tile-packed layout
+ *   of moe_pack_weights with 128-wide K tiles, [e][panel][K tile][256 rows]
+ *   [128], and scales [e][panel][K tile][256 rows][4]; gated = 1 for W1
+ *   ([gate; up] panels of 128 + 128 rows), 0 for W2.  Sizes from
+ *   moe_pack_weights_mx_size(E, rows, K, gated, scales = 0 / 1).
+ * moe_grouped_swiglu_fwd_mx: the forward on those operands:
+ *   xq, xs     moe_quantize_mx of x [T, d] (row_token given: fc1 gathers row
+ *              r from x[row_token[r]]) or of x_perm [N, d] (row_token NULL)
+ *   w1q, w1s   moe_pack_weights_mx(E, 2F, d, 1);  w2q, w2s: (E, d, F, 0)
+ *   y_perm     [N, d] bf16 out, (A Q(W2)^T) * row_scale
+ *   workspace  moe_grouped_swiglu_fwd_mx_workspace_size(N, F) bytes (the
+ *              quantised A and its scales)
+ * Limits: d % 32 == 0, F % 32 == 0, E <= 1024, one expert's packed codes and
+ * the token rows below 2^31 bytes.  Inference only: no G, U save.
+ * --------------------------------------------------------------------- */
+MOE_API size_t moe_quantize_mx_scales_size(int64_t R, int64_t K);
+MOE_API moe_status moe_quantize_mx(hipStream_t stream, int64_t R, int64_t K, const void* x,
+                           void* codes, void* scales);
+MOE_API size_t moe_pack_weights_mx_size(int32_t E, int64_t rows, int64_t K, int32_t gated,
+                                int32_t scales);
+MOE_API moe_status moe_pack_weights_mx(hipStream_t stream, int32_t E, int64_t rows, int64_t K,
+                               int32_t gated, const void* w, void* w_codes, void* w_scales);
+MOE_API size_t moe_grouped_swiglu_fwd_mx_workspace_size(int64_t N, int64_t F);
+MOE_API moe_status moe_grouped_swiglu_fwd_mx(hipStream_t stream, int64_t N, int64_t d, int64_t F,
+                                     int32_t E, int64_t T, const void* xq, const void* xs,
+                                     const int32_t* row_token, const void* w1q, const void* w1s,
+                                     const void* w2q, const void* w2s,
+                                     const int32_t* expert_offsets, const float* row_scale,
+                                     void* y_perm, void* ws, size_t ws_bytes);
+
+/* ------------------------------------------------------------------------
  * moe_grouped_swiglu_bwd -- grouped-GEMM dgrad and wgrad of the forward.
  *
  * Passage: "Megatron-Bridge 深度剖析", "通信隐藏与混合精度 / TP 通信重叠"

@@ -21,6 +21,7 @@ import torch
 __all__ = [
     "MoEError", "lib", "route", "permute", "grouped_swiglu_fwd", "grouped_swiglu_fwd_gather",
     "PackedWeights", "pack_weights", "grouped_swiglu_fwd_packed",
+    "MxTensor", "quantize_mx", "pack_weights_mx", "grouped_swiglu_fwd_mx",
     "grouped_swiglu_bwd", "unpermute_combine", "combine_backward", "route_backward",
     "moe_layer_forward",
     "MoELayer", "LIB_PATH", "EXPORTED",
@@ -55,6 +56,13 @@ EXPORTED = {
     "moe_pack_weights": (_i32, [_vp, _i32, _i32, _i64, _i64, _i32, _vp, _vp]),
     "moe_grouped_swiglu_fwd_packed": (_i32, [_vp, _i32, _i64, _i64, _i64, _i32, _i64,
                                              _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz]),
+    "moe_quantize_mx_scales_size": (_sz, [_i64, _i64]),
+    "moe_quantize_mx": (_i32, [_vp, _i64, _i64, _vp, _vp, _vp]),
+    "moe_pack_weights_mx_size": (_sz, [_i32, _i64, _i64, _i32, _i32]),
+    "moe_pack_weights_mx": (_i32, [_vp, _i32, _i64, _i64, _i32, _vp, _vp, _vp]),
+    "moe_grouped_swiglu_fwd_mx_workspace_size": (_sz, [_i64, _i64]),
+    "moe_grouped_swiglu_fwd_mx": (_i32, [_vp, _i64, _i64, _i64, _i32, _i64, _vp, _vp, _vp,
+                                         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz]),
     "moe_grouped_swiglu_bwd_workspace_size": (_sz, [_i64, _i64, _i32, _i32]),
     "moe_grouped_swiglu_bwd": (_i32, [_vp, _i32, _i64, _i64, _i64, _i32,
                                       _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
@@ -278,6 +286,69 @@ def grouped_swiglu_fwd_packed(x, row_token, w1p, w2p, expert_offsets, row_scale=
     return y, gu
 
 
+class MxTensor:
+    """MX (microscaled FP8 E4M3) data: uint8 codes and uint8 E8M0 scale bytes
+    in the layouts of include/moe.h, plus the logical shape."""
+
+    def __init__(self, codes, scales, shape, gated=None):
+        self.codes, self.scales, self.shape, self.gated = codes, scales, tuple(shape), gated
+
+
+def quantize_mx(x, out=None):
+    """x [R, K] bf16 -> MxTensor (codes [R, K], scales [ceil(K/128)][R][4])."""
+    R, K = x.shape
+    if out is None:
+        out = MxTensor(torch.empty((R, K), dtype=torch.uint8, device=x.device),
+                       torch.empty(lib().moe_quantize_mx_scales_size(R, K), dtype=torch.uint8,
+                                   device=x.device), (R, K))
+    _check(lib().moe_quantize_mx(_stream(), R, K, _p(x), _p(out.codes), _p(out.scales)),
+           "moe_quantize_mx")
+    return out
+
+
+def pack_weights_mx(w, gated):
+    """w [E, rows, K] bf16 -> MxTensor in the packed layout (gated: fc1 panels)."""
+    E, rows, K = w.shape
+    L = lib()
+    nc = L.moe_pack_weights_mx_size(E, rows, K, int(bool(gated)), 0)
+    ns = L.moe_pack_weights_mx_size(E, rows, K, int(bool(gated)), 1)
+    if nc == 0:
+        raise MoEError(f"cannot pack weights of shape {tuple(w.shape)} (gated={gated})")
+    codes = torch.empty(nc, dtype=torch.uint8, device=w.device)
+    scales = torch.empty(ns, dtype=torch.uint8, device=w.device)
+    _check(L.moe_pack_weights_mx(_stream(), E, rows, K, int(bool(gated)), _p(w), _p(codes),
+                                 _p(scales)), "moe_pack_weights_mx")
+    return MxTensor(codes, scales, (E, rows, K), gated)
+
+
+def fwd_mx_workspace_size(N, F):
+    return lib().moe_grouped_swiglu_fwd_mx_workspace_size(N, F)
+
+
+def grouped_swiglu_fwd_mx(xq, row_token, w1q, w2q, expert_offsets, row_scale=None, out=None,
+                          ws=None):
+    """MXFP8 grouped SwiGLU forward: xq = quantize_mx(x [T, d]) with row_token
+    (fc1 gathers x[row_token[r]]), or quantize_mx(x_perm [N, d]) without;
+    w1q = pack_weights_mx(w1, True), w2q = pack_weights_mx(w2, False).
+    -> y_perm [N, d] bf16"""
+    T, d = xq.shape
+    N = row_token.shape[0] if row_token is not None else T
+    E, twoF, _ = w1q.shape
+    F = twoF // 2
+    if not (w1q.gated and not w2q.gated and w1q.shape[2] == d and w2q.shape == (E, d, F)):
+        raise MoEError("MX weights do not match x and each other")
+    dev = xq.codes.device
+    y = out if out is not None else torch.empty((N, d), dtype=torch.bfloat16, device=dev)
+    if ws is None:
+        ws = _ws(fwd_mx_workspace_size(N, F), dev)
+    _check(lib().moe_grouped_swiglu_fwd_mx(_stream(), N, d, F, E, T, _p(xq.codes), _p(xq.scales),
+                                           _p(row_token), _p(w1q.codes), _p(w1q.scales),
+                                           _p(w2q.codes), _p(w2q.scales), _p(expert_offsets),
+                                           _p(row_scale), _p(y), _p(ws), ws.numel()),
+           "moe_grouped_swiglu_fwd_mx")
+    return y
+
+
 def bwd_workspace_size(N, F, dtype, recompute):
     return lib().moe_grouped_swiglu_bwd_workspace_size(
         N, F, MOE_BF16 if dtype == torch.bfloat16 else MOE_F32, int(bool(recompute)))
@@ -387,6 +458,12 @@ class MoELayer:
     weights also in the tile-packed layout (pack_weights) and runs the
     grouped GEMMs on it; call :meth:`repack` after changing the weights.
 
+    ``fp8`` runs the expert GEMMs (routed and shared) in MXFP8: the expert
+    weights are quantised once (pack_weights_mx; :meth:`repack` after a
+    change), x is quantised at the start of each forward, fc1 quantises its
+    SwiGLU output for fc2; routing stays in bf16 / fp32.  Inference only,
+    with gathered rows; d, F and the shared ffn must be multiples of 32.
+
     ``overlap_shared`` runs the shared expert, which depends only on x, on a
     second stream (default priority) concurrently with route, permute and
     the routed GEMM; its output stays unscaled and the combine applies the
@@ -400,8 +477,17 @@ class MoELayer:
     def __init__(self, w_router, w1, w2, k, T, score="softmax", normalize=True,
                  logit_bias=None, w_gate=None, ws1=None, ws2=None, save_gu=False,
                  gather=True, train=False, overlap_shared=False, selection_bias=None,
-                 packed=None):
+                 packed=None, fp8=False):
         self.train = train
+        self.fp8 = fp8
+        if fp8:
+            Fs_ = ws1.shape[0] // 2 if ws1 is not None else 32
+            if train or not gather or overlap_shared or w1.dtype != torch.bfloat16:
+                raise MoEError("fp8 serves the bf16 inference forward with gathered rows, "
+                               "without the shared-expert overlap")
+            if w1.shape[2] % 32 or w1.shape[1] % 64 or Fs_ % 32:
+                raise MoEError("fp8 needs d, F and the shared ffn to be multiples of 32")
+            packed = False
         if packed is None:
             packed = not train and w1.dtype == torch.bfloat16
         if packed and (train or w1.dtype != torch.bfloat16):
@@ -448,15 +534,30 @@ class MoELayer:
                 self.ev_x = torch.cuda.Event()
                 self.ev_sh = torch.cuda.Event()
                 self.shared_ws = _ws(fwd_workspace_size(T, Fs, dt), dev)
+        if fp8:
+            ws_f = fwd_mx_workspace_size(N, self.F)
+            if ws1 is not None:
+                ws_f = max(ws_f, fwd_mx_workspace_size(T, ws1.shape[0] // 2))
+            self.xq = MxTensor(torch.empty((T, d), dtype=torch.uint8, device=dev),
+                               torch.empty(lib().moe_quantize_mx_scales_size(T, d),
+                                           dtype=torch.uint8, device=dev), (T, d))
         self.ffn_ws = _ws(ws_f, dev)
         self.y = torch.empty((T, d), dtype=dt, device=dev)
         if train:
             self._alloc_backward(dev, dt)
-        if packed:
+        if packed or fp8:
             self.repack()
 
     def repack(self):
-        """(Re)build the tile-packed copies of the expert weights."""
+        """(Re)build the tile-packed (bf16) or MX-quantised (fp8) copies of
+        the expert weights."""
+        if self.fp8:
+            self.w1q = pack_weights_mx(self.w1, True)
+            self.w2q = pack_weights_mx(self.w2, False)
+            if self.ws1 is not None:
+                self.ws1q = pack_weights_mx(self.ws1_e, True)
+                self.ws2q = pack_weights_mx(self.ws2_e, False)
+            return
         self.w1p = pack_weights(self.w1, True)
         self.w2p = pack_weights(self.w2, False)
         if self.ws1 is not None:
@@ -486,7 +587,10 @@ class MoELayer:
         self.rbwd_ws = _ws(route_backward_workspace_size(T, d, k), dev)
 
     def _shared(self, x, scale, ws):
-        if self.packed:
+        if self.fp8:       # x quantised by _routed earlier in the forward
+            grouped_swiglu_fwd_mx(self.xq, None, self.ws1q, self.ws2q, self.shared_off,
+                                  row_scale=scale, out=self.y_shared, ws=ws)
+        elif self.packed:
             grouped_swiglu_fwd_packed(x, None, self.ws1p, self.ws2p, self.shared_off,
                                       row_scale=scale, out=self.y_shared, ws=ws)
         else:
@@ -499,7 +603,11 @@ class MoELayer:
 
     def _routed(self, x, xp, rtok, off, rs):
         """The routed grouped GEMMs (fc1 gathers x rows by rtok when xp is None)."""
-        if self.packed:
+        if self.fp8:
+            quantize_mx(x, out=self.xq)
+            grouped_swiglu_fwd_mx(self.xq, rtok, self.w1q, self.w2q, off, row_scale=rs,
+                                  out=self.y_perm, ws=self.ffn_ws)
+        elif self.packed:
             grouped_swiglu_fwd_packed(x if xp is None else xp, rtok if xp is None else None,
                                       self.w1p, self.w2p, off, row_scale=rs, out=self.y_perm,
                                       gu_out=self.gu, save_gu=self.gu is not None,

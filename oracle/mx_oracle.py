@@ -116,7 +116,8 @@ def _silu(z):
     return z / (1.0 + np.exp(-z))
 
 
-def grouped_swiglu_fwd_mx(x_perm, w1, w2, offsets, row_scale=None, return_a=False):
+def grouped_swiglu_fwd_mx(x_perm, w1, w2, offsets, row_scale=None, return_a=False,
+                          return_parts=False):
     """The grouped SwiGLU forward with MX-quantised GEMM operands.
 
     x_perm [N, d], w1 [E, 2F, d] (gate rows first), w2 [E, d, F]: the bf16
@@ -125,7 +126,10 @@ def grouped_swiglu_fwd_mx(x_perm, w1, w2, offsets, row_scale=None, return_a=Fals
         A    = silu(G) U;  Aq = Q(float32(A))
         Y    = (Aq Q(W2[e])^T) * row_scale
     with Q = MX quantise + dequantise along the reduction dimension, all sums
-    in float64.  -> Y [N, d] (and the dequantised A [N, F] with return_a)."""
+    in float64.  -> Y [N, d]; with return_a also the dequantised A [N, F];
+    with return_parts also a dict of the intermediates: "xq", "w1q", "w2q"
+    (dequantised operands), "g", "u" [N, F], "a32" (A in float32 before its
+    quantisation), "codes" [N, F] and "scales" [N, F / 32] (A's MX codes)."""
     N, d = x_perm.shape
     E, twoF, _ = w1.shape
     F = twoF // 2
@@ -134,6 +138,9 @@ def grouped_swiglu_fwd_mx(x_perm, w1, w2, offsets, row_scale=None, return_a=Fals
     w2q = mx_dequantize(*mx_quantize(w2))
     y = np.zeros((N, d))
     a_all = np.zeros((N, F))
+    a_codes = np.zeros((N, F), np.uint8)
+    a_scales = np.zeros((N, F // MX_BLOCK), np.uint8)
+    g_all, u_all, a32_all = np.zeros((N, F)), np.zeros((N, F)), np.zeros((N, F))
     for e in range(E):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         if hi <= lo:
@@ -142,9 +149,15 @@ def grouped_swiglu_fwd_mx(x_perm, w1, w2, offsets, row_scale=None, return_a=Fals
         g = xe @ w1q[e, :F].T
         u = xe @ w1q[e, F:].T
         a = (_silu(g) * u).astype(np.float32).astype(np.float64)
-        aq = mx_dequantize(*mx_quantize(a))
+        g_all[lo:hi], u_all[lo:hi], a32_all[lo:hi] = g, u, a
+        codes, scales = mx_quantize(a)
+        aq = mx_dequantize(codes, scales)
         a_all[lo:hi] = aq
+        a_codes[lo:hi], a_scales[lo:hi] = codes, scales
         y[lo:hi] = aq @ w2q[e].T
     if row_scale is not None:
         y = y * np.asarray(row_scale, dtype=np.float64)[:, None]
-    return (y, a_all) if return_a else y
+    parts = dict(xq=xq, w1q=w1q, w2q=w2q, g=g_all, u=u_all, a32=a32_all, codes=a_codes,
+                 scales=a_scales)
+    out = (y,) + ((a_all,) if return_a else ()) + ((parts,) if return_parts else ())
+    return out if len(out) > 1 else y

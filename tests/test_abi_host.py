@@ -142,6 +142,42 @@ def test_grouped_validation(L):
     assert comb(None, 1, 16, 64, 2, 32, P, P, None, None, P, P) == 1   # gate without y_shared
 
 
+def test_mx_validation(L):
+    q = L.moe_quantize_mx
+    assert q(None, 4, 48, P, P, P) == 4                     # K % 32
+    assert q(None, 0, 64, P, P, P) == 2
+    assert q(None, 4, 64, None, P, P) == 1
+    assert q(None, 4, 64, P, P, MIS) == 4
+    # scales: ceil(K / 128) K tiles x R rows x 4 bytes
+    assert L.moe_quantize_mx_scales_size(300, 96) == 1 * 300 * 4
+    assert L.moe_quantize_mx_scales_size(40, 2688) == 21 * 40 * 4
+    pk = L.moe_pack_weights_mx
+    assert pk(None, 2, 127, 64, 1, P, P, P) == 2            # odd rows with gate/up halves
+    assert pk(None, 2, 128, 40, 0, P, P, P) == 4            # K % 32
+    assert pk(None, 2, 128, 64, 0, P, None, P) == 1
+    # F = 96 -> 1 panel; d = 160 -> 2 K tiles of 128 (codes) / 4 scale bytes per row
+    assert L.moe_pack_weights_mx_size(3, 192, 160, 1, 0) == 3 * 1 * 2 * 256 * 128
+    assert L.moe_pack_weights_mx_size(3, 192, 160, 1, 1) == 3 * 1 * 2 * 256 * 4
+    assert L.moe_pack_weights_mx_size(2, 520, 32, 0, 0) == 2 * 3 * 1 * 256 * 128
+    assert L.moe_pack_weights_mx_size(2, 201, 32, 1, 0) == 0
+    f = L.moe_grouped_swiglu_fwd_mx
+    big = 1 << 30
+    ok = [None, 100, 64, 64, 4, 0, P, P, None, P, P, P, P, P, None, P, P, big]
+    def c(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert c(a2=48) == 4                       # d % 32
+    assert c(a3=40) == 4                       # F % 32
+    assert c(a4=2000) == 2                     # E > 1024
+    assert c(a8=P) == 2                        # row_token with T = 0
+    assert c(a6=None) == 1
+    assert c(a17=16) == 5                      # workspace
+    assert c(a15=MIS) == 4
+    assert L.moe_grouped_swiglu_fwd_mx_workspace_size(100, 96) >= 100 * 96 + 100 * 4
+
+
 def test_layer_backward_validation(L):
     cb = L.moe_combine_backward
     ok = [None, 1, 16, 64, 2, 32, P, P, P, P, None, P, P, None]

@@ -1,0 +1,421 @@
+"""GPU parity of the MXFP8 (microscaled FP8 E4M3) calls against the CPU
+oracle ``oracle.mx_oracle``.
+
+  * moe_quantize_mx and moe_pack_weights_mx are byte work: codes and scale
+    bytes equal the oracle's quantisation bit for bit, in the layouts that
+    include/moe.h states (written out here from that definition);
+  * moe_grouped_swiglu_fwd_mx: the kernel accumulates G and U on the FP8
+    MFMA and takes its own fp32 A = silu(G) U to E4M3.  The instruction's
+    sum of 64 products is not exact: an in-bounds probe (random codes over
+    the whole E4M3 range, random and fixed block scales, Gaussian MX data,
+    chains of 1 to 64 steps) measured an error of at most 2^-11.8 times
+    the sum over the 64-value steps of max|a| max|b| (the largest
+    magnitudes of the two operands in the step), consistent with products
+    aligned to the step's largest exponent in a fixed-point sum; the bound
+    used is EPS_STEP = 2^-11 of that sum, plus fp32 accumulation.  So A's codes (read from the workspace, whose layout the header
+    states) must equal the oracle's, except where the oracle's float32 A
+    lies within that error bound of the rounding boundary between the two
+    codes (or its block maximum within it of the power of two between two
+    scales); every such element is checked to be a correct rounding of a
+    value inside the bound.  The output is then bounded element by element:
+    bf16 rounding of the result, fc2's accumulation error, and the
+    difference of the two A's carried through Q(W2);
+  * the gathered form (fc1 reads quantised rows of x through row_token)
+    equals the form on materialised rows bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_workloads as mw
+from oracle import moe_oracle as mo
+from oracle import mx_oracle as mx
+import gpu_helpers as gh
+
+pytestmark = pytest.mark.gpu
+
+moe = pytest.importorskip("mixture_experts_layer_05_amd")
+
+EPS_STEP = 2.0 ** -11  # FP8 MFMA error / sum over 64-value steps of max|a| max|b|
+EPS_F32 = 2.0 ** -24   # fp32 accumulation across steps, per step, of sum |products|
+EPS_ACT = 2.0 ** -17   # relative error of the fp32 silu(G) U (hardware exp2 and reciprocal)
+TOL_MX_FRO = 5e-3      # relative Frobenius norm of the output error (a summary check)
+MAX_CODE_FLIPS = 0.01  # at most this fraction of A codes may take the neighbouring value
+MAX_SCALE_FLIPS = 1e-3
+
+
+def _varied(rng, shape):
+    """bf16 values over a wide range: rows scaled by 2^U(-20, 20), some
+    all-zero 32-blocks, some blocks with one outsized element, signed zeros."""
+    v = rng.standard_normal(shape).astype(np.float32)
+    v *= np.exp2(rng.integers(-20, 20, shape[:-1] + (1,))).astype(np.float32)
+    flat = v.reshape(-1, 32)
+    nb = flat.shape[0]
+    flat[rng.choice(nb, max(1, nb // 17), replace=False)] = 0.0
+    big = rng.choice(nb, max(1, nb // 13), replace=False)
+    flat[big, rng.integers(0, 32, big.size)] *= 300.0
+    flat[rng.choice(nb, max(1, nb // 19), replace=False), 5] = -0.0
+    return mw.round_to_bf16_bits(v)
+
+
+def _scales_tiled(sc, nkt):
+    """[R, K/32] scale codes -> the [nkt][R][4] layout, zero slots past K."""
+    R, nb = sc.shape
+    pad = np.zeros((R, nkt * 4), np.uint8)
+    pad[:, :nb] = sc
+    return pad.reshape(R, nkt, 4).transpose(1, 0, 2).copy()
+
+
+@pytest.mark.parametrize("R,K", [(1, 32), (300, 96), (65, 2048), (257, 160), (40, 2688)])
+def test_quantize_mx_bitexact(R, K):
+    rng = np.random.default_rng(R * 7 + K)
+    xb = _varied(rng, (R, K))
+    codes_ref, sc_ref = mx.mx_quantize(mw.bf16_bits_to_f32(xb))
+    x = gh.to_gpu(xb)
+    outs = []
+    for _ in range(2):
+        q = moe.MxTensor(gh.poison((R, K), torch.uint8),
+                         gh.poison((moe.lib().moe_quantize_mx_scales_size(R, K),), torch.uint8),
+                         (R, K))
+        moe.quantize_mx(x, out=q)
+        torch.cuda.synchronize()
+        outs.append(q)
+    assert torch.equal(outs[0].codes, outs[1].codes) and torch.equal(outs[0].scales, outs[1].scales)
+    codes = outs[0].codes.cpu().numpy()
+    scales = outs[0].scales.cpu().numpy()
+    nkt = -(-K // 128)
+    assert scales.size == nkt * R * 4
+    assert (scales.reshape(nkt, R, 4) == _scales_tiled(sc_ref, nkt)).all()
+    bad = np.nonzero(codes != codes_ref)
+    assert bad[0].size == 0, (f"{bad[0].size} codes differ, e.g. at {bad[0][:4]}, {bad[1][:4]}: "
+                              f"{codes[bad][:4]} vs {codes_ref[bad][:4]}")
+
+
+def _pack_mx_reference(a, gated, bn=256, bk=128):
+    """The packed layout of include/moe.h written out from its definition (a
+    reordering with zero fill): a [E, rows, Kc] -> [E, panels, ceil(Kc/bk), bn, bk]."""
+    E, rows, K = a.shape
+    if gated:
+        F = rows // 2
+        nt = -(-F // (bn // 2))
+    else:
+        nt = -(-rows // bn)
+    nkt = -(-K // bk)
+    out = np.zeros((E, nt, nkt, bn, bk), dtype=a.dtype)
+    for t in range(nt):
+        for r in range(bn):
+            if gated:
+                f = t * (bn // 2) + (r if r < bn // 2 else r - bn // 2)
+                row = (f if r < bn // 2 else F + f) if f < F else -1
+            else:
+                row = t * bn + r if t * bn + r < rows else -1
+            if row < 0:
+                continue
+            for kt in range(nkt):
+                k0, k1 = kt * bk, min(K, kt * bk + bk)
+                out[:, t, kt, r, :k1 - k0] = a[:, row, k0:k1]
+    return out
+
+
+@pytest.mark.parametrize("case", [(3, 2 * 96, 160, True), (2, 200, 96, False),
+                                  (1, 2 * 256, 128, True), (2, 520, 32, False)],
+                         ids=lambda c: "-".join(map(str, c)))
+def test_pack_weights_mx_layout(case):
+    """Codes and scales of every weight row land where the layout says; zero
+    codes and zero scale bytes fill the padding."""
+    E, rows, K, gated = case
+    rng = np.random.default_rng(rows + K + 1)
+    wb = _varied(rng, (E, rows, K))
+    codes_ref, sc_ref = mx.mx_quantize(mw.bf16_bits_to_f32(wb))
+    wq = moe.pack_weights_mx(gh.to_gpu(wb), gated)
+    torch.cuda.synchronize()
+    c_ref = _pack_mx_reference(codes_ref, gated, bk=128)
+    s_ref = _pack_mx_reference(sc_ref, gated, bk=4)
+    got_c = wq.codes.cpu().numpy()
+    got_s = wq.scales.cpu().numpy()
+    assert got_c.size == c_ref.size and got_s.size == s_ref.size
+    assert (got_c == c_ref.reshape(-1)).all()
+    assert (got_s == s_ref.reshape(-1)).all()
+
+
+def _segments(rng, E, pattern, scale):
+    if pattern == "ragged":
+        c = rng.integers(0, scale, E)
+        c[::3] = 0                              # empty experts
+        c[1] = 1                                # a one-row expert
+        return c
+    if pattern == "one_hot":
+        c = np.zeros(E, dtype=np.int64)
+        c[E // 2] = scale
+        return c
+    raise ValueError(pattern)
+
+
+_POS = mx.e4m3_decode(np.arange(127))                       # E4M3 magnitudes 0 .. 448
+_LO = np.r_[0.0, (_POS[:-1] + _POS[1:]) / 2]                 # rounding interval of each magnitude
+_HI = np.r_[(_POS[:-1] + _POS[1:]) / 2, np.inf]
+
+
+def _a_from_ws(ws, N, F, lo=0, hi=None):
+    """Rows [lo, hi) of A's codes [N, F] and scale codes [N, F / 32] from the
+    forward's workspace."""
+    hi = N if hi is None else hi
+    nkt = -(-F // 128)
+    q = (N * F + 255) // 256 * 256
+    codes = ws[lo * F:hi * F].cpu().numpy().reshape(hi - lo, F)
+    sc = ws[q:q + nkt * N * 4].view(nkt, N, 4)[:, lo:hi].cpu().numpy()
+    sc = sc.transpose(1, 0, 2).reshape(hi - lo, nkt * 4)
+    return codes, sc[:, :F // 32]
+
+
+def _step_max(a):
+    """[R, K] -> [R, ceil(K / 64)]: the largest magnitude of each 64-value MFMA step."""
+    R, K = a.shape
+    S = -(-K // 64)
+    pad = np.zeros((R, S * 64))
+    pad[:, :K] = np.abs(a)
+    return pad.reshape(R, S, 64).max(-1)
+
+
+def _acc_bound(a, b):
+    """Bound on |fp32 MFMA result - exact| of a [R, K] @ b [C, K]^T (MX-dequantised)."""
+    S = -(-a.shape[1] // 64)
+    return EPS_STEP * (_step_max(a) @ _step_max(b).T) + S * EPS_F32 * (np.abs(a) @ np.abs(b).T)
+
+
+def _check_mx_forward(y, codes, sc, y_ref, parts, off, rs, what):
+    """The checks of the module docstring for the rows of one forward that
+    ``parts`` covers (segments ``off``), with the kernel's A codes and scales."""
+    N, F = parts["codes"].shape
+    y = np.asarray(y, np.float64)
+    assert np.isfinite(y).all()
+    # the error bound of the kernel's fp32 A, per element
+    xq, w1q, w2q = parts["xq"], parts["w1q"], parts["w2q"]
+    g, u, a32 = parts["g"], parts["u"], parts["a32"]
+    dg, du = np.zeros((N, F)), np.zeros((N, F))
+    for e in range(len(off) - 1):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi > lo:
+            dg[lo:hi] = _acc_bound(xq[lo:hi], w1q[e, :F])
+            du[lo:hi] = _acc_bound(xq[lo:hi], w1q[e, F:])
+    sil = np.abs(g / (1.0 + np.exp(-g)))
+    da = 1.1 * np.abs(u) * dg + sil * du + 1.1 * dg * du + EPS_ACT * np.abs(a32) + 1e-37
+    # scales: equal, or one step apart with the block maximum at that power of two
+    dsc = sc.astype(np.int64) - parts["scales"].astype(np.int64)
+    assert (np.abs(dsc) <= 1).all(), f"[{what}] A scale codes differ by more than one step"
+    amax = np.abs(a32).reshape(N, F // 32, 32).max(-1)
+    damax = da.reshape(N, F // 32, 32).max(-1)
+    bound_pt = np.exp2(np.maximum(sc, parts["scales"]).astype(np.float64) - 119.0)
+    bad_sc = (dsc != 0) & (np.abs(amax - bound_pt) > damax)
+    assert not bad_sc.any(), f"[{what}] {int(bad_sc.sum())} A block scales off by more than the bound"
+    # codes: each kernel code is the rounding of a value within da of the oracle's float32 A
+    X = np.repeat(np.exp2(sc.astype(np.float64) - 127.0), 32, axis=1)
+    mag = codes.astype(np.int64) & 0x7F
+    assert (mag <= 126).all(), f"[{what}] NaN codes in A"
+    neg = (codes & 0x80) != 0
+    lo_i = np.where(mag == 0, -_HI[0], _LO[mag]) * X
+    hi_i = _HI[mag] * X
+    lo_i, hi_i = np.where(neg & (mag > 0), -hi_i, lo_i), np.where(neg & (mag > 0), -lo_i, hi_i)
+    bad = (a32 + da < lo_i) | (a32 - da > hi_i)
+    assert not bad.any(), (f"[{what}] {int(bad.sum())} A codes are not a rounding of a value "
+                           f"within the bound, e.g. at {np.argwhere(bad)[:3].tolist()}")
+    flips = (codes != parts["codes"]) & ~((mag == 0) & ((parts["codes"] & 0x7F) == 0))
+    Xr = np.repeat(np.exp2(parts["scales"].astype(np.float64) - 127.0), 32, axis=1)
+    mr = parts["codes"].astype(np.int64) & 0x7F
+    room = np.minimum(np.abs(a32) - _LO[mr] * Xr, _HI[mr] * Xr - np.abs(a32))
+    ambiguous = float((room <= da).mean())
+    f_code, f_sc = float(flips.mean()), float((dsc != 0).mean())
+    assert f_code <= MAX_CODE_FLIPS and f_sc <= MAX_SCALE_FLIPS
+    # output, element by element
+    a_gpu = mx.mx_dequantize(codes, sc)
+    dA = np.abs(a_gpu - mx.mx_dequantize(parts["codes"], parts["scales"]))
+    # |y - y_ref| <= T + 2^-9 |rs * acc| with T = |rs| (|dA| |Q(W2)|^T + fc2 accumulation)
+    # and |rs * acc| <= |y_ref| + T; 2^-8 covers the bf16 rounding and the fp32 row scaling
+    T = np.zeros_like(y_ref, dtype=np.float64)
+    ars = np.abs(np.asarray(rs, np.float64))[:, None] if rs is not None else None
+    for e in range(len(off) - 1):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi > lo:
+            r = ars[lo:hi] if rs is not None else 1.0
+            T[lo:hi] = r * (dA[lo:hi] @ np.abs(w2q[e]).T + _acc_bound(a_gpu[lo:hi], w2q[e]))
+    bound = 2.0 ** -8 * (np.abs(y_ref) + T) + T + 1e-30
+    err = np.abs(y - y_ref)
+    over = err > bound
+    fro = float(np.linalg.norm(y - y_ref) / max(np.linalg.norm(y_ref), 1e-300))
+    print(f"[{what}] A codes within the bound of a rounding boundary {ambiguous:.2e}, "
+          f"A code flips {f_code:.2e}, scale flips {f_sc:.2e}; output normwise "
+          f"{gh.normwise(y, y_ref):.3e}, frobenius {fro:.3e}, max err/bound {(err / bound).max():.3f}")
+    assert not over.any(), (f"[{what}] {int(over.sum())} outputs beyond the bound, e.g. "
+                            f"{np.argwhere(over)[:3].tolist()}")
+    assert fro <= TOL_MX_FRO
+
+
+MX_CASES = [
+    # E, d, F, T (rows of x; 0: no gather), pattern, scale, bad tokens
+    (6, 64, 64, 0, "ragged", 300, False),
+    (7, 160, 96, 45, "ragged", 200, False),      # K tails in both GEMMs, gathered rows
+    (3, 256, 192, 0, "one_hot", 517, False),
+    (9, 224, 160, 300, "ragged", 140, True),     # gathered, out-of-range tokens read as zero
+    (4, 512, 320, 0, "ragged", 600, False),      # several column tiles of both GEMMs
+]
+
+
+@pytest.mark.parametrize("case", MX_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_grouped_fwd_mx_parity(case):
+    E, d, F, T, pattern, scale, bad = case
+    rng = np.random.default_rng(E * 11 + d + F + T)
+    counts = _segments(rng, E, pattern, scale)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    N = int(off[-1])
+    rows = T if T else N
+    inp = mw.make_small_layer_inputs(E + d + F + 9, T=rows, d=d, E=E, F=F, dtype="bf16",
+                                     w_std=0.05)
+    rs = (rng.random(N) + 0.5).astype(np.float32)
+    xf = inp.as_f32("x").astype(np.float64)
+    x, w1, w2 = gh.to_gpu(inp.x), gh.to_gpu(inp.w1), gh.to_gpu(inp.w2)
+    go, grs = gh.to_gpu(off), gh.to_gpu(rs)
+    w1q, w2q = moe.pack_weights_mx(w1, True), moe.pack_weights_mx(w2, False)
+    xq = moe.quantize_mx(x)
+    if T:
+        rtok = rng.integers(0, T, N).astype(np.int32)
+        if bad:
+            rtok[rng.choice(N, 5, replace=False)] = np.array([-1, T, T + 7, -100, 2 ** 30],
+                                                             np.int32)
+        ok = (rtok >= 0) & (rtok < T)
+        xp_ref = np.where(ok[:, None], xf[np.clip(rtok, 0, T - 1)], 0.0)
+        gtok = gh.to_gpu(rtok)
+    else:
+        xp_ref, gtok = xf, None
+    ws = torch.empty(moe.fwd_mx_workspace_size(N, F), dtype=torch.uint8, device=x.device)
+    res = []
+    for _ in range(2):
+        y = gh.poison((N, d), torch.bfloat16)
+        moe.grouped_swiglu_fwd_mx(xq, gtok, w1q, w2q, go, grs, out=y, ws=ws)
+        torch.cuda.synchronize()
+        res.append(y)
+    assert gh.bits_equal(res[0], res[1])
+    if T:
+        # the same rows materialised (zero rows for out-of-range tokens)
+        xp = torch.zeros((N, d), dtype=x.dtype, device=x.device)
+        okg = torch.from_numpy(ok).to(x.device)
+        xp[okg] = x[gtok[okg].long()]
+        y2 = moe.grouped_swiglu_fwd_mx(moe.quantize_mx(xp), None, w1q, w2q, go, grs)
+        torch.cuda.synchronize()
+        assert gh.bits_equal(res[0], y2)
+    y_ref, parts = mx.grouped_swiglu_fwd_mx(xp_ref, inp.as_f32("w1"), inp.as_f32("w2"), off, rs,
+                                            return_parts=True)
+    codes, sc = _a_from_ws(ws, N, F)
+    _check_mx_forward(gh.to_f64(res[0]), codes, sc, y_ref, parts, off, rs, f"mx {case}")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["qwen3_30b", "dsv_30b", "skew_shared"])
+def test_grouped_fwd_mx_full_size(name):
+    """The MX forward at the workload's full size (T tokens, k experts each
+    of E, fc1 gathering token rows), the routing drawn on the host (each
+    token's k experts uniformly without replacement; Zipf-skewed for the
+    skewed workload) and permuted by the oracle; A and the output of the
+    experts with the fewest, the median and the most rows checked against
+    the oracle."""
+    cfg = mw.get(name)
+    inp = mw.make_layer_inputs(cfg)
+    T, d, E, k, F = cfg.T, cfg.d, cfg.E, cfg.k, cfg.F
+    rng = np.random.default_rng(100 + cfg.index)
+    keys = rng.random((T, E))
+    if cfg.skew:
+        keys = np.log(keys) / np.exp(mw.skew_bias(cfg).astype(np.float64))[None]
+    idx = np.argsort(-keys, axis=1)[:, :k].astype(np.int32)
+    pref = mo.permute(None, idx, None, E)
+    off, rtok = pref.offsets, pref.row_token
+    N = T * k
+    rs = (rng.random(N) + 0.5).astype(np.float32)
+    x = gh.to_gpu(inp.x)
+    w1q = moe.pack_weights_mx(gh.to_gpu(inp.w1), True)
+    w2q = moe.pack_weights_mx(gh.to_gpu(inp.w2), False)
+    ws = torch.empty(moe.fwd_mx_workspace_size(N, F), dtype=torch.uint8, device=x.device)
+    go, gtok, grs = gh.to_gpu(off), gh.to_gpu(rtok), gh.to_gpu(rs)
+    y = moe.grouped_swiglu_fwd_mx(moe.quantize_mx(x), gtok, w1q, w2q, go, grs, ws=ws)
+    y2 = moe.grouped_swiglu_fwd_mx(moe.quantize_mx(x), gtok, w1q, w2q, go, grs)
+    torch.cuda.synchronize()
+    assert gh.bits_equal(y, y2)
+    counts = np.diff(off)
+    order = np.argsort(counts, kind="stable")
+    nz = order[counts[order] > 0]
+    experts = sorted({int(nz[0]), int(nz[len(nz) // 2]), int(nz[-1])})
+    print(f"\n[{name} mx] rows per expert min/median/max = {counts.min()}/"
+          f"{int(np.median(counts))}/{counts.max()}; checking experts {experts}")
+    xf = inp.as_f32("x")
+    for e in experts:
+        lo, hi = int(off[e]), int(off[e + 1])
+        seg = np.array([0, hi - lo])
+        y_ref, parts = mx.grouped_swiglu_fwd_mx(xf[rtok[lo:hi]],
+                                                mw.bf16_bits_to_f32(inp.w1[e])[None],
+                                                mw.bf16_bits_to_f32(inp.w2[e])[None], seg,
+                                                rs[lo:hi], return_parts=True)
+        codes, sc = _a_from_ws(ws, N, F, lo, hi)
+        _check_mx_forward(gh.to_f64(y[lo:hi]), codes, sc, y_ref, parts, seg, rs[lo:hi],
+                          f"{name} mx expert {e} ({hi - lo} rows)")
+
+
+def test_grouped_fwd_mx_rejects_bad_shapes():
+    """d or F not a multiple of 32, or a short workspace, is an error, not a launch."""
+    L = moe.lib()
+    dev = gh.dev()
+    u8 = lambda n: torch.zeros(n, dtype=torch.uint8, device=dev)  # noqa: E731
+    off = torch.zeros(2, dtype=torch.int32, device=dev)
+    y = torch.zeros((4, 64), dtype=torch.bfloat16, device=dev)
+    ws = u8(1 << 16)
+    p = moe._p
+    st = moe._stream()
+    for d, F in ((48, 64), (64, 40)):
+        assert L.moe_grouped_swiglu_fwd_mx(st, 4, d, F, 1, 0, p(u8(4096)), p(u8(4096)), None,
+                                           p(u8(1 << 20)), p(u8(1 << 16)), p(u8(1 << 20)),
+                                           p(u8(1 << 16)), p(off), None, p(y), p(ws),
+                                           ws.numel()) != 0
+    assert L.moe_grouped_swiglu_fwd_mx(st, 4, 64, 64, 1, 0, p(u8(4096)), p(u8(4096)), None,
+                                       p(u8(1 << 20)), p(u8(1 << 16)), p(u8(1 << 20)),
+                                       p(u8(1 << 16)), p(off), None, p(y), p(ws), 16) != 0
+
+
+@pytest.mark.parametrize("case", [(300, 128, 9, 3, 96, 64, "softmax"),
+                                  (517, 256, 16, 4, 160, 0, "sigmoid")],
+                         ids=lambda c: "-".join(map(str, c)))
+def test_layer_fp8(case):
+    """MoELayer(fp8=True): its grouped output equals a direct MX forward on
+    the layer's own routing, bit for bit, and the layer output the oracle's
+    MX layer (the oracle's routing weights and gate for the GPU's expert
+    choice, MX forward of the routed and the shared expert, combine) to the
+    bf16 output tolerance, 2e-2 max-norm, with the Frobenius error <= 5e-3."""
+    T, d, E, k, F, Fs, score = case
+    inp = mw.make_small_layer_inputs(T + d + E, T=T, d=d, E=E, F=F, dtype="bf16", Fs=Fs,
+                                     w_std=0.05)
+    g = lambda a: None if a is None else gh.to_gpu(a)  # noqa: E731
+    layer = moe.MoELayer(g(inp.w_router), g(inp.w1), g(inp.w2), k, T, score, True, None,
+                         g(inp.w_gate), g(inp.ws1), g(inp.ws2), fp8=True)
+    x = g(inp.x)
+    y = layer.forward(x).clone()
+    y2 = layer.forward(x)
+    torch.cuda.synchronize()
+    assert gh.bits_equal(y, y2)
+    idx = layer.route_out[0].cpu().numpy()
+    off, slot, rtok, rw, _ = layer.perm_out
+    yp = moe.grouped_swiglu_fwd_mx(moe.quantize_mx(x), rtok, moe.pack_weights_mx(g(inp.w1), True),
+                                   moe.pack_weights_mx(g(inp.w2), False), off, rw)
+    torch.cuda.synchronize()
+    assert gh.bits_equal(yp, layer.y_perm)
+    f = inp.as_f32
+    xf = f("x").astype(np.float64)
+    w = mo.route_weights_for(xf, f("w_router"), idx, score, True)
+    p = mo.permute(None, idx, w, E)
+    y_perm = mx.grouped_swiglu_fwd_mx(xf[p.row_token], f("w1"), f("w2"), p.offsets, p.row_w)
+    y_sh = None
+    if Fs:
+        r = mo.route(xf, f("w_router"), k, score, True, None, f("w_gate"))
+        y_sh = mx.grouped_swiglu_fwd_mx(xf, f("ws1")[None], f("ws2")[None], np.array([0, T]),
+                                        r.gate)
+    y_ref = mo.unpermute_combine(y_perm, p.slot_of, None, y_sh)
+    yg = gh.to_f64(y)
+    nw = gh.normwise(yg, y_ref)
+    fro = float(np.linalg.norm(yg - y_ref) / np.linalg.norm(y_ref))
+    print(f"\n[layer fp8 {case}] normwise {nw:.3e} frobenius {fro:.3e}")
+    assert nw <= gh.TOL_BF16 and fro <= TOL_MX_FRO

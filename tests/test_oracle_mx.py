@@ -146,8 +146,15 @@ def test_forward_mx_against_loops():
     w2 = rng.standard_normal((E, d, F)) * 0.3
     rs = rng.random(5) + 0.5
     ref = _loop_forward_mx(x, w1, w2, off, rs)
-    got = mx.grouped_swiglu_fwd_mx(x, w1, w2, off, rs)
+    got, a, parts = mx.grouped_swiglu_fwd_mx(x, w1, w2, off, rs, return_a=True,
+                                             return_parts=True)
     assert np.abs(got - ref).max() <= 1e-9 * np.abs(ref).max()
+    # the returned codes and scales are A's quantisation, of a32 = float32(silu(g) u)
+    assert (mx.mx_dequantize(parts["codes"], parts["scales"]) == a).all()
+    assert parts["scales"].shape == (5, 1)
+    assert (mx.mx_quantize(parts["a32"])[0] == parts["codes"]).all()
+    sil = parts["g"] / (1.0 + np.exp(-parts["g"]))
+    assert np.allclose(parts["a32"], sil * parts["u"], rtol=2.0 ** -23, atol=0)
 
 
 def test_forward_mx_exact_inputs_equal_unquantised():
