@@ -273,8 +273,10 @@ MOE_API moe_status moe_grouped_swiglu_fwd_packed(hipStream_t stream, moe_dtype d
  * adds each 64-value product at reduced internal precision, ~2^-14 relative).
  *
  * moe_quantize_mx: rows [R, K] bf16 -> codes [R, K] u8 and scales laid out
- *   [ceil(K/128)][R][4] u8 (the 4 scale bytes of a row for one 128-wide K
- *   tile are adjacent; slots past K / 32 are 0).  K % 32 == 0.
+ *   [ceil(K/512)][R][16] u8: the scale of block b (values 32b .. 32b+31) of
+ *   row r at [b / 16][r][b % 16], so a row's scales for 512 consecutive K
+ *   values are 16 adjacent bytes; slots past K / 32 are 0.  K % 32 == 0.
+ *   Scales occupy moe_quantize_mx_scales_size(R, K) bytes.
  * moe_pack_weights_mx: W [E, rows, K] bf16 -> codes in the tile-packed layout
  *   of moe_pack_weights with 128-wide K tiles, [e][panel][K tile][256 rows]
  *   [128], and scales [e][panel][K tile][256 rows][4]; gated = 1 for W1
@@ -285,8 +287,10 @@ MOE_API moe_status moe_grouped_swiglu_fwd_packed(hipStream_t stream, moe_dtype d
  *              r from x[row_token[r]]) or of x_perm [N, d] (row_token NULL)
  *   w1q, w1s   moe_pack_weights_mx(E, 2F, d, 1);  w2q, w2s: (E, d, F, 0)
  *   y_perm     [N, d] bf16 out, (A Q(W2)^T) * row_scale
- *   workspace  moe_grouped_swiglu_fwd_mx_workspace_size(N, F) bytes (the
- *              quantised A and its scales)
+ *   workspace  moe_grouped_swiglu_fwd_mx_workspace_size(N, F) bytes; after
+ *              the call it holds A = silu(G) U quantised: codes [N, F] at
+ *              offset 0 and scales in the moe_quantize_mx layout at offset
+ *              round_up(N F, 256)
  * Limits: d % 32 == 0, F % 32 == 0, E <= 1024, one expert's packed codes and
  * the token rows below 2^31 bytes.  Inference only: no G, U save.
  * --------------------------------------------------------------------- */

@@ -295,7 +295,7 @@ class MxTensor:
 
 
 def quantize_mx(x, out=None):
-    """x [R, K] bf16 -> MxTensor (codes [R, K], scales [ceil(K/128)][R][4])."""
+    """x [R, K] bf16 -> MxTensor (codes [R, K], scales [ceil(K/512)][R][16])."""
     R, K = x.shape
     if out is None:
         out = MxTensor(torch.empty((R, K), dtype=torch.uint8, device=x.device),

@@ -10,14 +10,17 @@
 //     X = 2^(floor(log2 amax) - 8),  q = RNE(clamp(v / X, -448, 448)).
 //
 //   * mx_quant_rows_kernel: bf16 rows -> E4M3 codes [R, K] + scales laid out
-//     [K/128][R][4] (one K tile's scales of a row are 4 consecutive bytes);
+//     [K/512][R][16] (a row's scales of 4 consecutive 128-wide K tiles are 16
+//     consecutive bytes, so a gathered row brings 4 K tiles' scales in one
+//     16-byte read);
 //   * mx_pack_kernel: expert weights -> codes in the tile-packed layout of
 //     the bf16 path with 128-wide K tiles ([e][panel][K tile][256 rows][128
 //     bytes], gate/up panels for fc1) + scales [e][panel][K tile][256][4];
 //   * ggmx_kernel: the persistent grouped GEMM of moe_grouped_fwd.hip with
 //     byte-wide operands: 256 x 256 tiles, 8 wavefronts of 128 x 64, each
 //     K tile 128 values (one 128-byte line per staged row), two 2-slot rings
-//     plus 1 KB scale slots per operand (132 KB).  v_mfma_scale_f32_32x32x64
+//     with the weights' 1 KB of scales per slot (130 KB) and two 4 KB
+//     buffers of token-row scales, each filled once per 4 K tiles.  v_mfma_scale_f32_32x32x64
 //     _f8f6f4 takes 32 bytes of a row per lane: lanes r and r + 32 hold
 //     bytes 0-15 (k 0-15 and 16-31: the first 32-value block) and 16-31 (the
 //     second block), and lane r + 32 b supplies the scale of row r's block b
@@ -39,8 +42,10 @@ constexpr int kMxBK = 128;                       // K values (= bytes) per K til
 constexpr int kMxWaves = 8, kMxThreads = 512;    // 2 x 4 waves of 128 x 64 (256 registers each)
 constexpr int kMxRB = 4, kMxCB = 2;              // 32 x 32 blocks per wave
 constexpr int kMxTile = kMxBM * kMxBK;           // bytes of one operand tile
-constexpr int kMxSlot = 2 * kMxTile + 2 * 1024;  // A, B, A scales, B scales
-constexpr int kMxLds = 2 * kMxSlot;              // 2-slot rings
+constexpr int kMxSlot = 2 * kMxTile + 1024;      // A, B, B scales
+constexpr int kMxGroup = 4;                      // K tiles per group of row scales
+constexpr int kMxSgBuf = kMxBM * 4 * kMxGroup;   // one group's row scales (4 KB)
+constexpr int kMxLds = 2 * kMxSlot + 2 * kMxSgBuf;
 constexpr int kMxScanInts = 1040 + 64;
 
 // K tiles and sizes of the packed weights (panels of 256 rows; fc1 panels
@@ -49,6 +54,7 @@ inline int64_t mx_panels(int64_t rows, int gated) {
   return gated ? (rows / 2 + kMxBN / 2 - 1) / (kMxBN / 2) : (rows + kMxBN - 1) / kMxBN;
 }
 inline int64_t mx_ktiles(int64_t K) { return (K + kMxBK - 1) / kMxBK; }
+inline int64_t mx_sgroups(int64_t K) { return (K + kMxBK * kMxGroup - 1) / (kMxBK * kMxGroup); }
 
 __device__ __forceinline__ int mx_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
@@ -73,18 +79,19 @@ __device__ __forceinline__ uint32_t mx_pack4(float a, float b, float c, float d,
 }
 
 // One thread per 32-value block of a bf16 row: R rows of K values; the
-// scale slots of the last K tile past K get 0.
+// scale slots of the last group past K get 0.  Block b's scale byte sits at
+// [b / 16][r][b % 16].
 __global__ __launch_bounds__(256) void mx_quant_rows_kernel(int64_t R, int K,
                                                             const uint16_t* __restrict__ x,
                                                             uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales) {
-  const int nb = K / 32, nb4 = (K + kMxBK - 1) / kMxBK * 4;
+  const int nb = K / 32, nbg = (K + 511) / 512 * 16;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= R * nb4) return;
-  const int64_t r = i / nb4;
-  const int b = static_cast<int>(i - r * nb4);
+  if (i >= R * nbg) return;
+  const int64_t r = i / nbg;
+  const int b = static_cast<int>(i - r * nbg);
   if (b >= nb) {
-    scales[(static_cast<int64_t>(b / 4) * R + r) * 4 + (b & 3)] = 0;
+    scales[(static_cast<int64_t>(b / 16) * R + r) * 16 + (b & 15)] = 0;
     return;
   }
   const u32x4* src = reinterpret_cast<const u32x4*>(x + r * K + b * 32);
@@ -109,7 +116,7 @@ __global__ __launch_bounds__(256) void mx_quant_rows_kernel(int64_t R, int K,
   u32x4* dst = reinterpret_cast<u32x4*>(codes + r * K + b * 32);
   dst[0] = o[0];
   dst[1] = o[1];
-  scales[(static_cast<int64_t>(b / 4) * R + r) * 4 + (b & 3)] = static_cast<uint8_t>(code);
+  scales[(static_cast<int64_t>(b / 16) * R + r) * 16 + (b & 15)] = static_cast<uint8_t>(code);
 }
 
 // One thread per 32-value block of a packed weight row: quantise and place.
@@ -174,7 +181,7 @@ struct MxParams {
   int E, F, d, K, ntn, nkt;
   const int32_t* offsets;
   const uint8_t* a;            // codes: fc1 token rows [a_rows, K] (gathered), fc2 A [N, K]
-  const uint8_t* as;           // scales [nkt][a_rows or N][4]
+  const uint8_t* as;           // scales [ceil(nkt / 4)][a_rows or N][16]
   int a_rows;                  // rows indexed by the scale layout (T for fc1 gathers, N otherwise)
   const int32_t* gather;       // fc1: source row of each row, or NULL
   const uint8_t* b;            // packed weight codes
@@ -182,7 +189,7 @@ struct MxParams {
   int64_t b_estride;           // bytes of one expert's packed codes
   const float* scale;          // fc2 row scale or NULL
   uint8_t* out_q;              // fc1: A codes [N, F]
-  uint8_t* out_s;              // fc1: A scales [F/128][N][4]
+  uint8_t* out_s;              // fc1: A scales [ceil(F / 512)][N][16]
   uint16_t* out;               // fc2: Y [N, d] bf16
   int N;
 };
@@ -192,6 +199,7 @@ struct MxTile {
   __amdgpu_buffer_rsrc_t ra, rb, rsa, rsb;
   int vo[8];                   // per-lane byte offsets of the data loads (4 A, 4 B)
   int vs;                      // per-lane offset of the scale load (waves 0-3: A rows; wave 4: B)
+  int j;                       // the tile's position in this workgroup's walk
 };
 
 template <int kEpi>
@@ -205,6 +213,7 @@ __device__ __forceinline__ void ggmx_body(const MxParams& p) {
   const int r32 = lane & 31, h = lane >> 5;
   const int K = p.K, nk = p.nkt;
 
+  const int ng = (nk + kMxGroup - 1) / kMxGroup;  // row-scale groups per tile
   tile_prefix<kMxThreads>(p.offsets, p.E, kMxBM, p.ntn, s_cum, s_tmp);
   const int total = s_cum[p.E];
   const int g8 = static_cast<int>(gridDim.x >> 3);
@@ -227,6 +236,7 @@ __device__ __forceinline__ void ggmx_body(const MxParams& p) {
   const bool gath = p.gather != nullptr;
 
   auto setup = [&](int j, MxTile& st) {
+    st.j = j;
     st.ti = tile_decode(p.offsets, p.E, kMxBM, xbeg + pos + j * g8, s_cum);
     const TileIdx& ti = st.ti;
     const int m0 = ti.m0, last = ti.mend - 1 - m0;
@@ -235,7 +245,7 @@ __device__ __forceinline__ void ggmx_body(const MxParams& p) {
         (gath ? p.a_rows : ti.mend - m0) * K, kRsrcWord3);
     st.rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.b + ti.e * p.b_estride), 0,
                                               static_cast<int>(p.b_estride), kRsrcWord3);
-    st.rsa = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.as), 0, nk * p.a_rows * 4,
+    st.rsa = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.as), 0, ng * p.a_rows * 16,
                                                kRsrcWord3);
     st.rsb = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(p.bs + ti.e * (p.b_estride / kMxBK) * 4), 0,
@@ -247,10 +257,10 @@ __device__ __forceinline__ void ggmx_body(const MxParams& p) {
       st.vo[j2] = src >= 0 && (!gath || src < p.a_rows) ? src * K + kcl[j2] * 16 : kOob;
       st.vo[4 + j2] = (ti.nt * nk * kMxBN + r) * kMxBK + kcl[j2] * 16;
     }
-    if (wave < 4) {                     // A scales: one row per lane
+    if (wave < 4) {                     // A scales: one row per lane, 16 bytes (4 K tiles)
       const int r = wave * 64 + lane;
       const int src = r > last ? -1 : gath ? p.gather[m0 + r] : m0 + r;
-      st.vs = src >= 0 && src < p.a_rows ? src * 4 : kOob;
+      st.vs = src >= 0 && src < p.a_rows ? src * 16 : kOob;
     } else {                            // wave 4: the B scales' 1 KB, 16 bytes per lane
       st.vs = (ti.nt * nk * kMxBN) * 4 + lane * 16;
     }
@@ -267,11 +277,15 @@ __device__ __forceinline__ void ggmx_body(const MxParams& p) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(st.rb, (lds_void*)(sl + kMxTile + bb * 1024), 16,
                                                st.vo[4 + j], kt * kMxBN * kMxBK, 0, 0);
     }
-    if (wave < 4)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(st.rsa, (lds_void*)(sl + 2 * kMxTile + wave * 256), 4,
-                                               st.vs, kt * p.a_rows * 4, 0, 0);
-    else if (wave == 4)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(st.rsb, (lds_void*)(sl + 2 * kMxTile + 1024), 16,
+    if (wave < 4) {
+      if (kt % kMxGroup == 0) {         // the row scales of K tiles kt .. kt + 3
+        const int gi = st.j * ng + kt / kMxGroup;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            st.rsa, (lds_void*)(lds + 2 * kMxSlot + (gi & 1) * kMxSgBuf + wave * 1024), 16, st.vs,
+            kt / kMxGroup * p.a_rows * 16, 0, 0);
+      }
+    } else if (wave == 4)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(st.rsb, (lds_void*)(sl + 2 * kMxTile), 16,
                                                st.vs, kt * kMxBN * 4, 0, 0);
   };
 
@@ -289,16 +303,16 @@ __device__ __forceinline__ void ggmx_body(const MxParams& p) {
   };
 
   f32x16 acc[kMxRB][kMxCB];
-  auto compute = [&](int slot, int nrb) {
+  auto compute = [&](int slot, int nrb, int gi, int kq) {
     const uint8_t* As = slot_base(slot);
     const uint8_t* Bs = As + kMxTile;
-    const uint32_t* Ssa = reinterpret_cast<const uint32_t*>(As + 2 * kMxTile);
-    const uint32_t* Ssb = Ssa + 256;
+    const uint32_t* Ssb = reinterpret_cast<const uint32_t*>(As + 2 * kMxTile);
+    const uint32_t* Ssa = reinterpret_cast<const uint32_t*>(lds + 2 * kMxSlot + (gi & 1) * kMxSgBuf);
     uint32_t sb[kMxCB], sa[kMxRB];
 #pragma unroll
     for (int c = 0; c < kMxCB; ++c) sb[c] = Ssb[b_rd[c]];
 #pragma unroll
-    for (int i = 0; i < kMxRB; ++i) sa[i] = Ssa[a_rd[i]];
+    for (int i = 0; i < kMxRB; ++i) sa[i] = Ssa[a_rd[i] * kMxGroup + kq];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {                 // two 64-value MFMA steps per K tile
       i32x8 bv[2];
@@ -376,7 +390,9 @@ __device__ __forceinline__ void ggmx_body(const MxParams& p) {
         // blocks past F: zero scale (their codes are not read: fc2's K ends at F)
         const int nvalid = (p.F - n0) / 32;
         if (nvalid < 4) sc &= nvalid <= 0 ? 0u : (0xffffffffu >> (32 - 8 * nvalid));
-        *reinterpret_cast<uint32_t*>(p.out_s + (static_cast<size_t>(n0 / 128) * p.N + m0 + tid) * 4) = sc;
+        const int kt2 = n0 / kMxBK;           // fc2's K tile
+        *reinterpret_cast<uint32_t*>(
+            p.out_s + (static_cast<size_t>(kt2 / kMxGroup) * p.N + m0 + tid) * 16 + 4 * (kt2 % kMxGroup)) = sc;
       }
     } else {
       // Y rows (bf16, routing-weight scaled) through two 32 KB halves of the
@@ -439,7 +455,7 @@ __device__ __forceinline__ void ggmx_body(const MxParams& p) {
       asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
       if (kt + 1 < nk) issue(cur, kt + 1, (g + 1) & 1);
       else if (j + 1 < ntiles) issue(nxt, 0, (g + 1) & 1);
-      compute(g & 1, nrb);
+      compute(g & 1, nrb, j * ng + kt / kMxGroup, kt % kMxGroup);
     }
     asm volatile("s_barrier" ::: "memory");
     epilogue(cur.ti, nrb, (g - 1) & 1);
@@ -468,7 +484,7 @@ using namespace moe;
 
 extern "C" size_t moe_quantize_mx_scales_size(int64_t R, int64_t K) {
   if (R < 1 || K < 1) return 0;
-  return static_cast<size_t>(mx_ktiles(K) * R * 4);
+  return static_cast<size_t>(mx_sgroups(K) * R * 16);
 }
 
 extern "C" moe_status moe_quantize_mx(hipStream_t stream, int64_t R, int64_t K, const void* x,
@@ -477,8 +493,8 @@ extern "C" moe_status moe_quantize_mx(hipStream_t stream, int64_t R, int64_t K, 
   if (R < 1 || K < 1 || R >= (int64_t(1) << 31) || K >= (int64_t(1) << 20)) return MOE_ERR_SHAPE;
   if (K % 32) return MOE_ERR_ALIGNMENT;
   if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return MOE_ERR_ALIGNMENT;
-  if (mx_ktiles(K) * R * 4 >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
-  const int64_t n = R * mx_ktiles(K) * 4;
+  if (mx_sgroups(K) * R * 16 >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
+  const int64_t n = R * mx_sgroups(K) * 16;
   return hip_status(launch(mx_quant_rows_kernel, dim3(static_cast<unsigned>((n + 255) / 256)),
                            dim3(256), 0, stream, R, (int)K, static_cast<const uint16_t*>(x),
                            static_cast<uint8_t*>(codes), static_cast<uint8_t*>(scales)));
@@ -511,7 +527,7 @@ extern "C" moe_status moe_pack_weights_mx(hipStream_t stream, int32_t E, int64_t
 extern "C" size_t moe_grouped_swiglu_fwd_mx_workspace_size(int64_t N, int64_t F) {
   if (N < 0 || F < 1) return 0;
   const size_t q = (static_cast<size_t>(N) * F + 255) & ~static_cast<size_t>(255);
-  return q + static_cast<size_t>(mx_ktiles(F) * std::max<int64_t>(N, 1) * 4) + 256;
+  return q + static_cast<size_t>(mx_sgroups(F) * std::max<int64_t>(N, 1) * 16) + 256;
 }
 
 extern "C" moe_status moe_grouped_swiglu_fwd_mx(hipStream_t stream, int64_t N, int64_t d,
@@ -534,7 +550,8 @@ extern "C" moe_status moe_grouped_swiglu_fwd_mx(hipStream_t stream, int64_t N, i
   const int64_t b2 = mx_panels(d, 0) * mx_ktiles(F) * kMxBN * kMxBK;
   // byte offsets in 32 bits: one expert's packed codes, the token rows, A
   if (b1 >= (int64_t(1) << 31) || b2 >= (int64_t(1) << 31) || rows_a * d >= (int64_t(1) << 31) ||
-      N * F >= (int64_t(1) << 31) || mx_ktiles(d) * rows_a * 4 >= (int64_t(1) << 31))
+      N * F >= (int64_t(1) << 31) || mx_sgroups(d) * rows_a * 16 >= (int64_t(1) << 31) ||
+      mx_sgroups(F) * N * 16 >= (int64_t(1) << 31))
     return MOE_ERR_SHAPE;
   if (!aligned16(xq) || !aligned16(xs) || !aligned16(row_token) || !aligned16(w1q) ||
       !aligned16(w1s) || !aligned16(w2q) || !aligned16(w2s) || !aligned16(expert_offsets) ||

@@ -148,9 +148,9 @@ def test_mx_validation(L):
     assert q(None, 0, 64, P, P, P) == 2
     assert q(None, 4, 64, None, P, P) == 1
     assert q(None, 4, 64, P, P, MIS) == 4
-    # scales: ceil(K / 128) K tiles x R rows x 4 bytes
-    assert L.moe_quantize_mx_scales_size(300, 96) == 1 * 300 * 4
-    assert L.moe_quantize_mx_scales_size(40, 2688) == 21 * 40 * 4
+    # scales: ceil(K / 512) groups x R rows x 16 bytes
+    assert L.moe_quantize_mx_scales_size(300, 96) == 1 * 300 * 16
+    assert L.moe_quantize_mx_scales_size(40, 2688) == 6 * 40 * 16
     pk = L.moe_pack_weights_mx
     assert pk(None, 2, 127, 64, 1, P, P, P) == 2            # odd rows with gate/up halves
     assert pk(None, 2, 128, 40, 0, P, P, P) == 4            # K % 32

@@ -58,12 +58,13 @@ def _varied(rng, shape):
     return mw.round_to_bf16_bits(v)
 
 
-def _scales_tiled(sc, nkt):
-    """[R, K/32] scale codes -> the [nkt][R][4] layout, zero slots past K."""
+def _scales_grouped(sc, ng):
+    """[R, K/32] scale codes -> the [ng][R][16] layout (block b at [b/16][r][b%16]),
+    zero slots past K."""
     R, nb = sc.shape
-    pad = np.zeros((R, nkt * 4), np.uint8)
+    pad = np.zeros((R, ng * 16), np.uint8)
     pad[:, :nb] = sc
-    return pad.reshape(R, nkt, 4).transpose(1, 0, 2).copy()
+    return pad.reshape(R, ng, 16).transpose(1, 0, 2).copy()
 
 
 @pytest.mark.parametrize("R,K", [(1, 32), (300, 96), (65, 2048), (257, 160), (40, 2688)])
@@ -83,9 +84,9 @@ def test_quantize_mx_bitexact(R, K):
     assert torch.equal(outs[0].codes, outs[1].codes) and torch.equal(outs[0].scales, outs[1].scales)
     codes = outs[0].codes.cpu().numpy()
     scales = outs[0].scales.cpu().numpy()
-    nkt = -(-K // 128)
-    assert scales.size == nkt * R * 4
-    assert (scales.reshape(nkt, R, 4) == _scales_tiled(sc_ref, nkt)).all()
+    ng = -(-K // 512)
+    assert scales.size == ng * R * 16
+    assert (scales.reshape(ng, R, 16) == _scales_grouped(sc_ref, ng)).all()
     bad = np.nonzero(codes != codes_ref)
     assert bad[0].size == 0, (f"{bad[0].size} codes differ, e.g. at {bad[0][:4]}, {bad[1][:4]}: "
                               f"{codes[bad][:4]} vs {codes_ref[bad][:4]}")
@@ -160,11 +161,11 @@ def _a_from_ws(ws, N, F, lo=0, hi=None):
     """Rows [lo, hi) of A's codes [N, F] and scale codes [N, F / 32] from the
     forward's workspace."""
     hi = N if hi is None else hi
-    nkt = -(-F // 128)
+    ng = -(-F // 512)
     q = (N * F + 255) // 256 * 256
     codes = ws[lo * F:hi * F].cpu().numpy().reshape(hi - lo, F)
-    sc = ws[q:q + nkt * N * 4].view(nkt, N, 4)[:, lo:hi].cpu().numpy()
-    sc = sc.transpose(1, 0, 2).reshape(hi - lo, nkt * 4)
+    sc = ws[q:q + ng * N * 16].view(ng, N, 16)[:, lo:hi].cpu().numpy()
+    sc = sc.transpose(1, 0, 2).reshape(hi - lo, ng * 16)
     return codes, sc[:, :F // 32]
 
 
