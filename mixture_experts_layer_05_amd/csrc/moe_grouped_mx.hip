@@ -32,6 +32,7 @@
 #include <algorithm>
 
 #include "moe_gemm_common.h"
+#include "moe_sched.h"
 
 namespace moe {
 
@@ -46,7 +47,7 @@ constexpr int kMxSlot = 2 * kMxTile + 1024;      // A, B, B scales
 constexpr int kMxGroup = 4;                      // K tiles per group of row scales
 constexpr int kMxSgBuf = kMxBM * 4 * kMxGroup;   // one group's row scales (4 KB)
 constexpr int kMxLds = 2 * kMxSlot + 2 * kMxSgBuf;
-constexpr int kMxScanInts = 1040 + 64;
+constexpr int kMxScanInts = 1040 + 1024 + 1024 + 64;   // s_cum, s_perm, s_key, scan scratch
 
 // K tiles and sizes of the packed weights (panels of 256 rows; fc1 panels
 // hold 128 gate rows and the matching 128 up rows)
@@ -192,6 +193,7 @@ struct MxParams {
   uint8_t* out_s;              // fc1: A scales [ceil(F / 512)][N][16]
   uint16_t* out;               // fc2: Y [N, d] bf16
   int N;
+  int* counter;                // this launch's 8 tile counters, one per XCD (zero at launch)
 };
 
 struct MxTile {
@@ -200,13 +202,16 @@ struct MxTile {
   int vo[8];                   // per-lane byte offsets of the data loads (4 A, 4 B)
   int vs;                      // per-lane offset of the scale load (waves 0-3: A rows; wave 4: B)
   int j;                       // the tile's position in this workgroup's walk
+  int L;                       // the tile's index in the cost order
 };
 
 template <int kEpi>
 __device__ __forceinline__ void ggmx_body(const MxParams& p) {
   extern __shared__ __align__(16) uint8_t lds[];
   int* s_cum = reinterpret_cast<int*>(lds + kMxLds);
-  int* s_tmp = s_cum + 1040;
+  int* s_perm = s_cum + 1040;
+  int* s_key = s_perm + 1024;
+  int* s_tmp = s_key + 1024;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;      // wm: 128-row half, wn: 64-column quarter
@@ -214,14 +219,15 @@ __device__ __forceinline__ void ggmx_body(const MxParams& p) {
   const int K = p.K, nk = p.nkt;
 
   const int ng = (nk + kMxGroup - 1) / kMxGroup;  // row-scale groups per tile
-  tile_prefix<kMxThreads>(p.offsets, p.E, kMxBM, p.ntn, s_cum, s_tmp);
-  const int total = s_cum[p.E];
-  const int g8 = static_cast<int>(gridDim.x >> 3);
+  // this XCD's tiles (workgroup b runs on XCD b mod 8); its workgroups take
+  // tiles pos and pos + G first, then one fetch from the XCD's counter per
+  // tile started
   const int xcd = static_cast<int>(blockIdx.x & 7), pos = static_cast<int>(blockIdx.x >> 3);
-  const int q8 = total >> 3, rq = total & 7;
-  const int xbeg = xcd * q8 + min(xcd, rq), xcnt = q8 + (xcd < rq ? 1 : 0);
-  const int ntiles = xcnt > pos ? (xcnt - pos + g8 - 1) / g8 : 0;
-  if (ntiles == 0) return;
+  const int G = static_cast<int>(gridDim.x >> 3);
+  const int nx = tile_order_xcd<kMxThreads>(p.offsets, p.E, kMxBM, p.ntn, xcd, s_cum, s_perm, s_key,
+                                            s_tmp);
+  const int total = s_cum[nx];
+  if (pos >= total) return;
 
   // data loads: block bb = wave + 8 j (j = 0..3) of 8 rows x 128 bytes;
   // lane l: row 8 bb + l / 8, physical chunk l % 8 = logical chunk ^ swizzle
@@ -235,9 +241,10 @@ __device__ __forceinline__ void ggmx_body(const MxParams& p) {
   }
   const bool gath = p.gather != nullptr;
 
-  auto setup = [&](int j, MxTile& st) {
+  auto setup = [&](int j, int L, MxTile& st) {
     st.j = j;
-    st.ti = tile_decode(p.offsets, p.E, kMxBM, xbeg + pos + j * g8, s_cum);
+    st.L = L;
+    st.ti = tile_decode_xcd(p.offsets, nx, xcd, kMxBM, L, s_cum, s_perm);
     const TileIdx& ti = st.ti;
     const int m0 = ti.m0, last = ti.mend - 1 - m0;
     st.ra = __builtin_amdgcn_make_buffer_rsrc(
@@ -438,14 +445,18 @@ __device__ __forceinline__ void ggmx_body(const MxParams& p) {
   };
 
   MxTile cur, nxt;
-  setup(0, cur);
+  setup(0, pos, cur);
   __syncthreads();
   issue(cur, 0, 0);
-  if (ntiles > 1) setup(1, nxt);
+  bool has_nxt = pos + G < total;
+  if (has_nxt) setup(1, pos + G, nxt);
+  int* s_fetch = s_tmp + 32;
   int g = 0;
 #pragma unroll 1
-  for (int j = 0; j < ntiles; ++j) {
+  for (int j = 0;; ++j) {
     const int nrb = live_blocks(cur.ti);
+    int fetched = 0;
+    if (has_nxt && tid == 0) fetched = atomicAdd(p.counter + xcd, 1);   // the tile after nxt
 #pragma unroll
     for (int i = 0; i < kMxRB; ++i)
 #pragma unroll
@@ -454,15 +465,17 @@ __device__ __forceinline__ void ggmx_body(const MxParams& p) {
     for (int kt = 0; kt < nk; ++kt, ++g) {
       asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
       if (kt + 1 < nk) issue(cur, kt + 1, (g + 1) & 1);
-      else if (j + 1 < ntiles) issue(nxt, 0, (g + 1) & 1);
+      else if (has_nxt) issue(nxt, 0, (g + 1) & 1);
       compute(g & 1, nrb, j * ng + kt / kMxGroup, kt % kMxGroup);
     }
-    asm volatile("s_barrier" ::: "memory");
+    if (tid == 0) *s_fetch = 2 * G + fetched;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     epilogue(cur.ti, nrb, (g - 1) & 1);
-    if (j + 1 < ntiles) {
-      cur = nxt;
-      if (j + 2 < ntiles) setup(j + 2, nxt);
-    }
+    if (!has_nxt) break;
+    const int L2 = *s_fetch;
+    cur = nxt;
+    has_nxt = L2 < total;
+    if (has_nxt) setup(j + 2, L2, nxt);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
@@ -470,6 +483,14 @@ __device__ __forceinline__ void ggmx_body(const MxParams& p) {
 template <int kEpi>
 __global__ __launch_bounds__(kMxThreads, 1) void ggmx_kernel(MxParams p) {
   ggmx_body<kEpi>(p);
+}
+
+__global__ void zero_counters_kernel(int* __restrict__ c, int n) {
+  if (static_cast<int>(threadIdx.x) < n) c[threadIdx.x] = 0;
+}
+
+hipError_t launch_zero_counters(hipStream_t stream, int* c, int n) {
+  return launch(zero_counters_kernel, dim3(1), dim3(64), 0, stream, c, n);
 }
 
 static unsigned mx_grid(int64_t tiles) {
@@ -559,11 +580,15 @@ extern "C" moe_status moe_grouped_swiglu_fwd_mx(hipStream_t stream, int64_t N, i
     return MOE_ERR_ALIGNMENT;
   if (!ws || ws_bytes < moe_grouped_swiglu_fwd_mx_workspace_size(N, F)) return MOE_ERR_WORKSPACE;
   if (N == 0) return MOE_OK;
-  uint8_t* aq = static_cast<uint8_t*>(ws);
-  uint8_t* as = aq + ((static_cast<size_t>(N) * F + 255) & ~static_cast<size_t>(255));
   const size_t lds = kMxLds + kMxScanInts * sizeof(int);
   hipError_t err = allow_lds(ggmx_kernel<MX_FC1>, lds);
   if (err == hipSuccess) err = allow_lds(ggmx_kernel<MX_FC2>, lds);
+  if (err != hipSuccess) return MOE_ERR_HIP;
+  uint8_t* aq = static_cast<uint8_t*>(ws);
+  uint8_t* as = aq + ((static_cast<size_t>(N) * F + 255) & ~static_cast<size_t>(255));
+  // the two launches' tile counters (8 each) sit after A's scales, in the workspace's slack
+  int* counters = reinterpret_cast<int*>(as + mx_sgroups(F) * N * 16);
+  err = launch_zero_counters(stream, counters, 16);
   if (err != hipSuccess) return MOE_ERR_HIP;
   MxParams p{};
   p.E = E; p.F = (int)F; p.d = (int)d; p.K = (int)d; p.N = (int)N;
@@ -575,6 +600,7 @@ extern "C" moe_status moe_grouped_swiglu_fwd_mx(hipStream_t stream, int64_t N, i
   p.b = static_cast<const uint8_t*>(w1q); p.bs = static_cast<const uint8_t*>(w1s);
   p.b_estride = b1;
   p.out_q = aq; p.out_s = as;
+  p.counter = counters;
   const int64_t tiles1 = (N + kMxBM - 1) / kMxBM + E;
   err = launch(ggmx_kernel<MX_FC1>, dim3(mx_grid(tiles1 * p.ntn)), dim3(kMxThreads), lds, stream, p);
   if (err != hipSuccess) return MOE_ERR_HIP;
@@ -587,6 +613,7 @@ extern "C" moe_status moe_grouped_swiglu_fwd_mx(hipStream_t stream, int64_t N, i
   q.b = static_cast<const uint8_t*>(w2q); q.bs = static_cast<const uint8_t*>(w2s);
   q.b_estride = b2;
   q.scale = row_scale;
+  q.counter = counters + 8;
   q.out = static_cast<uint16_t*>(y_perm);
   return hip_status(launch(ggmx_kernel<MX_FC2>, dim3(mx_grid(tiles1 * q.ntn)), dim3(kMxThreads), lds,
                            stream, q));
