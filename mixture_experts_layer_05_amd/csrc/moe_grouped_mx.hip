@@ -47,7 +47,7 @@ constexpr int kMxSlot = 2 * kMxTile + 1024;      // A, B, B scales
 constexpr int kMxGroup = 4;                      // K tiles per group of row scales
 constexpr int kMxSgBuf = kMxBM * 4 * kMxGroup;   // one group's row scales (4 KB)
 constexpr int kMxLds = 2 * kMxSlot + 2 * kMxSgBuf;
-constexpr int kMxScanInts = 1040 + 1024 + 1024 + 64;   // s_cum, s_perm, s_key, scan scratch
+constexpr int kMxScanInts = 1040 + 64;
 
 // K tiles and sizes of the packed weights (panels of 256 rows; fc1 panels
 // hold 128 gate rows and the matching 128 up rows)
@@ -209,9 +209,7 @@ template <int kEpi>
 __device__ __forceinline__ void ggmx_body(const MxParams& p) {
   extern __shared__ __align__(16) uint8_t lds[];
   int* s_cum = reinterpret_cast<int*>(lds + kMxLds);
-  int* s_perm = s_cum + 1040;
-  int* s_key = s_perm + 1024;
-  int* s_tmp = s_key + 1024;
+  int* s_tmp = s_cum + 1040;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;      // wm: 128-row half, wn: 64-column quarter
@@ -219,14 +217,14 @@ __device__ __forceinline__ void ggmx_body(const MxParams& p) {
   const int K = p.K, nk = p.nkt;
 
   const int ng = (nk + kMxGroup - 1) / kMxGroup;  // row-scale groups per tile
-  // this XCD's tiles (workgroup b runs on XCD b mod 8); its workgroups take
-  // tiles pos and pos + G first, then one fetch from the XCD's counter per
-  // tile started
+  // this XCD's range of tiles (workgroup b runs on XCD b mod 8); its
+  // workgroups take tiles pos and pos + G of the range first, then one fetch
+  // from the XCD's counter per tile started
   const int xcd = static_cast<int>(blockIdx.x & 7), pos = static_cast<int>(blockIdx.x >> 3);
   const int G = static_cast<int>(gridDim.x >> 3);
-  const int nx = tile_order_xcd<kMxThreads>(p.offsets, p.E, kMxBM, p.ntn, xcd, s_cum, s_perm, s_key,
-                                            s_tmp);
-  const int total = s_cum[nx];
+  tile_prefix<kMxThreads>(p.offsets, p.E, kMxBM, p.ntn, s_cum, s_tmp);
+  const XcdRange xr = xcd_range(s_cum[p.E], xcd);
+  const int total = xr.xcnt;
   if (pos >= total) return;
 
   // data loads: block bb = wave + 8 j (j = 0..3) of 8 rows x 128 bytes;
@@ -244,7 +242,7 @@ __device__ __forceinline__ void ggmx_body(const MxParams& p) {
   auto setup = [&](int j, int L, MxTile& st) {
     st.j = j;
     st.L = L;
-    st.ti = tile_decode_xcd(p.offsets, nx, xcd, kMxBM, L, s_cum, s_perm);
+    st.ti = tile_decode(p.offsets, p.E, kMxBM, xr.xbeg + L, s_cum);
     const TileIdx& ti = st.ti;
     const int m0 = ti.m0, last = ti.mend - 1 - m0;
     st.ra = __builtin_amdgcn_make_buffer_rsrc(
