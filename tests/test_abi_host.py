@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.moe_abi_version() == 6
+    assert L.moe_abi_version() == 7
     assert L.moe_status_string(0) == b"MOE_OK"
     assert L.moe_status_string(5) == b"MOE_ERR_WORKSPACE"
 
