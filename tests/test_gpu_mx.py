@@ -420,3 +420,47 @@ def test_layer_fp8(case):
     fro = float(np.linalg.norm(yg - y_ref) / np.linalg.norm(y_ref))
     print(f"\n[layer fp8 {case}] normwise {nw:.3e} frobenius {fro:.3e}")
     assert nw <= gh.TOL_BF16 and fro <= TOL_MX_FRO
+
+
+@pytest.mark.parametrize("case", [
+    # E, d, F, counts pattern
+    (1, 32, 32, "one_row"),          # the smallest shapes: one row, one 32-value block each way
+    (1000, 64, 64, "sparse"),        # E = 1000: most experts empty, the rest one to three rows
+    (3, 128, 32, "empty"),           # N = 0: nothing launched, nothing written
+])
+def test_grouped_fwd_mx_edges(case):
+    E, d, F, pattern = case
+    rng = np.random.default_rng(E + d + F)
+    if pattern == "one_row":
+        counts = np.array([1])
+    elif pattern == "sparse":
+        counts = np.zeros(E, dtype=np.int64)
+        hot = rng.choice(E, 40, replace=False)
+        counts[hot] = rng.integers(1, 4, 40)
+    else:
+        counts = np.zeros(E, dtype=np.int64)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    N = int(off[-1])
+    inp = mw.make_small_layer_inputs(E + 3, T=max(N, 1), d=d, E=E, F=F, dtype="bf16", w_std=0.05)
+    x = gh.to_gpu(inp.x)
+    w1q = moe.pack_weights_mx(gh.to_gpu(inp.w1), True)
+    w2q = moe.pack_weights_mx(gh.to_gpu(inp.w2), False)
+    go = gh.to_gpu(off)
+    y = gh.poison((max(N, 1), d), torch.bfloat16)
+    ws = torch.empty(moe.fwd_mx_workspace_size(N, F), dtype=torch.uint8, device=x.device)
+    L = moe.lib()
+    xq = moe.quantize_mx(x)
+    st = L.moe_grouped_swiglu_fwd_mx(moe._stream(), N, d, F, E, 0, moe._p(xq.codes),
+                                     moe._p(xq.scales), None, moe._p(w1q.codes),
+                                     moe._p(w1q.scales), moe._p(w2q.codes), moe._p(w2q.scales),
+                                     moe._p(go), None, moe._p(y), moe._p(ws), ws.numel())
+    torch.cuda.synchronize()
+    assert st == 0
+    if N == 0:
+        assert torch.isnan(y.float()).all()          # untouched
+        return
+    y_ref, parts = mx.grouped_swiglu_fwd_mx(inp.as_f32("x").astype(np.float64)[:N],
+                                            inp.as_f32("w1"), inp.as_f32("w2"), off, None,
+                                            return_parts=True)
+    codes, sc = _a_from_ws(ws, N, F)
+    _check_mx_forward(gh.to_f64(y[:N]), codes, sc, y_ref, parts, off, None, f"mx edge {case}")
