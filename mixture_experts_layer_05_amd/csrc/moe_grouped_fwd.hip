@@ -109,9 +109,8 @@ using GemmCfg = FwdCfg<MOE_FWD_WM, MOE_FWD_WN, MOE_FWD_RB, MOE_FWD_CB, MOE_FWD_S
                        MOE_FWD_WG_PER_CU, MOE_FWD_W, MOE_FWD_SB>;
 // Router logits: 128 token rows x 128 experts per tile (the expert count of
 // the 128-expert models: no padded weight rows), 64-wide K, K split into
-// slabs of about four K tiles (see router_ksplit) so the small GEMM fills
-// the chip, and a 4-deep ring so that a slab's loads are all in flight at
-// once (one workgroup per CU).
+// slabs of at least eight K tiles (see router_ksplit) so that the small GEMM
+// has about one workgroup per CU, and a 4-deep ring (one workgroup per CU).
 using RouterCfg = FwdCfg<2, 2, 2, 2, 4, 64, 1>;
 
 enum FwdEpi { FWD_FC1 = 0, FWD_FC2 = 1, FWD_LOGITS = 2 };
@@ -952,12 +951,16 @@ hipError_t launch_grouped_fwd_bf16(hipStream_t stream, int64_t N, int64_t d, int
 }
 
 int router_ksplit(int64_t T, int64_t d, int32_t E) {
-  // enough K slabs for ~2 workgroups per CU, each slab at least 4 K tiles
+  // about one workgroup per CU, each slab at least 8 K tiles.  Measured on
+  // MI355X (route call, us; ksplit 1 / 2 / 4 / 8): T=4096 d=2048 E=128
+  // 38 / 31 / 29 / 31; T=8192 d=2688 E=128 46 / 36 / 34 / 47; T=16384
+  // d=2048 E=256 63 / 76 / 99 / -.  Fewer slabs also shrink the fp32 slab
+  // traffic that route_topk sums.
   using C = RouterCfg;
   const int64_t tiles = ((T + C::kBM - 1) / C::kBM) * ((E + C::kBN - 1) / C::kBN);
   const int64_t nk = (d + C::kBK - 1) / C::kBK;
-  int64_t s = (512 + tiles - 1) / tiles;
-  s = std::min<int64_t>(s, std::max<int64_t>(1, nk / 4));
+  int64_t s = (256 + tiles - 1) / tiles;
+  s = std::min<int64_t>(s, std::max<int64_t>(1, nk / 8));
   return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(s, 16)));
 }
 
