@@ -92,6 +92,33 @@ def test_quantize_mx_bitexact(R, K):
                               f"{codes[bad][:4]} vs {codes_ref[bad][:4]}")
 
 
+def test_quantize_mx_extreme_magnitudes():
+    """Blocks at the ends of bf16's range: subnormal values (the scale code
+    clamps at 0, so elements are scaled up by 2^127 through fp32 denormals),
+    blocks whose largest value is near 2^127, and mixtures of the two inside a
+    block (the small ones round to zero)."""
+    rng = np.random.default_rng(5)
+    R, K = 64, 256
+    v = rng.standard_normal((R, K)).astype(np.float64)
+    ex = np.zeros((R, K // 32))
+    ex[0::4] = -130.0                      # bf16 subnormals
+    ex[1::4] = -120.0                      # near the smallest normal
+    ex[2::4] = 120.0                       # near the largest exponent
+    ex[3::4] = rng.integers(-126, 126, (R // 4, K // 32))
+    v = v * np.exp2(np.repeat(ex, 32, axis=1))
+    v[5, 40] = 3.0e38                      # one huge element in a block of tiny ones
+    xb = mw.round_to_bf16_bits(v.astype(np.float32))
+    codes_ref, sc_ref = mx.mx_quantize(mw.bf16_bits_to_f32(xb))
+    q = moe.quantize_mx(gh.to_gpu(xb))
+    torch.cuda.synchronize()
+    ng = -(-K // 512)
+    assert (q.scales.cpu().numpy().reshape(ng, R, 16) == _scales_grouped(sc_ref, ng)).all()
+    codes = q.codes.cpu().numpy()
+    bad = np.nonzero(codes != codes_ref)
+    assert bad[0].size == 0, (f"{bad[0].size} codes differ, e.g. at {bad[0][:4]}, {bad[1][:4]}: "
+                              f"{codes[bad][:4]} vs {codes_ref[bad][:4]}")
+
+
 def _pack_mx_reference(a, gated, bn=256, bk=128):
     """The packed layout of include/moe.h written out from its definition (a
     reordering with zero fill): a [E, rows, Kc] -> [E, panels, ceil(Kc/bk), bn, bk]."""
