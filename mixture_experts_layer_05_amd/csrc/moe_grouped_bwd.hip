@@ -257,39 +257,107 @@ __device__ __forceinline__ void ggb_tile(const GGParams& p, int e, int lo, int h
         }
       }
     }
-  } else if constexpr (kNRB > 0) {
+  } else if constexpr (kEpi == EPI_DGRAD2) {
+    // fc2 dgrad + SwiGLU backward, staged through the free ring in four
+    // passes of 32 rows (pass q: the waves with wm == q / 2 own their row
+    // block q % 2): G and U come in as 16-byte vectors, each lane turns its
+    // elements into dG, dU (in place) and A * scale (a third array), and the
+    // results leave as 16-byte vectors.  Staged rows are padded to 264 bf16
+    // so that the two half-waves (rows 4 apart) read disjoint banks.  Every
+    // wave runs the same barriers.
+    constexpr int kSR = 32, kSW = kBN + 8, kCh = kBN / 8;   // staged rows, padded width, chunks
+    uint16_t* const GL = s_lds;
+    uint16_t* const UL = s_lds + kSR * kSW;
+    uint16_t* const AL = s_lds + 2 * kSR * kSW;
+    static_assert(3 * kSR * kSW * 2 <= static_cast<int>(kBwdLds), "staging fits the ring");
+    const int twoF = 2 * p.F;
+    __syncthreads();                                     // every wave is done with the ring
+#pragma unroll 1
+    for (int q = 0; q < kBM / kSR; ++q) {
+      const int r0 = m0 + q * kSR;
+      // (1) G and U of rows r0 .. r0 + 31, columns n0 .. n0 + 255
+#pragma unroll 1
+      for (int i = tid; i < 2 * kSR * kCh; i += kGT) {
+        const int arr = i / (kSR * kCh), rem = i % (kSR * kCh);
+        const int row = rem / kCh, ch = rem % kCh;
+        const int grow = r0 + row, f0 = n0 + ch * 8;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (grow < hi && f0 < p.F)
+          v = *reinterpret_cast<const u32x4*>(p.gu_in + static_cast<size_t>(grow) * twoF +
+                                              (arr ? p.F : 0) + f0);
+        *reinterpret_cast<u32x4*>((arr ? UL : GL) + row * kSW + ch * 8) = v;
+      }
+      __syncthreads();
+      // (2) the owning waves: dG, dU in place, A * scale into AL
+      if (wm == (q >> 1)) {
+        const int rb = q & 1;
+        if (rb < kNRB) {
 #pragma unroll
-    for (int rb = 0; rb < kNRB; ++rb) {
+          for (int r = 0; r < 16; ++r) {
+            const int lrow = 8 * (r >> 2) + 4 * h + (r & 3);
+            const int grow = r0 + lrow;
+            const float sc = (p.scale && grow < hi) ? p.scale[grow] : 1.0f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * kRB * 32 + rb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (row >= hi) continue;
-        const size_t rowz = static_cast<size_t>(row);
-        if constexpr (kEpi == EPI_DGRAD2) {
-          const float s = p.scale ? p.scale[row] : 1.0f;
-#pragma unroll
-          for (int c = 0; c < kCB; ++c) {
-            const int f = n0 + wn * kCB * 32 + c * 32 + r32;
-            if (f < p.F) {
-              const float da = acc[rb][c][r] * s;
-              const float g = bf16_to_f32(p.gu_in[rowz * 2 * p.F + f]);
-              const float u = bf16_to_f32(p.gu_in[rowz * 2 * p.F + p.F + f]);
+            for (int c = 0; c < kCB; ++c) {
+              const int li = lrow * kSW + wn * kCB * 32 + c * 32 + r32;
+              const float da = (rb == 0 ? acc[0][c][r] : acc[kAccRB - 1][c][r]) * sc;
+              const float g = bf16_to_f32(GL[li]);
+              const float u = bf16_to_f32(UL[li]);
               const float sg = sigmoid_fast(g);
               const float sl = g * sg;
-              const u32x2 o = pack4_bf16(da * u * sg * (1.0f + g * (1.0f - sg)), da * sl, s * sl * u, 0.0f);
-              p.out[rowz * 2 * p.F + f] = static_cast<uint16_t>(o[0]);
-              p.out[rowz * 2 * p.F + p.F + f] = static_cast<uint16_t>(o[0] >> 16);
-              p.out2[rowz * p.F + f] = static_cast<uint16_t>(o[1]);
+              const u32x2 o = pack4_bf16(da * u * sg * (1.0f + g * (1.0f - sg)), da * sl,
+                                         sc * sl * u, 0.0f);
+              GL[li] = static_cast<uint16_t>(o[0]);
+              UL[li] = static_cast<uint16_t>(o[0] >> 16);
+              AL[li] = static_cast<uint16_t>(o[1]);
             }
-          }
-        } else {  // EPI_DGRAD1
-#pragma unroll
-          for (int c = 0; c < kCB; ++c) {
-            const int n = n0 + wn * kCB * 32 + c * 32 + r32;
-            if (n < p.d) p.out[rowz * p.d + n] = static_cast<uint16_t>(pack4_bf16(acc[rb][c][r], 0.f, 0.f, 0.f)[0]);
+            // one row at a time: keeps the staged reads from piling up in registers
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
       }
+      __syncthreads();
+      // (3) dG, dU to dH[row][f], dH[row][F + f]; A * scale to out2[row][f]
+#pragma unroll 1
+      for (int i = tid; i < 3 * kSR * kCh; i += kGT) {
+        const int arr = i / (kSR * kCh), rem = i % (kSR * kCh);
+        const int row = rem / kCh, ch = rem % kCh;
+        const int grow = r0 + row, f0 = n0 + ch * 8;
+        if (grow < hi && f0 < p.F) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(s_lds + arr * kSR * kSW + row * kSW + ch * 8);
+          if (arr < 2)
+            *reinterpret_cast<u32x4*>(p.out + static_cast<size_t>(grow) * twoF + (arr ? p.F : 0) + f0) = v;
+          else
+            *reinterpret_cast<u32x4*>(p.out2 + static_cast<size_t>(grow) * p.F + f0) = v;
+        }
+      }
+      __syncthreads();
+    }
+  } else {                           // EPI_DGRAD1: dX rows, staged as 16-byte vectors
+    constexpr int kSW = kBN + 8, kCh = kBN / 8;          // padded staged row (bf16), chunks
+    static_assert(kBM * kSW * 2 <= static_cast<int>(kBwdLds), "staging fits the ring");
+    __syncthreads();                                     // every wave is done with the ring
+    if constexpr (kNRB > 0) {
+#pragma unroll
+      for (int rb = 0; rb < kNRB; ++rb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int lrow = wm * kRB * 32 + rb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+#pragma unroll
+          for (int c = 0; c < kCB; ++c)
+            s_lds[lrow * kSW + wn * kCB * 32 + c * 32 + r32] =
+                static_cast<uint16_t>(pack4_bf16(acc[rb][c][r], 0.f, 0.f, 0.f)[0]);
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int i = tid; i < kBM * kCh; i += kGT) {
+      const int row = i / kCh, ch = i % kCh;
+      const int grow = m0 + row, n = n0 + ch * 8;
+      if (grow < hi && n < p.d)
+        *reinterpret_cast<u32x4*>(p.out + static_cast<size_t>(grow) * p.d + n) =
+            *reinterpret_cast<const u32x4*>(s_lds + row * kSW + ch * 8);
     }
   }
 }
