@@ -646,7 +646,6 @@ __device__ __forceinline__ void ggfp_body(const FwdParams& p) {
           const int lp = wrow0 - ps * kPassRows + rb * 32 + r32;
           const int row = m0 + wrow0 + rb * 32 + r32;
           if constexpr (kEpi == FWD_FC1) {
-            const size_t rowz = static_cast<size_t>(row);
 #pragma unroll
             for (int c = 0; c < kCB / 2; ++c) {
 #pragma unroll
@@ -662,14 +661,6 @@ __device__ __forceinline__ void ggfp_body(const FwdParams& p) {
                 }
                 *reinterpret_cast<u32x2*>(staged(lp, fl * 2)) =
                     pack4_bf16(a4[0], a4[1], a4[2], a4[3]);
-                const int f = n0 + fl;
-                if (p.out2 && row < ti.mend && f < p.F) {
-                  uint16_t* gu = p.out2 + rowz * 2 * p.F;
-                  *reinterpret_cast<u32x2*>(gu + f) =
-                      pack4_bf16(G[4 * qq], G[4 * qq + 1], G[4 * qq + 2], G[4 * qq + 3]);
-                  *reinterpret_cast<u32x2*>(gu + p.F + f) =
-                      pack4_bf16(U[4 * qq], U[4 * qq + 1], U[4 * qq + 2], U[4 * qq + 3]);
-                }
               }
             }
           } else {
@@ -700,6 +691,44 @@ __device__ __forceinline__ void ggfp_body(const FwdParams& p) {
               *reinterpret_cast<const u32x4*>(staged(lp, ch * 16));
       }
       if (ps + 1 < kPass) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    if constexpr (kEpi == FWD_FC1) {
+      // G and U saved for the backward ([G | U] rows of 2F): staged like A,
+      // one pass each, so they leave as 16-byte lanes over whole rows
+      static_assert(kPass == 1, "one staging pass holds the fc1 tile");
+      if (p.out2) {
+#pragma unroll 1
+        for (int half = 0; half < 2; ++half) {
+          asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // staging free again
+#pragma unroll
+          for (int rb = 0; rb < kRB; ++rb) {
+            if (rb >= nrb) continue;
+            const int lp = wrow0 + rb * 32 + r32;
+#pragma unroll
+            for (int c = 0; c < kCB / 2; ++c) {
+#pragma unroll
+              for (int qq = 0; qq < 4; ++qq) {
+                const int fl = wn * (kCB / 2) * 32 + c * 32 + 8 * qq + 4 * h;
+                const f32x16& X = half ? acc[rb][c + kCB / 2] : acc[rb][c];
+                *reinterpret_cast<u32x2*>(staged(lp, fl * 2)) =
+                    pack4_bf16(X[4 * qq], X[4 * qq + 1], X[4 * qq + 2], X[4 * qq + 3]);
+              }
+            }
+          }
+          asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+          int t0 = tid;
+          asm volatile("" : "+v"(t0));   // keep this loop's addressing out of the kernel preamble
+#pragma unroll
+          for (int i = t0; i < kPassRows * kChunksRow; i += C::kThreads) {
+            const int lp = i / kChunksRow, ch = i - lp * kChunksRow;
+            const int row = m0 + lp;
+            const int col = n0 + ch * 8;
+            if (row < ti.mend && col < p.F)
+              *reinterpret_cast<u32x4*>(p.out2 + static_cast<size_t>(row) * 2 * p.F + half * p.F + col) =
+                  *reinterpret_cast<const u32x4*>(staged(lp, ch * 16));
+          }
+        }
+      }
     }
   };
 
