@@ -44,6 +44,38 @@ __device__ __forceinline__ void load8(const void* base, size_t chunk, float (&v)
     }
   }
 }
+// The same load split in two: the raw 16 (bf16) or 32 (fp32) bytes, then
+// their conversion.  Batches of raw loads issued without branches go out
+// together; a load under a branch, converted inside it, is waited for there.
+template <bool kBF16>
+struct Raw8 {
+  u32x4 c[kBF16 ? 1 : 2];
+};
+template <bool kBF16>
+__device__ __forceinline__ Raw8<kBF16> load_raw8(const void* base, size_t chunk) {
+  Raw8<kBF16> r;
+  if constexpr (kBF16) {
+    r.c[0] = static_cast<const u32x4*>(base)[chunk];
+  } else {
+    r.c[0] = static_cast<const u32x4*>(base)[2 * chunk];
+    r.c[1] = static_cast<const u32x4*>(base)[2 * chunk + 1];
+  }
+  return r;
+}
+template <bool kBF16>
+__device__ __forceinline__ void cvt8(const Raw8<kBF16>& r, float (&v)[8]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if constexpr (kBF16) {
+      v[2 * q] = bf16lo(r.c[0][q]);
+      v[2 * q + 1] = bf16hi(r.c[0][q]);
+    } else {
+      v[q] = __uint_as_float(r.c[0][q]);
+      v[4 + q] = __uint_as_float(r.c[1][q]);
+    }
+  }
+}
+
 template <bool kBF16>
 __device__ __forceinline__ void store8(void* base, size_t chunk, const float (&v)[8]) {
   if constexpr (kBF16) {
@@ -61,6 +93,33 @@ __device__ __forceinline__ void store8(void* base, size_t chunk, const float (&v
     static_cast<u32x4*>(base)[2 * chunk] = c0;
     static_cast<u32x4*>(base)[2 * chunk + 1] = c1;
   }
+}
+
+// sum over this lane's chunks c = lane, lane + 64, ... of <a[arow + c], b[brow + c]>
+// (8 values each), in chunk order; the loads of four chunks go out together
+template <bool kBF16>
+__device__ __forceinline__ float row_dot(const void* a, size_t arow, const void* b, size_t brow,
+                                         int nchunk, int lane) {
+  float dot = 0.0f;
+  for (int c0 = lane; c0 < nchunk; c0 += 4 * 64) {
+    Raw8<kBF16> ra[4], rb[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {   // chunks past the row re-read chunk c0 (not summed)
+      const int c = c0 + u * 64 < nchunk ? c0 + u * 64 : c0;
+      ra[u] = load_raw8<kBF16>(a, arow + c);
+      rb[u] = load_raw8<kBF16>(b, brow + c);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (c0 + u * 64 < nchunk) {
+        float av[8], bv[8];
+        cvt8<kBF16>(ra[u], av);
+        cvt8<kBF16>(rb[u], bv);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) dot = fmaf(av[q], bv[q], dot);
+      }
+  }
+  return dot;
 }
 
 // ---------------------------------------------------------------------------
@@ -83,30 +142,35 @@ __global__ __launch_bounds__(kLbThreads) void combine_bwd_kernel(
     if (row >= 0) {
       const float w = topk_w[static_cast<size_t>(t) * k + j];
       const size_t rrow = static_cast<size_t>(row) * nchunk;
-      for (int c = lane; c < nchunk; c += 64) {
-        float g[8], yv[8], o[8];
-        load8<kBF16>(dy, trow + c, g);
-        load8<kBF16>(y_perm, rrow + c, yv);
+      // four chunks' loads at a time (past the row: chunk c0 again, unused)
+      for (int c0 = lane; c0 < nchunk; c0 += 4 * 64) {
+        Raw8<kBF16> rg[4], ry[4];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          dot = fmaf(g[q], yv[q], dot);
-          o[q] = w * g[q];
+        for (int u = 0; u < 4; ++u) {
+          const int c = c0 + u * 64 < nchunk ? c0 + u * 64 : c0;
+          rg[u] = load_raw8<kBF16>(dy, trow + c);
+          ry[u] = load_raw8<kBF16>(y_perm, rrow + c);
         }
-        store8<kBF16>(dy_perm, rrow + c, o);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (c0 + u * 64 < nchunk) {
+            float g[8], yv[8], o[8];
+            cvt8<kBF16>(rg[u], g);
+            cvt8<kBF16>(ry[u], yv);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              dot = fmaf(g[q], yv[q], dot);
+              o[q] = w * g[q];
+            }
+            store8<kBF16>(dy_perm, rrow + c0 + u * 64, o);
+          }
       }
     }
     dot = wave_sum(dot);
     if (lane == 0) d_topk_w[static_cast<size_t>(t) * k + j] = row >= 0 ? dot : 0.0f;
   }
   if (y_shared && d_gate) {
-    float dot = 0.0f;
-    for (int c = lane; c < nchunk; c += 64) {
-      float g[8], yv[8];
-      load8<kBF16>(dy, trow + c, g);
-      load8<kBF16>(y_shared, trow + c, yv);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) dot = fmaf(g[q], yv[q], dot);
-    }
+    float dot = row_dot<kBF16>(dy, trow, y_shared, trow, nchunk, lane);
     dot = wave_sum(dot);
     if (lane == 0) d_gate[t] = dot;
   }
@@ -125,6 +189,9 @@ __global__ __launch_bounds__(kLbThreads) void combine_bwd_kernel(
 // The sigmoid forms need s_j = sigmoid(z_j): z_j = x[t] . W_r[e_j] (+ b) is
 // recomputed here in fp32.
 // ---------------------------------------------------------------------------
+constexpr int kDxBatch = 2;    // choices whose rows are loaded together in the dx pass
+constexpr int kDxChunks = 4;   // 16-byte chunks of a row per lane in the dx pass
+
 template <bool kBF16>
 __global__ __launch_bounds__(kLbThreads) void rbwd_token_kernel(
     int T, int k, int E, int N, int nchunk, int sigmoid, int normalize,
@@ -155,16 +222,8 @@ __global__ __launch_bounds__(kLbThreads) void rbwd_token_kernel(
     for (int j = 0; j < k; ++j) {
       const int ej = __shfl(e, j, kWave);
       float dot = 0.0f;
-      if (ej >= 0) {
-        const size_t erow = static_cast<size_t>(ej) * nchunk;
-        for (int c = lane; c < nchunk; c += 64) {
-          float xv[8], wv[8];
-          load8<kBF16>(x, trow + c, xv);
-          load8<kBF16>(w_router, erow + c, wv);
-#pragma unroll
-          for (int q = 0; q < 8; ++q) dot = fmaf(xv[q], wv[q], dot);
-        }
-      }
+      if (ej >= 0) dot = row_dot<kBF16>(x, trow, w_router, static_cast<size_t>(ej) * nchunk,
+                                        nchunk, lane);
       dot = wave_sum(dot);
       if (lane == j && ej >= 0) s = sigmoidf_(dot + (logit_bias ? logit_bias[ej] : 0.0f));
     }
@@ -184,81 +243,144 @@ __global__ __launch_bounds__(kLbThreads) void rbwd_token_kernel(
   // shared gate
   float dgl = 0.0f;
   if (w_gate && d_gate) {
-    float dot = 0.0f;
-    for (int cc = lane; cc < nchunk; cc += 64) {
-      float xv[8], gv[8];
-      load8<kBF16>(x, trow + cc, xv);
-      load8<kBF16>(w_gate, cc, gv);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) dot = fmaf(xv[q], gv[q], dot);
-    }
+    float dot = row_dot<kBF16>(x, trow, w_gate, 0, nchunk, lane);
     dot = wave_sum(dot);
     const float g = sigmoidf_(dot);
     dgl = d_gate[t] * g * (1.0f - g);
     if (lane == 0) dgl_tok[t] = dgl;
   }
-  // dx[t] = sum_j dX[row_j] + sum_j dz_j W_r[e_j] + dgl w_gate + dx_add[t]
-  for (int cc = lane; cc < nchunk; cc += 64) {
-    float acc[8];
+  // dx[t] = sum_j dX[row_j] + sum_j dz_j W_r[e_j] + dgl w_gate + dx_add[t].
+  // Four chunks of the row per lane at a time (1 KB each per wave): for each
+  // choice the loads cover 4 KB of its dX row and W_r row, two choices' loads
+  // go out together, and every column sums the choices in order (lanes >= k
+  // hold row = e = -1, so j >= k adds nothing).  Loads past the row or of an
+  // unused choice re-read valid memory and are not summed.
+  for (int c0 = lane; c0 < nchunk; c0 += kDxChunks * 64) {
+    float acc[kDxChunks][8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      const int rj = __shfl(row, j, kWave);
-      const int ej = __shfl(e, j, kWave);
-      const float dzj = __shfl(dz, j, kWave);
-      float v[8];
-      if (dx_perm && rj >= 0) {
-        load8<kBF16>(dx_perm, static_cast<size_t>(rj) * nchunk + cc, v);
+    for (int u = 0; u < kDxChunks; ++u)
 #pragma unroll
-        for (int q = 0; q < 8; ++q) acc[q] += v[q];
+      for (int q = 0; q < 8; ++q) acc[u][q] = 0.0f;
+    int cu[kDxChunks];
+#pragma unroll
+    for (int u = 0; u < kDxChunks; ++u) cu[u] = c0 + u * 64 < nchunk ? c0 + u * 64 : c0;
+    for (int j0 = 0; j0 < k; j0 += kDxBatch) {
+      Raw8<kBF16> rx[kDxBatch][kDxChunks], rw[kDxBatch][kDxChunks];
+      float dzj[kDxBatch];
+      bool hx[kDxBatch], hw[kDxBatch];
+#pragma unroll
+      for (int b = 0; b < kDxBatch; ++b) {
+        const int rj = __shfl(row, j0 + b, kWave);
+        const int ej = __shfl(e, j0 + b, kWave);
+        dzj[b] = __shfl(dz, j0 + b, kWave);
+        hx[b] = dx_perm && rj >= 0;
+        hw[b] = ej >= 0 && dzj[b] != 0.0f;
+        const size_t xr = static_cast<size_t>(hx[b] ? rj : 0) * nchunk;
+        const size_t wr = static_cast<size_t>(hw[b] ? ej : 0) * nchunk;
+#pragma unroll
+        for (int u = 0; u < kDxChunks; ++u) {
+          if (dx_perm) rx[b][u] = load_raw8<kBF16>(dx_perm, xr + cu[u]);
+          rw[b][u] = load_raw8<kBF16>(w_router, wr + cu[u]);
+        }
       }
-      if (ej >= 0 && dzj != 0.0f) {
-        load8<kBF16>(w_router, static_cast<size_t>(ej) * nchunk + cc, v);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) acc[q] = fmaf(dzj, v[q], acc[q]);
+      for (int b = 0; b < kDxBatch; ++b)
+#pragma unroll
+        for (int u = 0; u < kDxChunks; ++u) {
+          float v[8];
+          if (hx[b]) {
+            cvt8<kBF16>(rx[b][u], v);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc[u][q] += v[q];
+          }
+          if (hw[b]) {
+            cvt8<kBF16>(rw[b][u], v);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc[u][q] = fmaf(dzj[b], v[q], acc[u][q]);
+          }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kDxChunks; ++u) {
+      if (c0 + u * 64 >= nchunk) continue;
+      const int cc = c0 + u * 64;
+      if (w_gate && d_gate) {
+        float v[8];
+        load8<kBF16>(w_gate, cc, v);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[u][q] = fmaf(dgl, v[q], acc[u][q]);
       }
-    }
-    if (w_gate && d_gate) {
-      float v[8];
-      load8<kBF16>(w_gate, cc, v);
+      if (dx_add) {
+        float v[8];
+        load8<kBF16>(dx_add, trow + cc, v);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = fmaf(dgl, v[q], acc[q]);
+        for (int q = 0; q < 8; ++q) acc[u][q] += v[q];
+      }
+      store8<kBF16>(dx, trow + cc, acc[u]);
     }
-    if (dx_add) {
-      float v[8];
-      load8<kBF16>(dx_add, trow + cc, v);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] += v[q];
-    }
-    store8<kBF16>(dx, trow + cc, acc);
   }
 }
 
-// dW_r[e, cols] (+)= sum over expert e's rows r (in row order) of
-// dz_slot[r] * x[row_token[r], cols].  Grid (E, column blocks of 512); a
-// lane owns 8 columns.
+// dW_r[e, cols] (+)= sum over expert e's rows r of dz_slot[r] *
+// x[row_token[r], cols].  Grid (E, column blocks of 512); a lane owns 8
+// columns; wave w of the workgroup sums rows lo + w, lo + w + 4, ... in row
+// order, and the four wave sums are added in wave order (a fixed order: the
+// result does not depend on timing).  The row indices of 64 rows come in
+// with one load per lane; the x loads go out 16 rows at a time.
+constexpr int kDwrWaves = 4;
+constexpr int kDwrBatch = 16;
 template <bool kBF16>
-__global__ __launch_bounds__(64) void rbwd_dwr_kernel(int d, int nchunk,
-                                                      const int32_t* __restrict__ offsets,
-                                                      const int32_t* __restrict__ row_token,
-                                                      const float* __restrict__ dz_slot,
-                                                      const void* __restrict__ x,
-                                                      float* __restrict__ dw_router,
-                                                      int accumulate) {
+__global__ __launch_bounds__(64 * kDwrWaves) void rbwd_dwr_kernel(int d, int nchunk,
+                                                                  const int32_t* __restrict__ offsets,
+                                                                  const int32_t* __restrict__ row_token,
+                                                                  const float* __restrict__ dz_slot,
+                                                                  const void* __restrict__ x,
+                                                                  float* __restrict__ dw_router,
+                                                                  int accumulate) {
+  __shared__ float s_part[kDwrWaves - 1][64 * 8];
   const int e = blockIdx.x;
-  const int c = blockIdx.y * 64 + threadIdx.x;
-  if (c >= nchunk) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = blockIdx.y * 64 + lane;
+  const bool live = c < nchunk;
+  const int cl = live ? c : 0;   // lanes past the row read chunk 0 and store nothing
   const int lo = offsets[e], hi = offsets[e + 1];
   float acc[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
-  for (int r = lo; r < hi; ++r) {
-    const float g = dz_slot[r];
-    float v[8];
-    load8<kBF16>(x, static_cast<size_t>(row_token[r]) * nchunk + c, v);
+  for (int base = lo + wave; base < hi; base += 64 * kDwrWaves) {
+    // this wave's rows base + 4 u, u < 64: lane u fetches row u's token and dz
+    const int rl = base + kDwrWaves * lane;
+    const int tok_l = rl < hi ? row_token[rl] : 0;
+    const float g_l = rl < hi ? dz_slot[rl] : 0.0f;
+    for (int u0 = 0; u0 < 64 && base + kDwrWaves * u0 < hi; u0 += kDwrBatch) {
+      Raw8<kBF16> rv[kDwrBatch];
+      float g[kDwrBatch];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] = fmaf(g, v[q], acc[q]);
+      for (int u = 0; u < kDwrBatch; ++u) {   // rows past the segment read token 0 (not summed)
+        const int tk = __shfl(tok_l, u0 + u, kWave);
+        g[u] = __shfl(g_l, u0 + u, kWave);
+        rv[u] = load_raw8<kBF16>(x, static_cast<size_t>(tk) * nchunk + cl);
+      }
+#pragma unroll
+      for (int u = 0; u < kDwrBatch; ++u)
+        if (base + kDwrWaves * (u0 + u) < hi) {
+          float v[8];
+          cvt8<kBF16>(rv[u], v);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) acc[q] = fmaf(g[u], v[q], acc[q]);
+        }
+    }
   }
+  if (wave > 0) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) s_part[wave - 1][q * 64 + lane] = acc[q];
+  }
+  __syncthreads();
+  if (wave > 0 || !live) return;
+#pragma unroll
+  for (int w = 0; w < kDwrWaves - 1; ++w)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] += s_part[w][q * 64 + lane];
   float* dst = dw_router + static_cast<size_t>(e) * d + 8 * c;
 #pragma unroll
   for (int q = 0; q < 8; ++q) dst[q] = accumulate ? dst[q] + acc[q] : acc[q];
@@ -278,12 +400,24 @@ __global__ __launch_bounds__(64) void rbwd_dwg_partial_kernel(int T, int nchunk,
   float acc[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
-  for (int t = t0; t < t1; ++t) {
-    const float g = dgl_tok[t];
-    float v[8];
-    load8<kBF16>(x, static_cast<size_t>(t) * nchunk + c, v);
+  // 16 tokens' loads at a time, summed in token order
+  for (int tb = t0; tb < t1; tb += 16) {
+    Raw8<kBF16> rv[16];
+    float g[16];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] = fmaf(g, v[q], acc[q]);
+    for (int u = 0; u < 16; ++u) {   // tokens past the block re-read token tb (not summed)
+      const int t = tb + u < t1 ? tb + u : tb;
+      g[u] = dgl_tok[t];
+      rv[u] = load_raw8<kBF16>(x, static_cast<size_t>(t) * nchunk + c);
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (tb + u < t1) {
+        float v[8];
+        cvt8<kBF16>(rv[u], v);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = fmaf(g[u], v[q], acc[q]);
+      }
   }
   float* dst = part + static_cast<size_t>(blockIdx.y) * nchunk * 8 + 8 * c;
 #pragma unroll
@@ -378,8 +512,8 @@ extern "C" moe_status moe_route_backward(
   }
   if (err == hipSuccess) {
     auto kern = bf ? rbwd_dwr_kernel<true> : rbwd_dwr_kernel<false>;
-    err = launch(kern, dim3(E, (nchunk + 63) / 64), dim3(64), 0, stream, (int)d, nchunk,
-                 expert_offsets, row_token, dz_slot, x, dw_router, accumulate);
+    err = launch(kern, dim3(E, (nchunk + 63) / 64), dim3(64 * kDwrWaves), 0, stream, (int)d,
+                 nchunk, expert_offsets, row_token, dz_slot, x, dw_router, accumulate);
   }
   if (err == hipSuccess && w_gate) {
     auto kern = bf ? rbwd_dwg_partial_kernel<true> : rbwd_dwg_partial_kernel<false>;

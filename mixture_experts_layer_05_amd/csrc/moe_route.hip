@@ -139,23 +139,43 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
     if (my_e < E) atomicAdd(&s_cnt[my_e], 1);   // LDS integer atomics: order-free
   }
   if (gate) {
+    // the row's loads go out four (bf16: 4 x 1 KB per wave) or eight at a
+    // time before their products are summed, in the same order as one at a
+    // time (past d: 0 * 0, which leaves g unchanged)
     float g = 0.0f;
     if constexpr (kBF16) {
       const uint16_t* xr = static_cast<const uint16_t*>(xv) + static_cast<size_t>(t) * d;
       const uint16_t* wg = static_cast<const uint16_t*>(wgv);
-      for (int k8 = lane * 8; k8 < d; k8 += 512) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(xr + k8);
-        const u32x4 b = *reinterpret_cast<const u32x4*>(wg + k8);
+      for (int k0 = lane * 8; k0 < d; k0 += 4 * 512) {
+        u32x4 a[4], b[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          g = fmaf(bf16lo(a[q]), bf16lo(b[q]), g);
-          g = fmaf(bf16hi(a[q]), bf16hi(b[q]), g);
+        for (int u = 0; u < 4; ++u) {
+          const int k8 = k0 + u * 512;
+          a[u] = k8 < d ? *reinterpret_cast<const u32x4*>(xr + k8) : u32x4{0, 0, 0, 0};
+          b[u] = k8 < d ? *reinterpret_cast<const u32x4*>(wg + k8) : u32x4{0, 0, 0, 0};
         }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            g = fmaf(bf16lo(a[u][q]), bf16lo(b[u][q]), g);
+            g = fmaf(bf16hi(a[u][q]), bf16hi(b[u][q]), g);
+          }
       }
     } else {
       const float* xr = static_cast<const float*>(xv) + static_cast<size_t>(t) * d;
       const float* wg = static_cast<const float*>(wgv);
-      for (int i = lane; i < d; i += 64) g = fmaf(xr[i], wg[i], g);
+      for (int i0 = lane; i0 < d; i0 += 8 * 64) {
+        float a[8], b[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = i0 + u * 64;
+          a[u] = i < d ? xr[i] : 0.0f;
+          b[u] = i < d ? wg[i] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) g = fmaf(a[u], b[u], g);
+      }
     }
     g = wave_sum_dpp(g);
     if (lane == 0) gate[t] = sigmoidf_(g);
