@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, AMD's published figure
 PEAK_FP8_TFLOPS = 5000.0         # MI355X dense fp8 MFMA, AMD's published figure
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, AMD's published figure
+COLD_FLUSH_BYTES = 1 << 30        # scratch written before each cold stage (> L2 + 256 MB MALL)
 
 # HBM bytes per grouped-GEMM forward call (fc1 + fc2 dispatches), from
 # `rocprofv3 --pmc FETCH_SIZE` and `--pmc WRITE_SIZE` runs of this script,
@@ -269,6 +270,43 @@ def main():
             per_stage[s] += ev[j].elapsed_time(ev[j + 1])
         total_ev += ev[0].elapsed_time(ev[5])
     per_stage = {s: v / nbreak for s, v in per_stage.items()}  # ms per call
+
+    # Cold stages: a 1 GiB scratch fill (larger than L2 and the 256 MB
+    # Infinity Cache) before each stage, outside its event pair; the shared
+    # expert runs in line (untimed), its gate folded into its row scale.
+    scratch = torch.empty(COLD_FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    cold_stages = ["route", "permute", "grouped_gemm", "combine"]
+    ncold = 5
+    cev = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(ncold)]
+    for i in range(ncold):
+        L = layer
+        scratch.fill_(float(i))
+        cev[i][0].record(stream)
+        idx, w, cnt, gate = moe.route(x, L.w_router, L.k, L.score, L.normalize, L.logit_bias,
+                                      L.w_gate, out=L.route_out, ws=L.route_ws,
+                                      selection_bias=L.selection_bias)
+        cev[i][1].record(stream)
+        scratch.fill_(float(i))
+        cev[i][2].record(stream)
+        off, slot, rtok, rw, _ = moe.permute(x, idx, w, L.E, out=L.perm_out, ws=L.perm_ws,
+                                             copy_rows=False)
+        cev[i][3].record(stream)
+        scratch.fill_(float(i))
+        cev[i][4].record(stream)
+        L._routed(x, None, rtok, off, rw)
+        cev[i][5].record(stream)
+        ysh = None
+        if L.ws1 is not None:
+            L._shared(x, gate, L.ffn_ws)
+            ysh = L.y_shared
+        scratch.fill_(float(i))
+        cev[i][6].record(stream)
+        moe.unpermute_combine(L.y_perm, slot, None, ysh, out=L.y)
+        cev[i][7].record(stream)
+    torch.cuda.synchronize()
+    del scratch
+    cold = {s: sum(e[2 * j].elapsed_time(e[2 * j + 1]) for e in cev) / ncold
+            for j, s in enumerate(cold_stages)}
     ms_per_step = wall * 1e3 / args.steps
     tokens_per_s = cfg.T / (wall / args.steps)
 
@@ -299,9 +337,13 @@ def main():
     roof["avg_launch_ms"] = round(t_gemm_ms, 4)
     roof["traffic_unit"] = "bytes per call (HBM, counter-measured)"
 
-    def gbs(key, stage):
-        t = per_stage[stage] * 1e-3
+    def gbs(key, stage, table=None):
+        t = (table or per_stage)[stage] * 1e-3
         return round(alg[key] / t / 1e9, 1) if t > 0 else None
+
+    cold_gbs = {"route": gbs("route_bytes", "route", cold),
+                "permute": gbs("permute_bytes", "permute", cold),
+                "combine": gbs("combine_bytes", "combine", cold)}
 
     out = {
         "metric": "MoE layer tokens/sec + grouped-GEMM TFLOP/s (% bf16 MFMA peak), 1 MI355X",
@@ -330,6 +372,13 @@ def main():
                       "permute": gbs("permute_bytes", "permute"),
                       "combine": gbs("combine_bytes", "combine")},
         "event_ms_per_step": round(total_ev / nbreak, 4),
+        "stage_ms_cold": {s: round(v, 4) for s, v in cold.items()},
+        "stage_gbs_cold": cold_gbs,
+        "stage_hbm_frac_cold": {s: (round(v / PEAK_HBM_GBS, 4) if v else None)
+                                for s, v in cold_gbs.items()},
+        "stage_cold_note": (f"{ncold} further steps, a {COLD_FLUSH_BYTES >> 30} GiB scratch "
+                            "fill before each stage outside its events (L2 and Infinity Cache "
+                            "evicted); algorithmic bytes / event time"),
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
