@@ -164,16 +164,20 @@ __device__ __forceinline__ void ggb_tile(const GGParams& p, int e, int lo, int h
   }
 
   const int nk = (K + kBK - 1) / kBK;
+  // K tiles past the end (the ring's last kStages - 1 issues) load nothing:
+  // an empty descriptor or an out-of-range offset reads zero without a
+  // memory access, and the loads still count for the ring's fixed waits
   auto issue = [&](int kt) {
+    const bool past = kt >= nk;
     const int t = min(kt, nk - 1);
     const int k0 = t * kBK;
-    const int krows = min(kBK, K - k0);
+    const int krows = past ? 0 : min(kBK, K - k0);
     uint16_t* st = s_lds + (kt % kStages) * kStageE;
     if constexpr (kATr) {
       dma16(buf_desc(a_kbase + static_cast<size_t>(k0) * p.lda, krows * p.lda * 2),
             st + wave * 512, vo_a, 0);
     } else {
-      dma16(rs_a, st + wave * 512, (k0 + kcl_a * 8 < K) ? vo_a : kOob, k0 * 2);
+      dma16(rs_a, st + wave * 512, (!past && k0 + kcl_a * 8 < K) ? vo_a : kOob, k0 * 2);
     }
     const i32x4 rb = buf_desc(b_kbase + static_cast<size_t>(k0) * p.ldb, krows * p.ldb * 2);
 #pragma unroll
@@ -230,7 +234,7 @@ __device__ __forceinline__ void ggb_tile(const GGParams& p, int e, int lo, int h
       compute(kt % kStages);
     }
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain the clamped extra loads
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain the ring (the empty tail loads)
 
   // ---------------- epilogue ------------------------------------------------
   // accumulator register r of lane l: A-operand row 8(r / 4) + 4(l / 32) +
