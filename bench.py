@@ -334,6 +334,10 @@ def main():
                           "fc2+row-scale launches on tile-packed weights)")
     roof["algorithmic_flop"] = alg["gemm_flop"]
     roof["algorithmic_bytes"] = alg["gemm_bytes"]
+    # attainable rate on the roofline: min(MFMA peak, arithmetic intensity x HBM peak)
+    attain = min(peak_mfma, alg["gemm_flop"] / alg["gemm_bytes"] * PEAK_HBM_GBS / 1e3)
+    roof["attainable_tflops"] = round(attain, 1)
+    roof["attainable_frac"] = round(gemm_tflops / attain, 4)
     roof["avg_launch_ms"] = round(t_gemm_ms, 4)
     roof["traffic_unit"] = "bytes per call (HBM, counter-measured)"
 
