@@ -515,6 +515,29 @@ def bench_ep_share(args, cfg, dev):
         "fwd_ms": round(t_f, 4), "bwd_ms": round(t_b, 4),
         "fwd_tflops": round(flop_f / t_f / 1e9, 1), "bwd_tflops": round(flop_b / t_b / 1e9, 1),
     }
+    # roofline of the dominant call, the backward (dgrad + fp32 wgrad): its
+    # algorithmic bytes read dY, X_perm, W1, W2 and [G | U] once, write dX,
+    # dW1, dW2 (fp32) once, and write and read back dH [N, 2F] and the
+    # recomputed SwiGLU output [N, F] once each
+    b = 2
+    bytes_b = (2 * N * d * b + 3 * E * d * F * b + N * 2 * F * b + N * d * b + 3 * E * d * F * 4
+               + 2 * N * 2 * F * b + 2 * N * F * b)
+    t_mfma = flop_b / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = bytes_b / (PEAK_HBM_GBS * 1e9)
+    tf_b = flop_b / t_b / 1e9
+    gbs_b = bytes_b / t_b / 1e6
+    attain = min(PEAK_BF16_TFLOPS, flop_b / bytes_b * PEAK_HBM_GBS / 1e3)
+    if t_hbm > t_mfma:
+        roof = {"bound": "hbm", "achieved": round(gbs_b, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs_b / PEAK_HBM_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tf_b, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tf_b / PEAK_BF16_TFLOPS, 4)}
+    roof.update({"traffic": None, "kernel": "moe_grouped_swiglu_bwd (fc2 dgrad + SwiGLU backward, "
+                 "fc1 dgrad, fp32 wgrad of W1 and W2)", "algorithmic_flop": flop_b,
+                 "algorithmic_bytes": bytes_b, "avg_launch_ms": round(t_b, 4),
+                 "attainable_tflops": round(attain, 1), "attainable_frac": round(tf_b / attain, 4)})
+    out["roofline"] = roof
     print(json.dumps(out), flush=True)
 
 
