@@ -105,8 +105,10 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": COPY_CAL_BYTES, "dispatches": 5}), flush=True)
 
 
-def algorithmic(cfg, fp8=False):
-    """Per-call algorithmic work (what the method itself must move or do)."""
+def algorithmic(cfg, fp8=False, fold_shared=False):
+    """Per-call algorithmic work (what the method itself must move or do).
+    With fold_shared the grouped-GEMM call also runs the shared expert (T
+    more rows of ffn Fs, its weights read once, its output written)."""
     T, d, E, k, F = cfg.T, cfg.d, cfg.E, cfg.k, cfg.F
     N = T * k
     b = 2
@@ -122,6 +124,11 @@ def algorithmic(cfg, fp8=False):
         # expert weights read once + token rows read once (fc1 gathers them from x)
         # + A written and read + Y_perm written
         gemm_bytes = 3.0 * E * d * F * b + T * d * b + 2.0 * N * F * b + N * d * b
+    if fold_shared and cfg.Fs:
+        Fs = cfg.Fs
+        w = (1.0 + 1.0 / 32) if fp8 else b
+        gemm_flop += 6.0 * T * d * Fs
+        gemm_bytes += 3.0 * d * Fs * w + 2.0 * T * Fs * w + T * d * b
     route_bytes = T * (2 * d + 8 * k + 4) + E * d * b
     # permute without the row copy: topk_idx, topk_w read; slot_of, row_token, row_w written
     permute_bytes = T * 20 * k
@@ -199,48 +206,18 @@ def main():
     stages = ["route", "permute", "grouped_gemm", "shared", "combine"]
 
     def step(ev=None, gemm_ev=None):
-        # the layer's forward, stage by stage (MoELayer.forward), with events
-        # on the main stream (all stages: ev; the grouped GEMM only: gemm_ev);
-        # the shared expert runs on a second stream
-        L = layer
+        # the layer's forward, stage by stage (MoELayer.stages), with events
+        # on the stream (all stage boundaries: ev; the grouped GEMM only: gemm_ev)
+        for j, (name, fn) in enumerate(layer.stages(x)):
+            if ev is not None:
+                ev[j].record(stream)
+            if gemm_ev is not None and name == "grouped_gemm":
+                gemm_ev[0].record(stream)
+            fn()
+            if gemm_ev is not None and name == "grouped_gemm":
+                gemm_ev[1].record(stream)
         if ev is not None:
-            ev[0].record(stream)
-        if L.overlap_shared:
-            L.ev_x.record(stream)
-            L.side.wait_event(L.ev_x)
-            with torch.cuda.stream(L.side):
-                L._shared_unscaled(x)
-                L.ev_sh.record(L.side)
-        idx, w, cnt, gate = moe.route(x, L.w_router, L.k, L.score, L.normalize, L.logit_bias,
-                                      L.w_gate, out=L.route_out, ws=L.route_ws,
-                                      selection_bias=L.selection_bias)
-        if ev is not None:
-            ev[1].record(stream)
-        # permute folded into fc1: no row copy, fc1 gathers x rows by row_token
-        off, slot, rtok, rw, _ = moe.permute(x, idx, w, L.E, out=L.perm_out, ws=L.perm_ws,
-                                             copy_rows=False)
-        if ev is not None:
-            ev[2].record(stream)
-        if gemm_ev is not None:
-            gemm_ev[0].record(stream)
-        L._routed(x, None, rtok, off, rw)
-        if gemm_ev is not None:
-            gemm_ev[1].record(stream)
-        if ev is not None:
-            ev[3].record(stream)
-        ysh, sgate = None, None
-        if L.ws1 is not None:
-            if L.overlap_shared:
-                stream.wait_event(L.ev_sh)     # "shared" = the part not hidden by the overlap
-                sgate = gate
-            else:                              # gate folded into the shared fc2 row scale
-                L._shared(x, gate, L.ffn_ws)
-            ysh = L.y_shared
-        if ev is not None:
-            ev[4].record(stream)
-        moe.unpermute_combine(L.y_perm, slot, None, ysh, out=L.y, shared_gate=sgate)
-        if ev is not None:
-            ev[5].record(stream)
+            ev[len(stages)].record(stream)
 
     for _ in range(args.warmup):
         step()
@@ -272,37 +249,23 @@ def main():
     per_stage = {s: v / nbreak for s, v in per_stage.items()}  # ms per call
 
     # Cold stages: a 1 GiB scratch fill (larger than L2 and the 256 MB
-    # Infinity Cache) before each stage, outside its event pair; the shared
-    # expert runs in line (untimed), its gate folded into its row scale.
+    # Infinity Cache) before each stage, outside its event pair; a shared
+    # expert's own call (when not folded into the grouped GEMM) runs untimed.
     scratch = torch.empty(COLD_FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
     cold_stages = ["route", "permute", "grouped_gemm", "combine"]
     ncold = 5
     cev = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(ncold)]
     for i in range(ncold):
-        L = layer
-        scratch.fill_(float(i))
-        cev[i][0].record(stream)
-        idx, w, cnt, gate = moe.route(x, L.w_router, L.k, L.score, L.normalize, L.logit_bias,
-                                      L.w_gate, out=L.route_out, ws=L.route_ws,
-                                      selection_bias=L.selection_bias)
-        cev[i][1].record(stream)
-        scratch.fill_(float(i))
-        cev[i][2].record(stream)
-        off, slot, rtok, rw, _ = moe.permute(x, idx, w, L.E, out=L.perm_out, ws=L.perm_ws,
-                                             copy_rows=False)
-        cev[i][3].record(stream)
-        scratch.fill_(float(i))
-        cev[i][4].record(stream)
-        L._routed(x, None, rtok, off, rw)
-        cev[i][5].record(stream)
-        ysh = None
-        if L.ws1 is not None:
-            L._shared(x, gate, L.ffn_ws)
-            ysh = L.y_shared
-        scratch.fill_(float(i))
-        cev[i][6].record(stream)
-        moe.unpermute_combine(L.y_perm, slot, None, ysh, out=L.y)
-        cev[i][7].record(stream)
+        j = 0
+        for name, fn in layer.stages(x):
+            if name in cold_stages:
+                scratch.fill_(float(i))
+                cev[i][2 * j].record(stream)
+                fn()
+                cev[i][2 * j + 1].record(stream)
+                j += 1
+            else:
+                fn()
     torch.cuda.synchronize()
     del scratch
     cold = {s: sum(e[2 * j].elapsed_time(e[2 * j + 1]) for e in cev) / ncold
@@ -310,7 +273,7 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     tokens_per_s = cfg.T / (wall / args.steps)
 
-    alg = algorithmic(cfg, args.fp8)
+    alg = algorithmic(cfg, args.fp8, layer.fold_shared)
     peak_mfma = PEAK_FP8_TFLOPS if args.fp8 else PEAK_BF16_TFLOPS
     t_gemm = t_gemm_ms * 1e-3
     gemm_tflops = alg["gemm_flop"] / t_gemm / 1e12
@@ -332,6 +295,8 @@ def main():
     else:
         roof["kernel"] = ("moe_grouped_swiglu_fwd_packed (persistent fc1 gather+SwiGLU and "
                           "fc2+row-scale launches on tile-packed weights)")
+    if layer.fold_shared:
+        roof["kernel"] += "; the shared expert runs in the same call as group E"
     roof["algorithmic_flop"] = alg["gemm_flop"]
     roof["algorithmic_bytes"] = alg["gemm_bytes"]
     # attainable rate on the roofline: min(MFMA peak, arithmetic intensity x HBM peak)
@@ -365,6 +330,8 @@ def main():
         "config": {"workload": f"{cfg.name}: T={cfg.T} d={cfg.d} E={cfg.E} top-{cfg.k} "
                                f"{cfg.score} ffn={cfg.F}", "T": cfg.T, "d": cfg.d, "E": cfg.E,
                    "k": cfg.k, "F": cfg.F, "Fs": cfg.Fs, "score": cfg.score,
+                   "shared_expert": ("folded into the grouped GEMM" if layer.fold_shared else
+                                     "own grouped call") if cfg.Fs else None,
                    "expert_gemms": ("MXFP8: E4M3 values, E8M0 scale per 32 along K, fp32 "
                                     "accumulation; routing bf16/fp32") if args.fp8 else "bf16"},
         "grouped_gemm_tflops": round(gemm_tflops, 1),

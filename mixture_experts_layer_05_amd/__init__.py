@@ -464,6 +464,14 @@ class MoELayer:
     SwiGLU output for fc2; routing stays in bf16 / fp32.  Inference only,
     with gathered rows; d, F and the shared ffn must be multiples of 32.
 
+    ``fold_shared`` (default: on when it applies) runs a shared expert whose
+    ffn equals the routed experts' as one more group of the routed grouped
+    GEMM (inference, gathered rows, packed or fp8 weights): its T rows (row
+    t gathers x[t], row scale = the gate) follow the N routed rows, so one
+    persistent launch covers both and the shared output is read by the
+    combine from behind Y_perm.  The route writes the gate straight into
+    the row-scale array.
+
     ``overlap_shared`` runs the shared expert, which depends only on x, on a
     second stream (default priority) concurrently with route, permute and
     the routed GEMM; its output stays unscaled and the combine applies the
@@ -477,7 +485,7 @@ class MoELayer:
     def __init__(self, w_router, w1, w2, k, T, score="softmax", normalize=True,
                  logit_bias=None, w_gate=None, ws1=None, ws2=None, save_gu=False,
                  gather=True, train=False, overlap_shared=False, selection_bias=None,
-                 packed=None, fp8=False):
+                 packed=None, fp8=False, fold_shared=None):
         self.train = train
         self.fp8 = fp8
         if fp8:
@@ -541,6 +549,34 @@ class MoELayer:
             self.xq = MxTensor(torch.empty((T, d), dtype=torch.uint8, device=dev),
                                torch.empty(lib().moe_quantize_mx_scales_size(T, d),
                                            dtype=torch.uint8, device=dev), (T, d))
+        can_fold = (ws1 is not None and not train and gather and not self.overlap_shared
+                    and (packed or fp8) and ws1.shape[0] // 2 == self.F and N % 4 == 0)
+        if fold_shared is None:
+            fold_shared = can_fold
+        if fold_shared and not can_fold:
+            raise MoEError("fold_shared needs a shared expert with the routed ffn, inference, "
+                           "gathered rows, packed or fp8 weights, and T*k a multiple of 4")
+        self.fold_shared = bool(fold_shared)
+        if self.fold_shared:
+            # [routed rows | shared rows]: offsets gain group E = [N, N + T), the
+            # shared rows gather x[t] and take the gate (written by the route)
+            # as their row scale; Y_perm's tail is the shared output
+            self.off_ext = torch.empty((E + 2,), dtype=i32, device=dev)
+            self.off_ext[E + 1] = N + T
+            self.rtok_ext = torch.empty((N + T,), dtype=i32, device=dev)
+            self.rtok_ext[N:] = torch.arange(T, dtype=i32, device=dev)
+            self.rw_ext = torch.empty((N + T,), dtype=f32, device=dev)
+            self.y_perm_ext = torch.empty((N + T, d), dtype=dt, device=dev)
+            self.y_perm = self.y_perm_ext[:N]
+            self.y_shared = self.y_perm_ext[N:]
+            if w_gate is not None:
+                self.route_out = self.route_out[:3] + (self.rw_ext[N:],)
+            else:                                # an ungated shared expert: row scale 1
+                self.rw_ext[N:] = 1.0
+            self.perm_out = (self.off_ext[:E + 1], self.perm_out[1], self.rtok_ext[:N],
+                             self.rw_ext[:N], None)
+            ws_f = fwd_mx_workspace_size(N + T, self.F) if fp8 else \
+                fwd_workspace_size(N + T, self.F, dt)
         self.ffn_ws = _ws(ws_f, dev)
         self.y = torch.empty((T, d), dtype=dt, device=dev)
         if train:
@@ -551,16 +587,20 @@ class MoELayer:
     def repack(self):
         """(Re)build the tile-packed (bf16) or MX-quantised (fp8) copies of
         the expert weights."""
+        w1, w2 = self.w1, self.w2
+        if getattr(self, "fold_shared", False):    # the shared expert as group E
+            w1 = torch.cat([self.w1, self.ws1_e])
+            w2 = torch.cat([self.w2, self.ws2_e])
         if self.fp8:
-            self.w1q = pack_weights_mx(self.w1, True)
-            self.w2q = pack_weights_mx(self.w2, False)
-            if self.ws1 is not None:
+            self.w1q = pack_weights_mx(w1, True)
+            self.w2q = pack_weights_mx(w2, False)
+            if self.ws1 is not None and not self.fold_shared:
                 self.ws1q = pack_weights_mx(self.ws1_e, True)
                 self.ws2q = pack_weights_mx(self.ws2_e, False)
             return
-        self.w1p = pack_weights(self.w1, True)
-        self.w2p = pack_weights(self.w2, False)
-        if self.ws1 is not None:
+        self.w1p = pack_weights(w1, True)
+        self.w2p = pack_weights(w2, False)
+        if self.ws1 is not None and not self.fold_shared:
             self.ws1p = pack_weights(self.ws1_e, True)
             self.ws2p = pack_weights(self.ws2_e, False)
 
@@ -602,7 +642,18 @@ class MoELayer:
         self._shared(x, None, self.shared_ws if self.overlap_shared else self.ffn_ws)
 
     def _routed(self, x, xp, rtok, off, rs):
-        """The routed grouped GEMMs (fc1 gathers x rows by rtok when xp is None)."""
+        """The routed grouped GEMMs (fc1 gathers x rows by rtok when xp is None);
+        with fold_shared, the shared expert's rows ride along as group E."""
+        if self.fold_shared:
+            rtok, off, rs, out = self.rtok_ext, self.off_ext, self.rw_ext, self.y_perm_ext
+            if self.fp8:
+                quantize_mx(x, out=self.xq)
+                grouped_swiglu_fwd_mx(self.xq, rtok, self.w1q, self.w2q, off, row_scale=rs,
+                                      out=out, ws=self.ffn_ws)
+            else:
+                grouped_swiglu_fwd_packed(x, rtok, self.w1p, self.w2p, off, row_scale=rs,
+                                          out=out, ws=self.ffn_ws)
+            return
         if self.fp8:
             quantize_mx(x, out=self.xq)
             grouped_swiglu_fwd_mx(self.xq, rtok, self.w1q, self.w2q, off, row_scale=rs,
@@ -620,7 +671,46 @@ class MoELayer:
             grouped_swiglu_fwd(xp, self.w1, self.w2, off, row_scale=rs, out=self.y_perm,
                                gu_out=self.gu, save_gu=self.gu is not None, ws=self.ffn_ws)
 
+    def stages(self, x):
+        """The inference forward (no overlap) as named stages, run in order on
+        the current stream: route, permute, grouped_gemm (routed experts, and
+        a folded shared expert), shared (the shared expert's own call, when
+        not folded), combine.  forward() runs them back to back; a profiler
+        may bracket each."""
+        if self.train or self.overlap_shared:
+            raise MoEError("stages() covers the inference forward without the overlap")
+        st = {}
+
+        def route_():
+            st["r"] = route(x, self.w_router, self.k, self.score, self.normalize,
+                            self.logit_bias, self.w_gate, out=self.route_out, ws=self.route_ws,
+                            selection_bias=self.selection_bias)
+
+        def permute_():
+            idx, w, _, _ = st["r"]
+            st["p"] = permute(x, idx, w, self.E, out=self.perm_out, ws=self.perm_ws,
+                              copy_rows=not self.gather)
+
+        def experts_():
+            off, _, rtok, rw, xp = st["p"]
+            self._routed(x, None if self.gather else xp, rtok, off, rw)
+
+        def shared_():
+            if self.ws1 is not None and not self.fold_shared:
+                self._shared(x, st["r"][3], self.ffn_ws)
+
+        def combine_():
+            ysh = self.y_shared if self.ws1 is not None else None
+            unpermute_combine(self.y_perm, st["p"][1], None, ysh, out=self.y)
+
+        return [("route", route_), ("permute", permute_), ("grouped_gemm", experts_),
+                ("shared", shared_), ("combine", combine_)]
+
     def forward(self, x):
+        if not self.train and not self.overlap_shared:
+            for _, fn in self.stages(x):
+                fn()
+            return self.y
         main = torch.cuda.current_stream()
         if self.overlap_shared:
             self.ev_x.record(main)

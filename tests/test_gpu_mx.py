@@ -449,6 +449,23 @@ def test_layer_fp8(case):
     assert nw <= gh.TOL_BF16 and fro <= TOL_MX_FRO
 
 
+def test_layer_fp8_fold_shared():
+    """fp8 layer with a shared expert of the routed ffn: folded into the routed
+    MX call as group E, bit for bit the layer with its own shared call."""
+    T, d, E, k, F = 300, 128, 9, 3, 96
+    inp = mw.make_small_layer_inputs(11, T=T, d=d, E=E, F=F, dtype="bf16", Fs=F, w_std=0.05)
+    g = lambda a: None if a is None else gh.to_gpu(a)  # noqa: E731
+    args = (g(inp.w_router), g(inp.w1), g(inp.w2), k, T, "softmax", True, None,
+            g(inp.w_gate), g(inp.ws1), g(inp.ws2))
+    lf = moe.MoELayer(*args, fp8=True)
+    lu = moe.MoELayer(*args, fp8=True, fold_shared=False)
+    assert lf.fold_shared and not lu.fold_shared
+    x = g(inp.x)
+    y1, y2 = lf.forward(x).clone(), lu.forward(x).clone()
+    torch.cuda.synchronize()
+    assert gh.bits_equal(y1, y2)
+    assert gh.bits_equal(lf.y_shared, lu.y_shared)
+
 @pytest.mark.parametrize("case", [
     # E, d, F, counts pattern
     (1, 32, 32, "one_row"),          # the smallest shapes: one row, one 32-value block each way

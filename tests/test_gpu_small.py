@@ -138,6 +138,41 @@ def test_layer_packed_matches_unpacked():
     assert gh.bits_equal(y3, y4) and not gh.bits_equal(y1, y3)
 
 
+
+@pytest.mark.parametrize("gated", [True, False])
+def test_layer_fold_shared(gated):
+    """A shared expert whose ffn equals the routed experts' runs as group E of
+    the routed grouped GEMM (the layer's default then): bit for bit the
+    layer with its own shared call, and the oracle's layer to the bf16
+    tolerance (gated); without a gate its rows take row scale 1."""
+    T, k, F = 300, 4, 136
+    inp = mw.make_small_layer_inputs(10, T=T, d=192, E=12, F=F, dtype="bf16", Fs=F, bias=True,
+                                     w_std=0.05)
+    g = lambda a: None if a is None else gh.to_gpu(a)  # noqa: E731
+    wg = g(inp.w_gate) if gated else None
+    args = (g(inp.w_router), g(inp.w1), g(inp.w2), k, T, "softmax", True, g(inp.logit_bias),
+            wg, g(inp.ws1), g(inp.ws2))
+    x = gh.to_gpu(inp.x)
+    lf = moe.MoELayer(*args)
+    lu = moe.MoELayer(*args, fold_shared=False)
+    assert lf.fold_shared and not lu.fold_shared
+    y1, y2 = lf.forward(x).clone(), lu.forward(x).clone()
+    y3 = lf.forward(x).clone()
+    torch.cuda.synchronize()
+    assert gh.bits_equal(y1, y2) and gh.bits_equal(y1, y3)
+    assert gh.bits_equal(lf.y_shared, lu.y_shared)
+    if gated:      # the oracle's shared expert is the gated one
+        f = inp.as_f32
+        idx = lf.route_out[0].cpu().numpy()
+        ref, _, _ = mo.moe_layer_forward(f("x"), f("w_router"), f("w1"), f("w2"), k, "softmax",
+                                         True, inp.logit_bias, f("w_gate"), f("ws1"), f("ws2"),
+                                         topk_idx=idx)
+        assert gh.normwise(gh.to_f64(y1), ref) <= gh.TOL_BF16
+    with pytest.raises(moe.MoEError):   # ffn mismatch: cannot fold
+        moe.MoELayer(g(inp.w_router), g(inp.w1), g(inp.w2), k, T, "softmax", True, None, wg,
+                     g(inp.ws1)[: 2 * 64].contiguous(), g(inp.ws2)[:, :64].contiguous(),
+                     fold_shared=True)
+
 PERM_CASES = [
     # T, d, E, k, dtype, pattern
     (1, 64, 4, 1, "bf16", "random"),
