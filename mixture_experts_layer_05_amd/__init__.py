@@ -466,10 +466,10 @@ class MoELayer:
 
     ``fold_shared`` (default: on when it applies) runs a shared expert whose
     ffn equals the routed experts' as one more group of the routed grouped
-    GEMM (inference, gathered rows, packed or fp8 weights): its T rows (row
-    t gathers x[t], row scale = the gate) follow the N routed rows, so one
-    persistent launch covers both and the shared output is read by the
-    combine from behind Y_perm.  The route writes the gate straight into
+    GEMM (inference without save_gu, gathered rows, packed or fp8 weights):
+    its T rows (row t gathers x[t], row scale = the gate) follow the N
+    routed rows, so one persistent launch covers both and the shared output
+    is read by the combine from behind Y_perm.  The route writes the gate straight into
     the row-scale array.
 
     ``overlap_shared`` runs the shared expert, which depends only on x, on a
@@ -549,13 +549,15 @@ class MoELayer:
             self.xq = MxTensor(torch.empty((T, d), dtype=torch.uint8, device=dev),
                                torch.empty(lib().moe_quantize_mx_scales_size(T, d),
                                            dtype=torch.uint8, device=dev), (T, d))
-        can_fold = (ws1 is not None and not train and gather and not self.overlap_shared
-                    and (packed or fp8) and ws1.shape[0] // 2 == self.F and N % 4 == 0)
+        can_fold = (ws1 is not None and not train and not save_gu and gather
+                    and not self.overlap_shared and (packed or fp8)
+                    and ws1.shape[0] // 2 == self.F and N % 4 == 0)
         if fold_shared is None:
             fold_shared = can_fold
         if fold_shared and not can_fold:
-            raise MoEError("fold_shared needs a shared expert with the routed ffn, inference, "
-                           "gathered rows, packed or fp8 weights, and T*k a multiple of 4")
+            raise MoEError("fold_shared needs a shared expert with the routed ffn, inference "
+                           "without save_gu, gathered rows, packed or fp8 weights, and T*k a "
+                           "multiple of 4")
         self.fold_shared = bool(fold_shared)
         if self.fold_shared:
             # [routed rows | shared rows]: offsets gain group E = [N, N + T), the

@@ -168,6 +168,7 @@ def test_layer_fold_shared(gated):
                                          True, inp.logit_bias, f("w_gate"), f("ws1"), f("ws2"),
                                          topk_idx=idx)
         assert gh.normwise(gh.to_f64(y1), ref) <= gh.TOL_BF16
+    assert not moe.MoELayer(*args, save_gu=True).fold_shared   # G, U kept for the routed rows only
     with pytest.raises(moe.MoEError):   # ffn mismatch: cannot fold
         moe.MoELayer(g(inp.w_router), g(inp.w1), g(inp.w2), k, T, "softmax", True, None, wg,
                      g(inp.ws1)[: 2 * 64].contiguous(), g(inp.ws2)[:, :64].contiguous(),
