@@ -62,6 +62,19 @@ __device__ __forceinline__ Raw8<kBF16> load_raw8(const void* base, size_t chunk)
   }
   return r;
 }
+// the same for data read once (streamed past the caches: non-temporal)
+template <bool kBF16>
+__device__ __forceinline__ Raw8<kBF16> load_raw8_nt(const void* base, size_t chunk) {
+  Raw8<kBF16> r;
+  const u32x4* b = static_cast<const u32x4*>(base);
+  if constexpr (kBF16) {
+    r.c[0] = __builtin_nontemporal_load(b + chunk);
+  } else {
+    r.c[0] = __builtin_nontemporal_load(b + 2 * chunk);
+    r.c[1] = __builtin_nontemporal_load(b + 2 * chunk + 1);
+  }
+  return r;
+}
 template <bool kBF16>
 __device__ __forceinline__ void cvt8(const Raw8<kBF16>& r, float (&v)[8]) {
 #pragma unroll
@@ -149,7 +162,7 @@ __global__ __launch_bounds__(kLbThreads) void combine_bwd_kernel(
         for (int u = 0; u < 4; ++u) {
           const int c = c0 + u * 64 < nchunk ? c0 + u * 64 : c0;
           rg[u] = load_raw8<kBF16>(dy, trow + c);
-          ry[u] = load_raw8<kBF16>(y_perm, rrow + c);
+          ry[u] = load_raw8_nt<kBF16>(y_perm, rrow + c);
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u)
@@ -279,7 +292,7 @@ __global__ __launch_bounds__(kLbThreads) void rbwd_token_kernel(
         const size_t wr = static_cast<size_t>(hw[b] ? ej : 0) * nchunk;
 #pragma unroll
         for (int u = 0; u < kDxChunks; ++u) {
-          if (dx_perm) rx[b][u] = load_raw8<kBF16>(dx_perm, xr + cu[u]);
+          if (dx_perm) rx[b][u] = load_raw8_nt<kBF16>(dx_perm, xr + cu[u]);
           rw[b][u] = load_raw8<kBF16>(w_router, wr + cu[u]);
         }
       }
