@@ -24,7 +24,7 @@ What it computes, step by step, with the passage each step follows:
 * shared expert -- every token passes through it ("Shared Expert Overlap";
   "核心模块架构": shared_experts is optional), scaled by a per-token gate
   (TorchSpec pull request "Add Megatron-Core MTP training for Qwen3.5 MoE",
-  "What's in it": routed experts, shared expert and shared-expert gate);
+  "What's in it": the ported layer has a gate on its shared expert);
 * backward -- the grouped GEMM's dgrad and wgrad ("通信隐藏与混合精度 / TP
   通信重叠" names the backward's dgrad/wgrad GEMMs); the rest of the layer's
   backward runs through the router softmax and the dispatch permute, the

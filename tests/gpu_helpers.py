@@ -97,3 +97,48 @@ def check_routing(gpu_idx: np.ndarray, gpu_w: np.ndarray, ref, k: int):
         err = np.abs(ow[same] - gw[same]).max()
         assert err <= TOL_ROUTE_W, f"routing weights off by {err}"
     return int(excl.sum()), differing
+
+
+class Bf16Experts:
+    """Read-only view of a stacked bf16 weight tensor [E, ...] (uint16 bit
+    patterns) that hands out one expert at a time as float32, so that the
+    oracle's per-expert loops can run at full size without a float copy of
+    every expert at once.  Supports what the oracle uses: ``shape`` and
+    integer indexing."""
+
+    def __init__(self, bits: np.ndarray):
+        self.bits = bits
+        self.shape = bits.shape
+        self.dtype = np.float32
+
+    def __len__(self):
+        return self.shape[0]
+
+    def __getitem__(self, e):
+        if not isinstance(e, (int, np.integer)):
+            raise TypeError("expert index only")
+        b = self.bits[e]
+        return b.astype(np.float32) if b.dtype != np.uint16 else (
+            b.astype(np.uint32) << 16).view(np.float32)
+
+
+def expert_weights_view(inp, name):
+    """The workload's expert tensor as the oracle takes it: float32 arrays
+    unchanged, bf16 bit arrays through Bf16Experts."""
+    a = getattr(inp, name)
+    if a is None or a.dtype != np.uint16:
+        return a
+    return Bf16Experts(a)
+
+
+def normwise_per_expert(a, r, offsets=None):
+    """Largest normwise error over the experts of stacked gradients [E, ...]
+    (experts with no rows, when ``offsets`` is given, must be exactly 0 on
+    both sides and are left out of the maximum)."""
+    worst = 0.0
+    for e in range(r.shape[0]):
+        if offsets is not None and offsets[e + 1] == offsets[e]:
+            assert not np.any(a[e]), f"expert {e} has no rows but a nonzero gradient"
+            continue
+        worst = max(worst, normwise(a[e], r[e]))
+    return worst

@@ -9,9 +9,11 @@ expert-parallel rank's share.
     to be legal near-tie choices);
   * permutation: the GPU's maps equal the oracle's for the GPU's own expert
     choice, bit for bit, and every permuted row is a bitwise copy;
-  * layer output: a seeded sample of tokens recomputed one by one by the
-    oracle (float64) with the GPU's expert choice and the oracle's weights;
-  * backward: dW1, dW2 and dX of sampled experts recomputed by the oracle.
+  * layer output: every token, against the oracle (float64, expert segment
+    by expert segment) run with the GPU's expert choice and the oracle's
+    weights for it;
+  * backward: dX of every slot and dW1, dW2 of every expert, against the
+    oracle over all expert segments (dW: worst expert's normwise error).
 """
 import numpy as np
 import pytest
@@ -79,18 +81,22 @@ def test_layer_forward_full_size(name):
     assert gh.bits_equal(xp[slot[:, 0].long()], x)
     assert gh.bits_equal(y_c, y)
 
-    # ---- layer output on a seeded token sample (forced routing)
-    rng = np.random.default_rng(cfg.index)
-    ns = min(cfg.T, 192)
-    toks = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, ns, replace=False)]))
-    yref, _, _ = mo.moe_layer_forward(f("x")[toks], f("w_router"), f("w1"), f("w2"), cfg.k,
-                                      cfg.score, cfg.normalize, inp.logit_bias, f("w_gate"),
-                                      f("ws1"), f("ws2"), topk_idx=idx[toks])
-    yg = gh.to_f64(y[torch.from_numpy(toks).to(y.device)])
+    # ---- layer output on every token (forced routing): the oracle, float64,
+    # run expert segment by expert segment with the GPU's expert choice
+    yref, _, _ = mo.moe_layer_forward(f("x"), f("w_router"), gh.expert_weights_view(inp, "w1"),
+                                      gh.expert_weights_view(inp, "w2"), cfg.k, cfg.score,
+                                      cfg.normalize, inp.logit_bias, f("w_gate"), f("ws1"),
+                                      f("ws2"), topk_idx=idx)
+    yg = gh.to_f64(y)
     tol = gh.TOL_F32 if cfg.dtype == "f32" else gh.TOL_BF16
     err = gh.normwise(yg, yref)
-    print(f"[{name}] layer output normwise error on {toks.size} sampled tokens: {err:.3e}")
+    # the worst token (the measure is a max over all elements, so a fault
+    # confined to one tile of rows or columns shows in it)
+    row_err = np.abs(yg - yref).max(axis=1) / np.abs(yref).max()
+    print(f"[{name}] layer output normwise error on all {cfg.T} tokens: {err:.3e} "
+          f"(worst token {int(row_err.argmax())}: {row_err.max():.3e})")
     assert err <= tol
+    assert np.isfinite(yg).all()
 
 
 def test_ep_share_forward_backward_full_size():
@@ -106,24 +112,20 @@ def test_ep_share_forward_backward_full_size():
     # the recompute path gives the same bits (same kernels, same G/U rounding)
     assert gh.bits_equal(dx, dx_r) and gh.bits_equal(dw1, dw1_r) and gh.bits_equal(dw2, dw2_r)
     counts = inp.counts
-    order = np.argsort(counts)
-    experts = sorted({int(order[0]), int(order[len(order) // 2]), int(order[-1])})
     print(f"\n[ep_share] rows per expert min/median/max = {counts.min()}/"
-          f"{int(np.median(counts))}/{counts.max()}; checking experts {experts}")
+          f"{int(np.median(counts))}/{counts.max()}; checking all {cfg.E} experts")
     xf = mw.bf16_bits_to_f32(inp.x_perm)
     dyf = mw.bf16_bits_to_f32(inp.dy)
-    for e in experts:
-        lo, hi = int(inp.offsets[e]), int(inp.offsets[e + 1])
-        W1 = mw.bf16_bits_to_f32(inp.w1[e])[None]
-        W2 = mw.bf16_bits_to_f32(inp.w2[e])[None]
-        seg = np.array([0, hi - lo])
-        yr = mo.grouped_swiglu_fwd(xf[lo:hi], W1, W2, seg)
-        dxr, dw1r, dw2r = mo.grouped_swiglu_bwd(dyf[lo:hi], xf[lo:hi], W1, W2, seg)
-        e_y = gh.normwise(gh.to_f64(y[lo:hi]), yr)
-        e_dx = gh.normwise(gh.to_f64(dx[lo:hi]), dxr)
-        e_w1 = gh.normwise(gh.to_f64(dw1[e]), dw1r[0])
-        e_w2 = gh.normwise(gh.to_f64(dw2[e]), dw2r[0])
-        print(f"[ep_share] expert {e} ({hi - lo} rows): y {e_y:.2e} dx {e_dx:.2e} "
-              f"dw1 {e_w1:.2e} dw2 {e_w2:.2e}")
-        assert e_y <= gh.TOL_BF16
-        assert max(e_dx, e_w1, e_w2) <= gh.TOL_BF16_GRAD
+    w1v, w2v = gh.expert_weights_view(inp, "w1"), gh.expert_weights_view(inp, "w2")
+    # the oracle (float64) over every expert segment
+    yr = mo.grouped_swiglu_fwd(xf, w1v, w2v, inp.offsets)
+    dxr, dw1r, dw2r = mo.grouped_swiglu_bwd(dyf, xf, w1v, w2v, inp.offsets)
+    e_y = gh.normwise(gh.to_f64(y), yr)
+    e_dx = gh.normwise(gh.to_f64(dx), dxr)
+    dw1g, dw2g = dw1.cpu().numpy(), dw2.cpu().numpy()
+    e_w1 = gh.normwise_per_expert(dw1g, dw1r, inp.offsets)
+    e_w2 = gh.normwise_per_expert(dw2g, dw2r, inp.offsets)
+    print(f"[ep_share] all experts: y {e_y:.2e} dx {e_dx:.2e} dw1 (worst expert) {e_w1:.2e} "
+          f"dw2 (worst expert) {e_w2:.2e}")
+    assert e_y <= gh.TOL_BF16
+    assert max(e_dx, e_w1, e_w2) <= gh.TOL_BF16_GRAD

@@ -6,8 +6,9 @@ What pins it (none of these retypes the oracle's own formula):
   * special cases that reduce to library routines (k = E gives
     scipy.special.softmax / expit renormalised; k = 1 gives weight 1);
   * planted orders (unit-vector tokens with a hand-set router);
-  * the planted near-tie of the TorchSpec MTP pull request's parity result
-    (8th and 9th router logits 1.9e-6 apart) must be flagged as excluded;
+  * a planted near-tie like the one the TorchSpec MTP pull request reports
+    in its "Results" (a token whose 8th- and 9th-ranked logits differ by
+    about two millionths) must be flagged as excluded;
   * the weight-sum invariant in fp32 mode.
 """
 import json
@@ -109,7 +110,7 @@ def test_planted_order_unit_vector_tokens():
 
 def test_planted_near_tie_is_excluded_and_counted():
     # A top-8 near-tie like the one reported in the TorchSpec MTP pull
-    # request's HF-parity result: 8th and 9th logits 1.9e-6 apart.
+    # request's parity note: ranks 8 and 9 of one token separated by 1.9e-6.
     E, k = 16, 8
     z = np.linspace(3.0, -3.0, E)
     z[8] = z[7] - 1.9e-6
