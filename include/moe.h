@@ -150,6 +150,30 @@ MOE_API moe_status moe_permute(hipStream_t stream, moe_dtype dt, int64_t T, int6
                        void* ws, size_t ws_bytes);
 
 /* ------------------------------------------------------------------------
+ * moe_permute_noalloc -- moe_permute without a caller workspace.
+ *
+ * For callers that cannot allocate device memory around the call (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, outputs and results as moe_permute, minus ws / ws_bytes:
+ * the scratch (per-block expert histograms and per-expert totals) lives in a
+ * static device array of 4 MiB inside the library, one per GPU, held until
+ * the process ends.  Nothing is allocated or freed by the call.
+ *   Limit: moe_permute_workspace_size(T, E, k) <= 4 MiB (e.g. T*k/floor(256/k)
+ *   blocks of E counts: T = 16384, k = 8, E = 256 needs 0.5 MiB); larger
+ *   shapes return MOE_ERR_WORKSPACE.  MOE_ERR_HIP if the array's device
+ *   address cannot be obtained.
+ *   Concurrency: every call on one GPU uses the same array; calls that
+ *   overlap in time on one GPU (two streams, two threads) race and must be
+ *   serialised by the caller.  No part of the array needs to start at zero:
+ *   each call writes what it reads.
+ * --------------------------------------------------------------------- */
+MOE_API moe_status moe_permute_noalloc(hipStream_t stream, moe_dtype dt, int64_t T, int64_t d,
+                               int32_t E, int32_t k, const void* x,
+                               const int32_t* topk_idx, const float* topk_w,
+                               int32_t* expert_offsets, int32_t* slot_of,
+                               int32_t* row_token, float* row_w, void* x_perm);
+
+/* ------------------------------------------------------------------------
  * moe_grouped_swiglu_fwd -- every expert's SwiGLU FFN in one grouped GEMM.
  *
  * Passages: "Megatron-Bridge 深度剖析", "Grouped GEMM" (all experts' GEMMs

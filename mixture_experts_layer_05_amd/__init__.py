@@ -19,7 +19,7 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "MoEError", "lib", "route", "permute", "grouped_swiglu_fwd", "grouped_swiglu_fwd_gather",
+    "MoEError", "lib", "route", "permute", "permute_noalloc", "grouped_swiglu_fwd", "grouped_swiglu_fwd_gather",
     "PackedWeights", "pack_weights", "grouped_swiglu_fwd_packed",
     "MxTensor", "quantize_mx", "pack_weights_mx", "grouped_swiglu_fwd_mx",
     "grouped_swiglu_bwd", "unpermute_combine", "combine_backward", "route_backward",
@@ -45,6 +45,8 @@ EXPORTED = {
     "moe_route": (_i32, [_vp, _i32, _i64, _i64, _i32, _i32, _i32, _i32,
                          _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz]),
     "moe_permute_workspace_size": (_sz, [_i64, _i32, _i32]),
+    "moe_permute_noalloc": (_i32, [_vp, _i32, _i64, _i64, _i32, _i32, _vp, _vp, _vp,
+                                   _vp, _vp, _vp, _vp, _vp]),
     "moe_permute": (_i32, [_vp, _i32, _i64, _i64, _i32, _i32, _vp, _vp, _vp,
                            _vp, _vp, _vp, _vp, _vp, _vp, _sz]),
     "moe_grouped_swiglu_fwd_workspace_size": (_sz, [_i64, _i64, _i32]),
@@ -186,6 +188,29 @@ def permute(x, topk_idx, topk_w, E, out=None, ws=None, copy_rows=True):
     _check(lib().moe_permute(_stream(), _dt(x), T, d, E, k, _p(x), _p(topk_idx), _p(topk_w),
                              _p(off), _p(slot), _p(rtok), _p(rw), _p(xp), _p(ws), ws.numel()),
            "moe_permute")
+    return off, slot, rtok, rw, xp
+
+
+def permute_noalloc(x, topk_idx, topk_w, E, out=None, copy_rows=True):
+    """moe_permute_noalloc: permute() with the library's static scratch
+    instead of a workspace (for callers that cannot allocate around the call;
+    calls overlapping on one GPU race)."""
+    T, d = x.shape
+    k = topk_idx.shape[1]
+    N = T * k
+    dev = x.device
+    if out is None:
+        out = (torch.empty((E + 1,), dtype=torch.int32, device=dev),
+               torch.empty((T, k), dtype=torch.int32, device=dev),
+               torch.empty((N,), dtype=torch.int32, device=dev),
+               torch.empty((N,), dtype=torch.float32, device=dev) if topk_w is not None else None,
+               torch.empty((N, d), dtype=x.dtype, device=dev) if copy_rows else None)
+    off, slot, rtok, rw, xp = out
+    if not copy_rows:
+        xp = None
+    _check(lib().moe_permute_noalloc(_stream(), _dt(x), T, d, E, k, _p(x), _p(topk_idx),
+                                     _p(topk_w), _p(off), _p(slot), _p(rtok), _p(rw), _p(xp)),
+           "moe_permute_noalloc")
     return off, slot, rtok, rw, xp
 
 

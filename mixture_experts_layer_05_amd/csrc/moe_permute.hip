@@ -17,6 +17,8 @@
 //                ranks its pairs, writes slot_of / row_token / row_w
 //   K4 copy    : one wavefront per token reads x[t] once (16-byte lanes)
 //                and writes it to its k rows
+#include <mutex>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -165,6 +167,29 @@ __global__ __launch_bounds__(kPermThreads) void perm_copy_kernel(
   }
 }
 
+// Scratch of moe_permute_noalloc: the per-block expert histograms and the
+// per-expert totals of moe_permute, in a file-scope device array (each GPU
+// the library runs on holds one copy until the process ends).
+constexpr size_t kPermScratchInts = size_t(1) << 20;          // 4 MiB
+static __device__ __align__(256) int32_t scratch[kPermScratchInts];
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current); NULL if the lookup fails.  In host code
+// the array's name is only a host-side stand-in for the symbol: kernels,
+// copies and memsets must be given this address instead.
+static void* perm_scratch_ptr() {
+  constexpr int kMaxDev = 64;
+  static std::once_flag once[kMaxDev];
+  static void* ptr[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return nullptr;
+  std::call_once(once[dev], [dev] {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess) ptr[dev] = p;
+  });
+  return ptr[dev];
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -214,4 +239,20 @@ extern "C" moe_status moe_permute(hipStream_t stream, moe_dtype dt, int64_t T, i
                  0, stream, (int)T, k, static_cast<int>(row_bytes / 16), slot_of,
                  static_cast<const u32x4*>(x), static_cast<u32x4*>(x_perm));
   return hip_status(err);
+}
+
+extern "C" moe_status moe_permute_noalloc(hipStream_t stream, moe_dtype dt, int64_t T, int64_t d,
+                                          int32_t E, int32_t k, const void* x,
+                                          const int32_t* topk_idx, const float* topk_w,
+                                          int32_t* expert_offsets, int32_t* slot_of,
+                                          int32_t* row_token, float* row_w, void* x_perm) {
+  // the shape checks of moe_permute come first (its size function returns 0
+  // for shapes it rejects)
+  if (T < 1 || E < 1 || E > 1024 || k < 1 || k > 32) return MOE_ERR_SHAPE;
+  if (moe_permute_workspace_size(T, E, k) > kPermScratchInts * sizeof(int32_t))
+    return MOE_ERR_WORKSPACE;   // more scratch than the static array holds
+  void* ws = perm_scratch_ptr();
+  if (!ws) return MOE_ERR_HIP;
+  return moe_permute(stream, dt, T, d, E, k, x, topk_idx, topk_w, expert_offsets, slot_of,
+                     row_token, row_w, x_perm, ws, kPermScratchInts * sizeof(int32_t));
 }

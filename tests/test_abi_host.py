@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.moe_abi_version() == 7
+    assert L.moe_abi_version() == 8
     assert L.moe_status_string(0) == b"MOE_OK"
     assert L.moe_status_string(5) == b"MOE_ERR_WORKSPACE"
 
@@ -103,6 +103,14 @@ def test_permute_validation(L):
     assert f(None, 1, 16, 64, 8, 2, P, P, None, P, P, P, P, P, P, 1 << 20) == 1  # row_w w/o topk_w
     assert f(None, 1, 16, 60, 8, 2, P, P, P, P, P, P, P, P, P, 1 << 20) == 4     # 120 B rows
     assert f(None, 1, 16, 64, 0, 2, P, P, P, P, P, P, P, P, P, 1 << 20) == 2
+
+
+def test_permute_noalloc_limit(L):
+    # 2048 blocks x 1024 experts of int32 histograms: 8 MiB > the 4 MiB static
+    # scratch -> MOE_ERR_WORKSPACE before anything is launched
+    f = L.moe_permute_noalloc
+    assert f(None, 1, 65536, 64, 1024, 8, P, P, P, P, P, P, P, P) == 5
+    assert f(None, 1, 16, 64, 0, 2, P, P, P, P, P, P, P, P) == 2
 
 
 def test_grouped_validation(L):
