@@ -41,7 +41,7 @@ COLD_FLUSH_BYTES = 1 << 30        # scratch written before each cold stage (> L2
 # `rocprofv3 --pmc FETCH_SIZE` and `--pmc WRITE_SIZE` runs of this script,
 # each counter scaled by what it reads for a 1 GiB device copy
 # (--copy-calibration: FETCH_SIZE x 2.0, WRITE_SIZE x 1.0); summary in
-# profiles/grouped_gemm_fwd_qwen3_30b_hbm_bytes.md.  Valid only for the
+# profiles/grouped_gemm_fwd_<workload>_hbm_bytes.md.  Valid only for the
 # kernel sources the counters were taken on (sha256 over KERNEL_SOURCES):
 # reported as null once they change.
 KERNEL_SOURCES = ("mixture_experts_layer_05_amd/csrc/moe_grouped_fwd.hip",
@@ -55,6 +55,9 @@ KERNEL_SOURCES_FP8 = ("mixture_experts_layer_05_amd/csrc/moe_grouped_mx.hip",
 MEASURED_TRAFFIC = {
     "qwen3_30b": {"bytes": 1628074639,
                   "sources_sha256": "9ac5b346b3d4a16b0f90cb449fd61534b9ca9b89e45db3f95bbd6768c665d72a"},
+    # profiles/grouped_gemm_fwd_dsv_30b_hbm_bytes.md
+    "dsv_30b": {"bytes": 5297109980,
+                "sources_sha256": "9ac5b346b3d4a16b0f90cb449fd61534b9ca9b89e45db3f95bbd6768c665d72a"},
     "qwen3_30b:fp8": {"bytes": 968175082,
                       "sources_sha256": "fd3ccfc338831cb541c75dc991b9f4c50b4c92e76e3ee9485ef1455f23544ccd"},
 }
@@ -151,16 +154,20 @@ def _blas_threads():
     return int(threads)
 
 
-def _median_time(fn, reps=3, single_if_over=30.0):
-    """Median wall time of `reps` calls (one call when the first exceeds
-    `single_if_over` seconds); returns (seconds, last result)."""
+def _median_time(fn, min_total=6.0, max_reps=15, single_if_over=30.0):
+    """Median wall time of repeated calls: at least 3, and as many more (up to
+    `max_reps`) as fill about `min_total` seconds; one call when the first
+    exceeds `single_if_over` seconds.  Returns (seconds, last result)."""
     ts, out = [], None
-    for _ in range(reps):
-        t0 = time.perf_counter()
-        out = fn()
-        ts.append(time.perf_counter() - t0)
-        if ts[0] > single_if_over:
-            break
+    t0 = time.perf_counter()
+    out = fn()
+    ts.append(time.perf_counter() - t0)
+    if ts[0] <= single_if_over:
+        reps = min(max_reps, max(3, int(min_total / max(ts[0], 1e-6))))
+        for _ in range(reps - 1):
+            t0 = time.perf_counter()
+            out = fn()
+            ts.append(time.perf_counter() - t0)
     ts.sort()
     return ts[len(ts) // 2], out
 
@@ -169,8 +176,9 @@ def cpu_baseline(inp, cfg, ntok):
     """The oracle as it stands, in float32 (numpy; BLAS threads = the host's
     cores), stage by stage on the first `ntok` tokens of the batch: route,
     permute, expert FFN (all experts the tokens chose), shared expert,
-    combine.  Each stage is the median of 3 runs; the float32 copies of the
-    bf16 inputs are made before the clock starts."""
+    combine.  Each stage is the median of 3 to 15 runs (about 6 s of work per
+    stage at most); the float32 copies of the bf16 inputs are made before the
+    clock starts."""
     import numpy as np
     from oracle import moe_oracle as mo
     f = inp.as_f32
@@ -194,7 +202,7 @@ def cpu_baseline(inp, cfg, ntok):
     return {"value": round(ntok / total, 1), "unit": "tokens/s", "cores": _blas_threads(),
             "kind": "oracle",
             "sample": f"first {ntok} of {cfg.T} tokens of the {cfg.name} batch, all {cfg.E} "
-                      f"experts, float32 oracle forward stage by stage (median of 3 runs each)",
+                      f"experts, float32 oracle forward stage by stage (median of 3-15 runs each)",
             "stage_s": {kk: round(v, 4) for kk, v in st.items()}}
 
 
@@ -217,7 +225,7 @@ def cpu_baseline_ep_share(inp, cfg):
     return {"value": round(flop / sum(st.values()) / 1e12, 4), "unit": "TFLOP/s",
             "cores": _blas_threads(), "kind": "oracle",
             "sample": f"all {cfg.N} token-slots and {cfg.E} experts of the {cfg.name} batch, "
-                      "float32 oracle grouped forward + backward (median of 3 runs each)",
+                      "float32 oracle grouped forward + backward (median of 3-15 runs each)",
             "stage_s": {kk: round(v, 4) for kk, v in st.items()}}
 
 
