@@ -435,13 +435,18 @@ MOE_API moe_status moe_combine_backward(hipStream_t stream, moe_dtype dt, int64_
  *     sigmoid, normalised:  dz[t,e_j] = (d_topk_w[t,j] - c[t]) / S[t] s (1 - s)
  *     sigmoid:              dz[t,e_j] = d_topk_w[t,j] s (1 - s)
  * (s = sigmoid(z[t,e_j]) recomputed in fp32, S[t] = sum_j s); dz = 0 off
- * the selection.  Shared gate g = sigmoid(x . w_gate): dgl = d_gate g (1-g).
- *     dx[t]        = sum_j dx_perm[slot_of[t,j]] + sum_j dz[t,e_j] W_r[e_j]
+ * the selection.  Softmax without normalisation (w[t,j] = p[t,e_j], p the
+ * softmax over all E experts, recomputed in fp32) has a dense dz:
+ *     softmax:              dz[t,e]   = p[t,e] (ds[t,e] - c[t])
+ * with ds[t,e_j] = d_topk_w[t,j] and ds = 0 off the selection.
+ * Shared gate g = sigmoid(x . w_gate): dgl = d_gate g (1-g).
+ *     dx[t]        = sum_j dx_perm[slot_of[t,j]] + sum_e dz[t,e] W_r[e]
  *                    + dgl[t] w_gate + dx_add[t]          (rounded once)
- *     dw_router[e] (+)= sum over expert e's rows r of dz[r] x[row_token[r]]
+ *     dw_router[e] (+)= sum_t dz[t,e] x[t]  (sparse dz: over expert e's rows
+ *                       r, dz[r] x[row_token[r]])
  *     dw_gate      (+)= sum_t dgl[t] x[t]
- * All sums fp32 in a fixed order.  Softmax without normalisation (a dense
- * dz) returns MOE_ERR_UNSUPPORTED.
+ * All sums fp32 in a fixed order.  The dense case also needs T*E < 2^31 and
+ * T*d < 2^31 (else MOE_ERR_SHAPE).
  *
  *   x [T, d], w_router [E, d], w_gate [d] or NULL: dt, as in the forward
  *   logit_bias [E] fp32 or NULL
@@ -452,10 +457,14 @@ MOE_API moe_status moe_combine_backward(hipStream_t stream, moe_dtype dt, int64_
  *   dx_add  [T, d] dt or NULL (added to dx, e.g. the shared expert's dx)
  *   dx [T, d] dt out;  dw_router [E, d] fp32;  dw_gate [d] fp32 (with w_gate)
  *   accumulate int32: 0 dw = grad, 1 dw += grad (dx is always written)
- * Workspace: moe_route_backward_workspace_size(T, d, k) bytes.
+ * Workspace: moe_route_backward_workspace_size(T, d, E, k, dt, fn,
+ * normalize) bytes (0 for invalid sizes or dtype); the dense case holds the
+ * fp32 logits, dz [T, E] and its dx term [T, d] there.
  * Limits: 1 <= k <= min(E, 32), E <= 1024, d % 8 == 0.
  * --------------------------------------------------------------------- */
-MOE_API size_t moe_route_backward_workspace_size(int64_t T, int64_t d, int32_t k);
+MOE_API size_t moe_route_backward_workspace_size(int64_t T, int64_t d, int32_t E, int32_t k,
+                                                 moe_dtype dt, moe_score_fn fn,
+                                                 int32_t normalize);
 MOE_API moe_status moe_route_backward(hipStream_t stream, moe_dtype dt, int64_t T, int64_t d,
                               int32_t E, int32_t k, moe_score_fn fn, int32_t normalize,
                               const void* x, const void* w_router, const float* logit_bias,

@@ -73,7 +73,7 @@ EXPORTED = {
                                      _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_combine_backward": (_i32, [_vp, _i32, _i64, _i64, _i32, _i64,
                                     _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
-    "moe_route_backward_workspace_size": (_sz, [_i64, _i64, _i32]),
+    "moe_route_backward_workspace_size": (_sz, [_i64, _i64, _i32, _i32, _i32, _i32, _i32]),
     "moe_route_backward": (_i32, [_vp, _i32, _i64, _i64, _i32, _i32, _i32, _i32,
                                   _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                   _vp, _vp, _vp, _vp, _vp, _i32, _vp, _sz]),
@@ -434,8 +434,11 @@ def combine_backward(dy, y_perm, slot_of, topk_w, y_shared=None, dy_perm=None, d
     return dy_perm, d_topk_w, d_gate if y_shared is not None else None
 
 
-def route_backward_workspace_size(T, d, k):
-    return lib().moe_route_backward_workspace_size(T, d, k)
+def route_backward_workspace_size(T, d, E, k, dtype, score="softmax", normalize=True):
+    """Workspace bytes of route_backward; dtype is the activations' torch dtype."""
+    dt = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}[dtype]
+    return lib().moe_route_backward_workspace_size(T, d, E, k, dt, SCORE[score],
+                                                   int(bool(normalize)))
 
 
 def route_backward(x, w_router, topk_idx, topk_w, d_topk_w, expert_offsets, slot_of, row_token,
@@ -454,7 +457,7 @@ def route_backward(x, w_router, topk_idx, topk_w, d_topk_w, expert_offsets, slot
     if w_gate is not None and dw_gate is None:
         dw_gate = torch.zeros((d,), dtype=torch.float32, device=dev)
     if ws is None:
-        ws = _ws(route_backward_workspace_size(T, d, k), dev)
+        ws = _ws(route_backward_workspace_size(T, d, E, k, x.dtype, score, normalize), dev)
     _check(lib().moe_route_backward(_stream(), _dt(x), T, d, E, k, SCORE[score], int(bool(normalize)),
                                     _p(x), _p(w_router), _p(logit_bias), _p(w_gate), _p(topk_idx),
                                     _p(topk_w), _p(d_topk_w), _p(d_gate), _p(expert_offsets),
@@ -651,7 +654,8 @@ class MoELayer:
             self.dws2 = torch.zeros((1, d, Fs), dtype=f32, device=dev)
             self.dw_gate = torch.zeros((d,), dtype=f32, device=dev)
         self.bwd_ws = _ws(bwd_ws, dev)
-        self.rbwd_ws = _ws(route_backward_workspace_size(T, d, k), dev)
+        self.rbwd_ws = _ws(route_backward_workspace_size(T, d, E, k, dt, self.score,
+                                                          self.normalize), dev)
 
     def _shared(self, x, scale, ws):
         if self.fp8:       # x quantised by _routed earlier in the forward

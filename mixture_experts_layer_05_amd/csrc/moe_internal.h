@@ -50,4 +50,11 @@ int device_cu_count();
 
 inline size_t elt_size(moe_dtype dt) { return dt == MOE_BF16 ? 2 : 4; }
 
+// Router logits z[s][T][E] (fp32; s < route_logit_slabs K slabs whose sum is
+// the logit, the bias in slab 0), as moe_route computes them.
+int route_logit_slabs(moe_dtype dt, int64_t T, int64_t d, int32_t E);
+hipError_t launch_route_logits(hipStream_t stream, moe_dtype dt, int64_t T, int64_t d, int32_t E,
+                               const void* x, const void* w_router, const float* logit_bias,
+                               float* z);
+
 }  // namespace moe

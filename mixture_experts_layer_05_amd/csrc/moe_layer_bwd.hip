@@ -12,8 +12,10 @@
 //            dgate[t] = <dy[t], Ysh[t]>
 //   permute  dx[t] += sum_j dX[s(t,j)]
 //   router   w = normalise(score(z)) on the selection; dz is non-zero on the
-//            selected experts only (see rbwd_token_kernel);
-//            dx[t] += sum_j dz[t,j] W_r[e_j];  dW_r[e] = sum_{t: e chosen} dz x[t]
+//            selected experts only (see rbwd_token_kernel), except for
+//            softmax scores without renormalisation, where it is dense
+//            (rbwd_dense_dz_kernel);
+//            dx[t] += sum_e dz[t,e] W_r[e];  dW_r[e] = sum_t dz[t,e] x[t]
 //   gate     g = sigmoid(x . w_gate): dgl = dgate g (1 - g);
 //            dx[t] += dgl[t] w_gate;  dw_gate = sum_t dgl[t] x[t]
 // All sums run in fp32 in a fixed order (deterministic, no atomics); every
@@ -198,7 +200,8 @@ __global__ __launch_bounds__(kLbThreads) void combine_bwd_kernel(
 //                         (the full-softmax denominator cancels in w);
 //   sigmoid, normalised:  dz[e_j] = (dw_j - c) / S * s_j (1 - s_j);
 //   sigmoid:              dz[e_j] = dw_j s_j (1 - s_j).
-// (Softmax without renormalisation has a dense dz; the entry point rejects it.)
+// (Softmax without renormalisation has a dense dz: rbwd_dense_dz_kernel forms
+// it, two GEMMs give its dx term and dW_r, and this kernel adds the dx term.)
 // The sigmoid forms need s_j = sigmoid(z_j): z_j = x[t] . W_r[e_j] (+ b) is
 // recomputed here in fp32.
 // ---------------------------------------------------------------------------
@@ -214,7 +217,7 @@ __global__ __launch_bounds__(kLbThreads) void rbwd_token_kernel(
     const float* __restrict__ d_topk_w, const float* __restrict__ d_gate,
     const int32_t* __restrict__ slot_of, const void* __restrict__ dx_perm,
     const void* __restrict__ dx_add, void* __restrict__ dx, float* __restrict__ dz_slot,
-    float* __restrict__ dgl_tok) {
+    float* __restrict__ dgl_tok, const float* __restrict__ dx_dense) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (kLbThreads / 64) + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -287,7 +290,7 @@ __global__ __launch_bounds__(kLbThreads) void rbwd_token_kernel(
         const int ej = __shfl(e, j0 + b, kWave);
         dzj[b] = __shfl(dz, j0 + b, kWave);
         hx[b] = dx_perm && rj >= 0;
-        hw[b] = ej >= 0 && dzj[b] != 0.0f;
+        hw[b] = ej >= 0 && dzj[b] != 0.0f && !dx_dense;   // dense: in dx_dense
         const size_t xr = static_cast<size_t>(hx[b] ? rj : 0) * nchunk;
         const size_t wr = static_cast<size_t>(hw[b] ? ej : 0) * nchunk;
 #pragma unroll
@@ -329,7 +332,149 @@ __global__ __launch_bounds__(kLbThreads) void rbwd_token_kernel(
 #pragma unroll
         for (int q = 0; q < 8; ++q) acc[u][q] += v[q];
       }
+      if (dx_dense) {                             // sum_e dz[t,e] W_r[e] (fp32 rows)
+        float v[8];
+        load8<false>(dx_dense, trow + cc, v);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[u][q] += v[q];
+      }
       store8<kBF16>(dx, trow + cc, acc[u]);
+    }
+  }
+}
+
+// Dense logit gradient of softmax scores without renormalisation (the
+// weights are the scores of the chosen experts, w_j = p[e_j]):
+//     dz[t,e] = p[t,e] (ds[t,e] - c[t]),   c[t] = sum_j d_topk_w[t,j] p[t,e_j],
+// ds = d_topk_w on the selection and 0 elsewhere; p = softmax(z[t,:]) from the
+// recomputed fp32 logits (K slabs summed in slab order), max-subtracted as
+// in the forward.  One wavefront per token; lane l holds experts l + 64 i.
+template <int kPer>
+__global__ __launch_bounds__(kLbThreads) void rbwd_dense_dz_kernel(
+    int T, int E, int k, int nslab, const float* __restrict__ z, const int32_t* __restrict__ topk_idx,
+    const float* __restrict__ d_topk_w, float* __restrict__ dz) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kLbThreads / 64) + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const size_t slab = static_cast<size_t>(T) * E;
+  float p[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = lane + 64 * i;
+    float v = 0.0f;
+    for (int s = 0; s < nslab; ++s) v += e < E ? z[s * slab + static_cast<size_t>(t) * E + e] : 0.0f;
+    p[i] = v;
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    if (lane + 64 * i < E) m = fmaxf(m, p[i]);
+  m = wave_max_dpp(m);
+  float sum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    p[i] = (lane + 64 * i < E) ? expf(p[i] - m) : 0.0f;
+    sum += p[i];
+  }
+  sum = wave_sum_dpp(sum);
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) p[i] = (lane + 64 * i < E) ? p[i] / sum : 0.0f;
+  // choices: lane j < k holds (e_j, dw_j)
+  int ej = -1;
+  float dwj = 0.0f;
+  if (lane < k) {
+    ej = topk_idx[static_cast<size_t>(t) * k + lane];
+    dwj = d_topk_w[static_cast<size_t>(t) * k + lane];
+    if (ej < 0 || ej >= E) ej = -1;
+  }
+  // c = sum_j dw_j p[e_j] in choice order; ds of this lane's experts
+  float c = 0.0f;
+  float ds[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) ds[i] = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    const int e = __shfl(ej, j, kWave);
+    const float dw = __shfl(dwj, j, kWave);
+    if (e < 0) continue;                          // uniform: every lane reads the same e
+    float pe = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      if (i == (e >> 6)) pe = p[i];
+    pe = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pe), e & 63));
+    c += dw * pe;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      if (lane + 64 * i == e) ds[i] = dw;
+  }
+  float* row = dz + static_cast<size_t>(t) * E;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = lane + 64 * i;
+    if (e < E) row[e] = p[i] * (ds[i] - c);
+  }
+}
+
+// C[M, N] (+)= sum_k A(m, k) B(k, n) in fp32, k ascending (a fixed order):
+// A fp32 at A[m sam + k sak], B of the activation type, row-major with row
+// stride ldb, C fp32 row-major with row stride ldc.  64 x 64 tiles, 16-wide
+// K steps through LDS, 4 x 4 outputs per thread.  The dense router
+// gradient's two products: dx_dense = dz W_r and dW_r = dz^T x.
+constexpr int kRgM = 64, kRgN = 64, kRgK = 16;
+template <bool kBF16>
+__global__ __launch_bounds__(256) void rbwd_gemm_kernel(int M, int N, int K,
+                                                        const float* __restrict__ A, int64_t sam,
+                                                        int64_t sak, const void* __restrict__ B,
+                                                        int64_t ldb, float* __restrict__ C,
+                                                        int64_t ldc, int accumulate) {
+  __shared__ float As[kRgK][kRgM + 4];
+  __shared__ float Bs[kRgK][kRgN + 4];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int m0 = blockIdx.y * kRgM, n0 = blockIdx.x * kRgN;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += kRgK) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + 256 * i;              // 64 x 16 values; m fastest when A is m-contiguous
+      const int mm = sam == 1 ? idx % kRgM : idx / kRgK;
+      const int kk = sam == 1 ? idx / kRgM : idx % kRgK;
+      const int m = m0 + mm, kq = k0 + kk;
+      As[kk][mm] = (m < M && kq < K) ? A[m * sam + kq * sak] : 0.0f;
+      const int nn = idx % kRgN, kb = idx / kRgN; // n fastest
+      const int n = n0 + nn, kr = k0 + kb;
+      float bv = 0.0f;
+      if (n < N && kr < K) {
+        if constexpr (kBF16)
+          bv = bf16_to_f32(static_cast<const uint16_t*>(B)[kr * ldb + n]);
+        else
+          bv = static_cast<const float*>(B)[kr * ldb + n];
+      }
+      Bs[kb][nn] = bv;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kRgK; ++kk) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) av[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bv[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + ty * 4 + i;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + tx * 4 + j;
+      if (n >= N) continue;
+      float* c = C + m * ldc + n;
+      *c = accumulate ? *c + acc[i][j] : acc[i][j];
     }
   }
 }
@@ -472,12 +617,23 @@ extern "C" moe_status moe_combine_backward(hipStream_t stream, moe_dtype dt, int
                            y_shared, dy_perm, d_topk_w, d_gate));
 }
 
-extern "C" size_t moe_route_backward_workspace_size(int64_t T, int64_t d, int32_t k) {
-  if (T < 1 || d < 1 || k < 1) return 0;
+static bool rbwd_dense(moe_score_fn fn, int32_t normalize) {
+  return fn == MOE_SCORE_SOFTMAX && !normalize;
+}
+
+extern "C" size_t moe_route_backward_workspace_size(int64_t T, int64_t d, int32_t E, int32_t k,
+                                                    moe_dtype dt, moe_score_fn fn,
+                                                    int32_t normalize) {
+  if (T < 1 || d < 1 || E < 1 || k < 1 || (dt != MOE_F32 && dt != MOE_BF16)) return 0;
   const int64_t nblk = (T + kGateRows - 1) / kGateRows;
-  return align256(static_cast<size_t>(T) * k * sizeof(float)) +
-         align256(static_cast<size_t>(T) * sizeof(float)) +
-         align256(static_cast<size_t>(nblk) * d * sizeof(float));
+  size_t b = align256(static_cast<size_t>(T) * k * sizeof(float)) +
+             align256(static_cast<size_t>(T) * sizeof(float)) +
+             align256(static_cast<size_t>(nblk) * d * sizeof(float));
+  if (rbwd_dense(fn, normalize))   // logit slabs, dense dz [T, E], dx term [T, d]
+    b += align256(static_cast<size_t>(route_logit_slabs(dt, T, d, E)) * T * E * sizeof(float)) +
+         align256(static_cast<size_t>(T) * E * sizeof(float)) +
+         align256(static_cast<size_t>(T) * d * sizeof(float));
+  return b;
 }
 
 extern "C" moe_status moe_route_backward(
@@ -489,7 +645,6 @@ extern "C" moe_status moe_route_backward(
     float* dw_router, float* dw_gate, int32_t accumulate, void* ws, size_t ws_bytes) {
   if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_DTYPE;
   if (fn != MOE_SCORE_SOFTMAX && fn != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
-  if (fn == MOE_SCORE_SOFTMAX && !normalize) return MOE_ERR_UNSUPPORTED;
   if (!x || !w_router || !topk_idx || !topk_w || !d_topk_w || !expert_offsets || !slot_of ||
       !row_token || !dx || !dw_router)
     return MOE_ERR_INVALID_ARG;
@@ -504,7 +659,11 @@ extern "C" moe_status moe_route_backward(
       !aligned16(dx_perm) || !aligned16(dx_add) || !aligned16(dx) || !aligned16(dw_router) ||
       !aligned16(dw_gate) || !aligned16(ws))
     return MOE_ERR_ALIGNMENT;
-  if (!ws || ws_bytes < moe_route_backward_workspace_size(T, d, k)) return MOE_ERR_WORKSPACE;
+  if (!ws || ws_bytes < moe_route_backward_workspace_size(T, d, E, k, dt, fn, normalize))
+    return MOE_ERR_WORKSPACE;
+  if (rbwd_dense(fn, normalize) &&
+      (T * static_cast<int64_t>(E) >= (int64_t(1) << 31) || T * d >= (int64_t(1) << 31)))
+    return MOE_ERR_SHAPE;
   const int N = static_cast<int>(T * k);
   const int nchunk = static_cast<int>(d / 8);
   uint8_t* wsb = static_cast<uint8_t*>(ws);
@@ -515,15 +674,50 @@ extern "C" moe_status moe_route_backward(
   float* part = reinterpret_cast<float*>(wsb + off);
   const int nblk = static_cast<int>((T + kGateRows - 1) / kGateRows);
   const bool bf = dt == MOE_BF16;
-  hipError_t err;
+  hipError_t err = hipSuccess;
+  const bool dense = rbwd_dense(fn, normalize);
+  float* dx_dense = nullptr;
+  if (dense) {
+    // logits -> dense dz [T, E] -> dx_dense = dz W_r [T, d] (fp32)
+    off += align256(static_cast<size_t>(nblk) * d * sizeof(float));
+    float* z = reinterpret_cast<float*>(wsb + off);
+    off += align256(static_cast<size_t>(route_logit_slabs(dt, T, d, E)) * T * E * sizeof(float));
+    float* dz = reinterpret_cast<float*>(wsb + off);
+    off += align256(static_cast<size_t>(T) * E * sizeof(float));
+    dx_dense = reinterpret_cast<float*>(wsb + off);
+    err = launch_route_logits(stream, dt, T, d, E, x, w_router, logit_bias, z);
+    if (err == hipSuccess) {
+      auto kern = E <= 64 ? rbwd_dense_dz_kernel<1> : E <= 128 ? rbwd_dense_dz_kernel<2>
+                : E <= 256 ? rbwd_dense_dz_kernel<4> : E <= 512 ? rbwd_dense_dz_kernel<8>
+                : rbwd_dense_dz_kernel<16>;
+      err = launch(kern, dim3(static_cast<unsigned>((T + 3) / 4)), dim3(kLbThreads), 0, stream,
+                   (int)T, E, k, route_logit_slabs(dt, T, d, E), (const float*)z, topk_idx,
+                   d_topk_w, dz);
+    }
+    if (err == hipSuccess) {
+      auto kern = bf ? rbwd_gemm_kernel<true> : rbwd_gemm_kernel<false>;
+      err = launch(kern, dim3(static_cast<unsigned>((d + kRgN - 1) / kRgN),
+                              static_cast<unsigned>((T + kRgM - 1) / kRgM)),
+                   dim3(256), 0, stream, (int)T, (int)d, E, (const float*)dz, (int64_t)E,
+                   (int64_t)1, w_router, (int64_t)d, dx_dense, (int64_t)d, 0);
+    }
+    if (err == hipSuccess) {   // dW_r = dz^T x
+      auto kern = bf ? rbwd_gemm_kernel<true> : rbwd_gemm_kernel<false>;
+      err = launch(kern, dim3(static_cast<unsigned>((d + kRgN - 1) / kRgN),
+                              static_cast<unsigned>((E + kRgM - 1) / kRgM)),
+                   dim3(256), 0, stream, E, (int)d, (int)T, (const float*)dz, (int64_t)1,
+                   (int64_t)E, x, (int64_t)d, dw_router, (int64_t)d, accumulate);
+    }
+    if (err != hipSuccess) return MOE_ERR_HIP;
+  }
   {
     auto kern = bf ? rbwd_token_kernel<true> : rbwd_token_kernel<false>;
     err = launch(kern, dim3(static_cast<unsigned>((T + 3) / 4)), dim3(kLbThreads), 0, stream,
                  (int)T, k, E, N, nchunk, fn == MOE_SCORE_SIGMOID ? 1 : 0, normalize ? 1 : 0, x,
                  w_router, logit_bias, w_gate, topk_idx, topk_w, d_topk_w, d_gate, slot_of,
-                 dx_perm, dx_add, dx, dz_slot, dgl);
+                 dx_perm, dx_add, dx, dz_slot, dgl, (const float*)dx_dense);
   }
-  if (err == hipSuccess) {
+  if (err == hipSuccess && !dense) {
     auto kern = bf ? rbwd_dwr_kernel<true> : rbwd_dwr_kernel<false>;
     err = launch(kern, dim3(E, (nchunk + 63) / 64), dim3(64 * kDwrWaves), 0, stream, (int)d,
                  nchunk, expert_offsets, row_token, dz_slot, x, dw_router, accumulate);

@@ -275,3 +275,25 @@ extern "C" moe_status moe_route(hipStream_t stream, moe_dtype dt, int64_t T, int
                  expert_counts);
   return hip_status(err);
 }
+
+namespace moe {
+
+// Router logits alone (fp32, K slabs summed by the reader), shared with the
+// router backward, which recomputes every expert's score when the logit
+// gradient is dense.
+int route_logit_slabs(moe_dtype dt, int64_t T, int64_t d, int32_t E) {
+  return route_slabs(dt, T, d, E);
+}
+hipError_t launch_route_logits(hipStream_t stream, moe_dtype dt, int64_t T, int64_t d, int32_t E,
+                               const void* x, const void* w_router, const float* logit_bias,
+                               float* z) {
+  if (dt == MOE_BF16)
+    return launch_router_logits_bf16(stream, T, d, E, x, w_router, logit_bias, z,
+                                     route_slabs(dt, T, d, E));
+  const int64_t n = T * E;
+  return launch(route_logits_f32_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
+                stream, (int)T, (int)d, E, static_cast<const float*>(x),
+                static_cast<const float*>(w_router), logit_bias, z);
+}
+
+}  // namespace moe

@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.moe_abi_version() == 8
+    assert L.moe_abi_version() == 9
     assert L.moe_status_string(0) == b"MOE_OK"
     assert L.moe_status_string(5) == b"MOE_ERR_WORKSPACE"
 
@@ -200,8 +200,11 @@ def test_layer_backward_validation(L):
     assert c(a3=60) == 4                       # d % 8
     assert c(a4=33) == 2                       # k > 32
     rb = L.moe_route_backward
-    ws = L.moe_route_backward_workspace_size(16, 64, 2)
+    ws = L.moe_route_backward_workspace_size(16, 64, 8, 2, 1, 0, 1)
     assert ws >= 16 * 2 * 4 + 16 * 4
+    wsd = L.moe_route_backward_workspace_size(16, 64, 8, 2, 1, 0, 0)
+    assert wsd >= ws + 16 * 8 * 4 * 2 + 16 * 64 * 4   # logits, dz, dx term
+    assert L.moe_route_backward_workspace_size(16, 64, 8, 2, 7, 0, 1) == 0
     base = [None, 1, 16, 64, 8, 2, 0, 1, P, P, None, None, P, P, P, None, P, P, P, None, None,
             P, P, None, 0, P, ws]
     def r(**kw):
@@ -209,7 +212,7 @@ def test_layer_backward_validation(L):
         for i, v in kw.items():
             a[int(i[1:])] = v
         return rb(*a)
-    assert r(a7=0) == 6                        # softmax without renormalisation: unsupported
+    assert r(a7=0) == 5                        # dense softmax case needs the larger workspace
     assert r(a6=3) == 1                        # score function
     assert r(a11=P) == 1                       # w_gate without d_gate / dw_gate
     assert r(a5=9) == 2                        # k > E

@@ -3,8 +3,11 @@ router backward, shared expert and gate) against the oracle's
 moe_layer_backward, with the GPU's own expert selection held fixed.
 
 * small bf16 layers: softmax / sigmoid scores, with and without
-  renormalisation (sigmoid), logit bias and gated shared expert;
-* the combine and route backward kernels alone in fp32 (tolerance 1e-5);
+  renormalisation, logit bias and gated shared expert;
+* the combine and route backward kernels alone in fp32 (tolerance 1e-5),
+  and the dense router backward of softmax without renormalisation at
+  sizes that span several 64 x 64 tiles of its two products with ragged
+  edges and up to 1024 experts;
 * the qwen3_30b workload at full size: dx of every token, the router
   gradient and dW1 / dW2 of every expert.
 """
@@ -31,6 +34,7 @@ CASES = [
     (22, 130, 136, 10, 4, 72, 64, "sigmoid", True, True),
     (23, 77, 64, 8, 2, 64, 0, "sigmoid", False, False),
     (24, 160, 128, 16, 2, 96, 64, "softmax", True, True),
+    (25, 200, 136, 70, 4, 64, 64, "softmax", False, True),   # dense router dz
 ]
 
 
@@ -75,7 +79,8 @@ def test_combine_and_route_backward_fp32():
     wr = (rng.standard_normal((E, d)) * 0.3).astype(np.float32)
     wg = (rng.standard_normal(d) * 0.3).astype(np.float32)
     bias = (rng.standard_normal(E) * 0.2).astype(np.float32)
-    for score, normalize in (("softmax", True), ("sigmoid", True), ("sigmoid", False)):
+    for score, normalize in (("softmax", True), ("softmax", False), ("sigmoid", True),
+                             ("sigmoid", False)):
         r = mo.route(x, wr, k, score, normalize, bias, wg)
         idx = r.topk_idx
         w = r.topk_w.astype(np.float32)
@@ -136,3 +141,35 @@ def test_layer_backward_full_size_qwen3_30b():
           + ", ".join(f"{a} {b:.2e}" for a, b in errs.items()))
     for kk, e in errs.items():
         assert e <= tol, (kk, e)
+
+
+@pytest.mark.parametrize("T,d,E,k,dtype", [(1, 8, 1, 1, "f32"), (333, 200, 300, 8, "f32"),
+                                           (130, 72, 1024, 32, "f32"),
+                                           (517, 256, 128, 8, "bf16")])
+def test_route_backward_dense_softmax(T, d, E, k, dtype):
+    """Softmax scores without renormalisation: dz is dense over all E experts.
+    dx and dW_r against the oracle's route_backward (float64), with
+    accumulate onto a non-zero dW_r."""
+    rng = np.random.default_rng(T + E)
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    wr = (rng.standard_normal((E, d)) * 0.3).astype(np.float32)
+    bias = (rng.standard_normal(E) * 0.2).astype(np.float32)
+    if dtype == "bf16":
+        x = mw.bf16_bits_to_f32(mw.round_to_bf16_bits(x))
+        wr = mw.bf16_bits_to_f32(mw.round_to_bf16_bits(wr))
+    r = mo.route(x, wr, k, "softmax", False, bias)
+    idx = r.topk_idx
+    w = r.topk_w.astype(np.float32)
+    p = mo.permute(x, idx, w, E)
+    dtw = rng.standard_normal((T, k)).astype(np.float32)
+    dw0 = rng.standard_normal((E, d)).astype(np.float32)
+    dx_ref, dwr_ref, _, _ = mo.route_backward(x, wr, idx, dtw, "softmax", False, bias)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    dwr = _g(dw0)
+    dx, dwr_g, _ = moe.route_backward(
+        _g(x).to(tdt), _g(wr).to(tdt), _g(idx), _g(w), _g(dtw), _g(p.offsets), _g(p.slot_of),
+        _g(p.row_token), "softmax", False, _g(bias), accumulate=True, dw_router=dwr)
+    torch.cuda.synchronize()
+    tol_dx = gh.TOL_F32 if dtype == "f32" else gh.TOL_BF16
+    assert gh.normwise(gh.to_f64(dx), dx_ref) <= tol_dx
+    assert gh.normwise(gh.to_f64(dwr_g) - dw0, dwr_ref) <= gh.TOL_F32
