@@ -35,7 +35,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, AMD's published figure
 PEAK_FP8_TFLOPS = 5000.0         # MI355X dense fp8 MFMA, AMD's published figure
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, AMD's published figure
-COLD_FLUSH_BYTES = 1 << 30        # scratch written before each cold stage (> L2 + 256 MB MALL)
+COLD_FLUSH_BYTES = 1 << 30        # scratch read before each cold stage (> L2 + 256 MB MALL)
 
 # HBM bytes per grouped-GEMM forward call (fc1 + fc2 dispatches), from
 # `rocprofv3 --pmc FETCH_SIZE` and `--pmc WRITE_SIZE` runs of this script,
@@ -316,10 +316,12 @@ def main():
         total_ev += ev[0].elapsed_time(ev[5])
     per_stage = {s: v / nbreak for s, v in per_stage.items()}  # ms per call
 
-    # Cold stages: a 1 GiB scratch fill (larger than L2 and the 256 MB
+    # Cold stages: a 1 GiB scratch read (larger than L2 and the 256 MB
     # Infinity Cache) before each stage, outside its event pair; a shared
     # expert's own call (when not folded into the grouped GEMM) runs untimed.
-    scratch = torch.empty(COLD_FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    # A read, not a fill: a fill leaves up to 256 MB of dirty cache lines
+    # whose write-back would be charged to the stage that evicts them.
+    scratch = torch.ones(COLD_FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
     cold_stages = ["route", "permute", "grouped_gemm", "combine"]
     ncold = 5
     cev = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(ncold)]
@@ -327,7 +329,7 @@ def main():
         j = 0
         for name, fn in layer.stages(x):
             if name in cold_stages:
-                scratch.fill_(float(i))
+                scratch.amax()
                 cev[i][2 * j].record(stream)
                 fn()
                 cev[i][2 * j + 1].record(stream)
@@ -416,8 +418,8 @@ def main():
         "stage_hbm_frac_cold": {s: (round(v / PEAK_HBM_GBS, 4) if v else None)
                                 for s, v in cold_gbs.items()},
         "stage_cold_note": (f"{ncold} further steps, a {COLD_FLUSH_BYTES >> 30} GiB scratch "
-                            "fill before each stage outside its events (L2 and Infinity Cache "
-                            "evicted); algorithmic bytes / event time"),
+                            "read before each stage outside its events (L2 and Infinity Cache "
+                            "evicted, no dirty lines left); algorithmic bytes / event time"),
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

@@ -8,15 +8,20 @@
 // are summed in fp32 in slot order j = 0..k-1, the shared row is added last,
 // and the result is rounded to the storage type once.  Memory-bound: every
 // byte of y_perm is read exactly once, y once written.
-#include "moe_internal.h"
+#include "moe_gemm_common.h"
 
 namespace moe {
 
 constexpr int kCombThreads = 256;
 
-// kMaxK >= k: the k row loads of one column chunk are issued together (no
-// round trip per row); the sum still runs in slot order.
-template <bool kBF16, int kMaxK>
+// kMaxK >= k: the k row loads of kU column chunks per lane are issued
+// together (one round trip for up to kU KB of every row); each chunk's sum
+// still runs in slot order.  The loads are raw buffer loads with one
+// descriptor per row (the row's bytes, or none for a dropped choice), so a
+// chunk past the row or a missing row reads zero without a branch around
+// the load, and all of them leave before the first wait.  y is written with
+// non-temporal stores (this pass does not read it back).
+template <bool kBF16, int kMaxK, int kU>
 __global__ __launch_bounds__(kCombThreads) void combine_kernel(
     int T, int k, int N, int nchunk16, const u32x4* __restrict__ y_perm,
     const int32_t* __restrict__ slot_of, const float* __restrict__ topk_w,
@@ -32,75 +37,92 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
     if (my_row >= N) my_row = -1;
     if (topk_w) my_w = topk_w[static_cast<size_t>(t) * k + lane];
   }
+  const int row_bytes = nchunk16 * 16;
   // every lane holds all k rows and weights (wave-uniform)
-  const u32x4* src[kMaxK];
+  __amdgpu_buffer_rsrc_t rs[kMaxK];
+  bool has[kMaxK];
   float wj[kMaxK];
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) {
     const int row = j < k ? __builtin_amdgcn_readfirstlane(__shfl(my_row, j, kWave)) : -1;
-    src[j] = row >= 0 ? y_perm + static_cast<size_t>(row) * nchunk16 : nullptr;
+    has[j] = row >= 0;
+    rs[j] = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<u32x4*>(y_perm + static_cast<size_t>(has[j] ? row : 0) * nchunk16), 0,
+        has[j] ? row_bytes : 0, kRsrcWord3);
     wj[j] = j < k ? __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
                         __builtin_bit_cast(int, __shfl(my_w, j, kWave))))
                   : 0.0f;
   }
   const float g = (y_shared && shared_gate) ? shared_gate[t] : 1.0f;
-  const u32x4* sh = y_shared ? y_shared + static_cast<size_t>(t) * nchunk16 : nullptr;
+  const bool sh = y_shared != nullptr;
+  const __amdgpu_buffer_rsrc_t rsh = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u32x4*>(sh ? y_shared + static_cast<size_t>(t) * nchunk16 : y_perm), 0,
+      sh ? row_bytes : 0, kRsrcWord3);
   constexpr int kVals = kBF16 ? 8 : 4;
-  for (int c = lane; c < nchunk16; c += 64) {
-    u32x4 v[kMaxK];
+  constexpr int kNt = 2;   // cache policy: non-temporal
+  for (int c0 = lane; c0 < nchunk16; c0 += 64 * kU) {
+    u32x4 v[kU][kMaxK], vs[kU];
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j)
-      if (src[j]) v[j] = __builtin_nontemporal_load(src[j] + c);
-    u32x4 vs{};
-    if (sh) vs = __builtin_nontemporal_load(sh + c);
-    float acc[kVals];
+    for (int u = 0; u < kU; ++u) {
+      const int off = (c0 + 64 * u) * 16;
 #pragma unroll
-    for (int q = 0; q < kVals; ++q) acc[q] = 0.0f;
+      for (int j = 0; j < kMaxK; ++j)
+        v[u][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs[j], off, 0, kNt));
+      if (sh) vs[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsh, off, 0, kNt));
+    }
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      if (!src[j]) continue;
+    for (int u = 0; u < kU; ++u) {
+      const int c = c0 + 64 * u;
+      float acc[kVals];
+#pragma unroll
+      for (int q = 0; q < kVals; ++q) acc[q] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j) {
+        if (!has[j]) continue;                    // wave-uniform
+        if constexpr (kBF16) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[2 * q] = fmaf(wj[j], bf16lo(v[u][j][q]), acc[2 * q]);
+            acc[2 * q + 1] = fmaf(wj[j], bf16hi(v[u][j][q]), acc[2 * q + 1]);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[q] = fmaf(wj[j], __uint_as_float(v[u][j][q]), acc[q]);
+        }
+      }
+      if (sh) {
+        if constexpr (kBF16) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[2 * q] = fmaf(g, bf16lo(vs[u][q]), acc[2 * q]);
+            acc[2 * q + 1] = fmaf(g, bf16hi(vs[u][q]), acc[2 * q + 1]);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[q] = fmaf(g, __uint_as_float(vs[u][q]), acc[q]);
+        }
+      }
+      u32x4 o;
       if constexpr (kBF16) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[2 * q] = fmaf(wj[j], bf16lo(v[j][q]), acc[2 * q]);
-          acc[2 * q + 1] = fmaf(wj[j], bf16hi(v[j][q]), acc[2 * q + 1]);
-        }
+        for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
       } else {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[q] = fmaf(wj[j], __uint_as_float(v[j][q]), acc[q]);
+        for (int q = 0; q < 4; ++q) o[q] = __float_as_uint(acc[q]);
       }
+      if (c < nchunk16) __builtin_nontemporal_store(o, y + static_cast<size_t>(t) * nchunk16 + c);
     }
-    if (sh) {
-      if constexpr (kBF16) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[2 * q] = fmaf(g, bf16lo(vs[q]), acc[2 * q]);
-          acc[2 * q + 1] = fmaf(g, bf16hi(vs[q]), acc[2 * q + 1]);
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[q] = fmaf(g, __uint_as_float(vs[q]), acc[q]);
-      }
-    }
-    u32x4 o;
-    if constexpr (kBF16) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
-    } else {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) o[q] = __float_as_uint(acc[q]);
-    }
-    y[static_cast<size_t>(t) * nchunk16 + c] = o;
   }
 }
 
 template <bool kBF16>
 static auto pick_combine(int k) {
-  if (k <= 2) return combine_kernel<kBF16, 2>;
-  if (k <= 4) return combine_kernel<kBF16, 4>;
-  if (k <= 8) return combine_kernel<kBF16, 8>;
-  if (k <= 16) return combine_kernel<kBF16, 16>;
-  return combine_kernel<kBF16, 32>;
+  // kU * kMaxK <= 32 row chunks in flight per lane (<= 128 VGPRs of loads)
+  if (k <= 2) return combine_kernel<kBF16, 2, 4>;
+  if (k <= 4) return combine_kernel<kBF16, 4, 4>;
+  if (k <= 8) return combine_kernel<kBF16, 8, 4>;
+  if (k <= 16) return combine_kernel<kBF16, 16, 2>;
+  return combine_kernel<kBF16, 32, 1>;
 }
 
 }  // namespace moe
