@@ -6,11 +6,15 @@
 // (the backward's dgrad and wgrad GEMMs) and "其他融合优化"
 // (gradient_accumulation_fusion: fp32 weight-gradient accumulation).
 //
-// bf16 engine (gfx950), the forward's pipeline with a second operand layout:
-//   * workgroup = 8 wavefronts (2 x 4), output tile 128 x 256, wave tile
-//     64 x 64 = 2 x 2 v_mfma_f32_32x32x16_bf16 accumulators; a 3-deep ring
-//     of 32-wide K tiles filled global -> LDS directly (no staging
-//     registers), two workgroups per CU;
+// bf16 engines (gfx950):
+//   * dgrad (ggb_kernel): workgroup = 8 wavefronts (2 x 4), output tile
+//     128 x 256, wave tile 64 x 64 = 2 x 2 v_mfma_f32_32x32x16_bf16
+//     accumulators; a 3-deep ring of 32-wide K tiles filled global -> LDS
+//     directly (no staging registers), two workgroups per CU, so one's
+//     epilogue overlaps the other's K loop;
+//   * wgrad (ggw_persistent_kernel): 256 x 256 tiles, 16 wavefronts, a
+//     2-slot ring of 64-wide K tiles, one persistent workgroup per CU taking
+//     tiles longest first (see its comment);
 //   * a K-contiguous operand (dY and dH rows in dgrad) is staged as in the
 //     forward: [row][32 k] with XOR-swizzled 16-byte chunks, read with
 //     ds_read_b128;
@@ -30,14 +34,16 @@
 //   * dgrad tiles over ragged expert segments are decoded on the device from
 //     expert_offsets and handed to XCDs in contiguous ranges; a wave whose
 //     32-row blocks lie past the segment skips their MFMAs.  wgrad tiles are
-//     per expert (an empty expert yields zeros), listed expert-major so that
-//     the tiles reading one expert's token panels share an XCD;
+//     per expert (an empty expert yields zeros);
 //   * epilogues fuse the SwiGLU backward (dG = dA U silu'(G), dU = dA
 //     silu(G)) with A * row_scale for the fc2 wgrad, and the fp32
 //     (optionally accumulating) weight-gradient store.
 //   Deterministic: each output element is produced by one workgroup with a
-//   fixed K order; no atomics.
-#include "moe_gemm_common.h"
+//   fixed K order.  The one atomic, the wgrad's tile counter, decides which
+//   workgroup computes a tile, not how it is computed.
+#include <algorithm>
+
+#include "moe_sched.h"
 
 namespace moe {
 
@@ -63,29 +69,22 @@ static_assert(MOE_BWD_VMCNT == kLoads * (kStages - 2), "ring wait count");
 constexpr size_t kBwdLds = kStages * kStageE * sizeof(uint16_t);
 
 
-enum Epi { EPI_DGRAD2 = 2, EPI_DGRAD1 = 3, EPI_WGRAD = 4 };
+enum Epi { EPI_DGRAD2 = 2, EPI_DGRAD1 = 3 };
 
 struct GGParams {
   int E, F, d;
-  int K;                          // dgrad: contraction length
-  int ntn;                        // dgrad: column tiles per row tile
-  int mts, nts;                   // wgrad: tiles per expert along rows / columns
+  int K;                          // contraction length
+  int ntn;                        // column tiles per row tile
   const int32_t* offsets;         // [E+1]
-  // A operand (rows of C): dgrad: token rows [N, K]; wgrad: [N, out_m]
-  const uint16_t* a;
+  const uint16_t* a;              // A operand (rows of C): token rows [N, K]
   int lda;
-  // B operand (columns of C): dgrad: weights [E][K, ldb]; wgrad: [N, out_n]
-  const uint16_t* b;
+  const uint16_t* b;              // B operand (columns of C): weights [E][K, ldb]
   int ldb;
   size_t b_estride;
   const float* scale;             // [N] row scale or NULL (DGRAD2)
   const uint16_t* gu_in;          // [N, 2F] (DGRAD2)
   uint16_t* out;                  // DGRAD2: dH [N,2F]; DGRAD1: dX [N,d]
   uint16_t* out2;                 // DGRAD2: A*scale [N,F]
-  float* outf;                    // WGRAD: dW (expert 0)
-  size_t outf_estride;
-  int out_m, out_n;               // WGRAD: output rows / cols per expert
-  int accumulate;
 };
 
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
@@ -122,39 +121,24 @@ __device__ __forceinline__ bf16x8 frag_tr(const uint16_t* T, int base, int kk) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// One output tile.  dgrad: rows [m0, min(m0 + kBM, hi)) of expert e's
-// segment [lo, hi), output columns from n0.  wgrad: output rows from m0 and
-// columns from n0 of dW[e], K = the segment's token rows.  kNRB = live
-// 32-row blocks of this wave (dgrad; wgrad passes kRB).
+// One dgrad output tile: rows [m0, min(m0 + kBM, hi)) of expert e's segment
+// [lo, hi), output columns from n0.  kNRB = live 32-row blocks of this wave.
 template <int kEpi, int kNRB>
 __device__ __forceinline__ void ggb_tile(const GGParams& p, int e, int lo, int hi, int m0, int n0,
                                          uint16_t* s_lds) {
-  constexpr bool kATr = kEpi == EPI_WGRAD;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / kWN, wn = wave % kWN;
   const int r32 = lane & 31, h = lane >> 5;
-  const int K = kATr ? hi - lo : p.K;
+  const int K = p.K;
 
-  // --- A operand loads: block `wave` of the A tile --------------------------
-  // K-contiguous: one descriptor over the tile's rows (unused when K-strided)
+  // --- A operand loads: block `wave` of the A tile ([128 rows][32 k], 16
+  // rows per block), one descriptor over the tile's rows
   const i32x4 rs_a = buf_desc(p.a + static_cast<size_t>(m0) * p.lda, min(hi - m0, kBM) * p.lda * 2);
-  const uint16_t* a_kbase = nullptr;          // K-strided: element (k, col) at a_kbase + k lda + col
-  int vo_a, kcl_a = 0;
-  if constexpr (kATr) {
-    // [32 k][128 columns]: 256-byte k rows, 4 per block
-    const int krow = wave * 4 + (lane >> 4);
-    const int lc = (lane & 15) ^ ((krow & 3) << 2);
-    vo_a = (krow * p.lda + m0 + 8 * lc) * 2;
-    a_kbase = p.a + static_cast<size_t>(lo) * p.lda;
-  } else {
-    // [128 rows][32 k], 16 rows per block
-    const int r = wave * 16 + (lane >> 2);
-    kcl_a = (lane & 3) ^ swz_f(r);
-    vo_a = (min(r, hi - 1 - m0) * p.lda + kcl_a * 8) * 2;   // rows past the segment: dropped
-  }
+  const int r_a = wave * 16 + (lane >> 2);
+  const int kcl_a = (lane & 3) ^ swz_f(r_a);
+  const int vo_a = (min(r_a, hi - 1 - m0) * p.lda + kcl_a * 8) * 2;   // rows past the segment: dropped
   // --- B operand loads: blocks wave, wave + 8 of the [32 k][256 columns] tile
-  const uint16_t* b_kbase = kATr ? p.b + static_cast<size_t>(lo) * p.ldb
-                                 : p.b + static_cast<size_t>(e) * p.b_estride;
+  const uint16_t* b_kbase = p.b + static_cast<size_t>(e) * p.b_estride;
   int vo_b[kBLoads];
 #pragma unroll
   for (int j = 0; j < kBLoads; ++j) {
@@ -173,22 +157,15 @@ __device__ __forceinline__ void ggb_tile(const GGParams& p, int e, int lo, int h
     const int k0 = t * kBK;
     const int krows = past ? 0 : min(kBK, K - k0);
     uint16_t* st = s_lds + (kt % kStages) * kStageE;
-    if constexpr (kATr) {
-      dma16(buf_desc(a_kbase + static_cast<size_t>(k0) * p.lda, krows * p.lda * 2),
-            st + wave * 512, vo_a, 0);
-    } else {
-      dma16(rs_a, st + wave * 512, (!past && k0 + kcl_a * 8 < K) ? vo_a : kOob, k0 * 2);
-    }
+    dma16(rs_a, st + wave * 512, (!past && k0 + kcl_a * 8 < K) ? vo_a : kOob, k0 * 2);
     const i32x4 rb = buf_desc(b_kbase + static_cast<size_t>(k0) * p.ldb, krows * p.ldb * 2);
 #pragma unroll
     for (int j = 0; j < kBLoads; ++j)
       dma16(rb, st + kATileE + (wave + kWaves * j) * 512, vo_b[j], 0);
   };
 
-  // this wave's operand read offsets
-  int a_tr[kRB], b_tr[kCB];
-#pragma unroll
-  for (int i = 0; i < kRB; ++i) a_tr[i] = tr_base<kBM>(wm * kRB * 32 + i * 32, lane);
+  // this wave's operand read offsets (B, transposed reads)
+  int b_tr[kCB];
 #pragma unroll
   for (int c = 0; c < kCB; ++c) b_tr[c] = tr_base<kBN>(wn * kCB * 32 + c * 32, lane);
 
@@ -210,8 +187,7 @@ __device__ __forceinline__ void ggb_tile(const GGParams& p, int e, int lo, int h
         for (int c = 0; c < kCB; ++c) bv[c] = frag_tr<kBN>(Bs, b_tr[c], kk);
 #pragma unroll
         for (int rb = 0; rb < kNRB; ++rb) {
-          const bf16x8 av = kATr ? frag_tr<kBM>(As, a_tr[rb], kk)
-                                 : frag_row(As, wm * kRB * 32 + rb * 32, kk, lane);
+          const bf16x8 av = frag_row(As, wm * kRB * 32 + rb * 32, kk, lane);
 #pragma unroll
           for (int c = 0; c < kCB; ++c)
             acc[rb][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv[c], acc[rb][c], 0, 0, 0);
@@ -242,26 +218,7 @@ __device__ __forceinline__ void ggb_tile(const GGParams& p, int e, int lo, int h
   // (Taking the B block as the MFMAs' first operand instead, for 4
   // consecutive columns per lane and 8/16-byte accesses, measured slower
   // here: the SwiGLU backward's G, U reads then touch 32 rows per load.)
-  if constexpr (kEpi == EPI_WGRAD) {
-    float* dw = p.outf + static_cast<size_t>(e) * p.outf_estride;
-#pragma unroll
-    for (int rb = 0; rb < kRB; ++rb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * kRB * 32 + rb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (row >= p.out_m) continue;
-        float* dst = dw + static_cast<size_t>(row) * p.out_n;
-#pragma unroll
-        for (int c = 0; c < kCB; ++c) {
-          const int col = n0 + wn * kCB * 32 + c * 32 + r32;
-          if (col < p.out_n) {
-            const float v = acc[rb][c][r];
-            dst[col] = p.accumulate ? dst[col] + v : v;
-          }
-        }
-      }
-    }
-  } else if constexpr (kEpi == EPI_DGRAD2) {
+  if constexpr (kEpi == EPI_DGRAD2) {
     // fc2 dgrad + SwiGLU backward, staged through the free ring in four
     // passes of 32 rows (pass q: the waves with wm == q / 2 own their row
     // block q % 2): G and U come in as 16-byte vectors, each lane turns its
@@ -369,30 +326,249 @@ __device__ __forceinline__ void ggb_tile(const GGParams& p, int e, int lo, int h
 template <int kEpi>
 __global__ __launch_bounds__(kGT, 2) void ggb_kernel(GGParams p) {
   extern __shared__ __align__(16) uint16_t s_lds[];   // kStages x (A tile + B tile)
-  if constexpr (kEpi == EPI_WGRAD) {
-    const int per_e = p.mts * p.nts;
-    const int total = per_e * p.E;
-    if (static_cast<int>(blockIdx.x) >= total) return;
-    const int L = xcd_remap(blockIdx.x, total);
-    const int e = L / per_e, local = L - e * per_e;
-    const int nt = local / p.mts, mt = local - nt * p.mts;
-    ggb_tile<kEpi, kRB>(p, e, p.offsets[e], p.offsets[e + 1], mt * kBM, nt * kBN, s_lds);
-  } else {
-    __shared__ int s_cum[1025];
-    __shared__ int s_tmp[kWaves];
-    tile_prefix<kGT>(p.offsets, p.E, kBM, p.ntn, s_cum, s_tmp);
-    const int total = s_cum[p.E];
-    if (static_cast<int>(blockIdx.x) >= total) return;
-    const TileIdx ti = tile_decode(p.offsets, p.E, kBM, xcd_remap(blockIdx.x, total), s_cum);
-    const int m0 = ti.m0;
-    const int rows = ti.mend - m0 - (static_cast<int>(threadIdx.x >> 6) / kWN) * kRB * 32;
-    const int nrb = rows <= 0 ? 0 : min(kRB, (rows + 31) >> 5);
-    switch (nrb) {
-      case 0: ggb_tile<kEpi, 0>(p, ti.e, ti.lo, ti.mend, m0, ti.nt * kBN, s_lds); break;
-      case 1: ggb_tile<kEpi, 1>(p, ti.e, ti.lo, ti.mend, m0, ti.nt * kBN, s_lds); break;
-      default: ggb_tile<kEpi, 2>(p, ti.e, ti.lo, ti.mend, m0, ti.nt * kBN, s_lds); break;
-    }
+  __shared__ int s_cum[1025];
+  __shared__ int s_tmp[kWaves];
+  tile_prefix<kGT>(p.offsets, p.E, kBM, p.ntn, s_cum, s_tmp);
+  const int total = s_cum[p.E];
+  if (static_cast<int>(blockIdx.x) >= total) return;
+  const TileIdx ti = tile_decode(p.offsets, p.E, kBM, xcd_remap(blockIdx.x, total), s_cum);
+  const int m0 = ti.m0;
+  const int rows = ti.mend - m0 - (static_cast<int>(threadIdx.x >> 6) / kWN) * kRB * 32;
+  const int nrb = rows <= 0 ? 0 : min(kRB, (rows + 31) >> 5);
+  switch (nrb) {
+    case 0: ggb_tile<kEpi, 0>(p, ti.e, ti.lo, ti.mend, m0, ti.nt * kBN, s_lds); break;
+    case 1: ggb_tile<kEpi, 1>(p, ti.e, ti.lo, ti.mend, m0, ti.nt * kBN, s_lds); break;
+    default: ggb_tile<kEpi, 2>(p, ti.e, ti.lo, ti.mend, m0, ti.nt * kBN, s_lds); break;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Persistent weight-gradient engine: dW[e] (+)= A_e^T B_e over expert e's
+// token rows (K = the segment), both operands K-strided ([k][columns]).
+// 256 x 256 output tiles, 16 wavefronts (4 x 4) of 64 x 64 (2 x 2
+// accumulators), 64-wide K tiles in a 2-slot ring (A 32 KB + B 32 KB per
+// slot), one workgroup per CU.  The next tile's first K tile is loaded while
+// the current tile's last one is multiplied and while its epilogue stores
+// the fp32 result straight from the accumulators (32 consecutive columns per
+// row per store).  An empty expert runs one K tile of zeros, so its dW is
+// written as zeros (or left as it is when accumulating).
+//
+// Schedule.  A tile's cost grows with its expert's row count, and routing
+// makes those counts very unequal (one expert can hold a fifth of the rows,
+// so its tiles cost most of a workgroup's fair share each).  Every
+// workgroup ranks the experts by decreasing row count (ties by index) and
+// lists the tiles in that order, each expert's tiles together (row tiles
+// inner).  Workgroup b takes tiles b and b + grid, then fetches the next
+// from one counter as it starts each tile: the most expensive tiles go
+// first and the cheap ones fill the tail (longest-first list scheduling).
+constexpr int kPM = 256, kPN = 256, kPK = 64, kPWN = 4, kPRB = 2, kPCB = 2, kPWaves = 16;
+constexpr int kPThreads = 64 * kPWaves;
+constexpr int kPATileE = kPM * kPK, kPBTileE = kPN * kPK, kPSlotE = kPATileE + kPBTileE;
+constexpr size_t kPRing = 2 * kPSlotE * sizeof(uint16_t);   // 128 KB
+constexpr int kPLoads = kPATileE / 512 / kPWaves;          // 1 KB blocks per wave per operand (2)
+// LDS past the ring: expert order (1024 ints) and the fetch slot
+constexpr size_t kPLds = kPRing + (1024 + 4) * sizeof(int);
+
+// a descriptor the compiler cannot prove wave-uniform, moved to SGPRs
+__device__ __forceinline__ i32x4 uniform4(i32x4 v) {
+  return i32x4{__builtin_amdgcn_readfirstlane(v[0]), __builtin_amdgcn_readfirstlane(v[1]),
+               __builtin_amdgcn_readfirstlane(v[2]), __builtin_amdgcn_readfirstlane(v[3])};
+}
+
+struct WgradParams {
+  int E;
+  const int32_t* offsets;    // [E+1]
+  const uint16_t* a;         // [N, lda]: rows are k, columns the output rows m
+  int lda;
+  const uint16_t* b;         // [N, ldb]: columns the output columns n
+  int ldb;
+  float* outf;               // dW of expert 0, [out_m, out_n] fp32
+  size_t outf_estride;
+  int out_m, out_n;
+  int mts, nts;              // 256-tiles per expert along m and n
+  int accumulate;
+  int* counter;              // tile counter, zero at launch
+};
+
+__device__ __forceinline__ int wgrad_nk(int K) { return K > 0 ? (K + kPK - 1) / kPK : 1; }
+
+__global__ __launch_bounds__(kPThreads, 1) void ggw_persistent_kernel(WgradParams p) {
+  extern __shared__ __align__(16) uint16_t s_lds[];
+  int* s_order = reinterpret_cast<int*>(s_lds + kPRing / 2);   // rank -> expert (kept)
+  int* s_fetch = s_order + 1024;
+  int* s_K = reinterpret_cast<int*>(s_lds);   // [E] row counts, in the ring before its first load
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / kPWN, wn = wave % kPWN;
+  const int r32 = lane & 31, h = lane >> 5;
+  const int E = p.E;
+  const int per_e = p.mts * p.nts;
+  const int total = per_e * E;
+
+  // ---- expert order (identical in every workgroup) -----------------------
+  for (int e = tid; e < E; e += kPThreads) s_K[e] = p.offsets[e + 1] - p.offsets[e];
+  __syncthreads();
+  for (int e = tid; e < E; e += kPThreads) {
+    const int ke = s_K[e];
+    int rank = 0;
+    for (int f = 0; f < E; ++f) {
+      const int kf = s_K[f];
+      rank += (kf > ke || (kf == ke && f < e)) ? 1 : 0;
+    }
+    s_order[rank] = e;
+  }
+  __syncthreads();
+  if (static_cast<int>(blockIdx.x) >= total) return;   // uniform over the workgroup
+
+  struct Tile {
+    int e, lo, K, nk, m0, n0;
+  };
+  auto setup = [&](int gl) {    // gl: index in the tile list
+    Tile t;
+    const int r = gl / per_e;
+    t.e = __builtin_amdgcn_readfirstlane(s_order[r]);
+    const int local = gl - r * per_e;
+    const int nt = local / p.mts, mt = local - nt * p.mts;
+    t.lo = __builtin_amdgcn_readfirstlane(p.offsets[t.e]);
+    t.K = __builtin_amdgcn_readfirstlane(p.offsets[t.e + 1]) - t.lo;
+    t.nk = wgrad_nk(t.K);
+    t.m0 = mt * kPM;
+    t.n0 = nt * kPN;
+    return t;
+  };
+  // the wave's blocks: k rows 2 bb, 2 bb + 1 of a [64 k][256 columns] tile;
+  // lane l fills 16-byte position l % 32 of k row 2 bb + l / 32 with chunk
+  // (l % 32) ^ 4 (k % 4), the layout the transposed reads expect
+  int krow[kPLoads], lcol[kPLoads];
+#pragma unroll
+  for (int j = 0; j < kPLoads; ++j) {
+    const int bb = wave + kPWaves * j;
+    krow[j] = 2 * bb + (lane >> 5);
+    lcol[j] = 8 * ((lane & 31) ^ ((krow[j] & 3) << 2));
+  }
+  // K tile kt of tile t into ring slot `slot`; rows past the segment (and
+  // every row of an empty expert) read zero through the descriptors' size
+  auto issue = [&](const Tile& t, int kt, int slot) {
+    const int k0 = kt * kPK;
+    const int krows = max(0, min(kPK, t.K - k0));
+    uint16_t* da = s_lds + slot * kPSlotE;
+    uint16_t* db = da + kPATileE;
+    const size_t r0 = static_cast<size_t>(t.lo) + (krows > 0 ? k0 : 0);
+    const i32x4 ra = uniform4(buf_desc(p.a + r0 * p.lda, krows * p.lda * 2));
+    const i32x4 rb = uniform4(buf_desc(p.b + r0 * p.ldb, krows * p.ldb * 2));
+#pragma unroll
+    for (int j = 0; j < kPLoads; ++j)
+      dma16(ra, da + (wave + kPWaves * j) * 512, (krow[j] * p.lda + t.m0 + lcol[j]) * 2, 0);
+#pragma unroll
+    for (int j = 0; j < kPLoads; ++j)
+      dma16(rb, db + (wave + kPWaves * j) * 512, (krow[j] * p.ldb + t.n0 + lcol[j]) * 2, 0);
+  };
+
+  int a_tr[kPRB], b_tr[kPCB];
+#pragma unroll
+  for (int i = 0; i < kPRB; ++i) a_tr[i] = tr_base<kPM>(wm * kPRB * 32 + i * 32, lane);
+#pragma unroll
+  for (int c = 0; c < kPCB; ++c) b_tr[c] = tr_base<kPN>(wn * kPCB * 32 + c * 32, lane);
+
+  f32x16 acc[kPRB][kPCB];
+  auto compute = [&](int slot) {
+    const uint16_t* As = s_lds + slot * kPSlotE;
+    const uint16_t* Bs = As + kPATileE;
+#pragma unroll
+    for (int kk = 0; kk < kPK / 16; ++kk) {
+      bf16x8 bv[kPCB];
+#pragma unroll
+      for (int c = 0; c < kPCB; ++c) bv[c] = frag_tr<kPN>(Bs, b_tr[c], kk);
+#pragma unroll
+      for (int rb = 0; rb < kPRB; ++rb) {
+        const bf16x8 av = frag_tr<kPM>(As, a_tr[rb], kk);
+#pragma unroll
+        for (int c = 0; c < kPCB; ++c)
+          acc[rb][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv[c], acc[rb][c], 0, 0, 0);
+      }
+    }
+  };
+  // accumulator register r of lane l: output row 8 (r / 4) + 4 (l / 32) + r % 4
+  // of the 32-row block, column l % 32
+  auto epilogue = [&](const Tile& t) {
+    float* dw = p.outf + static_cast<size_t>(t.e) * p.outf_estride;
+#pragma unroll
+    for (int rb = 0; rb < kPRB; ++rb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = t.m0 + wm * kPRB * 32 + rb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (row >= p.out_m) continue;
+        float* dst = dw + static_cast<size_t>(row) * p.out_n;
+#pragma unroll
+        for (int c = 0; c < kPCB; ++c) {
+          const int col = t.n0 + wn * kPCB * 32 + c * 32 + r32;
+          if (col < p.out_n) {
+            const float v = acc[rb][c][r];
+            dst[col] = p.accumulate ? dst[col] + v : v;
+          }
+        }
+      }
+    }
+  };
+
+  const int G = static_cast<int>(gridDim.x);
+  Tile cur = setup(blockIdx.x);
+  bool has_nxt = static_cast<int>(blockIdx.x) + G < total;
+  Tile nxt = has_nxt ? setup(blockIdx.x + G) : cur;
+  issue(cur, 0, 0);
+  int g = 0;                    // global K step: ring slot g & 1
+#pragma unroll 1
+  for (;;) {
+    int fetched = 0;
+    if (has_nxt && tid == 0) fetched = atomicAdd(p.counter, 1);   // the tile after nxt
+#pragma unroll
+    for (int i = 0; i < kPRB; ++i)
+#pragma unroll
+      for (int c = 0; c < kPCB; ++c) acc[i][c] = f32x16{};
+#pragma unroll 1
+    for (int kt = 0; kt < cur.nk; ++kt, ++g) {
+      // this wave's loads (and the last epilogue's stores) have landed; the
+      // barrier makes K tile g visible and frees slot (g + 1) & 1
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      if (kt + 1 < cur.nk) issue(cur, kt + 1, (g + 1) & 1);
+      else if (has_nxt) issue(nxt, 0, (g + 1) & 1);
+      compute(g & 1);
+    }
+    if (tid == 0) *s_fetch = 2 * G + fetched;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const int L2 = *s_fetch;
+    epilogue(cur);
+    if (!has_nxt) break;
+    cur = nxt;
+    has_nxt = L2 < total;
+    if (has_nxt) nxt = setup(L2);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+static unsigned wgrad_grid(int64_t tiles) {   // one workgroup per CU, at most one per tile
+  return static_cast<unsigned>(std::max<int64_t>(1, std::min<int64_t>(device_cu_count(), tiles)));
+}
+
+// dW[e] (out_m x out_n) (+)= A[seg e]^T B[seg e] for every expert e.
+static hipError_t launch_wgrad(hipStream_t stream, int32_t E, const int32_t* offsets,
+                               const uint16_t* a, int lda, const uint16_t* b, int ldb, float* dw,
+                               int out_m, int out_n, int accumulate, int* counters) {
+  hipError_t err = launch_zero_counters(stream, counters, 1);
+  if (err != hipSuccess) return err;
+  WgradParams p{};
+  p.E = E; p.offsets = offsets;
+  p.a = a; p.lda = lda; p.b = b; p.ldb = ldb;
+  p.outf = dw; p.outf_estride = static_cast<size_t>(out_m) * out_n;
+  p.out_m = out_m; p.out_n = out_n;
+  p.mts = (out_m + kPM - 1) / kPM;
+  p.nts = (out_n + kPN - 1) / kPN;
+  p.accumulate = accumulate;
+  p.counter = counters;
+  err = allow_lds(ggw_persistent_kernel, kPLds);
+  if (err != hipSuccess) return err;
+  return launch(ggw_persistent_kernel, dim3(wgrad_grid(static_cast<int64_t>(p.mts) * p.nts * E)),
+                dim3(kPThreads), kPLds, stream, p);
 }
 
 }  // namespace moe
@@ -458,7 +634,6 @@ extern "C" moe_status moe_grouped_swiglu_bwd(hipStream_t stream, moe_dtype dt, i
   const size_t lds = kBwdLds;
   if (err == hipSuccess) err = allow_lds(ggb_kernel<EPI_DGRAD2>, lds);
   if (err == hipSuccess) err = allow_lds(ggb_kernel<EPI_DGRAD1>, lds);
-  if (err == hipSuccess) err = allow_lds(ggb_kernel<EPI_WGRAD>, lds);
   if (err == hipSuccess && N > 0) {
     // fc2 dgrad + SwiGLU backward: dH, A*scale
     GGParams p{};
@@ -481,28 +656,14 @@ extern "C" moe_status moe_grouped_swiglu_bwd(hipStream_t stream, moe_dtype dt, i
     err = launch(ggb_kernel<EPI_DGRAD1>, dim3(tiles_bound(N, E, kBM) * p.ntn), dim3(kGT), lds,
                  stream, p);
   }
-  if (err == hipSuccess) {
-    // fc2 wgrad: dW2[e] (d x F) = dY^T (A*scale)
-    GGParams p{};
-    p.E = E; p.F = (int)F; p.d = (int)d; p.offsets = expert_offsets;
-    p.a = static_cast<const uint16_t*>(dy_perm); p.lda = (int)d;
-    p.b = As; p.ldb = (int)F;
-    p.out_m = (int)d; p.out_n = (int)F; p.outf = dw2; p.outf_estride = static_cast<size_t>(d) * F;
-    p.mts = (int)((d + kBM - 1) / kBM); p.nts = (int)((F + kBN - 1) / kBN);
-    p.accumulate = accumulate;
-    err = launch(ggb_kernel<EPI_WGRAD>, dim3(p.mts * p.nts * E), dim3(kGT), lds, stream, p);
-  }
-  if (err == hipSuccess) {
-    // fc1 wgrad: dW1[e] (2F x d) = dH^T X
-    GGParams p{};
-    p.E = E; p.F = (int)F; p.d = (int)d; p.offsets = expert_offsets;
-    p.a = dH; p.lda = (int)(2 * F);
-    p.b = static_cast<const uint16_t*>(x_perm); p.ldb = (int)d;
-    p.out_m = (int)(2 * F); p.out_n = (int)d; p.outf = dw1;
-    p.outf_estride = static_cast<size_t>(2 * F) * d;
-    p.mts = (int)((2 * F + kBM - 1) / kBM); p.nts = (int)((d + kBN - 1) / kBN);
-    p.accumulate = accumulate;
-    err = launch(ggb_kernel<EPI_WGRAD>, dim3(p.mts * p.nts * E), dim3(kGT), lds, stream, p);
-  }
+  // the two wgrad launches' tile counters sit in the workspace's slack
+  int* counters = reinterpret_cast<int*>(wsb + off + (recompute ? round_up256(static_cast<size_t>(N) * 2 * F * 2) : 0));
+  if (err == hipSuccess)      // fc2 wgrad: dW2[e] (d x F) = dY^T (A*scale)
+    err = launch_wgrad(stream, E, expert_offsets, static_cast<const uint16_t*>(dy_perm), (int)d,
+                       As, (int)F, dw2, (int)d, (int)F, accumulate, counters);
+  if (err == hipSuccess)      // fc1 wgrad: dW1[e] (2F x d) = dH^T X
+    err = launch_wgrad(stream, E, expert_offsets, dH, (int)(2 * F),
+                       static_cast<const uint16_t*>(x_perm), (int)d, dw1, (int)(2 * F), (int)d,
+                       accumulate, counters + 1);
   return hip_status(err);
 }
