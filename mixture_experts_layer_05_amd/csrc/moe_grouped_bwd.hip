@@ -85,6 +85,8 @@ struct GGParams {
   const uint16_t* gu_in;          // [N, 2F] (DGRAD2)
   uint16_t* out;                  // DGRAD2: dH [N,2F]; DGRAD1: dX [N,d]
   uint16_t* out2;                 // DGRAD2: A*scale [N,F]
+  int* zero;                      // 2 ints set to zero by workgroup 0 (or NULL): the
+                                  // following wgrad launches' tile counters
 };
 
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
@@ -328,6 +330,7 @@ __global__ __launch_bounds__(kGT, 2) void ggb_kernel(GGParams p) {
   extern __shared__ __align__(16) uint16_t s_lds[];   // kStages x (A tile + B tile)
   __shared__ int s_cum[1025];
   __shared__ int s_tmp[kWaves];
+  if (p.zero && blockIdx.x == 0 && threadIdx.x < 2) p.zero[threadIdx.x] = 0;
   tile_prefix<kGT>(p.offsets, p.E, kBM, p.ntn, s_cum, s_tmp);
   const int total = s_cum[p.E];
   if (static_cast<int>(blockIdx.x) >= total) return;
@@ -551,11 +554,10 @@ static unsigned wgrad_grid(int64_t tiles) {   // one workgroup per CU, at most o
 }
 
 // dW[e] (out_m x out_n) (+)= A[seg e]^T B[seg e] for every expert e.
+// (counter: one int, zero when the launch starts)
 static hipError_t launch_wgrad(hipStream_t stream, int32_t E, const int32_t* offsets,
                                const uint16_t* a, int lda, const uint16_t* b, int ldb, float* dw,
-                               int out_m, int out_n, int accumulate, int* counters) {
-  hipError_t err = launch_zero_counters(stream, counters, 1);
-  if (err != hipSuccess) return err;
+                               int out_m, int out_n, int accumulate, int* counter) {
   WgradParams p{};
   p.E = E; p.offsets = offsets;
   p.a = a; p.lda = lda; p.b = b; p.ldb = ldb;
@@ -564,8 +566,8 @@ static hipError_t launch_wgrad(hipStream_t stream, int32_t E, const int32_t* off
   p.mts = (out_m + kPM - 1) / kPM;
   p.nts = (out_n + kPN - 1) / kPN;
   p.accumulate = accumulate;
-  p.counter = counters;
-  err = allow_lds(ggw_persistent_kernel, kPLds);
+  p.counter = counter;
+  hipError_t err = allow_lds(ggw_persistent_kernel, kPLds);
   if (err != hipSuccess) return err;
   return launch(ggw_persistent_kernel, dim3(wgrad_grid(static_cast<int64_t>(p.mts) * p.nts * E)),
                 dim3(kPThreads), kPLds, stream, p);
@@ -631,6 +633,11 @@ extern "C" moe_status moe_grouped_swiglu_bwd(hipStream_t stream, moe_dtype dt, i
                                   nullptr, gu_r, As, false);
     gu = gu_r;
   }
+  // the two wgrad launches' tile counters sit in the workspace's slack; fc1
+  // dgrad's first workgroup zeroes them (a kernel when there are no rows)
+  int* counters = reinterpret_cast<int*>(
+      wsb + off + (recompute ? round_up256(static_cast<size_t>(N) * 2 * F * 2) : 0));
+  if (err == hipSuccess && N == 0) err = launch_zero_counters(stream, counters, 2);
   const size_t lds = kBwdLds;
   if (err == hipSuccess) err = allow_lds(ggb_kernel<EPI_DGRAD2>, lds);
   if (err == hipSuccess) err = allow_lds(ggb_kernel<EPI_DGRAD1>, lds);
@@ -653,11 +660,10 @@ extern "C" moe_status moe_grouped_swiglu_bwd(hipStream_t stream, moe_dtype dt, i
     p.a = dH; p.lda = (int)(2 * F);
     p.b = static_cast<const uint16_t*>(w1); p.ldb = (int)d; p.b_estride = static_cast<size_t>(2 * F) * d;
     p.K = (int)(2 * F); p.out = static_cast<uint16_t*>(dx_perm);
+    p.zero = counters;
     err = launch(ggb_kernel<EPI_DGRAD1>, dim3(tiles_bound(N, E, kBM) * p.ntn), dim3(kGT), lds,
                  stream, p);
   }
-  // the two wgrad launches' tile counters sit in the workspace's slack
-  int* counters = reinterpret_cast<int*>(wsb + off + (recompute ? round_up256(static_cast<size_t>(N) * 2 * F * 2) : 0));
   if (err == hipSuccess)      // fc2 wgrad: dW2[e] (d x F) = dY^T (A*scale)
     err = launch_wgrad(stream, E, expert_offsets, static_cast<const uint16_t*>(dy_perm), (int)d,
                        As, (int)F, dw2, (int)d, (int)F, accumulate, counters);
