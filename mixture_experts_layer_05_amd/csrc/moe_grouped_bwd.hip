@@ -364,11 +364,21 @@ __global__ __launch_bounds__(kGT, 2) void ggb_kernel(GGParams p) {
 // inner).  Workgroup b takes tiles b and b + grid, then fetches the next
 // from one counter as it starts each tile: the most expensive tiles go
 // first and the cheap ones fill the tail (longest-first list scheduling).
+// When the caller gives scratch space, the tiles of the heaviest experts
+// (more K steps than a workgroup's fair share of the launch) are split in
+// two halves along K: the first half writes dW as usual, the second writes
+// its partial tile to the scratch, and a second launch (ggw_fixup_kernel)
+// adds it, so every element is still formed in a fixed order.  The
+// heaviest expert's tiles would otherwise end the launch on their own
+// when an expert has few output tiles.
 constexpr int kPM = 256, kPN = 256, kPK = 64, kPWN = 4, kPRB = 2, kPCB = 2, kPWaves = 16;
 constexpr int kPThreads = 64 * kPWaves;
 constexpr int kPATileE = kPM * kPK, kPBTileE = kPN * kPK, kPSlotE = kPATileE + kPBTileE;
 constexpr size_t kPRing = 2 * kPSlotE * sizeof(uint16_t);   // 128 KB
 constexpr int kPLoads = kPATileE / 512 / kPWaves;          // 1 KB blocks per wave per operand (2)
+constexpr int kPEpiSteps = 6;        // a tile's epilogue (256 KB of fp32 stores) in K steps
+constexpr int kPMaxSplit = 256;      // split tiles per launch at most
+constexpr size_t kPSplitMeta = 4096; // scratch header: count, then (e, mt, nt) per split tile
 // LDS past the ring: expert order (1024 ints) and the fetch slot
 constexpr size_t kPLds = kPRing + (1024 + 4) * sizeof(int);
 
@@ -391,6 +401,9 @@ struct WgradParams {
   int mts, nts;              // 256-tiles per expert along m and n
   int accumulate;
   int* counter;              // tile counter, zero at launch
+  int* split_meta;           // scratch header (NULL: no split) ...
+  float* split_tiles;        // ... and split_cap partial 256 x 256 tiles after it
+  int split_cap;
 };
 
 __device__ __forceinline__ int wgrad_nk(int K) { return K > 0 ? (K + kPK - 1) / kPK : 1; }
@@ -408,7 +421,7 @@ __global__ __launch_bounds__(kPThreads, 1) void ggw_persistent_kernel(WgradParam
   const int per_e = p.mts * p.nts;
   const int total = per_e * E;
 
-  // ---- expert order (identical in every workgroup) -----------------------
+  // ---- expert order and split set (identical in every workgroup) --------
   for (int e = tid; e < E; e += kPThreads) s_K[e] = p.offsets[e + 1] - p.offsets[e];
   __syncthreads();
   for (int e = tid; e < E; e += kPThreads) {
@@ -421,20 +434,68 @@ __global__ __launch_bounds__(kPThreads, 1) void ggw_persistent_kernel(WgradParam
     s_order[rank] = e;
   }
   __syncthreads();
-  if (static_cast<int>(blockIdx.x) >= total) return;   // uniform over the workgroup
+  // split the experts (a prefix of the ranking) whose tiles hold more K
+  // steps than the launch's cost per workgroup, as far as the scratch allows
+  if (wave == 0) {
+    float c = 0.0f;
+    for (int e = lane; e < E; e += 64) c += static_cast<float>(wgrad_nk(s_K[e]) + kPEpiSteps);
+    c = wave_sum(c) * static_cast<float>(per_e);
+    const float share = c / static_cast<float>(gridDim.x);
+    if (lane == 0) {
+      int rs = 0;
+      if (p.split_meta) {
+        while (rs < E && (rs + 1) * per_e <= p.split_cap) {
+          const int nk = wgrad_nk(s_K[s_order[rs]]);
+          if (nk < 2 || static_cast<float>(nk) <= share) break;
+          ++rs;
+        }
+      }
+      *s_fetch = rs;
+    }
+  }
+  __syncthreads();
+  const int rs = *s_fetch;                       // split experts: ranks [0, rs)
+  const int nsplit = rs * per_e;                 // split tiles, two halves each
+  const int total_list = 2 * nsplit + (E - rs) * per_e;
+  if (p.split_meta && blockIdx.x == 0) {         // the list of split tiles for the fixup
+    for (int o = tid; o < nsplit; o += kPThreads) {
+      const int r = o / per_e, local = o - r * per_e;
+      const int nt = local / p.mts;
+      p.split_meta[1 + 3 * o] = s_order[r];
+      p.split_meta[2 + 3 * o] = local - nt * p.mts;
+      p.split_meta[3 + 3 * o] = nt;
+    }
+    if (tid == 0) p.split_meta[0] = nsplit;
+  }
+  __syncthreads();              // s_fetch is reused below; s_K (in the ring) is read above
+  if (static_cast<int>(blockIdx.x) >= total_list) return;   // uniform over the workgroup
 
   struct Tile {
-    int e, lo, K, nk, m0, n0;
+    int e, lo, kbeg, kend, nk, m0, n0, part, ord;   // part -1: whole K; 0, 1: halves
   };
   auto setup = [&](int gl) {    // gl: index in the tile list
     Tile t;
-    const int r = gl / per_e;
+    int r, local;
+    if (gl < 2 * nsplit) {      // split tiles first: (tile, half) pairs
+      t.ord = gl >> 1;
+      t.part = gl & 1;
+      r = t.ord / per_e;
+      local = t.ord - r * per_e;
+    } else {
+      const int g2 = gl - 2 * nsplit;
+      r = rs + g2 / per_e;
+      local = g2 - (r - rs) * per_e;
+      t.part = -1;
+      t.ord = 0;
+    }
     t.e = __builtin_amdgcn_readfirstlane(s_order[r]);
-    const int local = gl - r * per_e;
     const int nt = local / p.mts, mt = local - nt * p.mts;
     t.lo = __builtin_amdgcn_readfirstlane(p.offsets[t.e]);
-    t.K = __builtin_amdgcn_readfirstlane(p.offsets[t.e + 1]) - t.lo;
-    t.nk = wgrad_nk(t.K);
+    const int K = __builtin_amdgcn_readfirstlane(p.offsets[t.e + 1]) - t.lo;
+    const int half = ((wgrad_nk(K) + 1) / 2) * kPK;
+    t.kbeg = t.part == 1 ? half : 0;
+    t.kend = t.part == 0 ? half : K;
+    t.nk = wgrad_nk(t.kend - t.kbeg);
     t.m0 = mt * kPM;
     t.n0 = nt * kPN;
     return t;
@@ -452,11 +513,11 @@ __global__ __launch_bounds__(kPThreads, 1) void ggw_persistent_kernel(WgradParam
   // K tile kt of tile t into ring slot `slot`; rows past the segment (and
   // every row of an empty expert) read zero through the descriptors' size
   auto issue = [&](const Tile& t, int kt, int slot) {
-    const int k0 = kt * kPK;
-    const int krows = max(0, min(kPK, t.K - k0));
+    const int k0 = t.kbeg + kt * kPK;
+    const int krows = max(0, min(kPK, t.kend - k0));
     uint16_t* da = s_lds + slot * kPSlotE;
     uint16_t* db = da + kPATileE;
-    const size_t r0 = static_cast<size_t>(t.lo) + (krows > 0 ? k0 : 0);
+    const size_t r0 = static_cast<size_t>(t.lo) + (krows > 0 ? k0 : 0);   // (t.lo: in bounds)
     const i32x4 ra = uniform4(buf_desc(p.a + r0 * p.lda, krows * p.lda * 2));
     const i32x4 rb = uniform4(buf_desc(p.b + r0 * p.ldb, krows * p.ldb * 2));
 #pragma unroll
@@ -494,6 +555,18 @@ __global__ __launch_bounds__(kPThreads, 1) void ggw_persistent_kernel(WgradParam
   // accumulator register r of lane l: output row 8 (r / 4) + 4 (l / 32) + r % 4
   // of the 32-row block, column l % 32
   auto epilogue = [&](const Tile& t) {
+    if (t.part == 1) {          // second half: the partial tile, row-major 256 x 256
+      float* dst = p.split_tiles + static_cast<size_t>(t.ord) * (kPM * kPN);
+#pragma unroll
+      for (int rb = 0; rb < kPRB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * kPRB * 32 + rb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+#pragma unroll
+          for (int c = 0; c < kPCB; ++c) dst[row * kPN + wn * kPCB * 32 + c * 32 + r32] = acc[rb][c][r];
+        }
+      return;
+    }
     float* dw = p.outf + static_cast<size_t>(t.e) * p.outf_estride;
 #pragma unroll
     for (int rb = 0; rb < kPRB; ++rb) {
@@ -516,7 +589,7 @@ __global__ __launch_bounds__(kPThreads, 1) void ggw_persistent_kernel(WgradParam
 
   const int G = static_cast<int>(gridDim.x);
   Tile cur = setup(blockIdx.x);
-  bool has_nxt = static_cast<int>(blockIdx.x) + G < total;
+  bool has_nxt = static_cast<int>(blockIdx.x) + G < total_list;
   Tile nxt = has_nxt ? setup(blockIdx.x + G) : cur;
   issue(cur, 0, 0);
   int g = 0;                    // global K step: ring slot g & 1
@@ -543,10 +616,44 @@ __global__ __launch_bounds__(kPThreads, 1) void ggw_persistent_kernel(WgradParam
     epilogue(cur);
     if (!has_nxt) break;
     cur = nxt;
-    has_nxt = L2 < total;
+    has_nxt = L2 < total_list;
     if (has_nxt) nxt = setup(L2);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// dW[e] tile (mt, nt) += the second half's partial, for each split tile
+// listed by ggw_persistent_kernel: kFixBlocks workgroups per tile, 16 rows
+// each, one 16-byte vector per thread and row group (out_n % 8 == 0, so a
+// vector is wholly inside or outside the matrix).
+constexpr int kFixBlocks = kPM / 16;
+__global__ __launch_bounds__(256) void ggw_fixup_kernel(const int* __restrict__ meta,
+                                                        const float* __restrict__ tiles,
+                                                        float* __restrict__ dw, size_t estride,
+                                                        int out_m, int out_n) {
+  const int o = blockIdx.x / kFixBlocks, part = blockIdx.x % kFixBlocks;
+  if (o >= meta[0]) return;
+  const int e = meta[1 + 3 * o], m0 = meta[2 + 3 * o] * kPM, n0 = meta[3 + 3 * o] * kPN;
+  const float4* src = reinterpret_cast<const float4*>(tiles + static_cast<size_t>(o) * (kPM * kPN));
+  float* d = dw + static_cast<size_t>(e) * estride;
+  constexpr int kVecRow = kPN / 4;                   // 64 vectors per tile row
+  float4 v[4], w[4];
+  int idx[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {                      // rows part * 16 + 4u + threadIdx.x / 64
+    const int i = part * 16 * kVecRow + u * 256 + threadIdx.x;
+    const int r = i / kVecRow, c = (i - r * kVecRow) * 4;
+    idx[u] = (m0 + r < out_m && n0 + c < out_n) ? (m0 + r) * out_n + n0 + c : -1;
+    v[u] = src[i];
+    if (idx[u] >= 0) w[u] = *reinterpret_cast<const float4*>(d + idx[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if (idx[u] >= 0) {
+      float4 t = w[u];
+      t.x += v[u].x; t.y += v[u].y; t.z += v[u].z; t.w += v[u].w;
+      *reinterpret_cast<float4*>(d + idx[u]) = t;
+    }
 }
 
 static unsigned wgrad_grid(int64_t tiles) {   // one workgroup per CU, at most one per tile
@@ -554,11 +661,23 @@ static unsigned wgrad_grid(int64_t tiles) {   // one workgroup per CU, at most o
 }
 
 // dW[e] (out_m x out_n) (+)= A[seg e]^T B[seg e] for every expert e.
-// (counter: one int, zero when the launch starts)
+// (counter: one int, zero when the launch starts; split: scratch of
+// split_bytes for the K-split of the heaviest experts' tiles, or NULL)
 static hipError_t launch_wgrad(hipStream_t stream, int32_t E, const int32_t* offsets,
                                const uint16_t* a, int lda, const uint16_t* b, int ldb, float* dw,
-                               int out_m, int out_n, int accumulate, int* counter) {
+                               int out_m, int out_n, int accumulate, int* counter, void* split,
+                               size_t split_bytes) {
   WgradParams p{};
+  const size_t tile_bytes = static_cast<size_t>(kPM) * kPN * sizeof(float);
+  const int cap = split && split_bytes > kPSplitMeta
+                      ? static_cast<int>(std::min<size_t>(kPMaxSplit,
+                                                          (split_bytes - kPSplitMeta) / tile_bytes))
+                      : 0;
+  if (cap > 0) {
+    p.split_meta = static_cast<int*>(split);
+    p.split_tiles = reinterpret_cast<float*>(static_cast<uint8_t*>(split) + kPSplitMeta);
+    p.split_cap = cap;
+  }
   p.E = E; p.offsets = offsets;
   p.a = a; p.lda = lda; p.b = b; p.ldb = ldb;
   p.outf = dw; p.outf_estride = static_cast<size_t>(out_m) * out_n;
@@ -568,9 +687,14 @@ static hipError_t launch_wgrad(hipStream_t stream, int32_t E, const int32_t* off
   p.accumulate = accumulate;
   p.counter = counter;
   hipError_t err = allow_lds(ggw_persistent_kernel, kPLds);
-  if (err != hipSuccess) return err;
-  return launch(ggw_persistent_kernel, dim3(wgrad_grid(static_cast<int64_t>(p.mts) * p.nts * E)),
-                dim3(kPThreads), kPLds, stream, p);
+  if (err == hipSuccess)
+    err = launch(ggw_persistent_kernel, dim3(wgrad_grid(static_cast<int64_t>(p.mts) * p.nts * E)),
+                 dim3(kPThreads), kPLds, stream, p);
+  if (err == hipSuccess && cap > 0)
+    err = launch(ggw_fixup_kernel, dim3(static_cast<unsigned>(cap * kFixBlocks)), dim3(256), 0, stream,
+                 (const int*)p.split_meta, (const float*)p.split_tiles, dw, p.outf_estride, out_m,
+                 out_n);
+  return err;
 }
 
 }  // namespace moe
@@ -664,12 +788,13 @@ extern "C" moe_status moe_grouped_swiglu_bwd(hipStream_t stream, moe_dtype dt, i
     err = launch(ggb_kernel<EPI_DGRAD1>, dim3(tiles_bound(N, E, kBM) * p.ntn), dim3(kGT), lds,
                  stream, p);
   }
-  if (err == hipSuccess)      // fc2 wgrad: dW2[e] (d x F) = dY^T (A*scale)
-    err = launch_wgrad(stream, E, expert_offsets, static_cast<const uint16_t*>(dy_perm), (int)d,
-                       As, (int)F, dw2, (int)d, (int)F, accumulate, counters);
   if (err == hipSuccess)      // fc1 wgrad: dW1[e] (2F x d) = dH^T X
     err = launch_wgrad(stream, E, expert_offsets, dH, (int)(2 * F),
                        static_cast<const uint16_t*>(x_perm), (int)d, dw1, (int)(2 * F), (int)d,
-                       accumulate, counters + 1);
+                       accumulate, counters + 1, nullptr, 0);
+  if (err == hipSuccess)      // fc2 wgrad: dW2[e] (d x F) = dY^T (A*scale); dH is free now
+    err = launch_wgrad(stream, E, expert_offsets, static_cast<const uint16_t*>(dy_perm), (int)d,
+                       As, (int)F, dw2, (int)d, (int)F, accumulate, counters, dH,
+                       static_cast<size_t>(N) * 2 * F * 2);
   return hip_status(err);
 }

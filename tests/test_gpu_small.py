@@ -251,6 +251,11 @@ def _segments(rng, E, pattern, scale):
         c = np.zeros(E, dtype=np.int64)
         c[E // 2] = scale
         return c
+    if pattern == "heavy":                      # one expert holds most rows
+        c = rng.integers(0, max(2, scale // 30), E)
+        c[0] = scale
+        c[2 % E] = 0
+        return c
     raise ValueError(pattern)
 
 
@@ -437,6 +442,9 @@ BWD_CASES = [
     (7, 136, 72, "ragged", 200, True, True, False),
     (4, 128, 128, "ragged", 300, False, True, True),
     (3, 256, 192, "one_hot", 517, True, False, True),
+    # one dominant expert: its weight-gradient tiles are split along K
+    (5, 128, 64, "heavy", 3000, True, True, False),
+    (4, 256, 192, "heavy", 2500, False, False, True),
 ]
 
 
