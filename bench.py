@@ -58,6 +58,9 @@ MEASURED_TRAFFIC = {
     # profiles/grouped_gemm_fwd_dsv_30b_hbm_bytes.md
     "dsv_30b": {"bytes": 5299556073,
                 "sources_sha256": "9ac5b346b3d4a16b0f90cb449fd61534b9ca9b89e45db3f95bbd6768c665d72a"},
+    # profiles/grouped_gemm_fwd_skew_shared_hbm_bytes.md
+    "skew_shared": {"bytes": 4135248019,
+                    "sources_sha256": "9ac5b346b3d4a16b0f90cb449fd61534b9ca9b89e45db3f95bbd6768c665d72a"},
     "qwen3_30b:fp8": {"bytes": 968175082,
                       "sources_sha256": "fd3ccfc338831cb541c75dc991b9f4c50b4c92e76e3ee9485ef1455f23544ccd"},
 }
