@@ -196,7 +196,9 @@ MOE_API moe_status moe_permute_noalloc(hipStream_t stream, moe_dtype dt, int64_t
  *                                (saved for the backward)
  * Workspace: moe_grouped_swiglu_fwd_workspace_size(N, F, dt) bytes.
  * Limits: E <= 1024, d % 8 == 0, F % 8 == 0, N >= 0, 4*F*d < 2^31 (one
- * expert's fc1 weights addressable with 32-bit byte offsets).
+ * expert's fc1 weights addressable with 32-bit byte offsets).  N = 0 (every
+ * expert empty) computes nothing; x_perm, y_perm and the workspace may then
+ * be NULL.
  * --------------------------------------------------------------------- */
 MOE_API size_t moe_grouped_swiglu_fwd_workspace_size(int64_t N, int64_t F, moe_dtype dt);
 MOE_API moe_status moe_grouped_swiglu_fwd(hipStream_t stream, moe_dtype dt, int64_t N,
@@ -354,7 +356,10 @@ MOE_API moe_status moe_grouped_swiglu_fwd_mx(hipStream_t stream, int64_t N, int6
  *   dx_perm    [N, d]      dt    out
  *   dw1        [E, 2F, d]  fp32  out
  *   dw2        [E, d, F]   fp32  out
- * Workspace: moe_grouped_swiglu_bwd_workspace_size(N, F, dt, recompute).
+ * Workspace: moe_grouped_swiglu_bwd_workspace_size(N, F, dt, recompute)
+ * (needed also when N = 0: it holds the weight gradient's tile counters).
+ * N = 0 (every expert empty) writes dw1, dw2 as zeros (or leaves them when
+ * accumulating); dy_perm, x_perm and dx_perm may then be NULL.
  * Only MOE_BF16 is implemented (MOE_F32 returns MOE_ERR_UNSUPPORTED).
  * --------------------------------------------------------------------- */
 MOE_API size_t moe_grouped_swiglu_bwd_workspace_size(int64_t N, int64_t F, moe_dtype dt,

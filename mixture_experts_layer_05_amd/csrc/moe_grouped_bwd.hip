@@ -733,7 +733,8 @@ extern "C" moe_status moe_grouped_swiglu_bwd(hipStream_t stream, moe_dtype dt, i
   moe_status st = moe_grouped_check(dt, N, d, F, E);
   if (st != MOE_OK) return st;
   if (dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
-  if (!dy_perm || !x_perm || !w1 || !w2 || !expert_offsets || !dx_perm || !dw1 || !dw2)
+  // with no rows (N = 0) the row buffers may be empty (NULL); dW is still written
+  if (!w1 || !w2 || !expert_offsets || !dw1 || !dw2 || (N > 0 && (!dy_perm || !x_perm || !dx_perm)))
     return MOE_ERR_INVALID_ARG;
   if (!aligned16(dy_perm) || !aligned16(x_perm) || !aligned16(w1) || !aligned16(w2) ||
       !aligned16(expert_offsets) || !aligned16(gu_save) || !aligned16(row_scale) ||

@@ -1039,13 +1039,14 @@ static moe_status grouped_fwd(hipStream_t stream, moe_dtype dt, int64_t N, int64
   if (packed && 2 * std::max(pack_expert_elems(2 * F, d, 1), pack_expert_elems(d, F, 0)) >=
                     (int64_t(1) << 31))
     return MOE_ERR_SHAPE;
-  if (!x || !w1 || !w2 || !expert_offsets || !y_perm) return MOE_ERR_INVALID_ARG;
+  // with no rows (N = 0) the row buffers may be empty (NULL) and nothing runs
+  if (!w1 || !w2 || !expert_offsets || (N > 0 && (!x || !y_perm))) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(w1) || !aligned16(w2) || !aligned16(expert_offsets) ||
       !aligned16(row_scale) || !aligned16(y_perm) || !aligned16(gu_save) || !aligned16(ws) ||
       !aligned16(gather))
     return MOE_ERR_ALIGNMENT;
-  if (!ws || ws_bytes < moe_grouped_swiglu_fwd_workspace_size(N, F, dt)) return MOE_ERR_WORKSPACE;
   if (N == 0) return MOE_OK;
+  if (!ws || ws_bytes < moe_grouped_swiglu_fwd_workspace_size(N, F, dt)) return MOE_ERR_WORKSPACE;
   if (dt == MOE_BF16) {
     return hip_status(launch_grouped_fwd_bf16(stream, N, d, F, E, x, w1, w2, expert_offsets,
                                               row_scale, y_perm, gu_save,

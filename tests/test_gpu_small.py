@@ -445,6 +445,8 @@ BWD_CASES = [
     # one dominant expert: its weight-gradient tiles are split along K
     (5, 128, 64, "heavy", 3000, True, True, False),
     (4, 256, 192, "heavy", 2500, False, False, True),
+    # the most experts the calls take, a third of them empty
+    (1024, 64, 64, "ragged", 8, True, True, False),
 ]
 
 
@@ -492,6 +494,29 @@ def test_grouped_bwd_parity(case):
             continue
         assert gh.normwise(dw1[e], dw1_ref[e]) <= gh.TOL_BF16_GRAD, e
         assert gh.normwise(dw2[e], dw2_ref[e]) <= gh.TOL_BF16_GRAD, e
+
+
+@pytest.mark.parametrize("acc", [False, True])
+def test_grouped_no_rows(acc):
+    """N = 0 (every expert empty, e.g. an expert-parallel rank that receives
+    no tokens): the forward computes nothing, the backward writes dW = 0, or
+    leaves dW as it was when accumulating."""
+    E, d, F = 3, 64, 64
+    inp = mw.make_small_layer_inputs(77, T=1, d=d, E=E, F=F, dtype="bf16", w_std=0.05)
+    w1, w2 = gh.to_gpu(inp.w1), gh.to_gpu(inp.w2)
+    off = gh.to_gpu(np.zeros(E + 1, dtype=np.int32))
+    x = torch.empty((0, d), dtype=torch.bfloat16, device=gh.dev())
+    y, _ = moe.grouped_swiglu_fwd(x, w1, w2, off)
+    torch.cuda.synchronize()
+    assert y.shape == (0, d)
+    base = 0.75 if acc else float("nan")
+    dw1 = torch.full((E, 2 * F, d), base, dtype=torch.float32, device=gh.dev())
+    dw2 = torch.full((E, d, F), base, dtype=torch.float32, device=gh.dev())
+    dx = torch.empty((0, d), dtype=torch.bfloat16, device=gh.dev())
+    moe.grouped_swiglu_bwd(x, x, w1, w2, off, None, None, acc, dw1, dw2, dx_out=dx)
+    torch.cuda.synchronize()
+    want = 0.75 if acc else 0.0
+    assert torch.all(dw1 == want).item() and torch.all(dw2 == want).item()
 
 
 COMB_CASES = [(1, 64, 1, "bf16", False), (300, 136, 6, "bf16", True),
