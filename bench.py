@@ -53,14 +53,15 @@ KERNEL_SOURCES_FP8 = ("mixture_experts_layer_05_amd/csrc/moe_grouped_mx.hip",
                       "mixture_experts_layer_05_amd/csrc/moe_device.h")
 # (fp8: profiles/fp8_grouped_gemm_qwen3_30b_hbm_bytes.md, the quantiser + fc1 + fc2)
 MEASURED_TRAFFIC = {
-    "qwen3_30b": {"bytes": 1628074639,
-                  "sources_sha256": "9ac5b346b3d4a16b0f90cb449fd61534b9ca9b89e45db3f95bbd6768c665d72a"},
+    # profiles/grouped_gemm_fwd_qwen3_30b_hbm_bytes.md
+    "qwen3_30b": {"bytes": 1626372661,
+                  "sources_sha256": "553b5e9f988cc230e30e89101303f4e532b0e1e4b583652613a5d852ff3bcd76"},
     # profiles/grouped_gemm_fwd_dsv_30b_hbm_bytes.md
-    "dsv_30b": {"bytes": 5299556073,
-                "sources_sha256": "9ac5b346b3d4a16b0f90cb449fd61534b9ca9b89e45db3f95bbd6768c665d72a"},
+    "dsv_30b": {"bytes": 5232850537,
+                "sources_sha256": "553b5e9f988cc230e30e89101303f4e532b0e1e4b583652613a5d852ff3bcd76"},
     # profiles/grouped_gemm_fwd_skew_shared_hbm_bytes.md
-    "skew_shared": {"bytes": 4135248019,
-                    "sources_sha256": "9ac5b346b3d4a16b0f90cb449fd61534b9ca9b89e45db3f95bbd6768c665d72a"},
+    "skew_shared": {"bytes": 4262793751,
+                    "sources_sha256": "553b5e9f988cc230e30e89101303f4e532b0e1e4b583652613a5d852ff3bcd76"},
     "qwen3_30b:fp8": {"bytes": 968175082,
                       "sources_sha256": "fd3ccfc338831cb541c75dc991b9f4c50b4c92e76e3ee9485ef1455f23544ccd"},
 }
