@@ -69,9 +69,15 @@ __device__ inline int xcd_remap(int b, int total) {
 // logical tile -> (expert, row tile, column tile) given s_cum from tile_prefix.
 // An expert's n rows are split over ceil(n / bm) row tiles of equal height
 // h = ceil(n / tiles) rounded up to 32 (h <= bm, every tile non-empty), e.g.
-// 260 rows at bm = 128 as 96 + 96 + 68 rather than 128 + 128 + 4.
-__device__ inline TileIdx tile_decode(const int32_t* __restrict__ offsets, int E, int bm, int L,
-                                      const int* s_cum) {
+// 260 rows at bm = 128 as 96 + 96 + 68 rather than 128 + 128 + 4.  An
+// expert's tiles are consecutive: column tiles outer and row tiles inner
+// (the row tiles of one weight panel run together and share it in L2), or,
+// for an expert with more row tiles than column tiles (a heavily routed one),
+// row tiles outer and column tiles inner, so that each row tile's token rows
+// are read by its ntn column tiles together instead of once per pass over
+// the expert's row tiles.
+__device__ inline TileIdx tile_decode(const int32_t* __restrict__ offsets, int E, int bm, int ntn,
+                                      int L, const int* s_cum) {
   int lo = 0, hi = E - 1;
   while (lo < hi) {  // largest e with s_cum[e] <= L (that expert is non-empty)
     const int mid = (lo + hi + 1) >> 1;
@@ -84,8 +90,13 @@ __device__ inline TileIdx tile_decode(const int32_t* __restrict__ offsets, int E
   const int n = t.hi - t.lo;
   const int mts = (n + bm - 1) / bm;
   const int local = L - s_cum[lo];
-  t.nt = local / mts;
-  t.mt = local - t.nt * mts;
+  if (mts > ntn) {
+    t.mt = local / ntn;
+    t.nt = local - t.mt * ntn;
+  } else {
+    t.nt = local / mts;
+    t.mt = local - t.nt * mts;
+  }
   const int h = ((n + mts - 1) / mts + 31) & ~31;
   t.m0 = t.lo + t.mt * h;
   t.mend = min(t.m0 + h, t.hi);

@@ -334,7 +334,7 @@ __global__ __launch_bounds__(kGT, 2) void ggb_kernel(GGParams p) {
   tile_prefix<kGT>(p.offsets, p.E, kBM, p.ntn, s_cum, s_tmp);
   const int total = s_cum[p.E];
   if (static_cast<int>(blockIdx.x) >= total) return;
-  const TileIdx ti = tile_decode(p.offsets, p.E, kBM, xcd_remap(blockIdx.x, total), s_cum);
+  const TileIdx ti = tile_decode(p.offsets, p.E, kBM, p.ntn, xcd_remap(blockIdx.x, total), s_cum);
   const int m0 = ti.m0;
   const int rows = ti.mend - m0 - (static_cast<int>(threadIdx.x >> 6) / kWN) * kRB * 32;
   const int nrb = rows <= 0 ? 0 : min(kRB, (rows + 31) >> 5);

@@ -432,7 +432,7 @@ __global__ __launch_bounds__(C::kThreads, C::kWgPerCu) void ggf_kernel(FwdParams
     tile_prefix<C::kThreads>(p.offsets, p.E, C::kBM, p.ntn, s_cum, s_tmp);
     const int total = s_cum[p.E];
     if (static_cast<int>(blockIdx.x) >= total) return;
-    ti = tile_decode(p.offsets, p.E, C::kBM, xcd_remap(blockIdx.x, total), s_cum);
+    ti = tile_decode(p.offsets, p.E, C::kBM, p.ntn, xcd_remap(blockIdx.x, total), s_cum);
     __syncthreads();   // every wave has decoded its tile before the ring overwrites s_cum
   } else {
     const int total = ((p.rows1 + C::kBM - 1) / C::kBM) * p.ntn;
@@ -530,7 +530,7 @@ __device__ __forceinline__ void ggfp_body(const FwdParams& p) {
   // per-tile addressing: decode, descriptors, per-lane source offsets
   using TileState = PersistTile<kLoads>;
   auto setup = [&](int j, TileState& st) {
-    st.ti = tile_decode(p.offsets, p.E, kBM, xbeg + pos + j * g8, s_cum);
+    st.ti = tile_decode(p.offsets, p.E, kBM, p.ntn, xbeg + pos + j * g8, s_cum);
     const TileIdx& ti = st.ti;
     const int m0 = ti.m0, n0 = ti.nt * nbn, last = ti.mend - 1 - m0;
     st.ra = __builtin_amdgcn_make_buffer_rsrc(
@@ -800,7 +800,7 @@ __global__ __launch_bounds__(256) void ggf_f32_kernel(int E, int F, int d, int K
   tile_prefix<256>(offsets, E, kFM, ntn, s_cum, s_tmp);
   const int total = s_cum[E];
   if (static_cast<int>(blockIdx.x) >= total) return;
-  const TileIdx ti = tile_decode(offsets, E, kFM, blockIdx.x, s_cum);
+  const TileIdx ti = tile_decode(offsets, E, kFM, ntn, blockIdx.x, s_cum);
   const int m0 = ti.m0;
   const int nt = ti.nt;
   const float* bexp = b + static_cast<size_t>(ti.e) * b_estride;

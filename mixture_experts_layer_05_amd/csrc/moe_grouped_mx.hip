@@ -242,7 +242,7 @@ __device__ __forceinline__ void ggmx_body(const MxParams& p) {
   auto setup = [&](int j, int L, MxTile& st) {
     st.j = j;
     st.L = L;
-    st.ti = tile_decode(p.offsets, p.E, kMxBM, xr.xbeg + L, s_cum);
+    st.ti = tile_decode(p.offsets, p.E, kMxBM, p.ntn, xr.xbeg + L, s_cum);
     const TileIdx& ti = st.ti;
     const int m0 = ti.m0, last = ti.mend - 1 - m0;
     st.ra = __builtin_amdgcn_make_buffer_rsrc(
