@@ -54,16 +54,16 @@ KERNEL_SOURCES_FP8 = ("mixture_experts_layer_05_amd/csrc/moe_grouped_mx.hip",
 # (fp8: profiles/fp8_grouped_gemm_qwen3_30b_hbm_bytes.md, the quantiser + fc1 + fc2)
 MEASURED_TRAFFIC = {
     # profiles/grouped_gemm_fwd_qwen3_30b_hbm_bytes.md
-    "qwen3_30b": {"bytes": 1626372661,
-                  "sources_sha256": "553b5e9f988cc230e30e89101303f4e532b0e1e4b583652613a5d852ff3bcd76"},
+    "qwen3_30b": {"bytes": 1628942193,
+                  "sources_sha256": "067e83380d4a868a195bc15b320f9427d0d749805293a2dc537b5e13ee592ad6"},
     # profiles/grouped_gemm_fwd_dsv_30b_hbm_bytes.md
-    "dsv_30b": {"bytes": 5232850537,
-                "sources_sha256": "553b5e9f988cc230e30e89101303f4e532b0e1e4b583652613a5d852ff3bcd76"},
+    "dsv_30b": {"bytes": 5322381764,
+                "sources_sha256": "067e83380d4a868a195bc15b320f9427d0d749805293a2dc537b5e13ee592ad6"},
     # profiles/grouped_gemm_fwd_skew_shared_hbm_bytes.md
-    "skew_shared": {"bytes": 4262793751,
-                    "sources_sha256": "553b5e9f988cc230e30e89101303f4e532b0e1e4b583652613a5d852ff3bcd76"},
-    "qwen3_30b:fp8": {"bytes": 968175082,
-                      "sources_sha256": "fd3ccfc338831cb541c75dc991b9f4c50b4c92e76e3ee9485ef1455f23544ccd"},
+    "skew_shared": {"bytes": 3677405320,
+                    "sources_sha256": "067e83380d4a868a195bc15b320f9427d0d749805293a2dc537b5e13ee592ad6"},
+    "qwen3_30b:fp8": {"bytes": 974513090,
+                      "sources_sha256": "cc9226e910fbe871cc4a62f7541fb53d030f83e6a9a61958ca382ade00700e93"},
 }
 
 
