@@ -68,6 +68,9 @@ typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
  * "Expert Parallel 基础" shows top-6 sigmoid routing). */
 typedef enum moe_score_fn { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score_fn;
 
+/* Tokens per histogram block of moe_route's block_counts and moe_permute. */
+#define MOE_ROUTE_BLOCK_TOKENS 64
+
 /* Version of this ABI (incremented on any signature change). */
 MOE_API int32_t moe_abi_version(void);
 /* Static, human-readable name of a status code. */
@@ -98,10 +101,16 @@ MOE_API const char* moe_status_string(moe_status s);
  *   topk_idx   [T, k]  int32     out
  *   topk_w     [T, k]  fp32      out
  *   expert_counts [E]  int32     out: tokens routed to each expert
+ *   block_counts [ceil(T / MOE_ROUTE_BLOCK_TOKENS), E] int32
+ *                                out, or NULL: row b counts the choices of
+ *                                tokens [64 b, 64 b + 64) per expert (the
+ *                                histogram moe_permute can take in place of
+ *                                its own counting pass)
  *   gate       [T]     fp32      out, or NULL
  * Limits: 1 <= k <= min(E, 32); 1 <= E <= 1024; d % 8 == 0; T >= 1;
  * 16*T*E < 2^31.  Workspace: moe_route_workspace_size(T, d, E, dt) bytes (the
- * fp32 logits, up to 16 K slabs).  A NaN score is never chosen; a token with fewer than k
+ * fp32 logits, up to 16 K slabs, and for bf16 the K slabs of the gate's dot
+ * product).  A NaN score is never chosen; a token with fewer than k
  * selectable scores gets index E (out of range) for the missing slots.
  * --------------------------------------------------------------------- */
 MOE_API size_t moe_route_workspace_size(int64_t T, int64_t d, int32_t E, moe_dtype dt);
@@ -110,7 +119,8 @@ MOE_API moe_status moe_route(hipStream_t stream, moe_dtype dt, int64_t T, int64_
                      const void* x, const void* w_router,
                      const float* logit_bias, const float* selection_bias,
                      const void* w_gate, int32_t* topk_idx, float* topk_w,
-                     int32_t* expert_counts, float* gate, void* ws, size_t ws_bytes);
+                     int32_t* expert_counts, int32_t* block_counts, float* gate,
+                     void* ws, size_t ws_bytes);
 
 /* ------------------------------------------------------------------------
  * moe_permute -- regroup token copies into per-expert contiguous segments.
@@ -128,6 +138,10 @@ MOE_API moe_status moe_route(hipStream_t stream, moe_dtype dt, int64_t T, int64_
  *   x          [T, d]  dt        in
  *   topk_idx   [T, k]  int32     in, values in [0, E)
  *   topk_w     [T, k]  fp32      in, or NULL (then row_w must be NULL)
+ *   block_counts [ceil(T / MOE_ROUTE_BLOCK_TOKENS), E] int32
+ *                                in, or NULL: moe_route's block_counts for
+ *                                this topk_idx (skips the counting pass; not
+ *                                modified); NULL: counted here
  *   expert_offsets [E+1] int32   out
  *   slot_of    [T, k]  int32     out
  *   row_token  [T*k]   int32     out
@@ -145,6 +159,7 @@ MOE_API size_t moe_permute_workspace_size(int64_t T, int32_t E, int32_t k);
 MOE_API moe_status moe_permute(hipStream_t stream, moe_dtype dt, int64_t T, int64_t d,
                        int32_t E, int32_t k, const void* x,
                        const int32_t* topk_idx, const float* topk_w,
+                       const int32_t* block_counts,
                        int32_t* expert_offsets, int32_t* slot_of,
                        int32_t* row_token, float* row_w, void* x_perm,
                        void* ws, size_t ws_bytes);
@@ -154,12 +169,13 @@ MOE_API moe_status moe_permute(hipStream_t stream, moe_dtype dt, int64_t T, int6
  *
  * For callers that cannot allocate device memory around the call (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
- * Same arguments, outputs and results as moe_permute, minus ws / ws_bytes:
+ * Same arguments, outputs and results as moe_permute, minus block_counts
+ * (always counted here) and ws / ws_bytes:
  * the scratch (per-block expert histograms and per-expert totals) lives in a
  * static device array of 4 MiB inside the library, one per GPU, held until
  * the process ends.  Nothing is allocated or freed by the call.
- *   Limit: moe_permute_workspace_size(T, E, k) <= 4 MiB (e.g. T*k/floor(256/k)
- *   blocks of E counts: T = 16384, k = 8, E = 256 needs 0.5 MiB); larger
+ *   Limit: moe_permute_workspace_size(T, E, k) <= 4 MiB (ceil(T / 64) rows
+ *   of E counts: T = 16384, E = 256 needs 0.25 MiB); larger
  *   shapes return MOE_ERR_WORKSPACE.  MOE_ERR_HIP if the array's device
  *   address cannot be obtained.
  *   Concurrency: every call on one GPU uses the same array; calls that

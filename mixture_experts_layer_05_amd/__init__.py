@@ -43,11 +43,11 @@ EXPORTED = {
     "moe_status_string": (ctypes.c_char_p, [_i32]),
     "moe_route_workspace_size": (_sz, [_i64, _i64, _i32, _i32]),
     "moe_route": (_i32, [_vp, _i32, _i64, _i64, _i32, _i32, _i32, _i32,
-                         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz]),
+                         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz]),
     "moe_permute_workspace_size": (_sz, [_i64, _i32, _i32]),
     "moe_permute_noalloc": (_i32, [_vp, _i32, _i64, _i64, _i32, _i32, _vp, _vp, _vp,
                                    _vp, _vp, _vp, _vp, _vp]),
-    "moe_permute": (_i32, [_vp, _i32, _i64, _i64, _i32, _i32, _vp, _vp, _vp,
+    "moe_permute": (_i32, [_vp, _i32, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp,
                            _vp, _vp, _vp, _vp, _vp, _vp, _sz]),
     "moe_grouped_swiglu_fwd_workspace_size": (_sz, [_i64, _i64, _i32]),
     "moe_grouped_swiglu_fwd": (_i32, [_vp, _i32, _i64, _i64, _i64, _i32,
@@ -141,9 +141,20 @@ def route_workspace_size(T, d, E, dtype):
     return lib().moe_route_workspace_size(T, d, E, MOE_BF16 if dtype == torch.bfloat16 else MOE_F32)
 
 
+ROUTE_BLOCK_TOKENS = 64   # MOE_ROUTE_BLOCK_TOKENS
+
+
+def route_block_counts(T, E, device):
+    """An int32 buffer for route()'s per-64-token-block expert histograms."""
+    return torch.empty(((T + ROUTE_BLOCK_TOKENS - 1) // ROUTE_BLOCK_TOKENS, E), dtype=torch.int32,
+                       device=device)
+
+
 def route(x, w_router, k, score="softmax", normalize=True, logit_bias=None,
-          w_gate=None, out=None, ws=None, selection_bias=None):
-    """-> (topk_idx [T,k] int32, topk_w [T,k] fp32, counts [E] int32, gate [T] or None)"""
+          w_gate=None, out=None, ws=None, selection_bias=None, block_counts=None):
+    """-> (topk_idx [T,k] int32, topk_w [T,k] fp32, counts [E] int32, gate [T] or None).
+    block_counts (route_block_counts(T, E)): also filled with the block
+    histograms that permute(block_counts=...) takes."""
     T, d = x.shape
     E = w_router.shape[0]
     dev = x.device
@@ -157,7 +168,8 @@ def route(x, w_router, k, score="softmax", normalize=True, logit_bias=None,
         ws = _ws(route_workspace_size(T, d, E, x.dtype), dev)
     _check(lib().moe_route(_stream(), _dt(x), T, d, E, k, SCORE[score], int(bool(normalize)),
                            _p(x), _p(w_router), _p(logit_bias), _p(selection_bias), _p(w_gate),
-                           _p(idx), _p(w), _p(cnt), _p(gate), _p(ws), ws.numel()), "moe_route")
+                           _p(idx), _p(w), _p(cnt), _p(block_counts), _p(gate), _p(ws), ws.numel()),
+           "moe_route")
     return idx, w, cnt, gate
 
 
@@ -165,10 +177,11 @@ def permute_workspace_size(T, E, k):
     return lib().moe_permute_workspace_size(T, E, k)
 
 
-def permute(x, topk_idx, topk_w, E, out=None, ws=None, copy_rows=True):
+def permute(x, topk_idx, topk_w, E, out=None, ws=None, copy_rows=True, block_counts=None):
     """-> (expert_offsets [E+1], slot_of [T,k], row_token [N], row_w [N] or None,
     x_perm [N,d] or None).  copy_rows=False skips the row copy (for a consumer
-    that gathers rows by row_token)."""
+    that gathers rows by row_token); block_counts: route()'s block histograms
+    of this topk_idx (skips the counting pass)."""
     T, d = x.shape
     k = topk_idx.shape[1]
     N = T * k
@@ -186,7 +199,8 @@ def permute(x, topk_idx, topk_w, E, out=None, ws=None, copy_rows=True):
     if not copy_rows:
         xp = None
     _check(lib().moe_permute(_stream(), _dt(x), T, d, E, k, _p(x), _p(topk_idx), _p(topk_w),
-                             _p(off), _p(slot), _p(rtok), _p(rw), _p(xp), _p(ws), ws.numel()),
+                             _p(block_counts), _p(off), _p(slot), _p(rtok), _p(rw), _p(xp),
+                             _p(ws), ws.numel()),
            "moe_permute")
     return off, slot, rtok, rw, xp
 
@@ -554,6 +568,7 @@ class MoELayer:
                          None if gather else torch.empty((N, d), dtype=dt, device=dev))
         self.perm_ws = _ws(permute_workspace_size(T, E, k), dev)
         self.route_ws = _ws(route_workspace_size(T, d, E, dt), dev)
+        self.block_counts = route_block_counts(T, E, dev)   # route -> permute
         self.y_perm = torch.empty((N, d), dtype=dt, device=dev)
         self.gu = torch.empty((N, 2 * self.F), dtype=dt, device=dev) if save_gu else None
         ws_f = fwd_workspace_size(N, self.F, dt)
@@ -715,12 +730,12 @@ class MoELayer:
         def route_():
             st["r"] = route(x, self.w_router, self.k, self.score, self.normalize,
                             self.logit_bias, self.w_gate, out=self.route_out, ws=self.route_ws,
-                            selection_bias=self.selection_bias)
+                            selection_bias=self.selection_bias, block_counts=self.block_counts)
 
         def permute_():
             idx, w, _, _ = st["r"]
             st["p"] = permute(x, idx, w, self.E, out=self.perm_out, ws=self.perm_ws,
-                              copy_rows=not self.gather)
+                              copy_rows=not self.gather, block_counts=self.block_counts)
 
         def experts_():
             off, _, rtok, rw, xp = st["p"]
@@ -752,9 +767,11 @@ class MoELayer:
             x.record_stream(self.side)
         idx, w, cnt, gate = route(x, self.w_router, self.k, self.score, self.normalize,
                                   self.logit_bias, self.w_gate, out=self.route_out,
-                                  ws=self.route_ws, selection_bias=self.selection_bias)
+                                  ws=self.route_ws, selection_bias=self.selection_bias,
+                                  block_counts=self.block_counts)
         off, slot, rtok, rw, xp = permute(x, idx, w, self.E, out=self.perm_out, ws=self.perm_ws,
-                                          copy_rows=not self.gather)
+                                          copy_rows=not self.gather,
+                                          block_counts=self.block_counts)
         rs = None if self.train else rw      # training: weights applied in combine
         self._routed(x, None if self.gather else xp, rtok, off, rs)
         ysh, sgate = None, None

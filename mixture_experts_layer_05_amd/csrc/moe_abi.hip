@@ -3,7 +3,7 @@
 
 #include "moe_internal.h"
 
-extern "C" int32_t moe_abi_version(void) { return 9; }
+extern "C" int32_t moe_abi_version(void) { return 10; }
 
 extern "C" const char* moe_status_string(moe_status s) {
   switch (s) {

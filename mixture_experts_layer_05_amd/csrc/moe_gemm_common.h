@@ -187,8 +187,14 @@ hipError_t launch_grouped_fwd_bf16(hipStream_t stream, int64_t N, int64_t d, int
 // `ksplit` slabs: logits[s][T][E] = x[:, slab s] W_r[:, slab s]^T (+ bias
 // on slab 0), fp32.  bf16 only.
 int router_ksplit(int64_t T, int64_t d, int32_t E);
+// With gate_w ([d] shared-gate weights), also gate_out[s][T] = x[:, slab s]
+// . gate_w[slab s] (fp32), when router_gate_fused(T, d, E) (the slab's gate
+// weights fit in LDS beside the rings).  zero_counts: E ints set to zero
+// (for the top-k kernel that follows), or NULL.
+bool router_gate_fused(int64_t T, int64_t d, int32_t E);
 hipError_t launch_router_logits_bf16(hipStream_t stream, int64_t T, int64_t d, int32_t E,
                                     const void* x, const void* w_router, const float* bias,
-                                    float* logits, int ksplit);
+                                    float* logits, int ksplit, const void* gate_w = nullptr,
+                                    float* gate_out = nullptr, int32_t* zero_counts = nullptr);
 
 }  // namespace moe

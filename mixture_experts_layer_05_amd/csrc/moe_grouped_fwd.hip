@@ -134,6 +134,10 @@ struct FwdParams {
   float* outf;                                // LOGITS: z [N, d] fp32 (d = output columns)
   int ksplit;                                 // K split into gridDim.y slabs (LOGITS)
   size_t outf_split;                          // LOGITS: elements between slabs
+  const uint16_t* gate_w;                     // LOGITS: [K] shared-gate weights, or NULL
+  float* gate_out;                            // LOGITS: [ksplit][rows1] x . gate_w per slab
+  int32_t* zero_i32;                          // LOGITS: zero_n ints zeroed by workgroup 0, or NULL
+  int zero_n;
 };
 
 // chunk permutation of staged row r (see the file comment)
@@ -213,6 +217,27 @@ __device__ __forceinline__ void ggf_tile(const FwdParams& p, const TileIdx& ti, 
   const int kt_lo = min(nk_all, static_cast<int>(blockIdx.y) * kchunk);
   const int kt_hi = min(nk_all, kt_lo + kchunk);
 
+  // Router logits with a shared-expert gate: the first column tile of each
+  // row block also forms x . gate_w over its K slab from the token rows
+  // already staged for the MFMAs (two threads per row, four 16-byte chunks
+  // each per K tile).  The slab's gate weights go to LDS behind the rings,
+  // 1 KB per direct load, issued before the ring's own loads, so the ring's
+  // first wait and barrier cover them.  (The top-k kernel sums the slabs.)
+  constexpr bool kGateOk = kEpi == FWD_LOGITS && C::kThreads == 2 * kBM && kChunks == 8;
+  const bool do_gate = kGateOk && p.gate_w != nullptr && ti.nt == 0;
+  uint16_t* const s_gw = s_lds + C::kLdsBytes / 2;      // [kchunk * kBK] bf16
+  float gsum = 0.0f;
+  if constexpr (kGateOk) {
+    if (do_gate) {
+      const __amdgpu_buffer_rsrc_t rs_g = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(p.gate_w), 0, K * 2, kRsrcWord3);   // past K: zeros
+      const int nblk = ((kt_hi - kt_lo) * kBK * 2 + 1023) / 1024;
+      for (int b = wave; b < nblk; b += kWaves)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_g, (lds_void*)(s_gw + b * 512), 16,
+                                                 kt_lo * kBK * 2 + b * 1024 + lane * 16, 0, 0, 0);
+    }
+  }
+
   // LDS: the A ring (kStages slots), then the B ring (kStagesB slots)
   uint16_t* const ring_b = s_lds + kStages * C::kATileE;
   // fetch the A (token rows) or B (weights) part of K tile kt (clamped to
@@ -286,6 +311,30 @@ __device__ __forceinline__ void ggf_tile(const FwdParams& p, const TileIdx& ti, 
     }
   };
 
+  // this thread's part of the gate dot product for K tile kt: row tid / 2,
+  // chunks 4 (tid % 2) .. +3 of the staged A tile
+  auto gate_step = [&](int kt) {
+    if constexpr (kGateOk) {
+      const uint16_t* As = s_lds + ((kt - kt_lo) % kStages) * C::kATileE;
+      const int r = tid >> 1;
+      const uint16_t* gw = s_gw + (kt - kt_lo) * kBK;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int kc = 4 * (tid & 1) + q;
+        const u32x4 a = *reinterpret_cast<const u32x4*>(As + swz(r, kc));
+        const u32x4 w = *reinterpret_cast<const u32x4*>(gw + kc * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // (through scalars: a bit_cast of a vector element itself reads
+          // element 0 whatever the index, with this compiler)
+          const uint32_t ae = a[e], we = w[e];
+          gsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, ae),
+                                                 __builtin_bit_cast(bf16x2v, we), gsum, false);
+        }
+      }
+    }
+  };
+
   // Rings: A tiles kt+1 .. kt+kStages-1 and B tiles kt+1 .. kt+kStagesB-1
   // stay in flight while tile kt is multiplied.  The wait leaves the later
   // tiles' loads in flight (kRingWait), the barrier extends "tile kt landed"
@@ -305,9 +354,19 @@ __device__ __forceinline__ void ggf_tile(const FwdParams& p, const TileIdx& ti, 
       issue_a(kt + kStages - 1);
       issue_b(kt + kStagesB - 1);
       compute(kt);
+      if (do_gate) gate_step(kt);
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain the clamped extra loads
+  if constexpr (kGateOk) {
+    if (do_gate) {
+      // the row = its low half's sum + its high half's sum
+      const float other = __shfl_xor(gsum, 1, kWave);
+      const int r = tid >> 1;
+      if ((tid & 1) == 0 && m0 + r < ti.mend)
+        p.gate_out[blockIdx.y * static_cast<size_t>(p.rows1) + m0 + r] = gsum + other;
+    }
+  }
 
   // ---------------- epilogue ------------------------------------------------
   // fc1 / fc2: the MFMAs take the weight block as their first operand, so
@@ -427,6 +486,8 @@ __global__ __launch_bounds__(C::kThreads, C::kWgPerCu) void ggf_kernel(FwdParams
   extern __shared__ __align__(16) uint16_t s_lds[];
   int* s_cum = reinterpret_cast<int*>(s_lds);
   int* s_tmp = s_cum + 1040;
+  if (p.zero_i32 && blockIdx.x == 0 && blockIdx.y == 0)   // (the next kernel's counters)
+    for (int i = threadIdx.x; i < p.zero_n; i += C::kThreads) p.zero_i32[i] = 0;
   TileIdx ti;
   if (p.offsets) {
     tile_prefix<C::kThreads>(p.offsets, p.E, C::kBM, p.ntn, s_cum, s_tmp);
@@ -625,7 +686,7 @@ __device__ __forceinline__ void ggfp_body(const FwdParams& p) {
   constexpr int kPass = (kBM + kPassRows - 1) / kPassRows;
   constexpr int kChunksRow = kCols / 8;
   static_assert(C::kATileE * 2 == 32768 && C::kBTileE * 2 == 32768, "32 KB ring slots");
-  static_assert(kRR % (kRB * 32) == 0 && kBM % kPassRows == 0, "waves stage whole regions");
+  static_assert(kPassRows % (kRB * 32) == 0 && kBM % kPassRows == 0, "waves stage whole passes");
   const int limit = kEpi == FWD_FC1 ? p.F : p.d;
   auto epilogue = [&](const TileIdx& ti, int nrb, int free_slot) {
     const int m0 = ti.m0, n0 = ti.nt * nbn;
@@ -993,9 +1054,21 @@ int router_ksplit(int64_t T, int64_t d, int32_t E) {
   return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(s, 16)));
 }
 
+static size_t router_lds(int64_t d, int ksplit, bool gate) {
+  using C = RouterCfg;
+  const int64_t kchunk = ((d + C::kBK - 1) / C::kBK + ksplit - 1) / ksplit;
+  const size_t gbytes = (static_cast<size_t>(kchunk) * C::kBK * 2 + 1023) / 1024 * 1024;
+  return C::kLdsBytes + (gate ? gbytes : 0);
+}
+
+bool router_gate_fused(int64_t T, int64_t d, int32_t E) {
+  return router_lds(d, router_ksplit(T, d, E), true) <= 160 * 1024;
+}
+
 hipError_t launch_router_logits_bf16(hipStream_t stream, int64_t T, int64_t d, int32_t E,
                                     const void* x, const void* w_router, const float* bias,
-                                    float* logits, int ksplit) {
+                                    float* logits, int ksplit, const void* gate_w,
+                                    float* gate_out, int32_t* zero_counts) {
   using C = RouterCfg;
   FwdParams p{};
   p.E = 1; p.F = 1; p.d = E; p.offsets = nullptr; p.rows1 = (int)T;
@@ -1008,10 +1081,17 @@ hipError_t launch_router_logits_bf16(hipStream_t stream, int64_t T, int64_t d, i
   p.outf = logits;
   p.ksplit = ksplit;
   p.outf_split = static_cast<size_t>(T) * E;
-  hipError_t err = allow_lds(ggf_kernel<C, FWD_LOGITS>, C::kLdsBytes);
+  p.gate_w = static_cast<const uint16_t*>(gate_w);
+  p.gate_out = gate_out;
+  p.zero_i32 = zero_counts;
+  p.zero_n = E;
+  // the gate weights of one K slab sit behind the rings
+  const size_t lds = router_lds(d, ksplit, gate_w != nullptr);
+  if (lds > 160 * 1024) return hipErrorInvalidValue;
+  hipError_t err = allow_lds(ggf_kernel<C, FWD_LOGITS>, lds);
   if (err != hipSuccess) return err;
   return launch(ggf_kernel<C, FWD_LOGITS>, dim3(tiles_bound(T, 1, C::kBM) * p.ntn, ksplit),
-                dim3(C::kThreads), C::kLdsBytes, stream, p);
+                dim3(C::kThreads), lds, stream, p);
 }
 
 }  // namespace moe

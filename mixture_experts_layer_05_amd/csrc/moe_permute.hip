@@ -5,16 +5,23 @@
 // (after dispatch the tokens sit grouped by expert) and section "Permute
 // Fusion" (the permute is a memory copy of the hidden states).
 //
-// Pairs are taken token-major (pair p = t*k + j) and cut into blocks of
-// P = floor(256 / k) * k pairs.  Row of a pair with expert e in block b:
+// Pairs are taken token-major (pair p = t*k + j) and cut into blocks of 64
+// tokens (the blocks of moe_route's histogram rows).  Row of a pair with
+// expert e in block b:
 //     off[e] + sum_{b' < b} H[b'][e] + #{earlier pairs of block b with e}
 // which is exactly the stable order (expert, token, slot).  No atomics
 // decide an order, so the result is deterministic.
-//   K1 hist    : H[b][e] per block (LDS histogram)
-//   K2 colscan : per expert, exclusive scan of H[.][e] over blocks, in
-//                place; total count per expert
+//   K1 hist    : H[b][e] per block (LDS histogram); skipped when the caller
+//                passes moe_route's block histograms
+//   K2 colscan : per expert, exclusive scan of H[.][e] over blocks; total
+//                count per expert
 //   K3 rows    : every block rebuilds off[] from the totals (LDS scan),
-//                ranks its pairs, writes slot_of / row_token / row_w
+//                ranks its pairs, writes slot_of / row_token / row_w.  The
+//                rank of a pair is the number of earlier tokens of the block
+//                that chose the same expert: a 64-bit mask of the block's
+//                tokens per expert (LDS atomic OR, order-free) and a
+//                popcount below the token.  A block where a token names one
+//                expert twice ranks by counting earlier pairs instead.
 //   K4 copy    : one wavefront per token reads x[t] once (16-byte lanes)
 //                and writes it to its k rows
 #include <mutex>
@@ -24,11 +31,11 @@
 namespace moe {
 
 constexpr int kPermThreads = 256;
-
-__host__ __device__ inline int perm_tokens_per_block(int k) {
-  const int tb = kPermThreads / k;
-  return tb > 0 ? tb : 1;
-}
+constexpr int kPermRow = MOE_ROUTE_BLOCK_TOKENS;   // tokens per histogram row
+constexpr int kPermBlk = 64;                       // tokens per ranking block (a 64-bit mask)
+constexpr int kRowsPerBlk = kPermBlk / kPermRow;
+constexpr int kPermMaxPairs = kPermBlk * 32;       // k <= 32
+static_assert(kPermBlk % kPermRow == 0, "rows tile the blocks");
 
 // inclusive scan of one value per thread over a 256-thread block
 __device__ inline int block_incl_scan(int v, int* s_tmp) {
@@ -49,13 +56,11 @@ __device__ inline int block_incl_scan(int v, int* s_tmp) {
 __global__ __launch_bounds__(kPermThreads) void perm_hist_kernel(
     int T, int E, int k, const int32_t* __restrict__ topk_idx, int32_t* __restrict__ H) {
   extern __shared__ int s_cnt[];
-  const int tb = perm_tokens_per_block(k);
-  const int64_t p0 = static_cast<int64_t>(blockIdx.x) * tb * k;
-  const int64_t pend = static_cast<int64_t>(T) * k;
+  const int64_t p0 = static_cast<int64_t>(blockIdx.x) * kPermRow * k;
+  const int64_t pend = min(static_cast<int64_t>(T) * k, p0 + static_cast<int64_t>(kPermRow) * k);
   for (int e = threadIdx.x; e < E; e += kPermThreads) s_cnt[e] = 0;
   __syncthreads();
-  const int64_t p = p0 + threadIdx.x;
-  if (threadIdx.x < tb * k && p < pend) {
+  for (int64_t p = p0 + threadIdx.x; p < pend; p += kPermThreads) {
     const int e = topk_idx[p];
     if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);
   }
@@ -64,18 +69,19 @@ __global__ __launch_bounds__(kPermThreads) void perm_hist_kernel(
   for (int e = threadIdx.x; e < E; e += kPermThreads) hrow[e] = s_cnt[e];
 }
 
-// one block per expert: exclusive scan of column e of H (in place)
+// one block per expert: exclusive scan of column e of H over the blocks
+// (dst may equal src)
 __global__ __launch_bounds__(kPermThreads) void perm_colscan_kernel(
-    int nblk, int E, int32_t* __restrict__ H, int32_t* __restrict__ total) {
+    int nblk, int E, const int32_t* src, int32_t* dst, int32_t* __restrict__ total) {
   __shared__ int s_tmp[4];
   __shared__ int s_last;
   const int e = blockIdx.x;
   int carry = 0;
   for (int b0 = 0; b0 < nblk; b0 += kPermThreads) {
     const int b = b0 + threadIdx.x;
-    const int v = b < nblk ? H[static_cast<size_t>(b) * E + e] : 0;
+    const int v = b < nblk ? src[static_cast<size_t>(b) * E + e] : 0;
     const int inc = block_incl_scan(v, s_tmp);
-    if (b < nblk) H[static_cast<size_t>(b) * E + e] = carry + inc - v;
+    if (b < nblk) dst[static_cast<size_t>(b) * E + e] = carry + inc - v;
     if (threadIdx.x == kPermThreads - 1) s_last = inc;   // chunk total
     __syncthreads();
     carry += s_last;
@@ -90,10 +96,12 @@ __global__ __launch_bounds__(kPermThreads) void perm_rows_kernel(
     const int32_t* __restrict__ total, int32_t* __restrict__ expert_offsets,
     int32_t* __restrict__ slot_of, int32_t* __restrict__ row_token,
     float* __restrict__ row_w) {
-  extern __shared__ int smem[];
-  int* s_off = smem;               // [E + 1]
-  int* s_e = smem + E + 1;         // [256]
+  extern __shared__ __align__(8) int smem[];
+  unsigned long long* s_mask = reinterpret_cast<unsigned long long*>(smem);   // [E]
+  int* s_off = smem + 2 * E;                                                  // [E + 1]
+  int* s_e = s_off + E + 1;                                                   // [64 k]
   __shared__ int s_tmp[4];
+  __shared__ int s_dup;
   const int tid = threadIdx.x;
 
   // off[] = exclusive scan of the per-expert totals (each thread 4 experts)
@@ -114,28 +122,46 @@ __global__ __launch_bounds__(kPermThreads) void perm_rows_kernel(
     run += loc[q];
   }
   if (tid == kPermThreads - 1) s_off[E] = incl;
+  for (int e = tid; e < E; e += kPermThreads) s_mask[e] = 0ull;
+  if (tid == 0) s_dup = 0;
   __syncthreads();
   if (blockIdx.x == 0)
     for (int e = tid; e <= E; e += kPermThreads) expert_offsets[e] = s_off[e];
 
-  const int tb = perm_tokens_per_block(k);
-  const int64_t p = static_cast<int64_t>(blockIdx.x) * tb * k + tid;
-  const bool inblk = tid < tb * k && p < static_cast<int64_t>(T) * k;
-  int e = inblk ? topk_idx[p] : -1;
-  if (e < 0 || e >= E) e = -1;
-  s_e[tid] = e;
-  __syncthreads();
-  if (!inblk) return;
-  if (e < 0) {
-    slot_of[p] = -1;
-    return;
+  // the block's pairs: expert of each (-1: dropped) and each expert's tokens
+  const int64_t p0 = static_cast<int64_t>(blockIdx.x) * kPermBlk * k;
+  const int np = static_cast<int>(min(static_cast<int64_t>(T) * k - p0,
+                                      static_cast<int64_t>(kPermBlk) * k));
+  for (int i = tid; i < np; i += kPermThreads) {
+    int e = topk_idx[p0 + i];
+    if (e < 0 || e >= E) e = -1;
+    s_e[i] = e;
+    if (e >= 0) {
+      const unsigned long long bit = 1ull << (i / k);
+      if (atomicOr(&s_mask[e], bit) & bit) s_dup = 1;   // a token names e twice
+    }
   }
-  int rank = 0;
-  for (int q = 0; q < tid; ++q) rank += (s_e[q] == e);
-  const int row = s_off[e] + H[static_cast<size_t>(blockIdx.x) * E + e] + rank;
-  slot_of[p] = row;
-  row_token[row] = static_cast<int>(p / k);
-  if (row_w) row_w[row] = topk_w[p];
+  __syncthreads();
+  const bool dup = s_dup != 0;
+  const int32_t* hrow = H + static_cast<size_t>(blockIdx.x) * kRowsPerBlk * E;   // its first row
+  for (int i = tid; i < np; i += kPermThreads) {
+    const int64_t p = p0 + i;
+    const int e = s_e[i];
+    if (e < 0) {
+      slot_of[p] = -1;
+      continue;
+    }
+    int rank = 0;
+    if (!dup) {
+      rank = __popcll(s_mask[e] & ((1ull << (i / k)) - 1ull));
+    } else {
+      for (int q = 0; q < i; ++q) rank += (s_e[q] == e);
+    }
+    const int row = s_off[e] + hrow[e] + rank;
+    slot_of[p] = row;
+    row_token[row] = static_cast<int>(p / k);
+    if (row_w) row_w[row] = topk_w[p];
+  }
 }
 
 // one wavefront per token: read the row once, write it to its k rows
@@ -196,14 +222,14 @@ using namespace moe;
 
 extern "C" size_t moe_permute_workspace_size(int64_t T, int32_t E, int32_t k) {
   if (T < 1 || E < 1 || k < 1) return 0;
-  const int64_t tb = perm_tokens_per_block(k);
-  const int64_t nblk = (T + tb - 1) / tb;
-  return static_cast<size_t>((nblk * E + E) * sizeof(int32_t) + 256);
+  const int64_t nrow = (T + kPermRow - 1) / kPermRow;
+  return static_cast<size_t>((nrow * E + E) * sizeof(int32_t) + 256);
 }
 
 extern "C" moe_status moe_permute(hipStream_t stream, moe_dtype dt, int64_t T, int64_t d,
                                   int32_t E, int32_t k, const void* x,
                                   const int32_t* topk_idx, const float* topk_w,
+                                  const int32_t* block_counts,
                                   int32_t* expert_offsets, int32_t* slot_of,
                                   int32_t* row_token, float* row_w, void* x_perm,
                                   void* ws, size_t ws_bytes) {
@@ -217,23 +243,27 @@ extern "C" moe_status moe_permute(hipStream_t stream, moe_dtype dt, int64_t T, i
   if (row_bytes % 16) return MOE_ERR_ALIGNMENT;
   if (!aligned16(x) || !aligned16(x_perm) || !aligned16(topk_idx) || !aligned16(topk_w) ||
       !aligned16(expert_offsets) || !aligned16(slot_of) || !aligned16(row_token) ||
-      !aligned16(row_w) || !aligned16(ws))
+      !aligned16(row_w) || !aligned16(block_counts) || !aligned16(ws))
     return MOE_ERR_ALIGNMENT;
   if (!ws || ws_bytes < moe_permute_workspace_size(T, E, k)) return MOE_ERR_WORKSPACE;
 
-  const int tb = perm_tokens_per_block(k);
-  const int nblk = static_cast<int>((T + tb - 1) / tb);
+  const int nrow = static_cast<int>((T + kPermRow - 1) / kPermRow);
+  const int nblk = static_cast<int>((T + kPermBlk - 1) / kPermBlk);
   int32_t* H = static_cast<int32_t*>(ws);
-  int32_t* total = H + static_cast<size_t>(nblk) * E;
+  int32_t* total = H + static_cast<size_t>(nrow) * E;
 
-  hipError_t err = launch(perm_hist_kernel, dim3(nblk), dim3(kPermThreads),
-                          E * sizeof(int), stream, (int)T, E, k, topk_idx, H);
+  hipError_t err = hipSuccess;
+  if (!block_counts)
+    err = launch(perm_hist_kernel, dim3(nrow), dim3(kPermThreads), E * sizeof(int), stream, (int)T,
+                 E, k, topk_idx, H);
   if (err == hipSuccess)
-    err = launch(perm_colscan_kernel, dim3(E), dim3(kPermThreads), 0, stream, nblk, E, H, total);
+    err = launch(perm_colscan_kernel, dim3(E), dim3(kPermThreads), 0, stream, nrow, E,
+                 block_counts ? block_counts : static_cast<const int32_t*>(H), H, total);
   if (err == hipSuccess)
     err = launch(perm_rows_kernel, dim3(nblk), dim3(kPermThreads),
-                 (E + 1 + kPermThreads) * sizeof(int), stream, (int)T, E, k, topk_idx, topk_w,
-                 H, total, expert_offsets, slot_of, row_token, row_w);
+                 (3 * E + 1 + kPermMaxPairs) * sizeof(int), stream, (int)T, E, k, topk_idx,
+                 topk_w, (const int32_t*)H, (const int32_t*)total, expert_offsets, slot_of,
+                 row_token, row_w);
   if (err == hipSuccess && x_perm)   // NULL x_perm: the consumer gathers rows by row_token
     err = launch(perm_copy_kernel, dim3(static_cast<unsigned>((T + 3) / 4)), dim3(kPermThreads),
                  0, stream, (int)T, k, static_cast<int>(row_bytes / 16), slot_of,
@@ -253,6 +283,6 @@ extern "C" moe_status moe_permute_noalloc(hipStream_t stream, moe_dtype dt, int6
     return MOE_ERR_WORKSPACE;   // more scratch than the static array holds
   void* ws = perm_scratch_ptr();
   if (!ws) return MOE_ERR_HIP;
-  return moe_permute(stream, dt, T, d, E, k, x, topk_idx, topk_w, expert_offsets, slot_of,
-                     row_token, row_w, x_perm, ws, kPermScratchInts * sizeof(int32_t));
+  return moe_permute(stream, dt, T, d, E, k, x, topk_idx, topk_w, nullptr, expert_offsets,
+                     slot_of, row_token, row_w, x_perm, ws, kPermScratchInts * sizeof(int32_t));
 }

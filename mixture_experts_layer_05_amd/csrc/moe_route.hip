@@ -1,35 +1,43 @@
-// moe_route: router logits, score function, wavefront top-k, weight
-// normalisation, per-expert counts and the shared-expert gate.
+// moe_route: router logits, score function, top-k, weight normalisation,
+// per-expert counts and the shared-expert gate.
 //
 // Passage: "Megatron-Bridge 深度剖析", section "MoE 加速深度剖析 / Expert
 // Parallel 基础", step 1 of the diagram: the router turns each token into
 // its top-k experts with scores (top-6 sigmoid in the example); the score
 // function is a TransformerConfig choice (section "Megatron-Core 架构速览").
 //
+// Two launches:
 //   1. logits z[T, E] (fp32, in the workspace): bf16 runs the grouped-GEMM
 //      forward kernel as a one-group GEMM with a bias epilogue (MFMA, LDS
-//      ring), K split into slabs; fp32 runs a plain FMA dot product per
-//      (token, expert);
-//   2. route_topk: one wavefront per token; lane l holds the scores of
-//      experts l, l+64, ...; k rounds of a wave-wide arg-max (ties to the
-//      lower expert index) pick the experts in descending score order (or
+//      ring), K split into slabs, and (when the slab's gate weights fit in
+//      LDS) the K slabs of x . w_gate from the same staged token rows; fp32
+//      runs a plain FMA dot product per (token, expert).  Either kernel
+//      also zeroes expert_counts.
+//   2. route_topk: a group of G lanes per token (G = 16 for E <= 256, four
+//      tokens per wavefront; G = 64 above), 64 tokens per workgroup; lane i
+//      of a group holds the scores of experts i, i + G, ...; k rounds of a
+//      group-wide arg-max (ties to the lower expert index, reduced with DPP
+//      row operations) pick the experts in descending score order (or
 //      descending score + selection bias, when a selection-only expert bias
-//      is given: the weights still come from the unbiased scores); the
-//      workgroup's choices are counted in LDS and written as one histogram
-//      row; the gate is a wave-wide dot product x[t] . w_gate;
-//   3. route_count: counts[e] = sum of the histogram rows (one workgroup per
-//      expert; no global atomics, so a hot expert costs nothing extra).
+//      is given: the weights still come from the unbiased scores).  The
+//      workgroup's choices are counted in LDS; the counts are added to
+//      expert_counts (integer atomics: the sums do not depend on their
+//      order) and optionally written as the 64-token block's histogram row,
+//      which moe_permute can take instead of counting again.
+#include <climits>
+
 #include "moe_gemm_common.h"
 
 namespace moe {
 
-constexpr int kTopkThreads = 1024;  // 16 tokens per workgroup, one per wave
-constexpr int kTopkTokens = kTopkThreads / 64;
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkBlk = MOE_ROUTE_BLOCK_TOKENS;   // tokens per workgroup and histogram row
 
 __global__ __launch_bounds__(256) void route_logits_f32_kernel(
     int T, int d, int E, const float* __restrict__ x, const float* __restrict__ wr,
-    const float* __restrict__ bias, float* __restrict__ z) {
+    const float* __restrict__ bias, float* __restrict__ z, int32_t* __restrict__ zero_counts) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (zero_counts && idx < E) zero_counts[idx] = 0;
   if (idx >= static_cast<int64_t>(T) * E) return;
   const int t = static_cast<int>(idx / E), e = static_cast<int>(idx - static_cast<int64_t>(t) * E);
   const float4* xr = reinterpret_cast<const float4*>(x + static_cast<size_t>(t) * d);
@@ -45,169 +53,241 @@ __global__ __launch_bounds__(256) void route_logits_f32_kernel(
   z[idx] = acc + (bias ? bias[e] : 0.0f);
 }
 
-// One wavefront per token.  kPer = scores held per lane (E <= 64 kPer).
-template <bool kBF16, int kPer>
+// Reductions over a group of G lanes (16: one DPP row; 64: the wavefront),
+// the result in every lane of the group, in a fixed order.
+template <int G>
+__device__ __forceinline__ float grp_max(float v) {
+  v = fmaxf(v, __int_as_float(dpp_<kDppXor1>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_<kDppXor2>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_<kDppHalfMirror>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_<kDppMirror>(__float_as_int(v))));
+  if constexpr (G == 64) {
+    const int b = __float_as_int(v);
+    v = fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 0)),
+                    __int_as_float(__builtin_amdgcn_readlane(b, 16))),
+              fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 32)),
+                    __int_as_float(__builtin_amdgcn_readlane(b, 48))));
+  }
+  return v;
+}
+template <int G>
+__device__ __forceinline__ int grp_min(int v) {
+  v = min(v, dpp_<kDppXor1>(v));
+  v = min(v, dpp_<kDppXor2>(v));
+  v = min(v, dpp_<kDppHalfMirror>(v));
+  v = min(v, dpp_<kDppMirror>(v));
+  if constexpr (G == 64)
+    v = min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+            min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+  return v;
+}
+// pairs, quads, half rows, rows (then rows 0..3 for G = 64)
+template <int G>
+__device__ __forceinline__ float grp_sum(float v) {
+  v += __int_as_float(dpp_<kDppXor1>(__float_as_int(v)));
+  v += __int_as_float(dpp_<kDppXor2>(__float_as_int(v)));
+  v += __int_as_float(dpp_<kDppHalfMirror>(__float_as_int(v)));
+  v += __int_as_float(dpp_<kDppMirror>(__float_as_int(v)));
+  if constexpr (G == 64) {
+    const int b = __float_as_int(v);
+    v = (__int_as_float(__builtin_amdgcn_readlane(b, 0)) +
+         __int_as_float(__builtin_amdgcn_readlane(b, 16))) +
+        (__int_as_float(__builtin_amdgcn_readlane(b, 32)) +
+         __int_as_float(__builtin_amdgcn_readlane(b, 48)));
+  }
+  return v;
+}
+
+// G lanes per token, kPer = ceil(E / G) scores per lane; 1024 threads take
+// the workgroup's 64 tokens in 64 / (16 * 64 / G) passes.  A token's lanes
+// are all active or all inactive, so the row-wise DPP reads only its own
+// lanes.
+template <bool kBF16, int G, int kPer>
 __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
     int T, int d, int E, int k, int score_fn, int normalize, int nslab, const float* __restrict__ z,
     const float* __restrict__ sel_bias, const void* __restrict__ xv, const void* __restrict__ wgv,
-    int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w, int32_t* __restrict__ hist, float* __restrict__ gate) {
+    const float* __restrict__ gz, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    int32_t* __restrict__ counts, int32_t* __restrict__ block_counts, float* __restrict__ gate) {
+  static_assert(G == 16 || G == 64, "group width");
+  constexpr int kTokPass = kTopkThreads / G;           // tokens per pass
+  static_assert(kTopkBlk % kTokPass == 0, "passes cover the block");
+  constexpr int kSlots = (32 + G - 1) / G;             // choices held per lane (k <= 32)
   extern __shared__ int s_cnt[];     // [E] histogram of this workgroup's choices
   for (int e = threadIdx.x; e < E; e += kTopkThreads) s_cnt[e] = 0;
   __syncthreads();
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * kTopkTokens + (threadIdx.x >> 6);
-  if (t < T) {
-  // logits = sum of the K slabs, in slab order (the loads of 8 slabs are
-  // issued before their sum, not one round trip per slab)
+  const int gi = threadIdx.x & (G - 1);
   const size_t slab = static_cast<size_t>(T) * E;
-  const float* zrow = z + static_cast<size_t>(t) * E;
-  float p[kPer];
+#pragma unroll 1
+  for (int pass = 0; pass < kTopkBlk / kTokPass; ++pass) {
+    const int t = blockIdx.x * kTopkBlk + pass * kTokPass + threadIdx.x / G;
+    if (t >= T) continue;
+    // logits = sum of the K slabs, in slab order (a batch of slabs' loads
+    // is issued before their sum)
+    const float* zrow = z + static_cast<size_t>(t) * E;
+    float p[kPer];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) p[i] = 0.0f;
-  for (int s0 = 0; s0 < nslab; s0 += 8) {
-    float v[8][kPer];
+    for (int j = 0; j < kPer; ++j) p[j] = 0.0f;
+    constexpr int kQ = kPer >= 16 ? 2 : (kPer >= 8 ? 4 : 8);   // slabs per batch
+    for (int s0 = 0; s0 < nslab; s0 += kQ) {
+      float v[kQ][kPer];
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
+      for (int q = 0; q < kQ; ++q)
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const int e = lane + 64 * i;
-        v[q][i] = (s0 + q < nslab && e < E) ? zrow[(s0 + q) * slab + e] : 0.0f;
-      }
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-#pragma unroll
-      for (int i = 0; i < kPer; ++i)
-        if (s0 + q < nslab) p[i] += v[q][i];
-  }
-  if (score_fn == MOE_SCORE_SOFTMAX) {
-    float m = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i)
-      if (lane + 64 * i < E) m = fmaxf(m, p[i]);
-    m = wave_max_dpp(m);
-    float s = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      p[i] = (lane + 64 * i < E) ? expf(p[i] - m) : 0.0f;
-      s += p[i];
-    }
-    s = wave_sum_dpp(s);
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) p[i] = (lane + 64 * i < E) ? p[i] / s : -INFINITY;
-  } else {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) p[i] = (lane + 64 * i < E) ? sigmoidf_(p[i]) : -INFINITY;
-  }
-  // ranking keys: the scores, or score + selection bias (fp32)
-  float key[kPer];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int e = lane + 64 * i;
-    key[i] = (sel_bias && e < E) ? p[i] + sel_bias[e] : p[i];
-  }
-  // k rounds: the largest remaining key (wave max), then the lowest expert
-  // index holding it (wave min); both reductions stay in registers (DPP).
-  uint32_t taken = 0;
-  int my_e = E;
-  float my_p = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = E;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      // strict '>' keeps the lower expert index among equal keys
-      if (!((taken >> i) & 1u) && key[i] > bv) { bv = key[i]; bi = lane + 64 * i; }
-    }
-    const float mv = wave_max_dpp(bv);
-    bi = wave_min_dpp(bv == mv ? bi : 0x7fffffff);
-    bi = bi < E ? bi : E;
-    // the winner's (unbiased) score, from the lane that holds it
-    float pw = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i)
-      if (i == (bi >> 6)) pw = p[i];
-    pw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pw), bi & 63));
-    if (bi < E && (bi & 63) == lane) taken |= 1u << (bi >> 6);
-    if (lane == j) { my_e = bi; my_p = pw; }
-  }
-  float denom = 1.0f;
-  if (normalize) denom = wave_sum_dpp(lane < k ? my_p : 0.0f);
-  if (lane < k) {
-    topk_idx[static_cast<size_t>(t) * k + lane] = my_e;
-    topk_w[static_cast<size_t>(t) * k + lane] = normalize ? my_p / denom : my_p;
-    if (my_e < E) atomicAdd(&s_cnt[my_e], 1);   // LDS integer atomics: order-free
-  }
-  if (gate) {
-    // the row's loads go out four (bf16: 4 x 1 KB per wave) or eight at a
-    // time before their products are summed, in the same order as one at a
-    // time (past d: 0 * 0, which leaves g unchanged)
-    float g = 0.0f;
-    if constexpr (kBF16) {
-      const uint16_t* xr = static_cast<const uint16_t*>(xv) + static_cast<size_t>(t) * d;
-      const uint16_t* wg = static_cast<const uint16_t*>(wgv);
-      for (int k0 = lane * 8; k0 < d; k0 += 4 * 512) {
-        u32x4 a[4], b[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int k8 = k0 + u * 512;
-          a[u] = k8 < d ? *reinterpret_cast<const u32x4*>(xr + k8) : u32x4{0, 0, 0, 0};
-          b[u] = k8 < d ? *reinterpret_cast<const u32x4*>(wg + k8) : u32x4{0, 0, 0, 0};
+        for (int j = 0; j < kPer; ++j) {
+          const int e = gi + G * j;
+          v[q][j] = (s0 + q < nslab && e < E) ? zrow[(s0 + q) * slab + e] : 0.0f;
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+      for (int q = 0; q < kQ; ++q)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            g = fmaf(bf16lo(a[u][q]), bf16lo(b[u][q]), g);
-            g = fmaf(bf16hi(a[u][q]), bf16hi(b[u][q]), g);
-          }
+        for (int j = 0; j < kPer; ++j)
+          if (s0 + q < nslab) p[j] += v[q][j];
+    }
+    if (score_fn == MOE_SCORE_SOFTMAX) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j)
+        if (gi + G * j < E) m = fmaxf(m, p[j]);
+      m = grp_max<G>(m);
+      float s = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        p[j] = (gi + G * j < E) ? expf(p[j] - m) : 0.0f;
+        s += p[j];
       }
+      s = grp_sum<G>(s);
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) p[j] = p[j] / s;
     } else {
-      const float* xr = static_cast<const float*>(xv) + static_cast<size_t>(t) * d;
-      const float* wg = static_cast<const float*>(wgv);
-      for (int i0 = lane; i0 < d; i0 += 8 * 64) {
-        float a[8], b[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int i = i0 + u * 64;
-          a[u] = i < d ? xr[i] : 0.0f;
-          b[u] = i < d ? wg[i] : 0.0f;
-        }
+      for (int j = 0; j < kPer; ++j) p[j] = sigmoidf_(p[j]);
+    }
+    // ranking keys: the scores, or score + selection bias (fp32); -inf for
+    // lanes past E and for experts already chosen
+    float key[kPer];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) g = fmaf(a[u], b[u], g);
+    for (int j = 0; j < kPer; ++j) {
+      const int e = gi + G * j;
+      key[j] = e < E ? (sel_bias ? p[j] + sel_bias[e] : p[j]) : -INFINITY;
+    }
+    // this lane's best remaining key (strict '>' in ascending expert order
+    // keeps the lower index among equal keys); E when none is selectable
+    float bv;
+    int bi;
+    auto local_best = [&]() {
+      bv = -INFINITY;
+      bi = E;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j)
+        if (key[j] > bv) { bv = key[j]; bi = gi + G * j; }
+    };
+    local_best();
+    int my_e[kSlots];
+    float my_p[kSlots];
+#pragma unroll
+    for (int r = 0; r < kSlots; ++r) { my_e[r] = E; my_p[r] = 0.0f; }
+    for (int j = 0; j < k; ++j) {
+      // the largest remaining key of the group, then the lowest expert index
+      // holding it
+      const float mv = grp_max<G>(bv);
+      int wi = grp_min<G>(bv == mv ? bi : INT_MAX);
+      wi = wi < E ? wi : E;
+      // the winner's (unbiased) score, from the lane that holds it (scores
+      // are >= 0, so a max over zeros elsewhere returns it)
+      const bool own = wi < E && (wi & (G - 1)) == gi;
+      float pw = 0.0f;
+#pragma unroll
+      for (int jj = 0; jj < kPer; ++jj)
+        if (own && jj == wi / G) { pw = p[jj]; key[jj] = -INFINITY; }
+      pw = grp_max<G>(pw);
+#pragma unroll
+      for (int r = 0; r < kSlots; ++r)
+        if (j == gi + G * r) { my_e[r] = wi; my_p[r] = pw; }
+      local_best();
+    }
+    float denom = 1.0f;
+    if (normalize) {
+      float s = 0.0f;
+#pragma unroll
+      for (int r = 0; r < kSlots; ++r)
+        if (gi + G * r < k) s += my_p[r];
+      denom = grp_sum<G>(s);
+    }
+#pragma unroll
+    for (int r = 0; r < kSlots; ++r) {
+      const int j = gi + G * r;
+      if (j < k) {
+        topk_idx[static_cast<size_t>(t) * k + j] = my_e[r];
+        topk_w[static_cast<size_t>(t) * k + j] = normalize ? my_p[r] / denom : my_p[r];
+        if (my_e[r] < E) atomicAdd(&s_cnt[my_e[r]], 1);   // LDS integer atomics: order-free
       }
     }
-    g = wave_sum_dpp(g);
-    if (lane == 0) gate[t] = sigmoidf_(g);
-  }
-  }
-  __syncthreads();
-  int32_t* hrow = hist + static_cast<size_t>(blockIdx.x) * E;
-  for (int e = threadIdx.x; e < E; e += kTopkThreads) hrow[e] = s_cnt[e];
-}
-
-// counts[e] = sum over workgroups of hist[b][e] (one workgroup per expert)
-__global__ __launch_bounds__(256) void route_count_kernel(int nblk, int E,
-                                                          const int32_t* __restrict__ hist,
-                                                          int32_t* __restrict__ counts) {
-  __shared__ int s_part[4];
-  const int e = blockIdx.x;
-  int v = 0;
-  for (int b = threadIdx.x; b < nblk; b += 256) v += hist[static_cast<size_t>(b) * E + e];
+    if (gate && gz) {
+      // the logits GEMM's K slabs of x[t] . w_gate, in slab order
+      if (gi == 0) {
+        float g = 0.0f;
+        for (int s = 0; s < nslab; ++s) g += gz[static_cast<size_t>(s) * T + t];
+        gate[t] = sigmoidf_(g);
+      }
+    } else if (gate) {
+      // x[t] . w_gate: lane i of the group takes 16-byte chunks i, i + G,
+      // ... (bf16) or 4-byte elements (fp32), four at a time, in order
+      float g = 0.0f;
+      if constexpr (kBF16) {
+        const uint16_t* xr = static_cast<const uint16_t*>(xv) + static_cast<size_t>(t) * d;
+        const uint16_t* wg = static_cast<const uint16_t*>(wgv);
+        for (int k0 = gi * 8; k0 < d; k0 += 4 * 8 * G) {
+          u32x4 a[4], b[4];
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = v;
+          for (int u = 0; u < 4; ++u) {
+            const int k8 = k0 + u * 8 * G;
+            a[u] = k8 < d ? *reinterpret_cast<const u32x4*>(xr + k8) : u32x4{0, 0, 0, 0};
+            b[u] = k8 < d ? *reinterpret_cast<const u32x4*>(wg + k8) : u32x4{0, 0, 0, 0};
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              g = fmaf(bf16lo(a[u][q]), bf16lo(b[u][q]), g);
+              g = fmaf(bf16hi(a[u][q]), bf16hi(b[u][q]), g);
+            }
+        }
+      } else {
+        const float* xr = static_cast<const float*>(xv) + static_cast<size_t>(t) * d;
+        const float* wg = static_cast<const float*>(wgv);
+        for (int i0 = gi; i0 < d; i0 += 4 * G) {
+          float a[4], b[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int i = i0 + u * G;
+            a[u] = i < d ? xr[i] : 0.0f;
+            b[u] = i < d ? wg[i] : 0.0f;
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) g = fmaf(a[u], b[u], g);
+        }
+      }
+      g = grp_sum<G>(g);
+      if (gi == 0) gate[t] = sigmoidf_(g);
+    }
+  }
   __syncthreads();
-  if (threadIdx.x == 0) counts[e] = s_part[0] + s_part[1] + s_part[2] + s_part[3];
+  for (int e = threadIdx.x; e < E; e += kTopkThreads) {
+    const int c = s_cnt[e];
+    if (block_counts) block_counts[static_cast<size_t>(blockIdx.x) * E + e] = c;
+    if (c) atomicAdd(&counts[e], c);
+  }
 }
 
 template <bool kBF16>
 static auto pick_topk(int E) {
-  if (E <= 64) return route_topk_kernel<kBF16, 1>;
-  if (E <= 128) return route_topk_kernel<kBF16, 2>;
-  if (E <= 256) return route_topk_kernel<kBF16, 4>;
-  if (E <= 512) return route_topk_kernel<kBF16, 8>;
-  return route_topk_kernel<kBF16, 16>;
+  if (E <= 16) return route_topk_kernel<kBF16, 16, 1>;
+  if (E <= 32) return route_topk_kernel<kBF16, 16, 2>;
+  if (E <= 64) return route_topk_kernel<kBF16, 16, 4>;
+  if (E <= 128) return route_topk_kernel<kBF16, 16, 8>;
+  if (E <= 256) return route_topk_kernel<kBF16, 16, 16>;
+  if (E <= 512) return route_topk_kernel<kBF16, 64, 8>;
+  return route_topk_kernel<kBF16, 64, 16>;
 }
 
 }  // namespace moe
@@ -218,16 +298,18 @@ static int route_slabs(moe_dtype dt, int64_t T, int64_t d, int32_t E) {
   return dt == MOE_BF16 ? router_ksplit(T, d, E) : 1;
 }
 
-static size_t route_hist_bytes(int64_t T, int32_t E) {
-  const int64_t nblk = (T + kTopkTokens - 1) / kTopkTokens;
-  return (static_cast<size_t>(nblk) * E * sizeof(int32_t) + 255) & ~static_cast<size_t>(255);
+// bf16 with the gate formed in the logits GEMM: one fp32 slab of gate dot
+// products per K split
+static size_t route_gate_bytes(moe_dtype dt, int64_t T, int64_t d, int32_t E) {
+  if (dt != MOE_BF16 || !router_gate_fused(T, d, E)) return 0;
+  return static_cast<size_t>(route_slabs(dt, T, d, E)) * T * sizeof(float);
 }
 
 extern "C" size_t moe_route_workspace_size(int64_t T, int64_t d, int32_t E, moe_dtype dt) {
   if (T < 1 || d < 1 || E < 1 || (dt != MOE_F32 && dt != MOE_BF16)) return 0;
-  // per-workgroup histograms; fp32 logits, one slab per K split
-  return route_hist_bytes(T, E) +
-         static_cast<size_t>(route_slabs(dt, T, d, E)) * T * E * sizeof(float);
+  // fp32 logits, one slab per K split; the gate's slabs
+  return static_cast<size_t>(route_slabs(dt, T, d, E)) * T * E * sizeof(float) +
+         route_gate_bytes(dt, T, d, E);
 }
 
 extern "C" moe_status moe_route(hipStream_t stream, moe_dtype dt, int64_t T, int64_t d,
@@ -235,7 +317,8 @@ extern "C" moe_status moe_route(hipStream_t stream, moe_dtype dt, int64_t T, int
                                 const void* x, const void* w_router,
                                 const float* logit_bias, const float* selection_bias,
                                 const void* w_gate, int32_t* topk_idx, float* topk_w,
-                                int32_t* expert_counts, float* gate, void* ws, size_t ws_bytes) {
+                                int32_t* expert_counts, int32_t* block_counts, float* gate,
+                                void* ws, size_t ws_bytes) {
   if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_DTYPE;
   if (fn != MOE_SCORE_SOFTMAX && fn != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
   if (!x || !w_router || !topk_idx || !topk_w || !expert_counts) return MOE_ERR_INVALID_ARG;
@@ -247,32 +330,32 @@ extern "C" moe_status moe_route(hipStream_t stream, moe_dtype dt, int64_t T, int
     return MOE_ERR_SHAPE;
   if (d % 8) return MOE_ERR_ALIGNMENT;
   if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || !aligned16(topk_idx) ||
-      !aligned16(topk_w) || !aligned16(expert_counts) || !aligned16(gate) ||
-      !aligned16(logit_bias) || !aligned16(selection_bias) || !aligned16(ws))
+      !aligned16(topk_w) || !aligned16(expert_counts) || !aligned16(block_counts) ||
+      !aligned16(gate) || !aligned16(logit_bias) || !aligned16(selection_bias) ||
+      !aligned16(ws))
     return MOE_ERR_ALIGNMENT;
   if (!ws || ws_bytes < moe_route_workspace_size(T, d, E, dt)) return MOE_ERR_WORKSPACE;
 
-  int32_t* hist = static_cast<int32_t*>(ws);
-  float* z = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + route_hist_bytes(T, E));
+  float* z = static_cast<float*>(ws);
   hipError_t err;
   const int nslab = route_slabs(dt, T, d, E);
+  float* gz = nullptr;
+  if (w_gate && route_gate_bytes(dt, T, d, E) > 0) gz = z + static_cast<size_t>(nslab) * T * E;
   if (dt == MOE_BF16) {
-    err = launch_router_logits_bf16(stream, T, d, E, x, w_router, logit_bias, z, nslab);
+    err = launch_router_logits_bf16(stream, T, d, E, x, w_router, logit_bias, z, nslab, w_gate, gz,
+                                    expert_counts);
   } else {
     const int64_t n = T * E;
     err = launch(route_logits_f32_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
                  stream, (int)T, (int)d, E, static_cast<const float*>(x),
-                 static_cast<const float*>(w_router), logit_bias, z);
+                 static_cast<const float*>(w_router), logit_bias, z, expert_counts);
   }
   if (err != hipSuccess) return MOE_ERR_HIP;
   auto kern = dt == MOE_BF16 ? pick_topk<true>(E) : pick_topk<false>(E);
-  const int nblk = static_cast<int>((T + kTopkTokens - 1) / kTopkTokens);
+  const int nblk = static_cast<int>((T + kTopkBlk - 1) / kTopkBlk);
   err = launch(kern, dim3(nblk), dim3(kTopkThreads), E * sizeof(int), stream, (int)T, (int)d, E, k,
-               (int)fn, normalize, nslab, (const float*)z, selection_bias, x, w_gate, topk_idx,
-               topk_w, hist, gate);
-  if (err == hipSuccess)
-    err = launch(route_count_kernel, dim3(E), dim3(256), 0, stream, nblk, E, (const int32_t*)hist,
-                 expert_counts);
+               (int)fn, normalize, nslab, (const float*)z, selection_bias, x, w_gate,
+               (const float*)gz, topk_idx, topk_w, expert_counts, block_counts, gate);
   return hip_status(err);
 }
 
@@ -293,7 +376,7 @@ hipError_t launch_route_logits(hipStream_t stream, moe_dtype dt, int64_t T, int6
   const int64_t n = T * E;
   return launch(route_logits_f32_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
                 stream, (int)T, (int)d, E, static_cast<const float*>(x),
-                static_cast<const float*>(w_router), logit_bias, z);
+                static_cast<const float*>(w_router), logit_bias, z, (int32_t*)nullptr);
 }
 
 }  // namespace moe

@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.moe_abi_version() == 9
+    assert L.moe_abi_version() == 10
     assert L.moe_status_string(0) == b"MOE_OK"
     assert L.moe_status_string(5) == b"MOE_ERR_WORKSPACE"
 
@@ -56,7 +56,7 @@ def test_version_and_status_strings(L):
 def test_workspace_sizes(L):
     T, E, k = 4096, 128, 8
     ws = L.moe_permute_workspace_size(T, E, k)
-    nblk = -(-T // (256 // k))
+    nblk = -(-T // 64)                     # 64-token rows of E counts
     assert ws >= (nblk * E + E) * 4
     assert L.moe_grouped_swiglu_fwd_workspace_size(32768, 768, 1) >= 32768 * 768 * 2
     a = L.moe_grouped_swiglu_bwd_workspace_size(32768, 768, 1, 0)
@@ -72,13 +72,13 @@ MIS = 0x100004
 def test_route_validation(L):
     r = L.moe_route
     args = dict(s=None, dt=1, T=16, d=64, E=8, k=2, fn=0, norm=1, x=P, w=P, b=None, sb=None,
-                g=None, idx=P, tw=P, cnt=P, gate=None, ws=P, wsb=1 << 20)
+                g=None, idx=P, tw=P, cnt=P, bc=None, gate=None, ws=P, wsb=1 << 20)
 
     def call(**kw):
         a = dict(args, **kw)
         return r(a["s"], a["dt"], a["T"], a["d"], a["E"], a["k"], a["fn"], a["norm"], a["x"],
-                 a["w"], a["b"], a["sb"], a["g"], a["idx"], a["tw"], a["cnt"], a["gate"], a["ws"],
-                 a["wsb"])
+                 a["w"], a["b"], a["sb"], a["g"], a["idx"], a["tw"], a["cnt"], a["bc"], a["gate"],
+                 a["ws"], a["wsb"])
 
     assert call(dt=7) == 3                 # MOE_ERR_DTYPE
     assert call(fn=5) == 1                 # bad score function
@@ -92,17 +92,20 @@ def test_route_validation(L):
     assert call(x=MIS) == 4                # misaligned pointer
     assert call(wsb=16) == 5               # workspace too small
     assert call(sb=MIS) == 4               # misaligned selection bias
+    assert call(bc=MIS) == 4               # misaligned block histograms
+    assert call(cnt=None) == 1             # counts are required
     assert L.moe_route_workspace_size(16, 64, 8, 0) >= 16 * 8 * 4
     assert L.moe_route_workspace_size(4096, 2048, 128, 1) >= 4096 * 128 * 4
 
 
 def test_permute_validation(L):
     f = L.moe_permute
-    ok = (None, 1, 16, 64, 8, 2, P, P, P, P, P, P, P, P, P)
+    ok = (None, 1, 16, 64, 8, 2, P, P, P, None, P, P, P, P, P, P)
     assert f(*ok, 0) == 5                                  # workspace too small
-    assert f(None, 1, 16, 64, 8, 2, P, P, None, P, P, P, P, P, P, 1 << 20) == 1  # row_w w/o topk_w
-    assert f(None, 1, 16, 60, 8, 2, P, P, P, P, P, P, P, P, P, 1 << 20) == 4     # 120 B rows
-    assert f(None, 1, 16, 64, 0, 2, P, P, P, P, P, P, P, P, P, 1 << 20) == 2
+    assert f(None, 1, 16, 64, 8, 2, P, P, None, None, P, P, P, P, P, P, 1 << 20) == 1  # row_w w/o topk_w
+    assert f(None, 1, 16, 60, 8, 2, P, P, P, None, P, P, P, P, P, P, 1 << 20) == 4     # 120 B rows
+    assert f(None, 1, 16, 64, 0, 2, P, P, P, None, P, P, P, P, P, P, 1 << 20) == 2
+    assert f(None, 1, 16, 64, 8, 2, P, P, P, MIS, P, P, P, P, P, P, 1 << 20) == 4      # block counts
 
 
 def test_permute_noalloc_limit(L):

@@ -32,7 +32,24 @@ ROUTE_CASES = [
     (700, 512, 256, 8, "softmax", True, True, "bf16"),
     (129, 264, 1000, 32, "softmax", False, False, "bf16"),
     (100, 64, 1, 1, "softmax", False, False, "bf16"),      # E = 1
+    (1000, 256, 256, 8, "softmax", True, True, "bf16"),   # 16 lanes x 16 scores per token
+    (77, 128, 17, 16, "sigmoid", False, False, "f32"),    # k > 16: two choices per lane
+    (200, 64, 300, 32, "softmax", False, True, "f32"),    # a wavefront per token, k = 32
+    (129, 72, 600, 3, "sigmoid", True, False, "bf16"),
 ]
+
+
+def _block_hist(idx, E, blk=64):
+    """Per-64-token-block expert counts of a [T, k] choice matrix (entries
+    outside [0, E) dropped)."""
+    T = idx.shape[0]
+    nb = -(-T // blk)
+    h = np.zeros((nb, E), dtype=np.int32)
+    for b in range(nb):
+        v = idx[b * blk:(b + 1) * blk].reshape(-1)
+        v = v[(v >= 0) & (v < E)]
+        h[b] = np.bincount(v, minlength=E)
+    return h
 
 
 @pytest.mark.parametrize("case", ROUTE_CASES, ids=lambda c: "-".join(map(str, c)))
@@ -46,19 +63,22 @@ def test_route_parity(case):
     wr = gh.to_gpu(inp.w_router)
     b = gh.to_gpu(inp.logit_bias) if bias else None
     wg = gh.to_gpu(inp.w_gate) if gate else None
-    outs = []
+    outs, bcs = [], []
     for _ in range(2):
         out = (gh.poison((T, k), torch.int32), gh.poison((T, k), torch.float32),
                gh.poison((E,), torch.int32), gh.poison((T,), torch.float32) if gate else None)
-        moe.route(x, wr, k, score, True, b, wg, out=out)
+        bc = gh.poison(((T + 63) // 64, E), torch.int32)
+        moe.route(x, wr, k, score, True, b, wg, out=out, block_counts=bc)
         torch.cuda.synchronize()
         outs.append(out)
+        bcs.append(bc)
     for a, c in zip(outs[0], outs[1]):
         if a is not None:
             assert gh.bits_equal(a, c)
     idx, w, cnt, g = (o.cpu().numpy() if o is not None else None for o in outs[0])
     gh.check_routing(idx, w, ref, k)
     assert (cnt == np.bincount(idx.reshape(-1), minlength=E)).all()
+    assert np.array_equal(bcs[0].cpu().numpy(), _block_hist(idx, E))
     if gate:
         assert np.abs(g - ref.gate).max() <= gh.TOL_ROUTE_W
 
@@ -183,12 +203,17 @@ PERM_CASES = [
     (500, 64, 64, 1, "bf16", "one_expert"),          # every token on expert 0
     (300, 64, 40, 8, "bf16", "few_experts"),         # most experts empty
     (99, 64, 1024, 32, "bf16", "random"),            # E = 1024, k = 32
+    (1000, 64, 256, 8, "bf16", "random"),            # 16 blocks of 64 tokens, a ragged last
+    (500, 64, 64, 4, "bf16", "dup"),                 # a token may name an expert twice
+    (130, 64, 8, 32, "bf16", "dup"),                 # k > E: every token repeats experts
 ]
 
 
 def _idx(rng, T, E, k, pattern):
     if pattern == "one_expert":
         return np.zeros((T, k), dtype=np.int32)
+    if pattern == "dup":
+        return rng.integers(0, E, (T, k)).astype(np.int32)
     pool = np.arange(E) if pattern == "random" else np.arange(0, E, 5)[: max(k, 8)]
     return np.stack([rng.choice(pool, size=k, replace=False) for _ in range(T)]).astype(np.int32)
 
@@ -212,8 +237,19 @@ def test_permute_parity(case):
         moe.permute(x, gi, gw, E, out=out)
         torch.cuda.synchronize()
         res.append(out)
-    for a, c in zip(res[0], res[1]):
-        assert gh.bits_equal(a, c)
+    # with the counts pass replaced by given block histograms (moe_route's)
+    bc = gh.to_gpu(_block_hist(idx, E))
+    bc_before = bc.clone()
+    out = (gh.poison((E + 1,), torch.int32), gh.poison((T, k), torch.int32),
+           gh.poison((N,), torch.int32), gh.poison((N,), torch.float32),
+           gh.poison((N, d), x.dtype))
+    moe.permute(x, gi, gw, E, out=out, block_counts=bc)
+    torch.cuda.synchronize()
+    res.append(out)
+    assert gh.bits_equal(bc, bc_before)         # an input only
+    for r in res[1:]:
+        for a, c in zip(res[0], r):
+            assert gh.bits_equal(a, c)
     off, slot, rtok, rw, xp = res[0]
     assert off.cpu().numpy().tolist() == ref.offsets.tolist()
     assert np.array_equal(slot.cpu().numpy(), ref.slot_of)
