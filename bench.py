@@ -54,16 +54,16 @@ KERNEL_SOURCES_FP8 = ("mixture_experts_layer_05_amd/csrc/moe_grouped_mx.hip",
 # (fp8: profiles/fp8_grouped_gemm_qwen3_30b_hbm_bytes.md, the quantiser + fc1 + fc2)
 MEASURED_TRAFFIC = {
     # profiles/grouped_gemm_fwd_qwen3_30b_hbm_bytes.md
-    "qwen3_30b": {"bytes": 1628942193,
-                  "sources_sha256": "067e83380d4a868a195bc15b320f9427d0d749805293a2dc537b5e13ee592ad6"},
+    "qwen3_30b": {"bytes": 1625055127,
+                  "sources_sha256": "3f8707a42a8016cc9dbf3469b409c93e9e19059d908d245a8fc9f19921c3af8d"},
     # profiles/grouped_gemm_fwd_dsv_30b_hbm_bytes.md
-    "dsv_30b": {"bytes": 5322381764,
-                "sources_sha256": "067e83380d4a868a195bc15b320f9427d0d749805293a2dc537b5e13ee592ad6"},
+    "dsv_30b": {"bytes": 5304634985,
+                "sources_sha256": "3f8707a42a8016cc9dbf3469b409c93e9e19059d908d245a8fc9f19921c3af8d"},
     # profiles/grouped_gemm_fwd_skew_shared_hbm_bytes.md
-    "skew_shared": {"bytes": 3677405320,
-                    "sources_sha256": "067e83380d4a868a195bc15b320f9427d0d749805293a2dc537b5e13ee592ad6"},
-    "qwen3_30b:fp8": {"bytes": 974513090,
-                      "sources_sha256": "cc9226e910fbe871cc4a62f7541fb53d030f83e6a9a61958ca382ade00700e93"},
+    "skew_shared": {"bytes": 3634693813,
+                    "sources_sha256": "3f8707a42a8016cc9dbf3469b409c93e9e19059d908d245a8fc9f19921c3af8d"},
+    "qwen3_30b:fp8": {"bytes": 971260000,
+                      "sources_sha256": "0c2294f5a2a387a1e28ce3015d04049ba25458a8f9d89e713cb196285c9cbcc9"},
 }
 
 
