@@ -54,16 +54,16 @@ KERNEL_SOURCES_FP8 = ("mixture_experts_layer_05_amd/csrc/moe_grouped_mx.hip",
 # (fp8: profiles/fp8_grouped_gemm_qwen3_30b_hbm_bytes.md, the quantiser + fc1 + fc2)
 MEASURED_TRAFFIC = {
     # profiles/grouped_gemm_fwd_qwen3_30b_hbm_bytes.md
-    "qwen3_30b": {"bytes": 1625055127,
-                  "sources_sha256": "3f8707a42a8016cc9dbf3469b409c93e9e19059d908d245a8fc9f19921c3af8d"},
+    "qwen3_30b": {"bytes": 1626257461,
+                  "sources_sha256": "c0d88af69e2b9890325e4ed821cd3e3d495ed03a3c34b2cf0529bd6764d8d7b3"},
     # profiles/grouped_gemm_fwd_dsv_30b_hbm_bytes.md
-    "dsv_30b": {"bytes": 5304634985,
-                "sources_sha256": "3f8707a42a8016cc9dbf3469b409c93e9e19059d908d245a8fc9f19921c3af8d"},
+    "dsv_30b": {"bytes": 5306369182,
+                "sources_sha256": "c0d88af69e2b9890325e4ed821cd3e3d495ed03a3c34b2cf0529bd6764d8d7b3"},
     # profiles/grouped_gemm_fwd_skew_shared_hbm_bytes.md
-    "skew_shared": {"bytes": 3634693813,
-                    "sources_sha256": "3f8707a42a8016cc9dbf3469b409c93e9e19059d908d245a8fc9f19921c3af8d"},
-    "qwen3_30b:fp8": {"bytes": 971260000,
-                      "sources_sha256": "0c2294f5a2a387a1e28ce3015d04049ba25458a8f9d89e713cb196285c9cbcc9"},
+    "skew_shared": {"bytes": 3645698929,
+                    "sources_sha256": "c0d88af69e2b9890325e4ed821cd3e3d495ed03a3c34b2cf0529bd6764d8d7b3"},
+    "qwen3_30b:fp8": {"bytes": 969889512,
+                      "sources_sha256": "b0b29d0cde5fa5331b7045cb561580f6e813dd4eb7905a37d057c41c0c94631a"},
 }
 
 

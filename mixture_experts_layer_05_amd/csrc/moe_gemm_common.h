@@ -103,15 +103,18 @@ __device__ inline TileIdx tile_decode(const int32_t* __restrict__ offsets, int E
   return t;
 }
 
-// The same decode for a single group of n rows (no offsets array).
-__device__ inline TileIdx tile_decode_one(int n, int bm, int L) {
+// The same decode for a single group of n rows (no offsets array), row tiles
+// outer: the ntn column tiles of a row tile are neighbours, so they run on
+// one XCD together and read its token rows from one L2 (the router's weight
+// is small and stays in every L2).
+__device__ inline TileIdx tile_decode_one(int n, int bm, int ntn, int L) {
   TileIdx t;
   t.e = 0;
   t.lo = 0;
   t.hi = n;
   const int mts = (n + bm - 1) / bm;
-  t.nt = L / mts;
-  t.mt = L - t.nt * mts;
+  t.mt = L / ntn;
+  t.nt = L - t.mt * ntn;
   const int h = ((n + mts - 1) / mts + 31) & ~31;
   t.m0 = t.mt * h;
   t.mend = min(t.m0 + h, n);

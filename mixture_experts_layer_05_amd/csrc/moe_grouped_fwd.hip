@@ -498,7 +498,7 @@ __global__ __launch_bounds__(C::kThreads, C::kWgPerCu) void ggf_kernel(FwdParams
   } else {
     const int total = ((p.rows1 + C::kBM - 1) / C::kBM) * p.ntn;
     if (static_cast<int>(blockIdx.x) >= total) return;
-    ti = tile_decode_one(p.rows1, C::kBM, xcd_remap(blockIdx.x, total));
+    ti = tile_decode_one(p.rows1, C::kBM, p.ntn, xcd_remap(blockIdx.x, total));
   }
   // live 32-row blocks of this wave's rows
   const int rows = ti.mend - ti.m0 -
