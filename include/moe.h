@@ -100,7 +100,7 @@ MOE_API const char* moe_status_string(moe_status s);
  *   w_gate     [d]     dt        or NULL (then `gate` must be NULL too)
  *   topk_idx   [T, k]  int32     out
  *   topk_w     [T, k]  fp32      out
- *   expert_counts [E]  int32     out: tokens routed to each expert
+ *   expert_counts [E]  int32     out, or NULL: tokens routed to each expert
  *   block_counts [ceil(T / MOE_ROUTE_BLOCK_TOKENS), E] int32
  *                                out, or NULL: row b counts the choices of
  *                                tokens [64 b, 64 b + 64) per expert (the

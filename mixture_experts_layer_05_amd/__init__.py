@@ -152,7 +152,8 @@ def route_block_counts(T, E, device):
 
 def route(x, w_router, k, score="softmax", normalize=True, logit_bias=None,
           w_gate=None, out=None, ws=None, selection_bias=None, block_counts=None):
-    """-> (topk_idx [T,k] int32, topk_w [T,k] fp32, counts [E] int32, gate [T] or None).
+    """-> (topk_idx [T,k] int32, topk_w [T,k] fp32, counts [E] int32 (None when `out`
+    holds None there: not computed), gate [T] or None).
     block_counts (route_block_counts(T, E)): also filled with the block
     histograms that permute(block_counts=...) takes."""
     T, d = x.shape
@@ -557,9 +558,10 @@ class MoELayer:
         N = T * k
         self.N = N
         i32, f32 = torch.int32, torch.float32
+        # (no per-expert counts: the permute's offsets hold them)
         self.route_out = (torch.empty((T, k), dtype=i32, device=dev),
                           torch.empty((T, k), dtype=f32, device=dev),
-                          torch.empty((E,), dtype=i32, device=dev),
+                          None,
                           torch.empty((T,), dtype=f32, device=dev) if w_gate is not None else None)
         self.perm_out = (torch.empty((E + 1,), dtype=i32, device=dev),
                          torch.empty((T, k), dtype=i32, device=dev),

@@ -12,7 +12,7 @@
 //      ring), K split into slabs, and (when the slab's gate weights fit in
 //      LDS) the K slabs of x . w_gate from the same staged token rows; fp32
 //      runs a plain FMA dot product per (token, expert).  Either kernel
-//      also zeroes expert_counts.
+//      also zeroes expert_counts (when asked for).
 //   2. route_topk: a group of G lanes per token (G = 16 for E <= 256, four
 //      tokens per wavefront; G = 64 above), 64 tokens per workgroup; lane i
 //      of a group holds the scores of experts i, i + G, ...; k rounds of a
@@ -109,6 +109,7 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
     const float* __restrict__ gz, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     int32_t* __restrict__ counts, int32_t* __restrict__ block_counts, float* __restrict__ gate) {
   static_assert(G == 16 || G == 64, "group width");
+  static_assert(kPer <= 32, "taken mask");
   constexpr int kTokPass = kTopkThreads / G;           // tokens per pass
   static_assert(kTopkBlk % kTokPass == 0, "passes cover the block");
   constexpr int kSlots = (32 + G - 1) / G;             // choices held per lane (k <= 32)
@@ -170,40 +171,98 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
       const int e = gi + G * j;
       key[j] = e < E ? (sel_bias ? p[j] + sel_bias[e] : p[j]) : -INFINITY;
     }
-    // this lane's best remaining key (strict '>' in ascending expert order
-    // keeps the lower index among equal keys); E when none is selectable
-    float bv;
-    int bi;
-    auto local_best = [&]() {
-      bv = -INFINITY;
-      bi = E;
-#pragma unroll
-      for (int j = 0; j < kPer; ++j)
-        if (key[j] > bv) { bv = key[j]; bi = gi + G * j; }
-    };
-    local_best();
     int my_e[kSlots];
     float my_p[kSlots];
 #pragma unroll
     for (int r = 0; r < kSlots; ++r) { my_e[r] = E; my_p[r] = 0.0f; }
-    for (int j = 0; j < k; ++j) {
-      // the largest remaining key of the group, then the lowest expert index
-      // holding it
-      const float mv = grp_max<G>(bv);
-      int wi = grp_min<G>(bv == mv ? bi : INT_MAX);
-      wi = wi < E ? wi : E;
-      // the winner's (unbiased) score, from the lane that holds it (scores
-      // are >= 0, so a max over zeros elsewhere returns it)
-      const bool own = wi < E && (wi & (G - 1)) == gi;
-      float pw = 0.0f;
+    if constexpr (G == 16) {
+      // This lane's three best remaining (key, score, expert) candidates,
+      // best first: a scan in ascending expert order with strict '>' keeps the
+      // lower index first among equal keys, and NaN or -inf keys never enter
+      // (index E marks an empty place).  A round takes the winner from the
+      // head of its owner's list; a lane whose list runs out (its third win)
+      // scans again, skipping the experts it already gave (`taken`).
+      float ka, kb, kc, sa, sb, sc;
+      int ia, ib, ic, left;
+      uint32_t taken = 0;
+      auto top3 = [&](bool skip_taken) {
+        ka = kb = kc = -INFINITY;
+        sa = sb = sc = 0.0f;
+        ia = ib = ic = E;
 #pragma unroll
-      for (int jj = 0; jj < kPer; ++jj)
-        if (own && jj == wi / G) { pw = p[jj]; key[jj] = -INFINITY; }
-      pw = grp_max<G>(pw);
+        for (int j = 0; j < kPer; ++j) {
+          const float v = (skip_taken && ((taken >> j) & 1u)) ? -INFINITY : key[j];
+          const int e = gi + G * j;
+          const bool c1 = v > ka, c2 = v > kb, c3 = v > kc;
+          kc = c2 ? kb : (c3 ? v : kc);
+          sc = c2 ? sb : (c3 ? p[j] : sc);
+          ic = c2 ? ib : (c3 ? e : ic);
+          kb = c1 ? ka : (c2 ? v : kb);
+          sb = c1 ? sa : (c2 ? p[j] : sb);
+          ib = c1 ? ia : (c2 ? e : ib);
+          ka = c1 ? v : ka;
+          sa = c1 ? p[j] : sa;
+          ia = c1 ? e : ia;
+        }
+        left = 3;
+      };
+      top3(false);
+      for (int j = 0; j < k; ++j) {
+        // the largest remaining key of the group, then the lowest expert index
+        // holding it; its owner is the lane whose list it heads
+        const float mv = grp_max<G>(ka);
+        int wi = grp_min<G>(ka == mv ? ia : INT_MAX);
+        wi = wi < E ? wi : E;
+        const bool own = wi < E && ia == wi;
+        // the winner's (unbiased) score from its owner (scores are >= 0, so a
+        // max over zeros elsewhere returns it)
+        const float pw = grp_max<G>(own ? sa : 0.0f);
 #pragma unroll
-      for (int r = 0; r < kSlots; ++r)
-        if (j == gi + G * r) { my_e[r] = wi; my_p[r] = pw; }
+        for (int r = 0; r < kSlots; ++r)
+          if (j == gi + G * r) { my_e[r] = wi; my_p[r] = pw; }
+        if (own) {
+          taken |= 1u << (wi / G);
+          ka = kb; sa = sb; ia = ib;
+          kb = kc; sb = sc; ib = ic;
+          kc = -INFINITY; sc = 0.0f; ic = E;
+          --left;
+        }
+        if (left == 0 && j + 1 < k) top3(true);   // rare: a lane's fourth choice
+      }
+    } else {
+      // A wavefront per token: a lane holds few scores, so it rescans them
+      // all after each of its wins.
+      // This lane's best remaining key (strict '>' in ascending expert order
+      // keeps the lower index among equal keys); E when none is selectable
+      float bv;
+      int bi;
+      auto local_best = [&]() {
+        bv = -INFINITY;
+        bi = E;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+          if (key[j] > bv) { bv = key[j]; bi = gi + G * j; }
+      };
       local_best();
+      for (int j = 0; j < k; ++j) {
+        // the largest remaining key of the group, then the lowest expert index
+        // holding it
+        const float mv = grp_max<G>(bv);
+        int wi = grp_min<G>(bv == mv ? bi : INT_MAX);
+        wi = wi < E ? wi : E;
+        // the winner's (unbiased) score, from the lane that holds it (scores
+        // are >= 0, so a max over zeros elsewhere returns it)
+        const bool own = wi < E && (wi & (G - 1)) == gi;
+        float pw = 0.0f;
+#pragma unroll
+        for (int jj = 0; jj < kPer; ++jj)
+          if (own && jj == wi / G) { pw = p[jj]; key[jj] = -INFINITY; }
+        pw = grp_max<G>(pw);
+#pragma unroll
+        for (int r = 0; r < kSlots; ++r)
+          if (j == gi + G * r) { my_e[r] = wi; my_p[r] = pw; }
+        local_best();
+      }
     }
     float denom = 1.0f;
     if (normalize) {
@@ -275,7 +334,7 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
   for (int e = threadIdx.x; e < E; e += kTopkThreads) {
     const int c = s_cnt[e];
     if (block_counts) block_counts[static_cast<size_t>(blockIdx.x) * E + e] = c;
-    if (c) atomicAdd(&counts[e], c);
+    if (c && counts) atomicAdd(&counts[e], c);
   }
 }
 
@@ -321,7 +380,7 @@ extern "C" moe_status moe_route(hipStream_t stream, moe_dtype dt, int64_t T, int
                                 void* ws, size_t ws_bytes) {
   if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_DTYPE;
   if (fn != MOE_SCORE_SOFTMAX && fn != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
-  if (!x || !w_router || !topk_idx || !topk_w || !expert_counts) return MOE_ERR_INVALID_ARG;
+  if (!x || !w_router || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
   if ((w_gate == nullptr) != (gate == nullptr)) return MOE_ERR_INVALID_ARG;
   if (T < 1 || d < 1 || E < 1 || E > 1024 || k < 1 || k > 32 || k > E) return MOE_ERR_SHAPE;
   if (T * static_cast<int64_t>(k) >= (int64_t(1) << 31) || d >= (int64_t(1) << 20) ||

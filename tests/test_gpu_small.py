@@ -75,6 +75,14 @@ def test_route_parity(case):
     for a, c in zip(outs[0], outs[1]):
         if a is not None:
             assert gh.bits_equal(a, c)
+    # without the per-expert counts (NULL): the same choice, weights and gate
+    out = (gh.poison((T, k), torch.int32), gh.poison((T, k), torch.float32), None,
+           gh.poison((T,), torch.float32) if gate else None)
+    moe.route(x, wr, k, score, True, b, wg, out=out)
+    torch.cuda.synchronize()
+    for a, c in zip(outs[0], out):
+        if c is not None:
+            assert gh.bits_equal(a, c)
     idx, w, cnt, g = (o.cpu().numpy() if o is not None else None for o in outs[0])
     gh.check_routing(idx, w, ref, k)
     assert (cnt == np.bincount(idx.reshape(-1), minlength=E)).all()

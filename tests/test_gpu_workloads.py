@@ -52,7 +52,8 @@ def test_layer_forward_full_size(name):
                    inp.logit_bias, f("w_gate"))
     idx = layer.route_out[0].cpu().numpy()
     w = layer.route_out[1].cpu().numpy()
-    cnt = layer.route_out[2].cpu().numpy()
+    # the layer's route skips the per-expert counts; the permute's offsets hold them
+    cnt = np.diff(layer.perm_out[0].cpu().numpy())
     n_excl, n_diff = gh.check_routing(idx, w, ref, cfg.k)
     assert (cnt == np.bincount(idx.reshape(-1), minlength=cfg.E)).all()
     if n_diff == 0:
