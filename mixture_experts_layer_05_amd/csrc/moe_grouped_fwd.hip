@@ -378,6 +378,23 @@ __device__ __forceinline__ void ggf_tile(const FwdParams& p, const TileIdx& ti, 
   if constexpr (kEpi == FWD_LOGITS) {
     if constexpr (kNRB > 0) {
     float* dst = p.outf + blockIdx.y * p.outf_split;
+    // This lane's columns' bias, loaded and waited for before the first
+    // store, with no branch around the loads (a descriptor of 0 bytes when
+    // there is no bias, or for slabs past the first; columns past d read
+    // zero): a load still pending at a store's operand would be waited for
+    // there with vmcnt(0), which also waits for every store before it (one
+    // round trip per store).
+    const bool has_bias = p.scale != nullptr && blockIdx.y == 0;
+    const __amdgpu_buffer_rsrc_t rs_bias = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(p.scale), 0, has_bias ? p.d * 4 : 0, kRsrcWord3);
+    float bias[kCB];
+#pragma unroll
+    for (int c = 0; c < kCB; ++c) {
+      const int n = n0 + wn * kCB * 32 + c * 32 + r32;
+      bias[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_bias, n * 4, 0, 0));
+    }
+#pragma unroll
+    for (int c = 0; c < kCB; ++c) asm volatile("" ::"v"(bias[c]));   // the one wait, here
 #pragma unroll
     for (int rb = 0; rb < kNRB; ++rb) {
 #pragma unroll
@@ -387,9 +404,7 @@ __device__ __forceinline__ void ggf_tile(const FwdParams& p, const TileIdx& ti, 
 #pragma unroll
         for (int c = 0; c < kCB; ++c) {
           const int n = n0 + wn * kCB * 32 + c * 32 + r32;
-          if (n < p.d)
-            dst[static_cast<size_t>(row) * p.d + n] =
-                acc[rb][c][r] + ((p.scale && blockIdx.y == 0) ? p.scale[n] : 0.0f);
+          if (n < p.d) dst[static_cast<size_t>(row) * p.d + n] = acc[rb][c][r] + bias[c];
         }
       }
     }
