@@ -713,6 +713,25 @@ __device__ __forceinline__ void ggfp_body(const FwdParams& p) {
       return base + rr * kRowB + ((((byte >> 4) ^ (rr & 15))) << 4) + (byte & 15);
     };
     const int wrow0 = wm * kRB * 32;
+    // fc2: the row scales of this lane's rows, loaded (branch-free: a
+    // descriptor over the tile's rows, 0 bytes when there is no scale) and
+    // waited for before the first pass: loaded inside a later pass, they
+    // would be waited for with vmcnt(0) behind the earlier pass's stores
+    float scl[kRB];
+    if constexpr (kEpi == FWD_FC2) {
+      const bool has_scale = p.scale != nullptr;
+      const __amdgpu_buffer_rsrc_t rs_s = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(p.scale + (has_scale ? m0 : 0)), 0,
+          has_scale ? (ti.mend - m0) * 4 : 0, kRsrcWord3);
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) {
+        const float v = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(rs_s, (wrow0 + rb * 32 + r32) * 4, 0, 0));
+        scl[rb] = has_scale ? v : 1.0f;
+      }
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) asm volatile("" ::"v"(scl[rb]));   // the one wait, here
+    }
 #pragma unroll
     for (int ps = 0; ps < kPass; ++ps) {
       if (wrow0 / kPassRows == ps) {
@@ -740,7 +759,7 @@ __device__ __forceinline__ void ggfp_body(const FwdParams& p) {
               }
             }
           } else {
-            const float sc = (p.scale && row < ti.mend) ? p.scale[row] : 1.0f;
+            const float sc = scl[rb];
 #pragma unroll
             for (int c = 0; c < kCB; ++c) {
 #pragma unroll
