@@ -568,20 +568,55 @@ __global__ __launch_bounds__(kPThreads, 1) void ggw_persistent_kernel(WgradParam
       return;
     }
     float* dw = p.outf + static_cast<size_t>(t.e) * p.outf_estride;
+    if (!p.accumulate) {
 #pragma unroll
-    for (int rb = 0; rb < kPRB; ++rb) {
+      for (int rb = 0; rb < kPRB; ++rb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = t.m0 + wm * kPRB * 32 + rb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (row >= p.out_m) continue;
-        float* dst = dw + static_cast<size_t>(row) * p.out_n;
+        for (int r = 0; r < 16; ++r) {
+          const int row = t.m0 + wm * kPRB * 32 + rb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (row >= p.out_m) continue;
+          float* dst = dw + static_cast<size_t>(row) * p.out_n;
 #pragma unroll
-        for (int c = 0; c < kPCB; ++c) {
-          const int col = t.n0 + wn * kPCB * 32 + c * 32 + r32;
-          if (col < p.out_n) {
-            const float v = acc[rb][c][r];
-            dst[col] = p.accumulate ? dst[col] + v : v;
+          for (int c = 0; c < kPCB; ++c) {
+            const int col = t.n0 + wn * kPCB * 32 + c * 32 + r32;
+            if (col < p.out_n) dst[col] = acc[rb][c][r];
           }
+        }
+      }
+    } else {
+      // dW += the tile: the old values of 8 elements at a time are loaded
+      // branch-free (elements outside dW get an offset past the buffer: they
+      // read zero and their stores are dropped) and waited for together; a
+      // wait per element would also wait for every store before it
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(dw, 0, p.out_m * p.out_n * 4, kRsrcWord3);
+#pragma unroll
+      for (int rb = 0; rb < kPRB; ++rb) {
+#pragma unroll
+        for (int r0 = 0; r0 < 16; r0 += 4) {
+          int off[4][kPCB];
+          float old[4][kPCB];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = t.m0 + wm * kPRB * 32 + rb * 32 + 8 * ((r0 + r) >> 2) + 4 * h + r;
+#pragma unroll
+            for (int c = 0; c < kPCB; ++c) {
+              const int col = t.n0 + wn * kPCB * 32 + c * 32 + r32;
+              off[r][c] = (row < p.out_m && col < p.out_n) ? (row * p.out_n + col) * 4 : kOob;
+              old[r][c] = __builtin_bit_cast(
+                  float, __builtin_amdgcn_raw_buffer_load_b32(rs, off[r][c], 0, 0));
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int c = 0; c < kPCB; ++c) asm volatile("" ::"v"(old[r][c]));   // one wait
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int c = 0; c < kPCB; ++c)
+              __builtin_amdgcn_raw_buffer_store_b32(
+                  __builtin_bit_cast(uint32_t, old[r][c] + acc[rb][c][r0 + r]), rs, off[r][c], 0, 0);
         }
       }
     }
