@@ -575,7 +575,12 @@ __device__ __forceinline__ void ggfp_body(const FwdParams& p) {
   uint16_t* const ring_b = s_lds + 2 * C::kATileE;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / kWN, wn = wave % kWN;
+  // Waves are dealt to the SIMDs round robin (SIMD = wave mod 4).  With 4 x 4
+  // waves, wave (wm, wn) sits on SIMD (wm + wn) mod 4, so the dead row blocks
+  // of a short tile (one wm) and the dead column blocks of the last column
+  // tile (the high wn) are spread over all four SIMDs.
+  const int wm = C::kWM == 4 && kWN == 4 ? wave >> 2 : wave / kWN;
+  const int wn = C::kWM == 4 && kWN == 4 ? ((wave & 3) - wm) & 3 : wave % kWN;
   const int r32 = lane & 31, h = lane >> 5;
   const int K = p.K;
   const int nk = (K + kBK - 1) / kBK;
@@ -621,19 +626,15 @@ __device__ __forceinline__ void ggfp_body(const FwdParams& p) {
       if (j2 < kALoads) {
         const int src = r > last ? -1 : gath ? p.gather[m0 + r] : r;
         st.vo[j2] = src >= 0 && (!gath || src < p.a_rows) ? (src * p.lda + kc * 8) * 2 : kOob;
-      } else if (p.packed_b) {
-        st.vo[j2] = ((ti.nt * p.nkt * kBN + r) * kBK + kc * 8) * 2;
       } else {
-        int wr;
-        if constexpr (kEpi == FWD_FC1) {
-          int f = n0 + (r % (kBN / 2));
-          f = f < p.F ? f : p.F - 1;
-          wr = r < kBN / 2 ? f : p.F + f;
-        } else {
-          wr = n0 + r;
-          wr = wr < p.d ? wr : p.d - 1;
-        }
-        st.vo[j2] = (wr * p.ldb + kc * 8) * 2;
+        // weight rows past the output (the last column tile's padding) are
+        // not read: an offset past the buffer reads zero, with no traffic
+        const int f = kEpi == FWD_FC1 ? n0 + (r % (kBN / 2)) : n0 + r;
+        const bool dead = f >= (kEpi == FWD_FC1 ? p.F : p.d);
+        const int wr = kEpi == FWD_FC1 && r >= kBN / 2 ? p.F + f : f;
+        st.vo[j2] = dead ? kOob
+                         : p.packed_b ? ((ti.nt * p.nkt * kBN + r) * kBK + kc * 8) * 2
+                                      : (wr * p.ldb + kc * 8) * 2;
       }
     }
   };
@@ -827,8 +828,12 @@ __device__ __forceinline__ void ggfp_body(const FwdParams& p) {
     }
   };
 
+  // live 32-row blocks of this wave; none when all its columns lie past the
+  // output (the last column tile's padding): its MFMAs are skipped
   auto live_blocks = [&](const TileIdx& ti) {
     const int rows = ti.mend - ti.m0 - wm * kRB * 32;
+    const int col0 = ti.nt * nbn + wn * (kEpi == FWD_FC1 ? kCB / 2 : kCB) * 32;
+    if (col0 >= limit) return 0;
     return rows <= 0 ? 0 : min(kRB, (rows + 31) >> 5);
   };
 
