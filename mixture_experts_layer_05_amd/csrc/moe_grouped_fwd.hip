@@ -581,7 +581,7 @@ __device__ __forceinline__ void ggfp_body(const FwdParams& p) {
   // tile (the high wn) are spread over all four SIMDs.
   const int wm = C::kWM == 4 && kWN == 4 ? wave >> 2 : wave / kWN;
   const int wn = C::kWM == 4 && kWN == 4 ? ((wave & 3) - wm) & 3 : wave % kWN;
-  const int r32 = lane & 31, h = lane >> 5;
+  const int r16 = lane & 15, q4 = lane >> 4;
   const int K = p.K;
   const int nk = (K + kBK - 1) / kBK;
 
@@ -655,38 +655,46 @@ __device__ __forceinline__ void ggfp_body(const FwdParams& p) {
     }
   };
 
-  // this wave's operand rows in the staged tiles
-  int a_rd[kRB], b_rd[kCB];
+  // The MFMAs are v_mfma_f32_16x16x32_bf16: a wave's 32-row / 32-column
+  // blocks (the tiling, the live-block counts) are each 2 x 2 blocks of 16;
+  // lane l reads 8 bf16 of K (16-byte chunk 4 kk + l / 16) of row l mod 16 of
+  // a block, and holds output columns 4 (l / 16) .. + 3 of row l mod 16.
+  // (Against 32 x 32 x 16 in a dense probe of the same loop: 3-7% faster,
+  // with the shader clock higher.)
+  constexpr int kR16 = 2 * kRB, kC16 = 2 * kCB;
+  // Every block starts at a multiple of 16 rows and the chunk swizzle
+  // depends on the row mod 16 only, so one lane offset per K sub-step
+  // addresses the same row of every block; the blocks differ by constants.
+  int lane_off[kBK / 32];
 #pragma unroll
-  for (int i = 0; i < kRB; ++i) a_rd[i] = wm * kRB * 32 + i * 32 + r32;
-#pragma unroll
-  for (int c = 0; c < kCB; ++c) {
-    if constexpr (kEpi == FWD_FC1) {
-      const int cc = c % (kCB / 2);
-      b_rd[c] = (c < kCB / 2 ? 0 : kBN / 2) + wn * (kCB / 2) * 32 + cc * 32 + r32;
-    } else {
-      b_rd[c] = wn * kCB * 32 + c * 32 + r32;
-    }
-  }
-  auto swz = [](int r, int kc) { return r * kBK + ((kc ^ swz_row<kChunks>(r)) << 3); };
+  for (int kk = 0; kk < kBK / 32; ++kk)
+    lane_off[kk] = r16 * kBK + (((4 * kk + q4) ^ swz_row<kChunks>(r16)) << 3);
+  const int a_row0 = wm * kRB * 32;
+  auto b_row0 = [&](int c16) {   // first row of this wave's 16-row block c16 of B
+    const int c = c16 >> 1, half = c16 & 1;
+    if constexpr (kEpi == FWD_FC1)
+      return (c < kCB / 2 ? 0 : kBN / 2) + wn * (kCB / 2) * 32 + (c % (kCB / 2)) * 32 + half * 16;
+    else
+      return wn * kCB * 32 + c * 32 + half * 16;
+  };
 
-  f32x16 acc[kRB][kCB];
+  f32x4 acc[kR16][kC16];
   auto compute = [&](int slot, int nrb) {
-    const uint16_t* As = ring_a + slot * C::kATileE;
+    const uint16_t* As = ring_a + slot * C::kATileE + a_row0 * kBK;
     const uint16_t* Bs = ring_b + slot * C::kBTileE;
 #pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      const int ck = 2 * kk + h;
-      bf16x8 bv[kCB];
+    for (int kk = 0; kk < kBK / 32; ++kk) {
+      bf16x8 bv[kC16];
 #pragma unroll
-      for (int c = 0; c < kCB; ++c) bv[c] = *reinterpret_cast<const bf16x8*>(Bs + swz(b_rd[c], ck));
+      for (int c = 0; c < kC16; ++c)
+        bv[c] = *reinterpret_cast<const bf16x8*>(Bs + b_row0(c) * kBK + lane_off[kk]);
 #pragma unroll
-      for (int rb = 0; rb < kRB; ++rb) {
-        if (rb < nrb) {
-          const bf16x8 av = *reinterpret_cast<const bf16x8*>(As + swz(a_rd[rb], ck));
+      for (int i = 0; i < kR16; ++i) {
+        if ((i >> 1) < nrb) {
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(As + i * 16 * kBK + lane_off[kk]);
 #pragma unroll
-          for (int c = 0; c < kCB; ++c)
-            acc[rb][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[c], av, acc[rb][c], 0, 0, 0);
+          for (int c = 0; c < kC16; ++c)
+            acc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv[c], av, acc[i][c], 0, 0, 0);
         }
       }
     }
@@ -714,63 +722,58 @@ __device__ __forceinline__ void ggfp_body(const FwdParams& p) {
       return base + rr * kRowB + ((((byte >> 4) ^ (rr & 15))) << 4) + (byte & 15);
     };
     const int wrow0 = wm * kRB * 32;
+    // the lane's row and column within a 16 x 16 block, re-derived here from
+    // an opaque copy of the lane index so that the staging addresses are
+    // formed per tile instead of being hoisted and kept live through the
+    // K loop (they would push its registers past the 128 of 4 waves per SIMD)
+    int le = lane;
+    asm volatile("" : "+v"(le));
+    const int r16 = le & 15, q4 = le >> 4;
     // fc2: the row scales of this lane's rows, loaded (branch-free: a
     // descriptor over the tile's rows, 0 bytes when there is no scale) and
     // waited for before the first pass: loaded inside a later pass, they
     // would be waited for with vmcnt(0) behind the earlier pass's stores
-    float scl[kRB];
+    float scl[kR16];
     if constexpr (kEpi == FWD_FC2) {
       const bool has_scale = p.scale != nullptr;
       const __amdgpu_buffer_rsrc_t rs_s = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<float*>(p.scale + (has_scale ? m0 : 0)), 0,
           has_scale ? (ti.mend - m0) * 4 : 0, kRsrcWord3);
 #pragma unroll
-      for (int rb = 0; rb < kRB; ++rb) {
+      for (int i = 0; i < kR16; ++i) {
         const float v = __builtin_bit_cast(
-            float, __builtin_amdgcn_raw_buffer_load_b32(rs_s, (wrow0 + rb * 32 + r32) * 4, 0, 0));
-        scl[rb] = has_scale ? v : 1.0f;
+            float, __builtin_amdgcn_raw_buffer_load_b32(rs_s, (wrow0 + i * 16 + r16) * 4, 0, 0));
+        scl[i] = has_scale ? v : 1.0f;
       }
 #pragma unroll
-      for (int rb = 0; rb < kRB; ++rb) asm volatile("" ::"v"(scl[rb]));   // the one wait, here
+      for (int i = 0; i < kR16; ++i) asm volatile("" ::"v"(scl[i]));   // the one wait, here
     }
 #pragma unroll
     for (int ps = 0; ps < kPass; ++ps) {
       if (wrow0 / kPassRows == ps) {
 #pragma unroll
-        for (int rb = 0; rb < kRB; ++rb) {
-          if (rb >= nrb) continue;
-          const int lp = wrow0 - ps * kPassRows + rb * 32 + r32;
-          const int row = m0 + wrow0 + rb * 32 + r32;
+        for (int i = 0; i < kR16; ++i) {
+          if ((i >> 1) >= nrb) continue;
+          const int lp = wrow0 - ps * kPassRows + i * 16 + r16;
           if constexpr (kEpi == FWD_FC1) {
 #pragma unroll
-            for (int c = 0; c < kCB / 2; ++c) {
+            for (int c16 = 0; c16 < kC16 / 2; ++c16) {   // G blocks; U is kC16 / 2 further
+              const int fl = wn * (kCB / 2) * 32 + c16 * 16 + 4 * q4;
+              const f32x4& G = acc[i][c16];
+              const f32x4& U = acc[i][c16 + kC16 / 2];
+              float a4[4];
 #pragma unroll
-              for (int qq = 0; qq < 4; ++qq) {
-                const int fl = wn * (kCB / 2) * 32 + c * 32 + 8 * qq + 4 * h;
-                const f32x16& G = acc[rb][c];
-                const f32x16& U = acc[rb][c + kCB / 2];
-                float a4[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                  const float g = G[4 * qq + i];
-                  a4[i] = g * sigmoid_fast(g) * U[4 * qq + i];
-                }
-                *reinterpret_cast<u32x2*>(staged(lp, fl * 2)) =
-                    pack4_bf16(a4[0], a4[1], a4[2], a4[3]);
-              }
+              for (int e = 0; e < 4; ++e) a4[e] = G[e] * sigmoid_fast(G[e]) * U[e];
+              *reinterpret_cast<u32x2*>(staged(lp, fl * 2)) = pack4_bf16(a4[0], a4[1], a4[2], a4[3]);
             }
           } else {
-            const float sc = scl[rb];
+            const float sc = scl[i];
 #pragma unroll
-            for (int c = 0; c < kCB; ++c) {
-#pragma unroll
-              for (int qq = 0; qq < 4; ++qq) {
-                const int nl = wn * kCB * 32 + c * 32 + 8 * qq + 4 * h;
-                const f32x16& Y = acc[rb][c];
-                *reinterpret_cast<u32x2*>(staged(lp, nl * 2)) =
-                    pack4_bf16(Y[4 * qq] * sc, Y[4 * qq + 1] * sc, Y[4 * qq + 2] * sc,
-                               Y[4 * qq + 3] * sc);
-              }
+            for (int c16 = 0; c16 < kC16; ++c16) {
+              const int nl = wn * kCB * 32 + c16 * 16 + 4 * q4;
+              const f32x4& Y = acc[i][c16];
+              *reinterpret_cast<u32x2*>(staged(lp, nl * 2)) =
+                  pack4_bf16(Y[0] * sc, Y[1] * sc, Y[2] * sc, Y[3] * sc);
             }
           }
         }
@@ -797,18 +800,14 @@ __device__ __forceinline__ void ggfp_body(const FwdParams& p) {
         for (int half = 0; half < 2; ++half) {
           asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // staging free again
 #pragma unroll
-          for (int rb = 0; rb < kRB; ++rb) {
-            if (rb >= nrb) continue;
-            const int lp = wrow0 + rb * 32 + r32;
+          for (int i = 0; i < kR16; ++i) {
+            if ((i >> 1) >= nrb) continue;
+            const int lp = wrow0 + i * 16 + r16;
 #pragma unroll
-            for (int c = 0; c < kCB / 2; ++c) {
-#pragma unroll
-              for (int qq = 0; qq < 4; ++qq) {
-                const int fl = wn * (kCB / 2) * 32 + c * 32 + 8 * qq + 4 * h;
-                const f32x16& X = half ? acc[rb][c + kCB / 2] : acc[rb][c];
-                *reinterpret_cast<u32x2*>(staged(lp, fl * 2)) =
-                    pack4_bf16(X[4 * qq], X[4 * qq + 1], X[4 * qq + 2], X[4 * qq + 3]);
-              }
+            for (int c16 = 0; c16 < kC16 / 2; ++c16) {
+              const int fl = wn * (kCB / 2) * 32 + c16 * 16 + 4 * q4;
+              const f32x4& X = half ? acc[i][c16 + kC16 / 2] : acc[i][c16];
+              *reinterpret_cast<u32x2*>(staged(lp, fl * 2)) = pack4_bf16(X[0], X[1], X[2], X[3]);
             }
           }
           asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -847,9 +846,9 @@ __device__ __forceinline__ void ggfp_body(const FwdParams& p) {
   for (int j = 0; j < ntiles; ++j) {
     const int nrb = live_blocks(cur.ti);
 #pragma unroll
-    for (int i = 0; i < kRB; ++i)
+    for (int i = 0; i < kR16; ++i)
 #pragma unroll
-      for (int c = 0; c < kCB; ++c) acc[i][c] = f32x16{};
+      for (int c = 0; c < kC16; ++c) acc[i][c] = f32x4{};
 #pragma unroll 1
     for (int kt = 0; kt < nk; ++kt, ++g) {
       // everything this wave issued has landed (the ring's loads, the gathers
