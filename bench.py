@@ -54,15 +54,15 @@ KERNEL_SOURCES_FP8 = ("mixture_experts_layer_05_amd/csrc/moe_grouped_mx.hip",
 # (fp8: profiles/fp8_grouped_gemm_qwen3_30b_hbm_bytes.md, the quantiser + fc1 + fc2)
 MEASURED_TRAFFIC = {
     # profiles/grouped_gemm_fwd_qwen3_30b_hbm_bytes.md
-    "qwen3_30b": {"bytes": 1625304523,
-                  "sources_sha256": "9d278faea3acedbfd2d7625f46cc7dfed76b977708d4ac61b03853f8e9bd5dd8"},
+    "qwen3_30b": {"bytes": 1656854957,
+                  "sources_sha256": "7cc6afd73b36afae2bcac6e0605e259d1da06f04cdca51dfc5cba6f9111e7bac"},
     # profiles/grouped_gemm_fwd_dsv_30b_hbm_bytes.md
-    "dsv_30b": {"bytes": 5283680422,
-                "sources_sha256": "9d278faea3acedbfd2d7625f46cc7dfed76b977708d4ac61b03853f8e9bd5dd8"},
+    "dsv_30b": {"bytes": 5541215691,
+                "sources_sha256": "7cc6afd73b36afae2bcac6e0605e259d1da06f04cdca51dfc5cba6f9111e7bac"},
     # profiles/grouped_gemm_fwd_skew_shared_hbm_bytes.md
-    "skew_shared": {"bytes": 3704603806,
-                    "sources_sha256": "9d278faea3acedbfd2d7625f46cc7dfed76b977708d4ac61b03853f8e9bd5dd8"},
-    "qwen3_30b:fp8": {"bytes": 977034534,
+    "skew_shared": {"bytes": 3966602436,
+                    "sources_sha256": "7cc6afd73b36afae2bcac6e0605e259d1da06f04cdca51dfc5cba6f9111e7bac"},
+    "qwen3_30b:fp8": {"bytes": 974744809,
                       "sources_sha256": "b0b29d0cde5fa5331b7045cb561580f6e813dd4eb7905a37d057c41c0c94631a"},
 }
 

@@ -10,7 +10,8 @@
 //   * expert GEMMs: one workgroup of 16 wavefronts (4 x 4) per CU = one
 //     output tile of 256 token rows x 256 weight rows (fc1: 128 gate rows +
 //     the 128 matching up rows; fc2: 256 output columns); each wave computes
-//     64 x 64 with 2 x 2 v_mfma_f32_32x32x16_bf16 accumulators; K tiles are
+//     64 x 64 as 4 x 4 blocks of v_mfma_f32_16x16x32_bf16 (the router
+//     logits tile keeps 32 x 32 x 16 blocks); K tiles are
 //     64 wide, so every staged row segment is one whole 128-byte cache line
 //     (a 32-wide K tile fetches half lines, which measured 1.5x slower from
 //     L2 into LDS), in a 2-deep ring (128 KB);
@@ -24,14 +25,16 @@
 //   * the LDS layout is [row][16-byte chunks] with the chunk index XOR a
 //     function of the row (f = (r1 ^ r3) | r2 << 1 for 4 chunks, (r mod 8)
 //     ^ r3 for 8 chunks; r_i = bit i of the row): lane l of a block fetches
-//     the chunk that lands at position l, and the MFMA operand reads (32
-//     consecutive rows, one chunk) and the block writes are free of bank
+//     the chunk that lands at position l, and the MFMA operand reads (16 or
+//     32 consecutive rows, one chunk) and the block writes are free of bank
 //     conflicts with 32 or 64 banks;
 //   * addresses are a buffer descriptor, a loop-invariant per-lane offset
 //     and a scalar K offset; a chunk past K gets an offset past the end of
 //     the buffer, which reads as zero, so K tails need no branches;
 //   * a wave whose 32-row blocks lie past the end of the expert's segment
-//     skips their MFMAs;
+//     skips their MFMAs, and so does a wave whose columns all lie past the
+//     output (the last column tile's padding, whose weight rows are not
+//     read);
 //   * tiles are decoded on the device from expert_offsets and handed to
 //     XCDs in contiguous ranges (the row tiles sharing a weight panel run
 //     together on one XCD and share its L2);
