@@ -682,23 +682,28 @@ __device__ __forceinline__ void ggfp_body(const FwdParams& p) {
   };
 
   f32x4 acc[kR16][kC16];
+  // A wave with any live row block multiplies all of its blocks (rows past
+  // the segment are zero in LDS): no branch inside the K step, so the next
+  // block's fragment can be read while this block's MFMAs run.
   auto compute = [&](int slot, int nrb) {
+    if (nrb == 0) return;
     const uint16_t* As = ring_a + slot * C::kATileE + a_row0 * kBK;
     const uint16_t* Bs = ring_b + slot * C::kBTileE;
 #pragma unroll
     for (int kk = 0; kk < kBK / 32; ++kk) {
-      bf16x8 bv[kC16];
+      bf16x8 bv[kC16], av[2];
 #pragma unroll
       for (int c = 0; c < kC16; ++c)
         bv[c] = *reinterpret_cast<const bf16x8*>(Bs + b_row0(c) * kBK + lane_off[kk]);
+      av[0] = *reinterpret_cast<const bf16x8*>(As + lane_off[kk]);
 #pragma unroll
       for (int i = 0; i < kR16; ++i) {
-        if ((i >> 1) < nrb) {
-          const bf16x8 av = *reinterpret_cast<const bf16x8*>(As + i * 16 * kBK + lane_off[kk]);
+        if (i + 1 < kR16)
+          av[(i + 1) & 1] = *reinterpret_cast<const bf16x8*>(As + (i + 1) * 16 * kBK + lane_off[kk]);
 #pragma unroll
-          for (int c = 0; c < kC16; ++c)
-            acc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv[c], av, acc[i][c], 0, 0, 0);
-        }
+        for (int c = 0; c < kC16; ++c)
+          acc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv[c], av[i & 1], acc[i][c], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
