@@ -703,7 +703,7 @@ __device__ __forceinline__ void ggfp_body(const FwdParams& p) {
 #pragma unroll
         for (int c = 0; c < kC16; ++c)
           acc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv[c], av[i & 1], acc[i][c], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
+        if (i + 1 < kR16) __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
