@@ -144,7 +144,13 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
         for (int j = 0; j < kPer; ++j)
           if (s0 + q < nslab) p[j] += v[q][j];
     }
-    if (score_fn == MOE_SCORE_SOFTMAX) {
+    // With normalised weights and no selection bias, the choice and the
+    // weights depend on the logits of the chosen experts only: softmax and
+    // sigmoid are increasing, so the logits rank the experts as the scores
+    // do, and the softmax's denominator over all E cancels in the
+    // renormalisation.  The scores are then formed for the k winners alone.
+    const bool on_logits = normalize && !sel_bias;
+    if (!on_logits && score_fn == MOE_SCORE_SOFTMAX) {
       float m = -INFINITY;
 #pragma unroll
       for (int j = 0; j < kPer; ++j)
@@ -159,12 +165,13 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
       s = grp_sum<G>(s);
 #pragma unroll
       for (int j = 0; j < kPer; ++j) p[j] = p[j] / s;
-    } else {
+    } else if (!on_logits) {
 #pragma unroll
       for (int j = 0; j < kPer; ++j) p[j] = sigmoidf_(p[j]);
     }
-    // ranking keys: the scores, or score + selection bias (fp32); -inf for
-    // lanes past E and for experts already chosen
+    // ranking keys: the scores (the logits when ranking on them), or score +
+    // selection bias (fp32); -inf for lanes past E and for experts already
+    // chosen
     float key[kPer];
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
@@ -216,7 +223,7 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
         const bool own = wi < E && ia == wi;
         // the winner's (unbiased) score from its owner (scores are >= 0, so a
         // max over zeros elsewhere returns it)
-        const float pw = grp_max<G>(own ? sa : 0.0f);
+        const float pw = on_logits ? mv : grp_max<G>(own ? sa : 0.0f);
 #pragma unroll
         for (int r = 0; r < kSlots; ++r)
           if (j == gi + G * r) { my_e[r] = wi; my_p[r] = pw; }
@@ -257,12 +264,21 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
 #pragma unroll
         for (int jj = 0; jj < kPer; ++jj)
           if (own && jj == wi / G) { pw = p[jj]; key[jj] = -INFINITY; }
-        pw = grp_max<G>(pw);
+        pw = on_logits ? mv : grp_max<G>(pw);
 #pragma unroll
         for (int r = 0; r < kSlots; ++r)
           if (j == gi + G * r) { my_e[r] = wi; my_p[r] = pw; }
         local_best();
       }
+    }
+    if (on_logits) {
+      // the winners' scores from their logits (the first winner's is the
+      // largest logit of the token: the softmax's shift); a place with no
+      // selectable expert (index E) holds -inf and scores 0
+      const float m0 = grp_max<G>(gi == 0 ? my_p[0] : -INFINITY);
+#pragma unroll
+      for (int r = 0; r < kSlots; ++r)
+        my_p[r] = score_fn == MOE_SCORE_SOFTMAX ? expf(my_p[r] - m0) : sigmoidf_(my_p[r]);
     }
     float denom = 1.0f;
     if (normalize) {
