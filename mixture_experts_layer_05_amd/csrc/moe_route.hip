@@ -102,7 +102,7 @@ __device__ __forceinline__ float grp_sum(float v) {
 // the workgroup's 64 tokens in 64 / (16 * 64 / G) passes.  A token's lanes
 // are all active or all inactive, so the row-wise DPP reads only its own
 // lanes.
-template <bool kBF16, int G, int kPer>
+template <bool kBF16, int G, int kPer, bool kOnLogits>
 __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
     int T, int d, int E, int k, int score_fn, int normalize, int nslab, const float* __restrict__ z,
     const float* __restrict__ sel_bias, const void* __restrict__ xv, const void* __restrict__ wgv,
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
     // sigmoid are increasing, so the logits rank the experts as the scores
     // do, and the softmax's denominator over all E cancels in the
     // renormalisation.  The scores are then formed for the k winners alone.
-    const bool on_logits = normalize && !sel_bias;
+    constexpr bool on_logits = kOnLogits;   // the host passes normalize && !sel_bias
     if (!on_logits && score_fn == MOE_SCORE_SOFTMAX) {
       float m = -INFINITY;
 #pragma unroll
@@ -202,14 +202,16 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
           const int e = gi + G * j;
           const bool c1 = v > ka, c2 = v > kb, c3 = v > kc;
           kc = c2 ? kb : (c3 ? v : kc);
-          sc = c2 ? sb : (c3 ? p[j] : sc);
           ic = c2 ? ib : (c3 ? e : ic);
           kb = c1 ? ka : (c2 ? v : kb);
-          sb = c1 ? sa : (c2 ? p[j] : sb);
           ib = c1 ? ia : (c2 ? e : ib);
           ka = c1 ? v : ka;
-          sa = c1 ? p[j] : sa;
           ia = c1 ? e : ia;
+          if constexpr (!kOnLogits) {        // the score rides along when it is not the key
+            sc = c2 ? sb : (c3 ? p[j] : sc);
+            sb = c1 ? sa : (c2 ? p[j] : sb);
+            sa = c1 ? p[j] : sa;
+          }
         }
         left = 3;
       };
@@ -354,15 +356,20 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
   }
 }
 
+template <bool kBF16, bool kOnLogits>
+static auto pick_topk_(int E) {
+  if (E <= 16) return route_topk_kernel<kBF16, 16, 1, kOnLogits>;
+  if (E <= 32) return route_topk_kernel<kBF16, 16, 2, kOnLogits>;
+  if (E <= 64) return route_topk_kernel<kBF16, 16, 4, kOnLogits>;
+  if (E <= 128) return route_topk_kernel<kBF16, 16, 8, kOnLogits>;
+  if (E <= 256) return route_topk_kernel<kBF16, 16, 16, kOnLogits>;
+  if (E <= 512) return route_topk_kernel<kBF16, 64, 8, kOnLogits>;
+  return route_topk_kernel<kBF16, 64, 16, kOnLogits>;
+}
+// ranking on the logits: normalised weights and no selection bias
 template <bool kBF16>
-static auto pick_topk(int E) {
-  if (E <= 16) return route_topk_kernel<kBF16, 16, 1>;
-  if (E <= 32) return route_topk_kernel<kBF16, 16, 2>;
-  if (E <= 64) return route_topk_kernel<kBF16, 16, 4>;
-  if (E <= 128) return route_topk_kernel<kBF16, 16, 8>;
-  if (E <= 256) return route_topk_kernel<kBF16, 16, 16>;
-  if (E <= 512) return route_topk_kernel<kBF16, 64, 8>;
-  return route_topk_kernel<kBF16, 64, 16>;
+static auto pick_topk(int E, bool on_logits) {
+  return on_logits ? pick_topk_<kBF16, true>(E) : pick_topk_<kBF16, false>(E);
 }
 
 }  // namespace moe
@@ -426,7 +433,8 @@ extern "C" moe_status moe_route(hipStream_t stream, moe_dtype dt, int64_t T, int
                  static_cast<const float*>(w_router), logit_bias, z, expert_counts);
   }
   if (err != hipSuccess) return MOE_ERR_HIP;
-  auto kern = dt == MOE_BF16 ? pick_topk<true>(E) : pick_topk<false>(E);
+  const bool on_logits = normalize && selection_bias == nullptr;
+  auto kern = dt == MOE_BF16 ? pick_topk<true>(E, on_logits) : pick_topk<false>(E, on_logits);
   const int nblk = static_cast<int>((T + kTopkBlk - 1) / kTopkBlk);
   err = launch(kern, dim3(nblk), dim3(kTopkThreads), E * sizeof(int), stream, (int)T, (int)d, E, k,
                (int)fn, normalize, nslab, (const float*)z, selection_bias, x, w_gate,
