@@ -114,6 +114,8 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
   static_assert(kTopkBlk % kTokPass == 0, "passes cover the block");
   constexpr int kSlots = (32 + G - 1) / G;             // choices held per lane (k <= 32)
   extern __shared__ int s_cnt[];     // [E] histogram of this workgroup's choices
+  // then (16-lane groups) the choices of the pass's tokens, 32 per token
+  int2* const s_ch = reinterpret_cast<int2*>(s_cnt + ((E + 1) & ~1));
   for (int e = threadIdx.x; e < E; e += kTopkThreads) s_cnt[e] = 0;
   __syncthreads();
   const int gi = threadIdx.x & (G - 1);
@@ -216,19 +218,37 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
         left = 3;
       };
       top3(false);
+      // choice j of this token, (expert, score), written by the lane that
+      // decides it and read back after the k rounds
+      int2* const ch = s_ch + (threadIdx.x / G) * 32;
       for (int j = 0; j < k; ++j) {
-        // the largest remaining key of the group, then the lowest expert index
-        // holding it; its owner is the lane whose list it heads
+        // the largest remaining key of the group; a single lane holding it
+        // is the winner (its list head).  When a group has several (equal
+        // keys, or no key left at all) the lowest expert index among them
+        // wins, found by a group min; the wavefront takes that path only
+        // when one of its groups needs it.
         const float mv = grp_max<G>(ka);
-        int wi = grp_min<G>(ka == mv ? ia : INT_MAX);
-        wi = wi < E ? wi : E;
-        const bool own = wi < E && ia == wi;
-        // the winner's (unbiased) score from its owner (scores are >= 0, so a
-        // max over zeros elsewhere returns it)
-        const float pw = on_logits ? mv : grp_max<G>(own ? sa : 0.0f);
-#pragma unroll
-        for (int r = 0; r < kSlots; ++r)
-          if (j == gi + G * r) { my_e[r] = wi; my_p[r] = pw; }
+        const bool cand = ka == mv;
+        const unsigned long long bal = __ballot(cand);
+        const bool multi = __popcll((bal >> (threadIdx.x & 48)) & 0xffffull) > 1;
+        bool own, writer;
+        int wi;
+        if (__ballot(multi) != 0ull) {
+          wi = grp_min<G>(cand ? ia : INT_MAX);
+          wi = wi < E ? wi : E;
+          own = wi < E && ia == wi;
+          writer = own || (wi == E && gi == 0);
+        } else {
+          wi = ia;
+          own = cand;
+          writer = own;
+        }
+        if (writer) {
+          // the winner's (unbiased) score: the key itself when ranking on
+          // logits, else its list head's score
+          const float pw = own ? (on_logits ? mv : sa) : 0.0f;
+          ch[j] = make_int2(own ? wi : E, __float_as_int(pw));
+        }
         if (own) {
           taken |= 1u << (wi / G);
           ka = kb; sa = sb; ia = ib;
@@ -237,6 +257,18 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
           --left;
         }
         if (left == 0 && j + 1 < k) top3(true);   // rare: a lane's fourth choice
+      }
+      // other lanes' LDS writes are read back: keep the compiler from moving
+      // the reads above them (one wavefront's LDS accesses execute in order)
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int r = 0; r < kSlots; ++r) {
+        const int j = gi + G * r;
+        if (j < k) {
+          const int2 c = ch[j];      // written by a lane of this wavefront, in order
+          my_e[r] = c.x;
+          my_p[r] = __int_as_float(c.y);
+        }
       }
     } else {
       // A wavefront per token: a lane holds few scores, so it rescans them
@@ -436,7 +468,9 @@ extern "C" moe_status moe_route(hipStream_t stream, moe_dtype dt, int64_t T, int
   const bool on_logits = normalize && selection_bias == nullptr;
   auto kern = dt == MOE_BF16 ? pick_topk<true>(E, on_logits) : pick_topk<false>(E, on_logits);
   const int nblk = static_cast<int>((T + kTopkBlk - 1) / kTopkBlk);
-  err = launch(kern, dim3(nblk), dim3(kTopkThreads), E * sizeof(int), stream, (int)T, (int)d, E, k,
+  // LDS: the histogram, then (16-lane groups) 32 choices per token of a pass
+  const size_t lds = ((E + 1) & ~1) * sizeof(int) + (E <= 256 ? kTopkThreads / 16 * 32 * 8 : 0);
+  err = launch(kern, dim3(nblk), dim3(kTopkThreads), lds, stream, (int)T, (int)d, E, k,
                (int)fn, normalize, nslab, (const float*)z, selection_bias, x, w_gate,
                (const float*)gz, topk_idx, topk_w, expert_counts, block_counts, gate);
   return hip_status(err);

@@ -91,6 +91,58 @@ def test_route_parity(case):
         assert np.abs(g - ref.gate).max() <= gh.TOL_ROUTE_W
 
 
+TIE_CASES = [
+    # T, d, E, k, score, normalize, bias ("logit": added to the logits,
+    # "select": selection only), dtype
+    (300, 128, 64, 7, "softmax", True, None, "bf16"),
+    (300, 128, 128, 6, "sigmoid", True, None, "bf16"),
+    (257, 64, 256, 8, "softmax", True, "logit", "f32"),
+    (129, 64, 130, 5, "sigmoid", True, "select", "bf16"),
+    (200, 64, 256, 8, "sigmoid", False, None, "bf16"),
+    (90, 64, 600, 9, "softmax", True, None, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", TIE_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_route_exact_ties(case):
+    """Expert 2i+1 is a copy of expert 2i (router row and bias), so every
+    token's scores come in exactly equal pairs.  Equal scores rank the lower
+    index first: a chosen odd expert has its even twin chosen at an earlier
+    place, with a bitwise equal weight."""
+    T, d, E, k, score, norm, bias, dt = case
+    inp = mw.make_small_layer_inputs(29 + T + E, T=T, d=d, E=E, F=8, dtype=dt,
+                                     Fs=0, bias=bias == "logit")
+    inp.w_router = inp.w_router.copy()
+    inp.w_router[1::2] = inp.w_router[0::2]
+    lb = sb = None
+    if bias == "logit":
+        lb = inp.logit_bias.copy()
+        lb[1::2] = lb[0::2]
+    elif bias == "select":
+        sb = (np.random.default_rng(E).standard_normal(E) * 0.1).astype(np.float32)
+        sb[1::2] = sb[0::2]
+    ref = mo.route(inp.as_f32("x"), inp.as_f32("w_router"), k, score, norm, lb, None,
+                   selection_bias=sb)
+    out = (gh.poison((T, k), torch.int32), gh.poison((T, k), torch.float32),
+           gh.poison((E,), torch.int32), None)
+    g = lambda a: None if a is None else gh.to_gpu(a)  # noqa: E731
+    moe.route(g(inp.x), g(inp.w_router), k, score, norm, g(lb), None, out=out,
+              selection_bias=g(sb))
+    torch.cuda.synchronize()
+    idx, w = out[0].cpu().numpy(), out[1].cpu().numpy()
+    gh.check_routing(idx, w, ref, k)
+    n_pairs = 0
+    for t in range(T):
+        place = {int(e): j for j, e in enumerate(idx[t])}
+        for e, j in place.items():
+            if e % 2:
+                assert e - 1 in place and place[e - 1] < j, (t, idx[t])
+                assert w[t, j] == w[t, place[e - 1]], (t, e)
+                n_pairs += 1
+    assert n_pairs > 0
+    assert (out[2].cpu().numpy() == np.bincount(idx.reshape(-1), minlength=E)).all()
+
+
 SELB_CASES = [
     # T, d, E, k, score, dtype, bias std
     (300, 64, 33, 5, "sigmoid", "f32", 0.1),
