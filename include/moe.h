@@ -86,7 +86,12 @@ MOE_API const char* moe_status_string(moe_status s);
  *     s[t,e] = softmax_e(z[t,:])  or  1 / (1 + exp(-z[t,e]))
  * The k experts with the largest fp32 scores are chosen, in descending
  * score order (equal scores: lower expert index first).  With `normalize`
- * the weights are s / (sum of the k chosen s), else the raw scores.
+ * the weights are s / (sum of the k chosen s), else the raw scores.  With
+ * `normalize` and no selection_bias the experts are ranked by their fp32
+ * logits z instead (softmax and sigmoid are increasing, so this is the score
+ * order except where two scores lie within rounding of each other; equal
+ * logits again rank the lower index first), and the scores are formed for
+ * the k chosen experts only.
  * selection_bias (the expert-bias correction of the MoE-acceleration and
  * recipe config listings, "moe_router_enable_expert_bias", DeepSeek-style)
  * shifts only the choice: experts are ranked by the fp32 sum s + b[e],
