@@ -116,7 +116,10 @@ MOE_API const char* moe_status_string(moe_status s);
  * 16*T*E < 2^31.  Workspace: moe_route_workspace_size(T, d, E, dt) bytes (the
  * fp32 logits, up to 16 K slabs, and for bf16 the K slabs of the gate's dot
  * product).  A NaN score is never chosen; a token with fewer than k
- * selectable scores gets index E (out of range) for the missing slots.
+ * selectable scores gets index E (out of range) for the missing slots.  An
+ * expert whose logit is -inf (masked, e.g. by a -inf logit_bias) has score
+ * 0 and weight 0; it is chosen only after every expert with a finite
+ * logit, lower index first.
  * --------------------------------------------------------------------- */
 MOE_API size_t moe_route_workspace_size(int64_t T, int64_t d, int32_t E, moe_dtype dt);
 MOE_API moe_status moe_route(hipStream_t stream, moe_dtype dt, int64_t T, int64_t d,

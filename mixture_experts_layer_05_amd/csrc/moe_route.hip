@@ -173,12 +173,16 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
     }
     // ranking keys: the scores (the logits when ranking on them), or score +
     // selection bias (fp32); -inf for lanes past E and for experts already
-    // chosen
+    // chosen.  A -inf logit (a masked expert) scores 0, which stays
+    // selectable: ranking on logits it becomes the lowest finite key, below
+    // every finite logit, and scores 0 again when its weight is formed.
     float key[kPer];
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int e = gi + G * j;
-      key[j] = e < E ? (sel_bias ? p[j] + sel_bias[e] : p[j]) : -INFINITY;
+      float kv = sel_bias ? p[j] + sel_bias[e < E ? e : 0] : p[j];
+      if (on_logits && kv == -INFINITY) kv = -__FLT_MAX__;
+      key[j] = e < E ? kv : -INFINITY;
     }
     int my_e[kSlots];
     float my_p[kSlots];
@@ -245,8 +249,9 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
         }
         if (writer) {
           // the winner's (unbiased) score: the key itself when ranking on
-          // logits, else its list head's score
-          const float pw = own ? (on_logits ? mv : sa) : 0.0f;
+          // logits (-inf for an empty place: its weight is 0), else its list
+          // head's score
+          const float pw = on_logits ? mv : (own ? sa : 0.0f);
           ch[j] = make_int2(own ? wi : E, __float_as_int(pw));
         }
         if (own) {

@@ -143,7 +143,8 @@ def route(x, w_router, k, score_fn="softmax", normalize=True,
         kth = order[:, k - 1]
         margin = (s32[np.arange(T), kth].astype(np.float64)
                   - s32[np.arange(T), nxt].astype(np.float64))
-        logit_margin = (z[np.arange(T), kth] - z[np.arange(T), nxt]).astype(np.float64)
+        with np.errstate(invalid="ignore"):   # two masked (-inf) logits: NaN margin
+            logit_margin = (z[np.arange(T), kth] - z[np.arange(T), nxt]).astype(np.float64)
     else:
         margin = np.full(T, np.inf)
         logit_margin = np.full(T, np.inf)

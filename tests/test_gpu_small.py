@@ -143,6 +143,70 @@ def test_route_exact_ties(case):
     assert (out[2].cpu().numpy() == np.bincount(idx.reshape(-1), minlength=E)).all()
 
 
+MASK_CASES = [
+    # T, d, E, k, score, normalize, masked experts, dtype
+    (200, 64, 16, 8, "softmax", True, 12, "bf16"),     # 4 finite: 4 masked places
+    (200, 64, 16, 8, "sigmoid", True, 12, "f32"),
+    (257, 64, 64, 8, "sigmoid", True, 20, "bf16"),     # masked never needed
+    (200, 64, 64, 6, "softmax", False, 60, "bf16"),    # ranking on scores
+    (150, 64, 300, 8, "softmax", True, 296, "bf16"),   # a wavefront per token
+]
+
+
+@pytest.mark.parametrize("case", MASK_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_route_masked_experts(case):
+    """A -inf logit bias masks an expert: its score and weight are 0 and it is
+    chosen only after every expert with a finite logit, lower index first,
+    as the oracle's descending stable sort of the scores does."""
+    T, d, E, k, score, norm, nmask, dt = case
+    inp = mw.make_small_layer_inputs(53 + T + E, T=T, d=d, E=E, F=8, dtype=dt, Fs=0, bias=True)
+    masked = np.random.default_rng(E + nmask).permutation(E)[:nmask]
+    lb = inp.logit_bias.copy()
+    lb[masked] = -np.inf
+    ref = mo.route(inp.as_f32("x"), inp.as_f32("w_router"), k, score, norm, lb, None)
+    g = lambda a: gh.to_gpu(a)  # noqa: E731
+    idx, w, cnt, _ = moe.route(g(inp.x), g(inp.w_router), k, score, norm, g(lb), None)
+    torch.cuda.synchronize()
+    idx, w, cnt = idx.cpu().numpy(), w.cpu().numpy(), cnt.cpu().numpy()
+    is_m = np.zeros(E, bool)
+    is_m[masked] = True
+    nfin = min(k, E - nmask)
+    # the finite experts: the oracle's choice (near ties aside)
+    fin_ref = ref.topk_idx[:, :nfin]
+    assert not is_m[fin_ref].any()
+    assert not is_m[idx[:, :nfin]].any()
+    same = (np.sort(idx[:, :nfin], 1) == np.sort(fin_ref, 1)).all(1)
+    assert same.mean() > 0.95, same.mean()
+    # the masked places: exactly the oracle's (lowest masked indices, ascending), weight 0
+    assert np.array_equal(idx[:, nfin:], ref.topk_idx[:, nfin:])
+    assert (w[:, nfin:] == 0.0).all()
+    ow = ref.topk_w[same][:, :nfin]
+    gw = w[same][:, :nfin]
+    o_order = np.argsort(ref.topk_idx[same][:, :nfin], 1)
+    g_order = np.argsort(idx[same][:, :nfin], 1)
+    assert np.abs(np.take_along_axis(ow, o_order, 1) -
+                  np.take_along_axis(gw, g_order, 1)).max() <= gh.TOL_ROUTE_W
+    assert (cnt == np.bincount(idx.reshape(-1), minlength=E)).all()
+
+
+def test_route_nan_token():
+    """A token whose logits are all NaN has no selectable expert: every place
+    gets index E (dropped by the permute); the other tokens are unaffected."""
+    T, d, E, k = 130, 64, 64, 6
+    inp = mw.make_small_layer_inputs(71, T=T, d=d, E=E, F=8, dtype="bf16", Fs=0)
+    x = inp.x.copy()
+    bad = np.array([0, 77, 129])
+    x[bad] = 0x7FC0                       # bf16 quiet NaN
+    idx, w, cnt, _ = moe.route(gh.to_gpu(x), gh.to_gpu(inp.w_router), k, "softmax", True)
+    torch.cuda.synchronize()
+    idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    assert (idx[bad] == E).all()
+    good = np.setdiff1d(np.arange(T), bad)
+    ref = mo.route(inp.as_f32("x")[good], inp.as_f32("w_router"), k, "softmax", True)
+    gh.check_routing(idx[good], w.cpu().numpy()[good], ref, k)
+    assert (cnt == np.bincount(idx[good].reshape(-1), minlength=E)).all()
+
+
 SELB_CASES = [
     # T, d, E, k, score, dtype, bias std
     (300, 64, 33, 5, "sigmoid", "f32", 0.1),
