@@ -65,6 +65,25 @@ def test_route_matches_brute_force(score, k, bias):
     np.testing.assert_allclose(r.topk_w, np.array(w_b), rtol=1e-12)
 
 
+@pytest.mark.parametrize("score", ["softmax", "sigmoid"])
+def test_masked_experts_against_brute_force(score):
+    """A -inf logit bias masks an expert: score 0, weight 0, chosen only after
+    every expert with a positive score, lower index first (k = 5 with three
+    finite experts of eight)."""
+    rng = np.random.default_rng(31)
+    T, d, E, k = 10, 8, 8, 5
+    x = rng.standard_normal((T, d))
+    w = rng.standard_normal((E, d)) / np.sqrt(d)
+    b = rng.standard_normal(E)
+    b[[0, 2, 3, 5, 7]] = -np.inf
+    r = mo.route(x, w, k, score, True, logit_bias=b)
+    idx_b, w_b = brute.route(x.tolist(), w.tolist(), k, score, True, b.tolist())
+    assert r.topk_idx.tolist() == idx_b
+    assert (r.topk_idx[:, 3:] == np.array([0, 2])).all()
+    assert (r.topk_w[:, 3:] == 0.0).all()
+    np.testing.assert_allclose(r.topk_w, np.array(w_b), rtol=1e-12)
+
+
 def test_k_equals_E_reduces_to_library_softmax_and_sigmoid():
     rng = np.random.default_rng(3)
     x = rng.standard_normal((20, 16))
